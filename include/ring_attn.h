@@ -1,0 +1,223 @@
+/*
+ * ring_attn.h -- C ABI of the MI355X (gfx950) ring-attention forward library.
+ *
+ * The library computes the per-device step of Ring Attention / Context
+ * Parallelism: exact blockwise softmax attention of a resident query chunk
+ * against a sequence of key/value blocks, merged with online softmax, with a
+ * causal mask taken from each block's GLOBAL sequence positions.
+ *
+ * Sources (page title, section):
+ *   [CP]  "Context Parallelism" (aiwiki.thehackersbrain.dev): "Ring attention",
+ *         "The causal imbalance", and the ring_attention code listing with its
+ *         flash_block(q, k, v, out, m, lse, source=...) call.
+ *   [SP]  "Sequence Parallelism in Large Language Models: How Megatron-SP,
+ *         DeepSpeed Ulysses, and RingAttention Distribute Long Contexts"
+ *         (llms.blog): "RingAttention and Blockwise Context Parallelism" --
+ *         the 4-GPU ring figure, "Algorithmic Mechanics" (online-softmax
+ *         equations for m_new, l_new, O_new), "Overlapping Compute and
+ *         Communication", "Causal Masking and Load Balancing".
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers are HIP device memory owned by the caller. The library
+ *     never allocates device memory; scratch space is passed in as
+ *     `workspace`.
+ *   - Tensors are dense, row-major and contiguous: q and out are
+ *     [B, Hq, rows, D]; k and v are [B, Hkv, rows, D]; lse is [B, Hq, rows].
+ *   - `stream` arguments are hipStream_t values passed as void*; NULL is the
+ *     default stream. Every call only enqueues work and returns; results are
+ *     visible after the caller synchronizes the stream.
+ *   - All arguments are checked on the host before anything is enqueued, so a
+ *     call that returns an error has enqueued nothing. A fault while a kernel
+ *     runs surfaces at the caller's next synchronization.
+ *   - lse is the natural-log log-sum-exp of the scaled, allowed scores, in
+ *     float32. The identity ("no key seen yet") state is out = 0, lse = -inf.
+ *   - Entry points are thread-safe with respect to each other; calls that
+ *     share output or workspace buffers must be ordered by the caller.
+ */
+#ifndef RING_ATTN_H
+#define RING_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RA_OK = 0,
+  RA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  RA_ERR_SHAPE = 2,       /* inconsistent sizes, divisibility, head map, pos   */
+  RA_ERR_DTYPE = 3,       /* unknown ra_dtype                                  */
+  RA_ERR_UNSUPPORTED = 4, /* valid but not implemented (e.g. D not 64 or 128) */
+  RA_ERR_ALIGN = 5,       /* pointer misaligned (16 B for tensors, 4 B lse)    */
+  RA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required          */
+  RA_ERR_ARG = 7,         /* other invalid value (scale not finite, flags)    */
+  RA_ERR_HIP = 8          /* a HIP runtime call failed; see ra_last_error()   */
+} ra_status;
+
+typedef enum { RA_BF16 = 0, RA_F32 = 1 } ra_dtype;
+
+/* Sequence layouts [SP "Algorithmic Mechanics" item 1; CP "The causal
+ * imbalance"]. CONTIGUOUS: rank r holds tokens [r*C, (r+1)*C), C = S/N.
+ * ZIGZAG: the sequence is cut into 2N chunks of c = S/(2N); rank r holds
+ * chunks r and 2N-1-r, the early chunk first in its memory. */
+typedef enum { RA_CONTIGUOUS = 0, RA_ZIGZAG = 1 } ra_layout;
+
+/* Global sequence positions of the rows of one block: row t (0 <= t < rows)
+ * sits at position start[t / seg_len] + (t % seg_len). nseg is 1 or 2 and
+ * nseg * seg_len must equal the block's row count. With nseg = 2,
+ * start[1] >= start[0] + seg_len (positions increase with t). This is the
+ * "source" of the pages' flash_block call generalised to any block: a
+ * contiguous rank is {1, C, {r*C}}, a zigzag rank is
+ * {2, c, {r*c, (2N-1-r)*c}}. A NULL ra_pos means {1, rows, {0}}. */
+typedef struct {
+  int32_t nseg;
+  int64_t seg_len;
+  int64_t start[2];
+} ra_pos;
+
+/* Human-readable name of a status code (static string). */
+const char* ra_status_str(ra_status s);
+
+/* Detail of the last error returned on the calling thread ("" if none). The
+ * string stays valid until the thread's next failing call. */
+const char* ra_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * ra_block_attn_fwd -- one block of ring attention (the pages' flash_block).
+ *
+ * [CP listing: flash_block(q, k, v, out, m, lse, source=(rank-step)%world);
+ *  SP "Algorithmic Mechanics", online-softmax update; SP "Causal Masking":
+ *  position i attends to positions j <= i.]
+ *
+ * For every batch b, query head h (KV head g = kv_head_of_q[h], or
+ * h / (Hq/Hkv) when the map is NULL) and query row i of the block, with
+ * allowed(i, j) = !causal || kpos(j) <= qpos(i):
+ *   s_ij    = scale * <q[b,h,i,:], k[b,g,j,:]>
+ *   lse_blk = ln sum_{allowed j} exp(s_ij)
+ *   out_blk = sum_{allowed j} exp(s_ij - lse_blk) * v[b,g,j,:]
+ * accumulate = 0: (out, lse) := (out_blk, lse_blk); rows with no allowed key
+ *   get out = 0, lse = -inf.
+ * accumulate = 1: (out, lse) := merge((out, lse), (out_blk, lse_blk)) with
+ *   lse' = ln(e^lse + e^lse_blk),
+ *   out' = out * e^(lse - lse') + out_blk * e^(lse_blk - lse');
+ *   rows with no allowed key are left untouched.
+ *
+ * q: [B,Hq,Cq,D]; k, v: [B,Hkv,Ck,D], all of `dtype`, 16-byte aligned.
+ * out: float32 [B,Hq,Cq,D] (16-byte aligned); lse: float32 [B,Hq,Cq].
+ * D must be 64 or 128. scale must be finite (pass 1/sqrt(D) for standard
+ * attention). workspace: device scratch of at least
+ * ra_block_attn_workspace_bytes(...) bytes, 256-byte aligned (may be NULL
+ * when that size is 0); it is clobbered. Cq = 0 or Ck = 0 are valid (a block
+ * with no keys is the identity for accumulate = 1).
+ * ---------------------------------------------------------------------- */
+size_t ra_block_attn_workspace_bytes(int32_t B, int32_t Hkv, int64_t Ck, int32_t D,
+                                     ra_dtype dtype);
+
+ra_status ra_block_attn_fwd(const void* q, const void* k, const void* v,
+                            float* out, float* lse,
+                            int32_t B, int32_t Hq, int32_t Hkv,
+                            int64_t Cq, int64_t Ck, int32_t D, ra_dtype dtype,
+                            const ra_pos* q_pos, const ra_pos* k_pos,
+                            const int32_t* kv_head_of_q, int32_t causal, float scale,
+                            int32_t accumulate, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
+ * ra_lse_merge -- fold one normalised partial into a running one, in place.
+ *
+ * [SP "Algorithmic Mechanics": m_new = max(m_prev, m_block), l_new, O_new.
+ *  With lse = m + ln l the three equations become the log-sum-exp form below;
+ *  the printed O_new is exact when O_block is the unnormalised block sum, and
+ *  this entry point takes the normalised partial out_b together with lse_b.]
+ *
+ * For each of `rows` rows (r = 0..rows-1):
+ *   lse'[r] = ln(e^lse[r] + e^lse_b[r])
+ *   out'[r] = out[r] * e^(lse[r]-lse'[r]) + out_b[r] * e^(lse_b[r]-lse'[r])
+ * A partial with lse = -inf contributes nothing; two empty partials stay
+ * (0, -inf). out, out_b: float32 [rows, D]; lse, lse_b: float32 [rows]. Any
+ * D >= 1; 16-byte aligned rows take the vector path.
+ * ---------------------------------------------------------------------- */
+ra_status ra_lse_merge(float* out, float* lse, const float* out_b, const float* lse_b,
+                       int64_t rows, int32_t D, void* stream);
+
+/* ------------------------------------------------------------------------
+ * ra_zigzag_permute -- sequence order <-> zigzag rank-major order.
+ *
+ * [CP "The causal imbalance": split into 2N chunks, rank i holds chunks i and
+ *  2N-1-i.]
+ *
+ * src and dst are [outer, S, row_bytes] byte arrays (row = one token's bytes,
+ * e.g. D*2 for a bf16 head row, 4 for an lse entry). With c = S/(2N), the
+ * rank-major index p = r*2c + t holds sequence position
+ *   chunk(p)*c + (t mod c),  chunk(p) = r if t < c else 2N-1-r.
+ * inverse = 0: dst[rank-major p] = src[sequence position of p] (gather).
+ * inverse = 1: dst[sequence position of p] = src[rank-major p] (scatter).
+ * The copy is bit-exact. S must be divisible by 2N; src and dst must not
+ * overlap. Any alignment is accepted; 16-byte aligned chunks are copied with
+ * 16-byte accesses.
+ * ---------------------------------------------------------------------- */
+ra_status ra_zigzag_permute(const void* src, void* dst, int64_t outer, int64_t S,
+                            int64_t row_bytes, int32_t N, int32_t inverse, void* stream);
+
+/* ------------------------------------------------------------------------
+ * ra_ring_sim_fwd -- the whole N-rank ring, simulated on one GPU.
+ *
+ * [CP listing ring_attention(q, k, v, group) and "Ring attention"; SP figure
+ *  "Ring Topology (4 GPUs)" and "Algorithmic Mechanics" item 2: at step k
+ *  device i holds the KV block of source (i - k) mod N; SP "Overlapping
+ *  Compute and Communication": the next block moves while the current one is
+ *  computed.]
+ *
+ * q: [B,Hq,S,D], k, v: [B,Hkv,S,D] of `dtype`; out: [B,Hq,S,D] of `dtype`;
+ * lse: float32 [B,Hq,S]. The sequence axis is in RANK-MAJOR order: rank r's
+ * C = S/N rows are rows [r*C, (r+1)*C). For RA_CONTIGUOUS that is sequence
+ * order; for RA_ZIGZAG apply ra_zigzag_permute(inverse=0) to q, k, v before
+ * and ra_zigzag_permute(inverse=1) to out and lse after.
+ *
+ * For every virtual rank r = 0..N-1 and step k = 0..N-1 the driver attends
+ * rank r's queries to the KV block of rank (r - k) mod N, masked by global
+ * positions, and merges it into an fp32 running state; the last step writes
+ * out (rounded to `dtype`, round-to-nearest-even) and lse. While step k
+ * runs on `compute_stream`, the KV block for step k+1 is copied into the
+ * other half of a two-slot buffer on `copy_stream`, ordered by events (the
+ * copy waits until the slot's previous reader has finished; the compute waits
+ * until the copy has landed). A NULL copy_stream runs the copies on
+ * compute_stream. The result equals full attention over the sequence.
+ *
+ * S must be divisible by N (by 2N for RA_ZIGZAG); D must be 64 or 128;
+ * workspace: at least ra_ring_sim_workspace_bytes(...) bytes, 256-byte
+ * aligned, clobbered.
+ * ---------------------------------------------------------------------- */
+size_t ra_ring_sim_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D,
+                                   ra_dtype dtype, int32_t N);
+
+ra_status ra_ring_sim_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                          int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D,
+                          ra_dtype dtype, int32_t N, ra_layout layout, int32_t causal,
+                          float scale, const int32_t* kv_head_of_q,
+                          void* workspace, size_t workspace_bytes,
+                          void* compute_stream, void* copy_stream);
+
+/* ------------------------------------------------------------------------
+ * Kernel timing for measurement (not part of the computation).
+ *
+ * While enabled, every attention-kernel launch made by ra_block_attn_fwd and
+ * ra_ring_sim_fwd is bracketed by a pair of HIP events recorded on the
+ * stream it is launched on, and the allowed (query, key) pairs it processes
+ * are counted on the host. ra_kernel_timing_read waits for the recorded
+ * events, returns the summed kernel time in milliseconds, the number of
+ * launches and the useful flops (4*D per allowed pair), and clears the
+ * record. Up to 65536 launches are recorded between reads; later ones are
+ * not timed (launches still counts them; total_ms then covers only the
+ * first 65536). Enabling creates the events once per process.
+ * ---------------------------------------------------------------------- */
+ra_status ra_kernel_timing_enable(int32_t enable);
+ra_status ra_kernel_timing_read(double* total_ms, int64_t* launches, double* useful_flops);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RING_ATTN_H */

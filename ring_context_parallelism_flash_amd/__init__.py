@@ -1,0 +1,302 @@
+"""Python binding of the MI355X ring-attention library (``libringattn.so``).
+
+The functions below carry the C ABI's names and only marshal arguments:
+torch tensors provide device memory and ``torch.cuda`` streams provide the
+HIP stream handles; every step of the computation runs in the library's HIP
+kernels. There is no fallback: if the library is not built or cannot be
+loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "RAError", "lib", "library_path", "RA_BF16", "RA_F32", "RA_CONTIGUOUS", "RA_ZIGZAG",
+    "ra_pos", "ra_status_str", "ra_last_error", "ra_block_attn_workspace_bytes",
+    "ra_block_attn_fwd", "ra_lse_merge", "ra_zigzag_permute", "ra_ring_sim_workspace_bytes",
+    "ra_ring_sim_fwd", "ra_kernel_timing_enable", "ra_kernel_timing_read", "zigzag_pos",
+    "contiguous_pos", "ring_attention_sim", "EXPORTS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libringattn.so")
+
+RA_BF16, RA_F32 = 0, 1
+RA_CONTIGUOUS, RA_ZIGZAG = 0, 1
+_DTYPES = {torch.bfloat16: RA_BF16, torch.float32: RA_F32}
+_LAYOUTS = {"contiguous": RA_CONTIGUOUS, "zigzag": RA_ZIGZAG}
+
+# Every symbol include/ring_attn.h declares.
+EXPORTS = (
+    "ra_status_str", "ra_last_error", "ra_block_attn_workspace_bytes", "ra_block_attn_fwd",
+    "ra_lse_merge", "ra_zigzag_permute", "ra_ring_sim_workspace_bytes", "ra_ring_sim_fwd",
+    "ra_kernel_timing_enable", "ra_kernel_timing_read",
+)
+
+
+class RAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class ra_pos(ctypes.Structure):
+    _fields_ = [("nseg", ctypes.c_int32), ("seg_len", ctypes.c_int64),
+                ("start", ctypes.c_int64 * 2)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load (once) and return the library; raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RAError(-1, f"HIP library not built: {library_path} is missing "
+                          "(run __graft_entry__.build())")
+    L = ctypes.CDLL(library_path)
+    c_void_p, c_int32, c_int64, c_size_t, c_float = (ctypes.c_void_p, ctypes.c_int32,
+                                                      ctypes.c_int64, ctypes.c_size_t,
+                                                      ctypes.c_float)
+    P = ctypes.POINTER
+    sig = {
+        "ra_status_str": (ctypes.c_char_p, [c_int32]),
+        "ra_last_error": (ctypes.c_char_p, []),
+        "ra_block_attn_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int64, c_int32, c_int32]),
+        "ra_block_attn_fwd": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_int32, c_int32, c_int32, c_int64, c_int64, c_int32,
+                                        c_int32, P(ra_pos), P(ra_pos), P(c_int32), c_int32,
+                                        c_float, c_int32, c_void_p, c_size_t, c_void_p]),
+        "ra_lse_merge": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32,
+                                   c_void_p]),
+        "ra_zigzag_permute": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int32,
+                                        c_int32, c_void_p]),
+        "ra_ring_sim_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int64, c_int32,
+                                                   c_int32, c_int32]),
+        "ra_ring_sim_fwd": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_int32, c_int32, c_int32, c_int64, c_int32, c_int32,
+                                      c_int32, c_int32, c_int32, c_float, P(c_int32),
+                                      c_void_p, c_size_t, c_void_p, c_void_p]),
+        "ra_kernel_timing_enable": (c_int32, [c_int32]),
+        "ra_kernel_timing_read": (c_int32, [P(ctypes.c_double), P(c_int64),
+                                            P(ctypes.c_double)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def ra_status_str(status: int) -> str:
+    return lib().ra_status_str(status).decode()
+
+
+def ra_last_error() -> str:
+    return lib().ra_last_error().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise RAError(status, f"{ra_status_str(status)}: {ra_last_error()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(s):
+    if s is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(s, torch.cuda.Stream):
+        return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(int(s))
+
+
+def _pos(p):
+    """None, an ra_pos, or a tuple (nseg, seg_len, start0[, start1])."""
+    if p is None or isinstance(p, ra_pos):
+        return p
+    nseg, seg_len, *starts = p
+    starts = list(starts) + [0] * (2 - len(starts))
+    return ra_pos(nseg, seg_len, (ctypes.c_int64 * 2)(*starts))
+
+
+def _kvmap(m, Hq):
+    if m is None:
+        return None
+    m = [int(x) for x in m]
+    if len(m) != Hq:
+        raise ValueError("kv_head_of_q must have Hq entries")
+    return (ctypes.c_int32 * Hq)(*m)
+
+
+def _dtype(t):
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def contiguous_pos(S: int, N: int, rank: int):
+    C = S // N
+    return (1, C, rank * C)
+
+
+def zigzag_pos(S: int, N: int, rank: int):
+    c = S // (2 * N)
+    return (2, c, rank * c, (2 * N - 1 - rank) * c)
+
+
+# ------------------------------------------------------------------ entry points
+def ra_block_attn_workspace_bytes(B, Hkv, Ck, D, dtype) -> int:
+    dt = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib().ra_block_attn_workspace_bytes(B, Hkv, Ck, D, dt))
+
+
+def ra_block_attn_fwd(q, k, v, out, lse, *, q_pos=None, k_pos=None, kv_head_of_q=None,
+                      causal=True, scale=None, accumulate=False, workspace=None, stream=None):
+    """One block (the pages' flash_block): q [B,Hq,Cq,D], k/v [B,Hkv,Ck,D];
+    out fp32 [B,Hq,Cq,D] and lse fp32 [B,Hq,Cq] are the running state."""
+    B, Hq, Cq, D = q.shape
+    Hkv, Ck = k.shape[1], k.shape[2]
+    dt = _dtype(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = ra_block_attn_workspace_bytes(B, Hkv, Ck, D, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    qp, kp = _pos(q_pos), _pos(k_pos)
+    _check(lib().ra_block_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Cq, Ck, D, dt,
+        ctypes.byref(qp) if qp is not None else None,
+        ctypes.byref(kp) if kp is not None else None,
+        _kvmap(kv_head_of_q, Hq), int(bool(causal)), float(scale), int(bool(accumulate)),
+        _ptr(workspace), wbytes, _stream(stream)))
+    return out, lse
+
+
+def ra_lse_merge(out, lse, out_b, lse_b, stream=None):
+    """In place: (out, lse) <- merge((out, lse), (out_b, lse_b)); out [..., D]."""
+    D = out.shape[-1]
+    rows = out.numel() // D
+    _check(lib().ra_lse_merge(_ptr(out), _ptr(lse), _ptr(out_b), _ptr(lse_b), rows, D,
+                              _stream(stream)))
+    return out, lse
+
+
+def ra_zigzag_permute(src, dst, N, inverse=False, seq_dim=-2, stream=None):
+    """Zigzag permute along ``seq_dim`` (-2 for [..., S, D], -1 for lse [..., S])."""
+    seq_dim = seq_dim % src.dim()
+    S = src.shape[seq_dim]
+    outer = math.prod(src.shape[:seq_dim])
+    row_bytes = math.prod(src.shape[seq_dim + 1:]) * src.element_size()
+    _check(lib().ra_zigzag_permute(_ptr(src), _ptr(dst), outer, S, row_bytes, N,
+                                   int(bool(inverse)), _stream(stream)))
+    return dst
+
+
+def ra_ring_sim_workspace_bytes(B, Hq, Hkv, S, D, dtype, N) -> int:
+    dt = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib().ra_ring_sim_workspace_bytes(B, Hq, Hkv, S, D, dt, N))
+
+
+def ra_ring_sim_fwd(q, k, v, out, lse, *, N, layout="zigzag", causal=True, scale=None,
+                    kv_head_of_q=None, workspace=None, compute_stream=None, copy_stream=None):
+    """The simulated N-rank ring on rank-major inputs (see include/ring_attn.h)."""
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    dt = _dtype(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        workspace = torch.empty(ra_ring_sim_workspace_bytes(B, Hq, Hkv, S, D, dt, N),
+                                dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    cs = _stream(compute_stream)
+    xs = None if copy_stream is None else _stream(copy_stream)
+    _check(lib().ra_ring_sim_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, S, D, dt, N,
+        _LAYOUTS[layout] if isinstance(layout, str) else int(layout), int(bool(causal)),
+        float(scale), _kvmap(kv_head_of_q, Hq), _ptr(workspace), wbytes, cs, xs))
+    return out, lse
+
+
+def ra_kernel_timing_enable(enable=True):
+    _check(lib().ra_kernel_timing_enable(int(bool(enable))))
+
+
+def ra_kernel_timing_read():
+    """Returns (total_ms, launches, useful_flops) and clears the record."""
+    ms, n, fl = ctypes.c_double(), ctypes.c_int64(), ctypes.c_double()
+    _check(lib().ra_kernel_timing_read(ctypes.byref(ms), ctypes.byref(n), ctypes.byref(fl)))
+    return ms.value, n.value, fl.value
+
+
+# ------------------------------------------------------------------ convenience
+class RingRunner:
+    """Owns the buffers of repeated ring calls on one shape (allocated once)."""
+
+    def __init__(self, B, Hq, Hkv, S, D, dtype, N, layout="zigzag", causal=True, scale=None,
+                 kv_head_of_q=None, device="cuda", copy_stream=True):
+        self.shape = (B, Hq, Hkv, S, D)
+        self.N, self.layout, self.causal = N, layout, causal
+        self.scale = 1.0 / math.sqrt(D) if scale is None else scale
+        self.kv_head_of_q = kv_head_of_q
+        self.dtype = dtype
+        dev = torch.device(device)
+        self.workspace = torch.empty(ra_ring_sim_workspace_bytes(B, Hq, Hkv, S, D, dtype, N),
+                                     dtype=torch.uint8, device=dev)
+        self.out_rm = torch.empty((B, Hq, S, D), dtype=dtype, device=dev)
+        self.lse_rm = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+        self.copy_stream = torch.cuda.Stream(device=dev) if copy_stream else None
+        if layout == "zigzag":
+            self.q_rm = torch.empty((B, Hq, S, D), dtype=dtype, device=dev)
+            self.k_rm = torch.empty((B, Hkv, S, D), dtype=dtype, device=dev)
+            self.v_rm = torch.empty((B, Hkv, S, D), dtype=dtype, device=dev)
+
+    def permute_inputs(self, q, k, v):
+        if self.layout != "zigzag":
+            return q, k, v
+        ra_zigzag_permute(q, self.q_rm, self.N)
+        ra_zigzag_permute(k, self.k_rm, self.N)
+        ra_zigzag_permute(v, self.v_rm, self.N)
+        return self.q_rm, self.k_rm, self.v_rm
+
+    def ring(self, q_rm, k_rm, v_rm):
+        return ra_ring_sim_fwd(q_rm, k_rm, v_rm, self.out_rm, self.lse_rm, N=self.N,
+                               layout=self.layout, causal=self.causal, scale=self.scale,
+                               kv_head_of_q=self.kv_head_of_q, workspace=self.workspace,
+                               copy_stream=self.copy_stream)
+
+    def unpermute_outputs(self, out, lse):
+        if self.layout != "zigzag":
+            out.copy_(self.out_rm)
+            lse.copy_(self.lse_rm)
+            return out, lse
+        ra_zigzag_permute(self.out_rm, out, self.N, inverse=True)
+        ra_zigzag_permute(self.lse_rm, lse, self.N, inverse=True, seq_dim=-1)
+        return out, lse
+
+    def __call__(self, q, k, v, out, lse):
+        """Whole step in sequence order: permute, ring, inverse permute."""
+        self.ring(*self.permute_inputs(q, k, v))
+        return self.unpermute_outputs(out, lse)
+
+
+def ring_attention_sim(q, k, v, *, N, layout="zigzag", causal=True, scale=None,
+                       kv_head_of_q=None):
+    """Sequence-order inputs in, sequence-order (out, lse) out."""
+    B, Hq, S, D = q.shape
+    r = RingRunner(B, Hq, k.shape[1], S, D, q.dtype, N, layout, causal, scale, kv_head_of_q,
+                   device=q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    return r(q, k, v, out, lse)

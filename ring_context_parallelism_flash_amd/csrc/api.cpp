@@ -1,0 +1,586 @@
+// Host side of the ring-attention library: the C ABI declared in
+// include/ring_attn.h. Every entry point validates its arguments completely
+// before it enqueues anything, then launches the gfx950 kernels.
+//
+// The virtual-ring driver follows "Context Parallelism" (aiwiki), the
+// ring_attention listing (start the next hop, compute on the held block, wait,
+// swap) and "Sequence Parallelism in Large Language Models ..." (llms.blog),
+// "Algorithmic Mechanics" item 2 and the 4-GPU ring figure (at step k device
+// i holds the block of source (i - k) mod N), with the point-to-point
+// transfer replaced by an asynchronous device copy into a two-slot buffer.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
+#include "ra_internal.h"
+
+using namespace ra;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ra_status fail(ra_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ra_status hip_fail(hipError_t e, const char* what) {
+  return fail(RA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define RA_HIP(call)                                       \
+  do {                                                     \
+    hipError_t e_ = (call);                                \
+    if (e_ != hipSuccess) return hip_fail(e_, #call);      \
+  } while (0)
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline size_t esize(ra_dtype dt) { return dt == RA_BF16 ? 2 : 4; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Block positions as a PosDesc, with the validation rules of ra_pos.
+ra_status make_pos(const ra_pos* p, int64_t rows, const char* name, PosDesc& out) {
+  if (p == nullptr) {
+    out = PosDesc{1, (int32_t)rows, 0, 0};
+    return RA_OK;
+  }
+  if (p->nseg != 1 && p->nseg != 2)
+    return fail(RA_ERR_SHAPE, "%s.nseg must be 1 or 2 (got %d)", name, p->nseg);
+  if (p->seg_len < 1 || p->nseg * p->seg_len != rows)
+    return fail(RA_ERR_SHAPE, "%s: nseg*seg_len (%d*%lld) must equal the row count %lld", name,
+                p->nseg, (long long)p->seg_len, (long long)rows);
+  if (p->start[0] < 0) return fail(RA_ERR_SHAPE, "%s.start[0] must be >= 0", name);
+  if (p->nseg == 2 && p->start[1] < p->start[0] + p->seg_len)
+    return fail(RA_ERR_SHAPE, "%s: start[1] must be >= start[0] + seg_len", name);
+  const int64_t last = p->start[p->nseg - 1] + p->seg_len - 1;
+  if (last > INT32_MAX) return fail(RA_ERR_UNSUPPORTED, "%s: positions beyond 2^31-1", name);
+  out = PosDesc{p->nseg, (int32_t)p->seg_len, (int32_t)p->start[0],
+                (int32_t)(p->nseg == 2 ? p->start[1] : 0)};
+  return RA_OK;
+}
+
+int64_t pos_at(const PosDesc& p, int64_t t) {
+  return (p.nseg == 2 && t >= p.seg) ? p.start1 + (t - p.seg) : p.start0 + t;
+}
+
+// Allowed (query, key) pairs between two position descriptors (per head).
+int64_t pairs_segment(int64_t a, int64_t La, int64_t b, int64_t Lb) {
+  // sum over i in [0, La) of clamp(a + i - b + 1, 0, Lb)
+  const int64_t x0 = a - b + 1;
+  int64_t total = 0;
+  // i where x0 + i >= Lb contributes Lb
+  int64_t i_full = std::max<int64_t>(0, Lb - x0);  // first i with x0+i >= Lb
+  int64_t i_pos = std::max<int64_t>(0, 1 - x0);    // first i with x0+i >= 1
+  i_full = std::min(i_full, La);
+  i_pos = std::min(i_pos, La);
+  if (i_full > i_pos) {
+    const int64_t n = i_full - i_pos;
+    const int64_t first = x0 + i_pos;
+    total += n * first + n * (n - 1) / 2;
+  }
+  total += (La - std::max(i_full, i_pos)) * Lb;
+  return total;
+}
+
+int64_t pairs_between(const PosDesc& q, int64_t Cq, const PosDesc& k, int64_t Ck, bool causal) {
+  if (!causal) return Cq * Ck;
+  int64_t total = 0;
+  for (int sq = 0; sq < q.nseg; ++sq)
+    for (int sk = 0; sk < k.nseg; ++sk) {
+      const int64_t a = sq == 0 ? q.start0 : q.start1, La = q.nseg == 1 ? Cq : q.seg;
+      const int64_t b = sk == 0 ? k.start0 : k.start1, Lb = k.nseg == 1 ? Ck : k.seg;
+      total += pairs_segment(a, La, b, Lb);
+    }
+  return total;
+}
+
+// ---------------------------------------------------------------- timing
+struct Timing {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<hipEvent_t> ev;  // pairs: start, stop
+  size_t used = 0;             // pairs recorded since the last read
+  int64_t launches = 0;
+  double flops = 0.0;
+};
+Timing g_timing;
+constexpr size_t kMaxTimed = 65536;
+
+// Launch an attention kernel, bracketed by timing events when enabled.
+ra_status timed_launch(const AttnArgs& a, ra_dtype dt, int D, hipStream_t s, double flops) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (g_timing.enabled) {
+      g_timing.launches++;
+      g_timing.flops += flops;
+      if (g_timing.used < kMaxTimed) {
+        if (2 * g_timing.used + 2 > g_timing.ev.size()) {
+          for (int i = 0; i < 256; ++i) {
+            hipEvent_t e;
+            RA_HIP(hipEventCreate(&e));
+            g_timing.ev.push_back(e);
+          }
+        }
+        e0 = g_timing.ev[2 * g_timing.used];
+        e1 = g_timing.ev[2 * g_timing.used + 1];
+        g_timing.used++;
+      }
+    }
+  }
+  if (e0) RA_HIP(hipEventRecord(e0, s));
+  hipError_t e = launch_attn(a, dt, D, s);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  if (e1) RA_HIP(hipEventRecord(e1, s));
+  return RA_OK;
+}
+
+// ---------------------------------------------------------------- ring events
+struct RingEvents {
+  hipEvent_t ready[2], freed[2], vt_done;
+};
+std::mutex g_ev_mu;
+RingEvents* g_ring_ev[64] = {nullptr};
+
+ra_status ring_events(RingEvents*& out) {
+  int dev = 0;
+  RA_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(RA_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lk(g_ev_mu);
+  if (!g_ring_ev[dev]) {
+    RingEvents* r = new RingEvents;
+    for (int i = 0; i < 2; ++i) {
+      RA_HIP(hipEventCreateWithFlags(&r->ready[i], hipEventDisableTiming));
+      RA_HIP(hipEventCreateWithFlags(&r->freed[i], hipEventDisableTiming));
+    }
+    RA_HIP(hipEventCreateWithFlags(&r->vt_done, hipEventDisableTiming));
+    g_ring_ev[dev] = r;
+  }
+  out = g_ring_ev[dev];
+  return RA_OK;
+}
+
+// ---------------------------------------------------------------- shared checks
+ra_status check_common(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, ra_dtype dt,
+                       const int32_t* kv_map, float scale, std::vector<uint8_t>& kv_of,
+                       std::vector<uint8_t>& order) {
+  if (dt != RA_BF16 && dt != RA_F32) return fail(RA_ERR_DTYPE, "unknown dtype %d", (int)dt);
+  if (B < 1 || Hq < 1 || Hkv < 1)
+    return fail(RA_ERR_SHAPE, "B, Hq, Hkv must be >= 1 (got %d, %d, %d)", B, Hq, Hkv);
+  if (D != 64 && D != 128) return fail(RA_ERR_UNSUPPORTED, "head dim D=%d (supported: 64, 128)", D);
+  if (Hq > kMaxHeads || Hkv > kMaxHeads)
+    return fail(RA_ERR_UNSUPPORTED, "more than %d heads", kMaxHeads);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(RA_ERR_ARG, "scale must be finite and > 0 (got %g)", (double)scale);
+  kv_of.assign(Hq, 0);
+  if (kv_map == nullptr) {
+    if (Hq % Hkv) return fail(RA_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    for (int h = 0; h < Hq; ++h) kv_of[h] = (uint8_t)(h / (Hq / Hkv));
+  } else {
+    for (int h = 0; h < Hq; ++h) {
+      if (kv_map[h] < 0 || kv_map[h] >= Hkv)
+        return fail(RA_ERR_SHAPE, "kv_head_of_q[%d]=%d outside [0, %d)", h, kv_map[h], Hkv);
+      kv_of[h] = (uint8_t)kv_map[h];
+    }
+  }
+  // query heads ordered by KV head (stable), so heads sharing K/V are adjacent
+  order.resize(Hq);
+  for (int h = 0; h < Hq; ++h) order[h] = (uint8_t)h;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](uint8_t x, uint8_t y) { return kv_of[x] < kv_of[y]; });
+  return RA_OK;
+}
+
+void fill_work(AttnArgs& a, int32_t B, int32_t Hq, int64_t Cq, const std::vector<uint8_t>& kv_of,
+               const std::vector<uint8_t>& order) {
+  memset(a.head_order, 0, sizeof a.head_order);
+  memset(a.kv_of, 0, sizeof a.kv_of);
+  for (int h = 0; h < Hq; ++h) {
+    a.head_order[h] = order[h];
+    a.kv_of[h] = kv_of[h];
+  }
+  a.B = B;
+  a.Hq = Hq;
+  const int32_t n_qt_all = (int32_t)((Cq + kQTile - 1) / kQTile);
+  // With accumulate = 1, leading query tiles that see no key are skipped:
+  // positions increase with the row index, so these are the rows whose
+  // position is below the block's first key position. Not on the final step
+  // of the ring, where every row still has to be written out.
+  int32_t lo = 0;
+  if (a.causal && a.accumulate && a.fin_out == nullptr) {
+    int64_t row = Cq;
+    if (a.Ck > 0) {
+      const int64_t kmin = a.kp.start0;
+      const PosDesc& p = a.qp;
+      const int64_t seg0 = p.nseg == 2 ? p.seg : Cq;
+      if (kmin <= (int64_t)p.start0 + seg0 - 1)
+        row = std::max<int64_t>(0, kmin - p.start0);
+      else if (p.nseg == 2 && kmin <= (int64_t)p.start1 + p.seg - 1)
+        row = p.seg + std::max<int64_t>(0, kmin - p.start1);
+    }
+    lo = (int32_t)(row / kQTile);
+  }
+  a.qt_lo = lo;
+  a.n_qt = n_qt_all - lo;
+  const int64_t items = (int64_t)B * Hq * a.n_qt;
+  a.n_items = (int32_t)items;
+  a.per_xcd = (int32_t)((items + kXcds - 1) / kXcds);
+}
+
+}  // namespace
+
+// ============================================================================
+extern "C" {
+
+const char* ra_status_str(ra_status s) {
+  switch (s) {
+    case RA_OK: return "RA_OK";
+    case RA_ERR_NULL: return "RA_ERR_NULL";
+    case RA_ERR_SHAPE: return "RA_ERR_SHAPE";
+    case RA_ERR_DTYPE: return "RA_ERR_DTYPE";
+    case RA_ERR_UNSUPPORTED: return "RA_ERR_UNSUPPORTED";
+    case RA_ERR_ALIGN: return "RA_ERR_ALIGN";
+    case RA_ERR_WORKSPACE: return "RA_ERR_WORKSPACE";
+    case RA_ERR_ARG: return "RA_ERR_ARG";
+    case RA_ERR_HIP: return "RA_ERR_HIP";
+  }
+  return "RA_ERR_UNKNOWN";
+}
+
+const char* ra_last_error(void) { return g_err; }
+
+size_t ra_block_attn_workspace_bytes(int32_t B, int32_t Hkv, int64_t Ck, int32_t D,
+                                     ra_dtype dtype) {
+  if (dtype != RA_BF16 || B < 1 || Hkv < 1 || Ck < 1 || D < 1) return 0;
+  return (size_t)B * Hkv * D * round_up(Ck, kVtAlign) * 2;
+}
+
+ra_status ra_block_attn_fwd(const void* q, const void* k, const void* v, float* out, float* lse,
+                            int32_t B, int32_t Hq, int32_t Hkv, int64_t Cq, int64_t Ck, int32_t D,
+                            ra_dtype dtype, const ra_pos* q_pos, const ra_pos* k_pos,
+                            const int32_t* kv_head_of_q, int32_t causal, float scale,
+                            int32_t accumulate, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  g_err[0] = 0;
+  std::vector<uint8_t> kv_of, order;
+  ra_status st = check_common(B, Hq, Hkv, D, dtype, kv_head_of_q, scale, kv_of, order);
+  if (st != RA_OK) return st;
+  if (Cq < 0 || Ck < 0) return fail(RA_ERR_SHAPE, "negative row count");
+  if (Cq > INT32_MAX || Ck > INT32_MAX) return fail(RA_ERR_UNSUPPORTED, "block rows beyond 2^31-1");
+  if ((causal != 0 && causal != 1) || (accumulate != 0 && accumulate != 1))
+    return fail(RA_ERR_ARG, "causal and accumulate must be 0 or 1");
+  if (Cq == 0) return RA_OK;
+  if (!q || !out || !lse) return fail(RA_ERR_NULL, "q, out and lse must not be NULL");
+  if (Ck > 0 && (!k || !v)) return fail(RA_ERR_NULL, "k and v must not be NULL");
+  if (!aligned(q, 16) || !aligned(out, 16) || (Ck > 0 && (!aligned(k, 16) || !aligned(v, 16))))
+    return fail(RA_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(RA_ERR_ALIGN, "lse must be 4-byte aligned");
+  PosDesc qp, kp;
+  if ((st = make_pos(q_pos, Cq, "q_pos", qp)) != RA_OK) return st;
+  if (Ck > 0) {
+    if ((st = make_pos(k_pos, Ck, "k_pos", kp)) != RA_OK) return st;
+  } else {
+    kp = PosDesc{1, 0, 0, 0};
+  }
+  const size_t need = ra_block_attn_workspace_bytes(B, Hkv, Ck, D, dtype);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need,
+                  workspace_bytes);
+    if (!aligned(workspace, 256)) return fail(RA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = q;
+  a.k = k;
+  a.run_out = out;
+  a.run_lse = lse;
+  a.q_bs = (int64_t)Hq * Cq * D;
+  a.q_hs = Cq * D;
+  a.k_bs = (int64_t)Hkv * Ck * D;
+  a.k_hs = Ck * D;
+  a.ro_bs = a.q_bs;
+  a.ro_hs = a.q_hs;
+  a.rl_bs = (int64_t)Hq * Cq;
+  a.rl_hs = Cq;
+  a.Cq = (int32_t)Cq;
+  a.Ck = (int32_t)Ck;
+  a.qp = qp;
+  a.kp = kp;
+  a.causal = causal;
+  a.accumulate = accumulate;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  if (dtype == RA_BF16 && Ck > 0) {
+    const int64_t Cpad = round_up(Ck, kVtAlign);
+    hipError_t e = launch_vt_transpose(v, workspace, (int64_t)B * Hkv, 1, Ck, Cpad, D, Ck * D, s);
+    if (e != hipSuccess) return hip_fail(e, "V transpose launch");
+    a.v = workspace;
+    a.v_bs = (int64_t)Hkv * D * Cpad;
+    a.v_hs = (int64_t)D * Cpad;
+    a.v_ld = Cpad;
+  } else {
+    a.v = v;
+    a.v_bs = a.k_bs;
+    a.v_hs = a.k_hs;
+    a.v_ld = D;
+  }
+  fill_work(a, B, Hq, Cq, kv_of, order);
+  const double flops = 4.0 * D * B * Hq * (double)(Ck > 0 ? pairs_between(qp, Cq, kp, Ck, causal) : 0);
+  return timed_launch(a, dtype, D, s, flops);
+}
+
+ra_status ra_lse_merge(float* out, float* lse, const float* out_b, const float* lse_b,
+                       int64_t rows, int32_t D, void* stream) {
+  g_err[0] = 0;
+  if (rows < 0 || D < 1) return fail(RA_ERR_SHAPE, "rows must be >= 0 and D >= 1");
+  if (rows == 0) return RA_OK;
+  if (!out || !lse || !out_b || !lse_b) return fail(RA_ERR_NULL, "NULL pointer");
+  if (!aligned(out, 4) || !aligned(lse, 4) || !aligned(out_b, 4) || !aligned(lse_b, 4))
+    return fail(RA_ERR_ALIGN, "float arrays must be 4-byte aligned");
+  hipError_t e = launch_lse_merge(out, lse, out_b, lse_b, rows, D, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "lse merge launch");
+  return RA_OK;
+}
+
+ra_status ra_zigzag_permute(const void* src, void* dst, int64_t outer, int64_t S, int64_t row_bytes,
+                            int32_t N, int32_t inverse, void* stream) {
+  g_err[0] = 0;
+  if (N < 1) return fail(RA_ERR_SHAPE, "N must be >= 1");
+  if (outer < 0 || S < 0 || row_bytes < 1) return fail(RA_ERR_SHAPE, "bad sizes");
+  if (S % (2 * (int64_t)N)) return fail(RA_ERR_SHAPE, "S=%lld not divisible by 2N=%d", (long long)S, 2 * N);
+  if (inverse != 0 && inverse != 1) return fail(RA_ERR_ARG, "inverse must be 0 or 1");
+  if (outer == 0 || S == 0) return RA_OK;
+  if (!src || !dst) return fail(RA_ERR_NULL, "NULL pointer");
+  const uintptr_t bytes = (uintptr_t)outer * S * row_bytes;
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(RA_ERR_ARG, "src and dst overlap");
+  hipError_t e = launch_zigzag_permute(src, dst, outer, S, row_bytes, N, inverse,
+                                       reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "permute launch");
+  return RA_OK;
+}
+
+// Workspace of the ring: [V^T home blocks (bf16)] [2 KV slots] [fp32 running out]
+namespace {
+struct RingLayout {
+  int64_t C, Cpad;
+  size_t vt_home, slot_k, slot_v, slot, acc, total;
+};
+RingLayout ring_layout(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D, ra_dtype dt,
+                       int32_t N) {
+  RingLayout L{};
+  L.C = S / N;
+  L.Cpad = round_up(L.C, kVtAlign);
+  const size_t es = esize(dt);
+  auto up = [](size_t x) { return (size_t)round_up((int64_t)x, 256); };
+  L.vt_home = dt == RA_BF16 ? up((size_t)B * Hkv * N * D * L.Cpad * es) : 0;
+  L.slot_k = up((size_t)B * Hkv * L.C * D * es);
+  L.slot_v = dt == RA_BF16 ? up((size_t)B * Hkv * D * L.Cpad * es) : L.slot_k;
+  L.slot = L.slot_k + L.slot_v;
+  L.acc = up((size_t)B * Hq * L.C * D * 4);
+  L.total = L.vt_home + 2 * L.slot + L.acc;
+  return L;
+}
+}  // namespace
+
+size_t ra_ring_sim_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D,
+                                   ra_dtype dtype, int32_t N) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || N < 1 || D < 1 || S % N) return 0;
+  if (dtype != RA_BF16 && dtype != RA_F32) return 0;
+  return ring_layout(B, Hq, Hkv, S, D, dtype, N).total;
+}
+
+ra_status ra_ring_sim_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                          int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D,
+                          ra_dtype dtype, int32_t N, ra_layout layout, int32_t causal,
+                          float scale, const int32_t* kv_head_of_q, void* workspace,
+                          size_t workspace_bytes, void* compute_stream, void* copy_stream) {
+  g_err[0] = 0;
+  std::vector<uint8_t> kv_of, order;
+  ra_status st = check_common(B, Hq, Hkv, D, dtype, kv_head_of_q, scale, kv_of, order);
+  if (st != RA_OK) return st;
+  if (layout != RA_CONTIGUOUS && layout != RA_ZIGZAG) return fail(RA_ERR_ARG, "unknown layout");
+  if (causal != 0 && causal != 1) return fail(RA_ERR_ARG, "causal must be 0 or 1");
+  if (N < 1) return fail(RA_ERR_SHAPE, "N must be >= 1");
+  if (S < 0) return fail(RA_ERR_SHAPE, "S must be >= 0");
+  const int64_t div = layout == RA_ZIGZAG ? 2 * (int64_t)N : N;
+  if (S % div) return fail(RA_ERR_SHAPE, "S=%lld not divisible by %lld", (long long)S, (long long)div);
+  if (S == 0) return RA_OK;
+  if (S > INT32_MAX) return fail(RA_ERR_UNSUPPORTED, "S beyond 2^31-1");
+  if (!q || !k || !v || !out || !lse) return fail(RA_ERR_NULL, "NULL tensor pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(RA_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(RA_ERR_ALIGN, "lse must be 4-byte aligned");
+  const RingLayout L = ring_layout(B, Hq, Hkv, S, D, dtype, N);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", L.total, workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(RA_ERR_ALIGN, "workspace must be 256-byte aligned");
+
+  RingEvents* ev = nullptr;
+  if ((st = ring_events(ev)) != RA_OK) return st;
+  hipStream_t cs = reinterpret_cast<hipStream_t>(compute_stream);
+  hipStream_t xs = copy_stream ? reinterpret_cast<hipStream_t>(copy_stream) : cs;
+  const size_t es = esize(dtype);
+  const int64_t C = L.C, Cpad = L.Cpad;
+  char* ws = reinterpret_cast<char*>(workspace);
+  char* vt_home = ws;
+  char* slot[2] = {ws + L.vt_home, ws + L.vt_home + L.slot};
+  float* acc = reinterpret_cast<float*>(ws + L.vt_home + 2 * L.slot);
+  const bool bf16 = dtype == RA_BF16;
+
+  // V^T home blocks, once per call: [B*Hkv][N][D][Cpad].
+  if (bf16) {
+    hipError_t e = launch_vt_transpose(v, vt_home, (int64_t)B * Hkv, N, C, Cpad, D, S * D, cs);
+    if (e != hipSuccess) return hip_fail(e, "V transpose launch");
+  }
+  if (xs != cs) {
+    RA_HIP(hipEventRecord(ev->vt_done, cs));
+    RA_HIP(hipStreamWaitEvent(xs, ev->vt_done, 0));
+  }
+
+  auto pos_of_rank = [&](int r) {
+    PosDesc p;
+    if (layout == RA_ZIGZAG) {
+      const int64_t c = S / (2 * N);
+      p = PosDesc{2, (int32_t)c, (int32_t)(r * c), (int32_t)((2 * N - 1 - r) * c)};
+    } else {
+      p = PosDesc{1, (int32_t)C, (int32_t)(r * C), 0};
+    }
+    return p;
+  };
+  // Enqueue the copy of source rank `src`'s K and V blocks into slot `sl`.
+  auto copy_block = [&](int src, int sl) -> ra_status {
+    const size_t row_k = (size_t)C * D * es;
+    RA_HIP(hipMemcpy2DAsync(slot[sl], row_k, (const char*)k + (size_t)src * row_k, (size_t)S * D * es,
+                            row_k, (size_t)B * Hkv, hipMemcpyDeviceToDevice, xs));
+    char* sv = slot[sl] + L.slot_k;
+    if (bf16) {
+      const size_t blk = (size_t)D * Cpad * es;
+      RA_HIP(hipMemcpy2DAsync(sv, blk, vt_home + (size_t)src * blk, (size_t)N * blk, blk,
+                              (size_t)B * Hkv, hipMemcpyDeviceToDevice, xs));
+    } else {
+      RA_HIP(hipMemcpy2DAsync(sv, row_k, (const char*)v + (size_t)src * row_k, (size_t)S * D * es,
+                              row_k, (size_t)B * Hkv, hipMemcpyDeviceToDevice, xs));
+    }
+    return RA_OK;
+  };
+
+  for (int r = 0; r < N; ++r) {
+    const PosDesc qp = pos_of_rank(r);
+    for (int step = 0; step < N; ++step) {
+      const int src = ((r - step) % N + N) % N;
+      // Start the next hop before computing on the held block.
+      if (step + 1 < N) {
+        const int nsrc = ((r - step - 1) % N + N) % N;
+        const int sl = (step + 1) & 1;
+        if (xs != cs) RA_HIP(hipStreamWaitEvent(xs, ev->freed[sl], 0));
+        if ((st = copy_block(nsrc, sl)) != RA_OK) return st;
+        if (xs != cs) RA_HIP(hipEventRecord(ev->ready[sl], xs));
+      }
+      AttnArgs a;
+      memset(&a, 0, sizeof a);
+      a.q = (const char*)q + (size_t)r * C * D * es;
+      a.q_bs = (int64_t)Hq * S * D;
+      a.q_hs = S * D;
+      if (step == 0) {  // the rank's own block, read in place
+        a.k = (const char*)k + (size_t)r * C * D * es;
+        a.k_bs = (int64_t)Hkv * S * D;
+        a.k_hs = S * D;
+        if (bf16) {
+          a.v = vt_home + (size_t)r * D * Cpad * es;
+          a.v_bs = (int64_t)Hkv * N * D * Cpad;
+          a.v_hs = (int64_t)N * D * Cpad;
+          a.v_ld = Cpad;
+        } else {
+          a.v = (const char*)v + (size_t)r * C * D * es;
+          a.v_bs = a.k_bs;
+          a.v_hs = a.k_hs;
+          a.v_ld = D;
+        }
+      } else {
+        const int sl = step & 1;
+        if (xs != cs) RA_HIP(hipStreamWaitEvent(cs, ev->ready[sl], 0));
+        a.k = slot[sl];
+        a.k_bs = (int64_t)Hkv * C * D;
+        a.k_hs = C * D;
+        a.v = slot[sl] + L.slot_k;
+        if (bf16) {
+          a.v_bs = (int64_t)Hkv * D * Cpad;
+          a.v_hs = (int64_t)D * Cpad;
+          a.v_ld = Cpad;
+        } else {
+          a.v_bs = a.k_bs;
+          a.v_hs = a.k_hs;
+          a.v_ld = D;
+        }
+      }
+      a.run_out = acc;
+      a.ro_bs = (int64_t)Hq * C * D;
+      a.ro_hs = C * D;
+      a.run_lse = lse + (size_t)r * C;  // the lse output doubles as running lse
+      a.rl_bs = (int64_t)Hq * S;
+      a.rl_hs = S;
+      if (step == N - 1) {
+        a.fin_out = (char*)out + (size_t)r * C * D * es;
+        a.fo_bs = (int64_t)Hq * S * D;
+        a.fo_hs = S * D;
+        a.fin_lse = lse + (size_t)r * C;
+        a.fl_bs = a.rl_bs;
+        a.fl_hs = a.rl_hs;
+      }
+      a.Cq = (int32_t)C;
+      a.Ck = (int32_t)C;
+      a.qp = qp;
+      a.kp = pos_of_rank(src);
+      a.causal = causal;
+      a.accumulate = step > 0;
+      a.scale = scale;
+      a.scale_log2 = scale * 1.4426950408889634f;
+      fill_work(a, B, Hq, C, kv_of, order);
+      const double flops = 4.0 * D * B * Hq * (double)pairs_between(a.qp, C, a.kp, C, causal);
+      if ((st = timed_launch(a, dtype, D, cs, flops)) != RA_OK) return st;
+      if (step > 0 && xs != cs) RA_HIP(hipEventRecord(ev->freed[step & 1], cs));
+    }
+  }
+  return RA_OK;
+}
+
+ra_status ra_kernel_timing_enable(int32_t enable) {
+  g_err[0] = 0;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.enabled = enable != 0;
+  return RA_OK;
+}
+
+ra_status ra_kernel_timing_read(double* total_ms, int64_t* launches, double* useful_flops) {
+  g_err[0] = 0;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  double ms = 0.0;
+  for (size_t i = 0; i < g_timing.used; ++i) {
+    RA_HIP(hipEventSynchronize(g_timing.ev[2 * i + 1]));
+    float t = 0.f;
+    RA_HIP(hipEventElapsedTime(&t, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]));
+    ms += t;
+  }
+  if (total_ms) *total_ms = ms;
+  if (launches) *launches = g_timing.launches;
+  if (useful_flops) *useful_flops = g_timing.flops;
+  g_timing.used = 0;
+  g_timing.launches = 0;
+  g_timing.flops = 0.0;
+  return RA_OK;
+}
+
+}  // extern "C"

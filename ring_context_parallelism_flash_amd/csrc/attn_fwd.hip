@@ -1,0 +1,478 @@
+// Blockwise attention of one query block against one KV block, merged into a
+// running (out, lse) state -- the per-step kernel of ring attention.
+//
+// Method: "Context Parallelism" (aiwiki), ring_attention listing (flash_block
+// with a source-dependent mask) and "Ring attention" (exact, blockwise);
+// "Sequence Parallelism in Large Language Models ..." (llms.blog),
+// "Algorithmic Mechanics" (online-softmax running max / sum / rescaled output)
+// and "Causal Masking and Load Balancing" (j <= i on global positions).
+//
+// gfx950 design
+//  * A workgroup is 4 wave64s; each wave owns 32 query rows (128 per WG).
+//  * Scores are computed transposed, S^T = K * Q^T, with
+//    v_mfma_f32_32x32x16_bf16: a lane then holds 16 keys of ONE query, so the
+//    row max and row sum of the online softmax are in-lane reductions plus a
+//    single exchange with the lane 32 away. Q stays in registers.
+//  * The output is accumulated transposed too, O^T += V^T * P^T: the fp32
+//    score registers, rounded to bf16, are directly the B operand (no
+//    shuffles), and the per-query rescale factor is in-lane.
+//  * K is staged in LDS as [key][d]; V is staged as V^T [d][key] (the host
+//    transposes V once per call) so both MFMA operands are 16-byte LDS reads.
+//    The rows of each 32-key S^T tile are permuted so that the keys a lane
+//    holds after the first MFMA are exactly the 8 consecutive keys its V^T
+//    operand needs in the second.
+//  * Key tiles are classified from global positions: tiles past the causal
+//    frontier are never visited, fully visible tiles skip the mask, and only
+//    the diagonal / ragged tiles evaluate a per-element mask.
+//  * Workgroup ids are remapped so each XCD (ids dealt round-robin over 8
+//    XCDs) runs a contiguous range of (head, query tile) items: query heads
+//    that share a KV head, and neighbouring query tiles, then read the same
+//    K/V tiles through that XCD's L2.
+//  * The fp32 kernel (v_mfma_f32_32x32x2_f32) keeps the same structure with
+//    one element per lane per operand, so V needs no transpose there.
+#include <math.h>
+
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ int pos_of(const PosDesc& p, int t) {
+  const bool second = (p.nseg == 2) & (t >= p.seg);
+  return second ? p.start1 + (t - p.seg) : p.start0 + t;
+}
+
+// Score with the causal / ragged mask applied, as a select. The mask is
+// evaluated without short-circuit branches on purpose: a divergent
+// short-circuit condition guarding a store into one element of an MFMA
+// accumulator vector was compiled into code that dropped the store.
+__device__ __forceinline__ float masked(float s, int key, int Ck, int causal, const PosDesc& kp,
+                                        int qpos) {
+  const bool ok = (key < Ck) & ((causal == 0) | (pos_of(kp, key) <= qpos));
+  return ok ? s : -INFINITY;
+}
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Number of keys whose position is <= P. Positions increase with the row
+// index, so these keys are a prefix of the block.
+__device__ __forceinline__ int allowed_prefix(const PosDesc& p, int P) {
+  int n = clampi(P - p.start0 + 1, 0, p.seg);
+  if (p.nseg == 2) n += clampi(P - p.start1 + 1, 0, p.seg);
+  return n;
+}
+
+// Row of the K tile that feeds MFMA row m of a 32-key S^T tile (bf16 kernel).
+// MFMA output row m = 4*h + (j%4) + 8*(j/4) + 16*w (h = lane half, j = slot)
+// is sent to key 16*w + 8*h + j, so lane half h ends up holding keys
+// {8h..8h+7, 16+8h..16+8h+7}: one 16-byte V^T read per PV step.
+__device__ __forceinline__ int kperm(int m) {
+  const int w = m >> 4, r = m & 15;
+  return 16 * w + 8 * ((r >> 2) & 1) + (r & 3) + 4 * (r >> 3);
+}
+
+struct WorkItem {
+  int b, h, g, q0;
+};
+
+__device__ __forceinline__ bool decode_item(const AttnArgs& a, WorkItem& it) {
+  const int w = blockIdx.x;
+  const int L = (w % kXcds) * a.per_xcd + (w / kXcds);
+  if (L >= a.n_items) return false;
+  const int qt_rel = L % a.n_qt;
+  const int rest = L / a.n_qt;
+  const int hidx = rest % a.Hq;
+  it.b = rest / a.Hq;
+  it.h = a.head_order[hidx];
+  it.g = a.kv_of[it.h];
+  // heaviest (latest-position) query tiles first
+  it.q0 = (a.qt_lo + (a.n_qt - 1 - qt_rel)) * kQTile;
+  return true;
+}
+
+// Online-softmax update for one key tile, on the scores of one lane. S holds
+// NSC score vectors of 16; masked entries are -inf. Returns the scale that was
+// applied to the running output (alpha) and turns S into probabilities.
+template <int NSC>
+__device__ __forceinline__ float softmax_tile(floatx16 (&S)[NSC], float& m_run, float& l_part,
+                                              float scale_log2) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < NSC; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[t][i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m_run, mx);
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2);
+  const float moff = m_use * scale_log2;
+  float rs = 0.f;
+#pragma unroll
+  for (int t = 0; t < NSC; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(S[t][i], scale_log2, -moff));
+      S[t][i] = p;
+      rs += p;
+    }
+  l_part = l_part * alpha + rs;
+  m_run = m_new;
+  return alpha;
+}
+
+// Merge the block result into the running state (or write it) for the lane's
+// query row. O holds the unnormalised O^T accumulators: lane (n, hh) holds
+// d = 32*T + 4*hh + (i%4) + 8*(i/4) of query n.
+template <int DT, bool BF16>
+__device__ __forceinline__ void epilogue(const AttnArgs& a, const WorkItem& it, int qi, int hh,
+                                         floatx16 (&O)[DT], float m_run, float l_part) {
+  constexpr int D = DT * 32;
+  const float l = l_part + __shfl_xor(l_part, 32);
+  if (qi >= a.Cq) return;
+  const bool fin = a.fin_out != nullptr;
+  const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+  const float lse_blk = (l > 0.f) ? fmaf(m_use, a.scale, logf(l)) : -INFINITY;
+  if (a.accumulate && lse_blk == -INFINITY && !fin) return;  // nothing to fold in
+
+  float* ro = a.run_out + it.b * a.ro_bs + it.h * a.ro_hs + (int64_t)qi * D;
+  float* rl = a.run_lse + it.b * a.rl_bs + it.h * a.rl_hs + qi;
+  const float lse_old = a.accumulate ? *rl : -INFINITY;
+  const float mx = fmaxf(lse_old, lse_blk);
+  float lse_new, ca, cb;
+  if (mx == -INFINITY) {
+    lse_new = -INFINITY;
+    ca = 0.f;
+    cb = 0.f;
+  } else {
+    const float mn = fminf(lse_old, lse_blk);
+    lse_new = mx + log1pf(expf(mn - mx));
+    ca = (lse_old == -INFINITY) ? 0.f : expf(lse_old - lse_new);
+    cb = (lse_blk == -INFINITY) ? 0.f : expf(lse_blk - lse_new) / l;
+  }
+
+#pragma unroll
+  for (int T = 0; T < DT; ++T)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = 32 * T + 8 * g4 + 4 * hh;
+      float4 r;
+      r.x = O[T][4 * g4 + 0] * cb;
+      r.y = O[T][4 * g4 + 1] * cb;
+      r.z = O[T][4 * g4 + 2] * cb;
+      r.w = O[T][4 * g4 + 3] * cb;
+      if (ca != 0.f) {
+        const float4 old = *reinterpret_cast<const float4*>(ro + d0);
+        r.x = fmaf(old.x, ca, r.x);
+        r.y = fmaf(old.y, ca, r.y);
+        r.z = fmaf(old.z, ca, r.z);
+        r.w = fmaf(old.w, ca, r.w);
+      }
+      if (fin) {
+        if constexpr (BF16) {
+          __bf16* fo = reinterpret_cast<__bf16*>(a.fin_out) + it.b * a.fo_bs + it.h * a.fo_hs +
+                       (int64_t)qi * D + d0;
+          bf16x4 pk;
+          pk[0] = (__bf16)r.x;
+          pk[1] = (__bf16)r.y;
+          pk[2] = (__bf16)r.z;
+          pk[3] = (__bf16)r.w;
+          *reinterpret_cast<bf16x4*>(fo) = pk;
+        } else {
+          float* fo = reinterpret_cast<float*>(a.fin_out) + it.b * a.fo_bs + it.h * a.fo_hs +
+                      (int64_t)qi * D + d0;
+          *reinterpret_cast<float4*>(fo) = r;
+        }
+      } else {
+        *reinterpret_cast<float4*>(ro + d0) = r;
+      }
+    }
+  if (hh == 0) {
+    if (fin)
+      a.fin_lse[it.b * a.fl_bs + it.h * a.fl_hs + qi] = lse_new;
+    else
+      *rl = lse_new;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernel: 64-key tiles, MFMA 32x32x16.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
+  constexpr int KS = D / 16;    // MFMA k-steps of the score product
+  constexpr int DT = D / 32;    // 32-wide d tiles of the output
+  constexpr int KLD = D + 8;    // LDS row of K (bf16), padded by 16 B
+  constexpr int VLD = 64 + 8;   // LDS row of V^T (bf16), padded by 16 B
+  constexpr int KCH = 64 * D / 8 / kThreads;  // 16-byte K chunks per thread
+  constexpr int VCH = D * 8 / kThreads;       // 16-byte V^T chunks per thread
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[64 * KLD];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[D * VLD];
+
+  WorkItem it;
+  if (!decode_item(a, it)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  const int qw0 = it.q0 + 32 * wv;
+  const int qi = qw0 + n;
+  const int qlast = a.Cq - 1;
+  const int qpos = pos_of(a.qp, min(qi, qlast));
+  const int wave_qmin = pos_of(a.qp, min(qw0, qlast));
+  const int wg_qmax = pos_of(a.qp, min(it.q0 + kQTile - 1, qlast));
+  const int n_keys = a.causal ? allowed_prefix(a.kp, wg_qmax) : a.Ck;
+  const int n_kt = (n_keys + 63) / 64;
+
+  const __bf16* qb = reinterpret_cast<const __bf16*>(a.q) + it.b * a.q_bs + it.h * a.q_hs;
+  const __bf16* kbp = reinterpret_cast<const __bf16*>(a.k) + it.b * a.k_bs + it.g * a.k_hs;
+  const __bf16* vtb = reinterpret_cast<const __bf16*>(a.v) + it.b * a.v_bs + it.g * a.v_hs;
+
+  bf16x8 qreg[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (qi < a.Cq)
+      qreg[s] = *reinterpret_cast<const bf16x8*>(qb + (int64_t)qi * D + 16 * s + 8 * hh);
+    else
+      for (int j = 0; j < 8; ++j) qreg[s][j] = (__bf16)0.f;
+  }
+
+  floatx16 O[DT];
+#pragma unroll
+  for (int T = 0; T < DT; ++T)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[T][i] = 0.f;
+  float m_run = -INFINITY, l_part = 0.f;
+
+  uint4 kreg[KCH], vreg[VCH];
+  auto load_tile = [&](int kt) {
+    const int kb = kt * 64;
+#pragma unroll
+    for (int r = 0; r < KCH; ++r) {
+      const int c = tid + kThreads * r;
+      const int row = c / (D / 8), col = c % (D / 8);
+      const int key = kb + row;
+      if (key < a.Ck)
+        kreg[r] = *reinterpret_cast<const uint4*>(kbp + (int64_t)key * D + col * 8);
+      else
+        kreg[r] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < VCH; ++r) {
+      const int c = tid + kThreads * r;
+      const int d = c / 8, col = c % 8;
+      vreg[r] = *reinterpret_cast<const uint4*>(vtb + (int64_t)d * a.v_ld + kb + col * 8);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int r = 0; r < KCH; ++r) {
+      const int c = tid + kThreads * r;
+      const int row = c / (D / 8), col = c % (D / 8);
+      *reinterpret_cast<uint4*>(&Ks[row * KLD + col * 8]) = kreg[r];
+    }
+#pragma unroll
+    for (int r = 0; r < VCH; ++r) {
+      const int c = tid + kThreads * r;
+      const int d = c / 8, col = c % 8;
+      *reinterpret_cast<uint4*>(&Vs[d * VLD + col * 8]) = vreg[r];
+    }
+  };
+
+  if (n_kt > 0) load_tile(0);
+  const int krow0 = kperm(n);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (kt + 1 < n_kt) load_tile(kt + 1);
+
+    // S^T = K Q^T for two 32-key halves.
+    floatx16 S[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) S[t][i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(&Ks[(32 * t + krow0) * KLD + 16 * s + 8 * hh]);
+        S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[s], S[t], 0, 0, 0);
+      }
+    }
+
+    // Mask diagonal and ragged tiles (wave-uniform decision).
+    const int kb = kt * 64;
+    const bool ragged = kb + 64 > a.Ck;
+    const bool diag = a.causal && pos_of(a.kp, min(kb + 63, a.Ck - 1)) > wave_qmin;
+    if (ragged || diag) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb + 32 * t + 16 * (i >> 3) + 8 * hh + (i & 7);
+          S[t][i] = masked(S[t][i], key, a.Ck, a.causal, a.kp, qpos);
+        }
+    }
+
+    const float alpha = softmax_tile<2>(S, m_run, l_part, a.scale_log2);
+#pragma unroll
+    for (int T = 0; T < DT; ++T)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) O[T][i] *= alpha;
+
+    // O^T += V^T P^T over four 16-key groups.
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      bf16x8 pf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pf[j] = (__bf16)S[u >> 1][8 * (u & 1) + j];
+#pragma unroll
+      for (int T = 0; T < DT; ++T) {
+        const bf16x8 vf =
+            *reinterpret_cast<const bf16x8*>(&Vs[(32 * T + n) * VLD + 16 * u + 8 * hh]);
+        O[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, O[T], 0, 0, 0);
+      }
+    }
+  }
+  epilogue<DT, true>(a, it, qi, hh, O, m_run, l_part);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: 32-key tiles, MFMA 32x32x2 f32, V row-major.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_f32(const AttnArgs a) {
+  constexpr int KS = D / 2;
+  constexpr int DT = D / 32;
+  constexpr int KLD = D + 1;
+  constexpr int VLD = D + 4;
+  constexpr int CH = 32 * D / 4 / kThreads;  // float4 chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) float Ks[32 * KLD];
+  __shared__ __attribute__((aligned(16))) float Vs[32 * VLD];
+
+  WorkItem it;
+  if (!decode_item(a, it)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  const int qw0 = it.q0 + 32 * wv;
+  const int qi = qw0 + n;
+  const int qlast = a.Cq - 1;
+  const int qpos = pos_of(a.qp, min(qi, qlast));
+  const int wave_qmin = pos_of(a.qp, min(qw0, qlast));
+  const int wg_qmax = pos_of(a.qp, min(it.q0 + kQTile - 1, qlast));
+  const int n_keys = a.causal ? allowed_prefix(a.kp, wg_qmax) : a.Ck;
+  const int n_kt = (n_keys + 31) / 32;
+
+  const float* qb = reinterpret_cast<const float*>(a.q) + it.b * a.q_bs + it.h * a.q_hs;
+  const float* kbp = reinterpret_cast<const float*>(a.k) + it.b * a.k_bs + it.g * a.k_hs;
+  const float* vbp = reinterpret_cast<const float*>(a.v) + it.b * a.v_bs + it.g * a.v_hs;
+
+  float qreg[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qreg[s] = (qi < a.Cq) ? qb[(int64_t)qi * D + 2 * s + hh] : 0.f;
+
+  floatx16 O[DT];
+#pragma unroll
+  for (int T = 0; T < DT; ++T)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[T][i] = 0.f;
+  float m_run = -INFINITY, l_part = 0.f;
+
+  float4 kreg[CH], vreg[CH];
+  auto load_tile = [&](int kt) {
+    const int kb = kt * 32;
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+      const int c = tid + kThreads * r;
+      const int row = c / (D / 4), col = c % (D / 4);
+      const int key = kb + row;
+      if (key < a.Ck) {
+        kreg[r] = *reinterpret_cast<const float4*>(kbp + (int64_t)key * D + col * 4);
+        vreg[r] = *reinterpret_cast<const float4*>(vbp + (int64_t)key * D + col * 4);
+      } else {
+        kreg[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        vreg[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+      const int c = tid + kThreads * r;
+      const int row = c / (D / 4), col = c % (D / 4);
+      float* kd = &Ks[row * KLD + col * 4];
+      kd[0] = kreg[r].x;
+      kd[1] = kreg[r].y;
+      kd[2] = kreg[r].z;
+      kd[3] = kreg[r].w;
+      *reinterpret_cast<float4*>(&Vs[row * VLD + col * 4]) = vreg[r];
+    }
+  };
+
+  if (n_kt > 0) load_tile(0);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (kt + 1 < n_kt) load_tile(kt + 1);
+
+    floatx16 S[1];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S[0][i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      S[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[n * KLD + 2 * s + hh], qreg[s], S[0], 0, 0,
+                                                   0);
+
+    // Lane (n, hh), register i holds key kb + 4*hh + (i%4) + 8*(i/4).
+    const int kb = kt * 32;
+    const bool ragged = kb + 32 > a.Ck;
+    const bool diag = a.causal && pos_of(a.kp, min(kb + 31, a.Ck - 1)) > wave_qmin;
+    if (ragged || diag) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb + 4 * hh + (i & 3) + 8 * (i >> 2);
+        S[0][i] = masked(S[0][i], key, a.Ck, a.causal, a.kp, qpos);
+      }
+    }
+
+    const float alpha = softmax_tile<1>(S, m_run, l_part, a.scale_log2);
+#pragma unroll
+    for (int T = 0; T < DT; ++T)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) O[T][i] *= alpha;
+
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int krow = 4 * hh + (i & 3) + 8 * (i >> 2);
+#pragma unroll
+      for (int T = 0; T < DT; ++T)
+        O[T] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[krow * VLD + 32 * T + n], S[0][i], O[T],
+                                                     0, 0, 0);
+    }
+  }
+  epilogue<DT, false>(a, it, qi, hh, O, m_run, l_part);
+}
+
+}  // namespace
+
+hipError_t launch_attn(const AttnArgs& a, ra_dtype dt, int D, hipStream_t s) {
+  if (a.n_items <= 0) return hipSuccess;
+  const dim3 grid((unsigned)(a.per_xcd * kXcds)), block(kThreads);
+  if (dt == RA_BF16) {
+    if (D == 128)
+      hipLaunchKernelGGL(attn_fwd_bf16<128>, grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL(attn_fwd_bf16<64>, grid, block, 0, s, a);
+  } else {
+    if (D == 128)
+      hipLaunchKernelGGL(attn_fwd_f32<128>, grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL(attn_fwd_f32<64>, grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ra

@@ -1,0 +1,220 @@
+// Memory-bound helper kernels: the V -> V^T block transpose that feeds the
+// bf16 attention kernel, the standalone log-sum-exp merge, and the zigzag
+// layout permute.
+#include <math.h>
+
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+// ---------------------------------------------------------------------------
+// V^T blocks. One workgroup transposes a 64-key x D tile through LDS: it reads
+// 16-byte chunks along D (coalesced) and writes 16-byte chunks along keys.
+// Columns C..Cpad-1 of every block are written as zeros so the attention
+// kernel can read whole 64-key tiles without bounds checks.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void vt_transpose_kernel(const __bf16* __restrict__ v,
+                                                           __bf16* __restrict__ vt, int64_t nblk,
+                                                           int64_t C, int64_t Cpad, int64_t v_bh) {
+  constexpr int LD = D + 8;  // bf16 elements per LDS row (16-byte pad)
+  __shared__ __attribute__((aligned(16))) __bf16 tile[64 * LD];
+  const int64_t bh = blockIdx.z, blk = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * 64;  // first column of this tile
+  const __bf16* src = v + bh * v_bh + (blk * C) * D;
+  __bf16* dst = vt + ((bh * nblk) + blk) * (int64_t)D * Cpad;
+  const int tid = threadIdx.x;
+  constexpr int CPR = D / 8;  // 16-byte chunks per V row
+  for (int c = tid; c < 64 * CPR; c += 256) {
+    const int row = c / CPR, col = c % CPR;
+    const int64_t t = t0 + row;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (t < C) val = *reinterpret_cast<const uint4*>(src + t * D + col * 8);
+    *reinterpret_cast<uint4*>(&tile[row * LD + col * 8]) = val;
+  }
+  __syncthreads();
+  // each thread assembles 8 consecutive keys of one d row
+  for (int c = tid; c < D * 8; c += 256) {
+    const int d = c / 8, kc = c % 8;
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    bf16x8 out;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out[j] = tile[(kc * 8 + j) * LD + d];
+    const int64_t t = t0 + kc * 8;
+    if (t < Cpad) *reinterpret_cast<bf16x8*>(dst + (int64_t)d * Cpad + t) = out;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// lse merge: (out, lse) <- merge((out, lse), (out_b, lse_b)). Pass 1 updates
+// the output rows reading both lse arrays; pass 2, ordered after it on the
+// same stream, rewrites lse. No thread can therefore read a merged lse. The
+// output pass moves four consecutive floats per thread on the vector path.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void merge_weights(float la, float lb, float& ln, float& ca, float& cb) {
+  const float mx = fmaxf(la, lb);
+  if (mx == -INFINITY) {
+    ln = -INFINITY;
+    ca = 0.f;
+    cb = 0.f;
+    return;
+  }
+  const float mn = fminf(la, lb);
+  ln = mx + log1pf(expf(mn - mx));
+  ca = (la == -INFINITY) ? 0.f : expf(la - ln);
+  cb = (lb == -INFINITY) ? 0.f : expf(lb - ln);
+}
+
+__global__ __launch_bounds__(256) void lse_merge_vec4(float* __restrict__ out,
+                                                      const float* __restrict__ lse,
+                                                      const float* __restrict__ out_b,
+                                                      const float* __restrict__ lse_b,
+                                                      int64_t rows, int dq) {
+  // dq = D / 4 float4 groups per row
+  const int64_t total = rows * dq;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / dq;
+    const float la = lse[r], lb = lse_b[r];
+    float ln, ca, cb;
+    merge_weights(la, lb, ln, ca, cb);
+    const float4 a = reinterpret_cast<const float4*>(out)[i];
+    const float4 b = reinterpret_cast<const float4*>(out_b)[i];
+    float4 o;
+    o.x = fmaf(a.x, ca, b.x * cb);
+    o.y = fmaf(a.y, ca, b.y * cb);
+    o.z = fmaf(a.z, ca, b.z * cb);
+    o.w = fmaf(a.w, ca, b.w * cb);
+    reinterpret_cast<float4*>(out)[i] = o;
+  }
+}
+
+__global__ __launch_bounds__(256) void lse_merge_scalar(float* __restrict__ out,
+                                                        const float* __restrict__ lse,
+                                                        const float* __restrict__ out_b,
+                                                        const float* __restrict__ lse_b,
+                                                        int64_t rows, int D) {
+  const int64_t total = rows * D;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / D;
+    float ln, ca, cb;
+    merge_weights(lse[r], lse_b[r], ln, ca, cb);
+    out[i] = fmaf(out[i], ca, out_b[i] * cb);
+  }
+}
+
+__global__ __launch_bounds__(256) void lse_merge_lse_only(float* __restrict__ lse,
+                                                          const float* __restrict__ lse_b,
+                                                          int64_t rows) {
+  for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < rows;
+       r += (int64_t)gridDim.x * blockDim.x) {
+    float ln, ca, cb;
+    merge_weights(lse[r], lse_b[r], ln, ca, cb);
+    lse[r] = ln;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Zigzag permute: 2N chunks of c rows per outer slice. Rank-major chunk pc
+// (rank pc/2, half pc%2) holds sequence chunk pc/2 (half 0) or 2N-1-pc/2.
+// ---------------------------------------------------------------------------
+template <typename V>
+__global__ __launch_bounds__(256) void zigzag_permute_kernel(const char* __restrict__ src,
+                                                             char* __restrict__ dst, int64_t outer,
+                                                             int twoN, int64_t chunk_vecs,
+                                                             int inverse) {
+  const int64_t nchunks = outer * twoN;
+  for (int64_t y = blockIdx.y; y < nchunks; y += gridDim.y) {
+    const int64_t o = y / twoN;
+    const int pc = (int)(y - o * twoN);
+    const int sc = (pc & 1) ? (twoN - 1 - (pc >> 1)) : (pc >> 1);
+    const int64_t from = o * twoN + (inverse ? pc : sc);
+    const int64_t to = o * twoN + (inverse ? sc : pc);
+    const V* s = reinterpret_cast<const V*>(src) + from * chunk_vecs;
+    V* d = reinterpret_cast<V*>(dst) + to * chunk_vecs;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < chunk_vecs;
+         e += (int64_t)gridDim.x * blockDim.x)
+      d[e] = s[e];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_vt_transpose(const void* v, void* vt, int64_t BH, int64_t nblk, int64_t C,
+                               int64_t Cpad, int D, int64_t v_bh, hipStream_t s) {
+  if (BH == 0 || nblk == 0 || Cpad == 0) return hipSuccess;
+  const dim3 grid((unsigned)(Cpad / 64), (unsigned)nblk, (unsigned)BH), block(256);
+  if (D == 128)
+    hipLaunchKernelGGL(vt_transpose_kernel<128>, grid, block, 0, s,
+                       reinterpret_cast<const __bf16*>(v), reinterpret_cast<__bf16*>(vt), nblk, C,
+                       Cpad, v_bh);
+  else
+    hipLaunchKernelGGL(vt_transpose_kernel<64>, grid, block, 0, s,
+                       reinterpret_cast<const __bf16*>(v), reinterpret_cast<__bf16*>(vt), nblk, C,
+                       Cpad, v_bh);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_merge(float* out, float* lse, const float* out_b, const float* lse_b,
+                            int64_t rows, int D, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const bool vec = (D % 4 == 0) && ((uintptr_t)out % 16 == 0) && ((uintptr_t)out_b % 16 == 0);
+  const int64_t work = vec ? rows * (D / 4) : rows * D;
+  const int64_t blocks = (work + 255) / 256;
+  const unsigned grid = (unsigned)(blocks < 65536 ? blocks : 65536);
+  if (vec)
+    hipLaunchKernelGGL(lse_merge_vec4, dim3(grid), dim3(256), 0, s, out, lse, out_b, lse_b, rows,
+                       D / 4);
+  else
+    hipLaunchKernelGGL(lse_merge_scalar, dim3(grid), dim3(256), 0, s, out, lse, out_b, lse_b, rows,
+                       D);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t lblocks = (rows + 255) / 256;
+  hipLaunchKernelGGL(lse_merge_lse_only, dim3((unsigned)(lblocks < 65536 ? lblocks : 65536)),
+                     dim3(256), 0, s, lse, lse_b, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_zigzag_permute(const void* src, void* dst, int64_t outer, int64_t S,
+                                 int64_t row_bytes, int N, int inverse, hipStream_t s) {
+  const int twoN = 2 * N;
+  const int64_t chunk_bytes = (S / twoN) * row_bytes;
+  if (outer == 0 || chunk_bytes == 0) return hipSuccess;
+  const uintptr_t al = (uintptr_t)src | (uintptr_t)dst | (uintptr_t)chunk_bytes;
+  int vb = 16;
+  while (vb > 1 && (al % vb)) vb >>= 1;
+  const int64_t chunk_vecs = chunk_bytes / vb;
+  const int64_t nchunks = outer * twoN;
+  const int64_t gx = (chunk_vecs + 255) / 256;
+  const dim3 grid((unsigned)(gx < 1024 ? gx : 1024), (unsigned)(nchunks < 65535 ? nchunks : 65535));
+  const char* sp = reinterpret_cast<const char*>(src);
+  char* dp = reinterpret_cast<char*>(dst);
+  switch (vb) {
+    case 16:
+      hipLaunchKernelGGL(zigzag_permute_kernel<uint4>, grid, dim3(256), 0, s, sp, dp, outer, twoN,
+                         chunk_vecs, inverse);
+      break;
+    case 8:
+      hipLaunchKernelGGL(zigzag_permute_kernel<uint2>, grid, dim3(256), 0, s, sp, dp, outer, twoN,
+                         chunk_vecs, inverse);
+      break;
+    case 4:
+      hipLaunchKernelGGL(zigzag_permute_kernel<uint32_t>, grid, dim3(256), 0, s, sp, dp, outer,
+                         twoN, chunk_vecs, inverse);
+      break;
+    case 2:
+      hipLaunchKernelGGL(zigzag_permute_kernel<uint16_t>, grid, dim3(256), 0, s, sp, dp, outer,
+                         twoN, chunk_vecs, inverse);
+      break;
+    default:
+      hipLaunchKernelGGL(zigzag_permute_kernel<uint8_t>, grid, dim3(256), 0, s, sp, dp, outer,
+                         twoN, chunk_vecs, inverse);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ra

@@ -1,0 +1,71 @@
+// Internal declarations shared by the gfx950 kernels and the host side of the
+// ring-attention library. Not part of the public C ABI (include/ring_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ring_attn.h"
+
+namespace ra {
+
+// One attention workgroup: 4 wave64s, each owning 32 query rows.
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQTile = 32 * kWaves;  // query rows per workgroup
+constexpr int kKTileBf16 = 64;       // keys per LDS tile, bf16 kernel
+constexpr int kKTileF32 = 32;        // keys per LDS tile, fp32 kernel
+constexpr int kVtAlign = 64;         // V^T rows are padded to a multiple of this
+constexpr int kMaxHeads = 256;       // head maps travel in the kernel arguments
+constexpr int kXcds = 8;             // MI355X: 8 XCDs, workgroups dealt round-robin
+
+// Global positions of a block's rows: row t sits at
+// start0 + t (t < seg or nseg == 1) or start1 + (t - seg) (nseg == 2).
+struct PosDesc {
+  int32_t nseg, seg, start0, start1;
+};
+
+// Everything one attention launch needs. Strides are in elements; rows are
+// contiguous (row stride D) except V^T, whose rows have length v_ld.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;          // bf16: V^T blocks [.., D, v_ld]; fp32: row-major V
+  float* run_out;         // fp32 running output
+  float* run_lse;         // fp32 running lse
+  void* fin_out;          // non-null: final step, write out here in the input dtype
+  float* fin_lse;         // final lse (used with fin_out)
+  int64_t q_bs, q_hs;
+  int64_t k_bs, k_hs;
+  int64_t v_bs, v_hs, v_ld;
+  int64_t ro_bs, ro_hs;
+  int64_t rl_bs, rl_hs;
+  int64_t fo_bs, fo_hs;
+  int64_t fl_bs, fl_hs;
+  int32_t B, Hq, Cq, Ck;
+  PosDesc qp, kp;
+  int32_t causal, accumulate;
+  float scale;       // natural-units softmax scale
+  float scale_log2;  // scale * log2(e)
+  int32_t qt_lo;     // first query tile launched
+  int32_t n_qt;      // query tiles launched per (b, head)
+  int32_t n_items;   // B * Hq * n_qt
+  int32_t per_xcd;   // ceil(n_items / kXcds)
+  uint8_t head_order[kMaxHeads];  // query heads grouped by KV head
+  uint8_t kv_of[kMaxHeads];       // KV head of each query head
+};
+
+hipError_t launch_attn(const AttnArgs& a, ra_dtype dt, int D, hipStream_t s);
+
+// v: [BH][nblk*C][D] bf16 with per-bh stride v_bh (elements) -> vt:
+// [BH][nblk][D][Cpad] bf16, zero for columns C..Cpad-1.
+hipError_t launch_vt_transpose(const void* v, void* vt, int64_t BH, int64_t nblk, int64_t C,
+                               int64_t Cpad, int D, int64_t v_bh, hipStream_t s);
+
+hipError_t launch_lse_merge(float* out, float* lse, const float* out_b, const float* lse_b,
+                            int64_t rows, int D, hipStream_t s);
+
+hipError_t launch_zigzag_permute(const void* src, void* dst, int64_t outer, int64_t S,
+                                 int64_t row_bytes, int N, int inverse, hipStream_t s);
+
+}  // namespace ra

@@ -1,0 +1,144 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, reports sizes, and rejects bad arguments on the host before
+it touches the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ring_context_parallelism_flash_amd as ra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ring_attn.h")
+
+BF16, F32 = ra.RA_BF16, ra.RA_F32
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: every call below fails validation
+FAKE_ODD = ctypes.c_void_p(0x10008)  # 8-byte aligned only
+
+
+def _declared():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_builds_and_loads():
+    assert os.path.exists(ra.library_path), "run __graft_entry__.build() first"
+    ra.lib()
+
+
+def test_every_declared_symbol_is_exported():
+    declared = _declared()
+    assert len(declared) >= 10
+    assert sorted(ra.EXPORTS) == declared
+    lib = ctypes.CDLL(ra.library_path)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    names = [ra.ra_status_str(s) for s in range(9)]
+    assert names == ["RA_OK", "RA_ERR_NULL", "RA_ERR_SHAPE", "RA_ERR_DTYPE", "RA_ERR_UNSUPPORTED",
+                     "RA_ERR_ALIGN", "RA_ERR_WORKSPACE", "RA_ERR_ARG", "RA_ERR_HIP"]
+
+
+def test_workspace_sizes():
+    # bf16 block: V^T padded to 64 keys
+    assert ra.ra_block_attn_workspace_bytes(1, 8, 100, 128, BF16) == 1 * 8 * 128 * 128 * 2
+    assert ra.ra_block_attn_workspace_bytes(1, 8, 100, 128, F32) == 0
+    # ring at the 128k GQA shape: V^T home + 2 slots (K + V^T) + fp32 running out
+    C = 131072 // 8
+    expect = 8 * 8 * 128 * C * 2 + 2 * (8 * C * 128 * 2 + 8 * 128 * C * 2) + 64 * C * 128 * 4
+    assert ra.ra_ring_sim_workspace_bytes(1, 64, 8, 131072, 128, BF16, 8) == expect
+    assert ra.ra_ring_sim_workspace_bytes(1, 64, 8, 131071, 128, BF16, 8) == 0  # S % N != 0
+
+
+def _block(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, B=1, Hq=2, Hkv=2, Cq=128, Ck=128, D=64,
+             dt=F32, qp=None, kp=None, kvmap=None, causal=1, scale=0.125, acc=0, ws=None, wsb=0)
+    a.update(kw)
+    return ra.lib().ra_block_attn_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"],
+                                      a["Hkv"], a["Cq"], a["Ck"], a["D"], a["dt"], a["qp"],
+                                      a["kp"], a["kvmap"], a["causal"], a["scale"], a["acc"],
+                                      a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), "RA_ERR_UNSUPPORTED"),
+    (dict(dt=7), "RA_ERR_DTYPE"),
+    (dict(Hq=3, Hkv=2), "RA_ERR_SHAPE"),
+    (dict(B=0), "RA_ERR_SHAPE"),
+    (dict(Cq=-1), "RA_ERR_SHAPE"),
+    (dict(scale=0.0), "RA_ERR_ARG"),
+    (dict(scale=float("nan")), "RA_ERR_ARG"),
+    (dict(causal=2), "RA_ERR_ARG"),
+    (dict(q=None), "RA_ERR_NULL"),
+    (dict(k=None), "RA_ERR_NULL"),
+    (dict(out=FAKE_ODD), "RA_ERR_ALIGN"),
+    (dict(dt=BF16), "RA_ERR_WORKSPACE"),
+    (dict(dt=BF16, ws=FAKE, wsb=10), "RA_ERR_WORKSPACE"),
+    (dict(Hq=300, Hkv=300), "RA_ERR_UNSUPPORTED"),
+])
+def test_block_attn_rejects(kw, status):
+    st = _block(**kw)
+    assert ra.ra_status_str(st) == status, ra.ra_last_error()
+    assert ra.ra_last_error() != ""
+
+
+def test_block_attn_rejects_bad_positions_and_map():
+    bad = [ra.ra_pos(3, 128, (ctypes.c_int64 * 2)(0, 0)),        # nseg
+           ra.ra_pos(2, 60, (ctypes.c_int64 * 2)(0, 100)),       # 2*60 != 128
+           ra.ra_pos(2, 64, (ctypes.c_int64 * 2)(0, 10)),        # overlapping segments
+           ra.ra_pos(1, 128, (ctypes.c_int64 * 2)(-5, 0))]       # negative start
+    for p in bad:
+        assert ra.ra_status_str(_block(qp=ctypes.byref(p))) == "RA_ERR_SHAPE"
+    m = (ctypes.c_int32 * 2)(0, 2)  # kv head 2 of 2
+    assert ra.ra_status_str(_block(kvmap=m)) == "RA_ERR_SHAPE"
+
+
+def test_empty_query_block_is_a_no_op():
+    assert _block(Cq=0, q=None, out=None, lse=None) == 0
+
+
+def test_ring_rejects():
+    L = ra.lib()
+
+    def ring(**kw):
+        a = dict(S=1024, N=4, layout=1, dt=BF16, ws=None, wsb=0, D=128, Hq=8, Hkv=2)
+        a.update(kw)
+        return ra.ra_status_str(L.ra_ring_sim_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, a["Hq"], a["Hkv"],
+                                                  a["S"], a["D"], a["dt"], a["N"], a["layout"], 1,
+                                                  0.088, None, a["ws"], a["wsb"], None, None))
+    assert ring(S=1020) == "RA_ERR_SHAPE"         # divisible by N=4 but not by 2N (zigzag)
+    assert ring(S=1028, layout=0) == "RA_ERR_WORKSPACE"  # divisible by N: ok until workspace
+    assert ring(N=0) == "RA_ERR_SHAPE"
+    assert ring(layout=5) == "RA_ERR_ARG"
+    assert ring() == "RA_ERR_WORKSPACE"
+    assert ring(S=0) == "RA_OK"
+
+
+def test_permute_and_merge_reject():
+    L = ra.lib()
+    assert ra.ra_status_str(L.ra_zigzag_permute(FAKE, FAKE, 1, 1000, 2, 8, 0, None)) == "RA_ERR_SHAPE"
+    assert ra.ra_status_str(L.ra_zigzag_permute(FAKE, FAKE, 1, 1024, 2, 8, 0, None)) == "RA_ERR_ARG"
+    assert ra.ra_status_str(L.ra_zigzag_permute(None, FAKE, 1, 1024, 2, 8, 0, None)) == "RA_ERR_NULL"
+    assert ra.ra_status_str(L.ra_zigzag_permute(FAKE, FAKE, 1, 1024, 2, 8, 3, None)) == "RA_ERR_ARG"
+    assert ra.ra_status_str(L.ra_lse_merge(None, FAKE, FAKE, FAKE, 10, 4, None)) == "RA_ERR_NULL"
+    assert ra.ra_status_str(L.ra_lse_merge(FAKE, FAKE, FAKE, FAKE, 10, 0, None)) == "RA_ERR_SHAPE"
+    assert L.ra_lse_merge(None, None, None, None, 0, 4, None) == 0
+
+
+def test_timing_read_without_launches():
+    ra.ra_kernel_timing_enable(True)
+    ms, n, fl = ra.ra_kernel_timing_read()
+    ra.ra_kernel_timing_enable(False)
+    assert (ms, n, fl) == (0.0, 0, 0.0)
+
+
+def test_no_cpu_fallback_when_library_missing(monkeypatch, tmp_path):
+    monkeypatch.setattr(ra, "_lib", None)
+    monkeypatch.setattr(ra, "library_path", str(tmp_path / "missing.so"))
+    with pytest.raises(ra.RAError):
+        ra.lib()

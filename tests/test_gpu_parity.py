@@ -1,0 +1,330 @@
+"""GPU parity: the HIP path, called through the C ABI, against the fp64 oracle.
+
+Tolerances: bf16 inputs (fp32 accumulation) out max-abs <= 2e-2, mean-abs <=
+2e-3, lse max-abs <= 1e-3; fp32 inputs <= 1e-4; the zigzag permute and
+the masked-row / empty-block identities are bit-exact.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity_util import TOL_BF16, TOL_F32, check_rows, compare, pooled_attention
+
+pytestmark = pytest.mark.gpu
+
+ra = pytest.importorskip("ring_context_parallelism_flash_amd")
+DEV = "cuda"
+
+
+def _rnd(shape, seed, dtype, scale=1.0):
+    return workloads.make_random(shape, seed, dtype, scale)
+
+
+def _pos_array(desc, rows):
+    if desc is None:
+        return np.arange(rows)
+    nseg, seg, *starts = desc
+    t = np.arange(rows)
+    if nseg == 1:
+        return starts[0] + t
+    return np.where(t < seg, starts[0] + t, starts[1] + t - seg)
+
+
+def _np(t):
+    return t.detach().double().cpu().numpy()
+
+
+# ---------------------------------------------------------------- permute
+@pytest.mark.parametrize("shape,N,dtype,seq_dim", [
+    ((2, 3, 64, 8), 4, torch.bfloat16, -2),
+    ((1, 2, 1024), 8, torch.float32, -1),
+    ((1, 5, 48, 3), 3, torch.int16, -2),      # 6-byte rows: 2-byte accesses
+    ((1, 1, 4096, 128), 16, torch.bfloat16, -2),
+])
+def test_zigzag_permute_bitexact(shape, N, dtype, seq_dim):
+    g = torch.Generator().manual_seed(5)
+    src = torch.randint(-30000, 30000, shape, generator=g, dtype=torch.int32).to(dtype)
+    S = shape[seq_dim]
+    order = oracle.zigzag_order(S, N)
+    expect = np.take(src.numpy() if dtype != torch.bfloat16 else src.view(torch.int16).numpy(),
+                     order, axis=seq_dim % len(shape))
+    s_dev = src.to(DEV)
+    dst = torch.empty_like(s_dev)
+    ra.ra_zigzag_permute(s_dev, dst, N, inverse=False, seq_dim=seq_dim)
+    back = torch.empty_like(s_dev)
+    ra.ra_zigzag_permute(dst, back, N, inverse=True, seq_dim=seq_dim)
+    torch.cuda.synchronize()
+    got = dst.cpu()
+    got = got.view(torch.int16).numpy() if dtype == torch.bfloat16 else got.numpy()
+    assert np.array_equal(got, expect)
+    assert torch.equal(back.cpu().view(torch.int16) if dtype == torch.bfloat16 else back.cpu(),
+                       src.view(torch.int16) if dtype == torch.bfloat16 else src)
+
+
+# ---------------------------------------------------------------- merge
+@pytest.mark.parametrize("rows,D", [(1000, 128), (77, 5), (4096, 64)])
+def test_lse_merge_vs_oracle(rows, D):
+    g = torch.Generator().manual_seed(rows)
+    out_a = torch.randn(rows, D, generator=g)
+    out_b = torch.randn(rows, D, generator=g)
+    lse_a = torch.randn(rows, generator=g) * 5
+    lse_b = torch.randn(rows, generator=g) * 5
+    lse_a[::7] = -math.inf       # empty running state
+    lse_b[::5] = -math.inf       # empty partial
+    out_a[::7] = 0
+    out_b[::5] = 0
+    ref_out, ref_lse = oracle.merge(out_a, lse_a, out_b, lse_b)
+    o, l_ = out_a.to(DEV), lse_a.to(DEV)
+    ra.ra_lse_merge(o, l_, out_b.to(DEV), lse_b.to(DEV))
+    torch.cuda.synchronize()
+    compare(_np(o), _np(l_), ref_out, ref_lse, dict(max_abs=1e-5, mean_abs=1e-6, lse=1e-5),
+            f"merge rows={rows} D={D}")
+    both = (lse_a == -math.inf) & (lse_b == -math.inf)
+    assert torch.all(l_.cpu()[both] == -math.inf) and torch.all(o.cpu()[both] == 0)
+
+
+# ---------------------------------------------------------------- block
+def _block_case(dtype, D, Cq, Ck, q_pos, k_pos, causal, Hq=4, Hkv=2, kv_map=None, seed=0,
+                accumulate=False):
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q = _rnd((1, Hq, Cq, D), seed + 1, dt)
+    k = _rnd((1, Hkv, Ck, D), seed + 2, dt)
+    v = _rnd((1, Hkv, Ck, D), seed + 3, dt)
+    qp, kp = _pos_array(q_pos, Cq), _pos_array(k_pos, Ck)
+    ref_out, ref_lse = oracle.attention(q, k, v, causal=causal, kv_head_of_q=kv_map,
+                                        q_pos=qp, k_pos=kp)
+    if accumulate:
+        # a running state from an earlier block of keys at positions below kp
+        k0 = _rnd((1, Hkv, 96, D), seed + 4, dt)
+        v0 = _rnd((1, Hkv, 96, D), seed + 5, dt)
+        o0, l0 = oracle.attention(q, k0, v0, causal=causal, kv_head_of_q=kv_map, q_pos=qp,
+                                  k_pos=np.arange(96) + int(kp.min()) - 96 if len(kp) else
+                                  np.arange(96))
+        out = torch.from_numpy(o0).float()
+        lse = torch.from_numpy(l0).float()
+        ref_out, ref_lse = oracle.merge(out, lse, ref_out, ref_lse)
+    else:
+        out = torch.full((1, Hq, Cq, D), 7.0)      # garbage: must be overwritten
+        lse = torch.full((1, Hq, Cq), 3.0)
+    o, l_ = out.to(DEV), lse.to(DEV)
+    ra.ra_block_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), o, l_, q_pos=q_pos, k_pos=k_pos,
+                         kv_head_of_q=kv_map, causal=causal, accumulate=accumulate)
+    torch.cuda.synchronize()
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    compare(_np(o), _np(l_), ref_out, ref_lse, tol,
+            f"block {dtype} D={D} Cq={Cq} Ck={Ck} qpos={q_pos} kpos={k_pos} acc={accumulate}")
+
+
+BLOCK_CASES = [
+    # Cq, Ck, q_pos, k_pos, causal
+    (128, 64, None, None, True),                      # one diagonal tile
+    (300, 200, None, None, True),                     # ragged q and k tiles
+    (257, 513, (1, 257, 1000), None, True),           # all keys visible: no mask
+    (256, 256, (2, 128, 0, 768), (2, 128, 256, 512), True),  # zigzag-like: empty + full
+    (384, 320, (2, 192, 100, 700), (2, 160, 0, 600), True),  # diagonals inside both segments
+    (200, 333, None, None, False),
+    (1, 1, None, None, True),
+    (5, 3, (1, 5, 2), None, True),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("case", range(len(BLOCK_CASES)))
+def test_block_attn_vs_oracle(dtype, D, case):
+    Cq, Ck, qp, kp, causal = BLOCK_CASES[case]
+    _block_case(dtype, D, Cq, Ck, qp, kp, causal, seed=10 * case)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_block_attn_accumulate_and_gqa_map(dtype):
+    _block_case(dtype, 128, 300, 200, (1, 300, 500), (1, 200, 400), True, Hq=4, Hkv=2,
+                kv_map=[1, 0, 1, 0], seed=3, accumulate=True)
+    _block_case(dtype, 64, 200, 264, None, None, False, Hq=6, Hkv=3, seed=4, accumulate=True)
+
+
+def test_block_hand_case():
+    """The hand-derived S=3 example embedded in D=64 (scale 1/8, q[:,0]=8)."""
+    import json
+    with open(os.path.join(os.path.dirname(__file__), "golden", "hand_case_causal_s3.json")) as f:
+        fx = json.load(f)
+    for dt, tol in ((torch.float32, 1e-6), (torch.bfloat16, 2e-2)):
+        q = torch.zeros(1, 1, 3, 64)
+        q[..., 0] = 8.0
+        k = torch.zeros(1, 1, 3, 64)
+        k[0, 0, :, 0] = torch.tensor(fx["k"])[:, 0]
+        v = torch.zeros(1, 1, 3, 64)
+        v[0, 0, :, 0] = torch.tensor(fx["v"])[:, 0]
+        q, k, v = q.to(dt), k.to(dt), v.to(dt)
+        o = torch.zeros(1, 1, 3, 64, device=DEV)
+        l_ = torch.zeros(1, 1, 3, device=DEV)
+        ra.ra_block_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), o, l_, causal=True)
+        torch.cuda.synchronize()
+        exp_out = np.array(fx["out"])[:, 0]
+        exp_lse = np.array(fx["lse"])
+        if dt == torch.bfloat16:   # the bf16-rounded keys move the exact answer slightly
+            exp_out, exp_lse = (x[0, 0] for x in oracle.attention(q, k, v, causal=True))
+            exp_out = exp_out[:, 0]
+        assert np.abs(_np(o)[0, 0, :, 0] - exp_out).max() <= tol
+        assert np.abs(_np(l_)[0, 0] - exp_lse).max() <= tol
+        assert torch.all(o[0, 0, :, 1:] == 0)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_block_future_keys_identity(dtype):
+    """A block entirely after the queries: accumulate leaves the state bit-identical,
+    overwrite gives out=0, lse=-inf. An empty key block behaves the same way."""
+    q = _rnd((1, 2, 200, 128), 1, dtype).to(DEV)
+    k = _rnd((1, 2, 130, 128), 2, dtype).to(DEV)
+    v = _rnd((1, 2, 130, 128), 3, dtype).to(DEV)
+    out0 = torch.randn(1, 2, 200, 128, device=DEV)
+    lse0 = torch.randn(1, 2, 200, device=DEV)
+    for kk, vv, kp in ((k, v, (1, 130, 500)), (k[:, :, :0], v[:, :, :0], None)):
+        o, l_ = out0.clone(), lse0.clone()
+        ra.ra_block_attn_fwd(q, kk, vv, o, l_, q_pos=(1, 200, 0), k_pos=kp, causal=True,
+                             accumulate=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o, out0) and torch.equal(l_, lse0)
+        ra.ra_block_attn_fwd(q, kk, vv, o, l_, q_pos=(1, 200, 0), k_pos=kp, causal=True,
+                             accumulate=False)
+        torch.cuda.synchronize()
+        assert torch.all(o == 0) and torch.all(l_ == -math.inf)
+
+
+# ---------------------------------------------------------------- ring
+def _ring_check(w, rows=None, tol=None, copy_stream=True):
+    q, k, v = workloads.make_inputs(w)
+    B, Hq, S, D = q.shape
+    r = ra.RingRunner(B, Hq, w.Hkv, S, D, q.dtype, w.N, w.layout, w.causal, device=DEV,
+                      copy_stream=copy_stream)
+    out = torch.empty(q.shape, dtype=q.dtype, device=DEV)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+    r(q.to(DEV), k.to(DEV), v.to(DEV), out, lse)
+    torch.cuda.synchronize()
+    tol = tol or (TOL_F32 if w.dtype == "f32" else TOL_BF16)
+    if rows is None:
+        ref_out, ref_lse = (pooled_attention(q, k, v, causal=w.causal,
+                                             rows=np.tile(np.arange(S), (Hq, 1)))
+                            if B == 1 and S >= 4096 else
+                            oracle.attention(q, k, v, causal=w.causal))
+        if B == 1 and S >= 4096:
+            ref_out, ref_lse = ref_out[None], ref_lse[None]
+        got_out, got_lse = _np(out), _np(lse)
+    else:
+        ref_out, ref_lse = pooled_attention(q, k, v, causal=w.causal, rows=rows)
+        idx = torch.from_numpy(rows)
+        o = out[0].cpu()
+        got_out = np.stack([o[h, idx[h]].double().numpy() for h in range(Hq)])
+        got_lse = np.stack([lse[0, h].cpu()[idx[h]].double().numpy() for h in range(Hq)])
+    compare(got_out, got_lse, ref_out, ref_lse, tol, f"ring {w.name}")
+    return out, lse
+
+
+SMALL_RINGS = [
+    workloads.Workload("ragged_zigzag_gqa", B=1, Hq=4, Hkv=2, D=128, S=1000, dtype="bf16",
+                       seed=21, causal=True, N=4, layout="zigzag"),
+    workloads.Workload("batch2_contig_d64", B=2, Hq=4, Hkv=1, D=64, S=768, dtype="bf16",
+                       seed=22, causal=True, N=3, layout="contiguous"),
+    workloads.Workload("single_rank", B=1, Hq=2, Hkv=2, D=128, S=640, dtype="bf16", seed=23,
+                       causal=True, N=1, layout="zigzag"),
+    workloads.Workload("f32_zigzag_ragged", B=1, Hq=2, Hkv=1, D=128, S=600, dtype="f32",
+                       seed=24, causal=True, N=3, layout="zigzag"),
+    workloads.Workload("stress_scores_q_x8", B=1, Hq=2, Hkv=2, D=128, S=2048, dtype="bf16",
+                       seed=25, causal=True, N=4, layout="zigzag"),
+    workloads.Workload("contig_s8192_n8_rank0_0_1023", B=1, Hq=2, Hkv=2, D=128, S=8192,
+                       dtype="bf16", seed=26, causal=True, N=8, layout="contiguous"),
+]
+
+
+@pytest.mark.parametrize("w", SMALL_RINGS, ids=[w.name for w in SMALL_RINGS])
+def test_ring_small_vs_oracle(w):
+    if w.name.startswith("stress"):
+        # large scores exercise the running-max rescale: q scaled by 8
+        q, k, v = workloads.make_inputs(w)
+        q = (q.float() * 8).to(q.dtype)
+        out, lse = ra.ring_attention_sim(q.to(DEV), k.to(DEV), v.to(DEV), N=w.N,
+                                         layout=w.layout, causal=True)
+        torch.cuda.synchronize()
+        ref = oracle.attention(q, k, v, causal=True)
+        compare(_np(out), _np(lse), *ref, TOL_BF16, w.name)
+        return
+    _ring_check(w)
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_ring_config_all_rows(idx):
+    """The tiny fp32 ring and the non-causal 8k ring, every row checked."""
+    _ring_check(workloads.WORKLOADS[idx])
+
+
+def test_ring_config_causal_zigzag_32k_sampled():
+    w = workloads.WORKLOADS[2]
+    n = int(os.environ.get("RA_ORACLE_ROWS", "256"))
+    rows = check_rows(w.S, w.Hq, n, w.seed, 2 * w.N) if n < w.S else np.tile(np.arange(w.S), (w.Hq, 1))
+    _ring_check(w, rows=rows)
+
+
+def test_ring_headline_gqa_128k_sampled():
+    w = workloads.HEADLINE
+    n = int(os.environ.get("RA_ORACLE_ROWS", "32"))
+    _ring_check(w, rows=check_rows(w.S, w.Hq, n, w.seed, 2 * w.N))
+
+
+def test_ring_million_token_mqa_sampled():
+    w = workloads.WORKLOADS[4]
+    n = int(os.environ.get("RA_ORACLE_ROWS", "16"))
+    _ring_check(w, rows=check_rows(w.S, w.Hq, n, w.seed, 2 * w.N))
+
+
+def test_ring_zigzag_equals_contiguous_and_no_copy_stream():
+    base = dict(B=1, Hq=4, Hkv=2, D=128, S=4096, dtype="bf16", seed=31, causal=True, N=8)
+    wz = workloads.Workload("z", layout="zigzag", **base)
+    wc = workloads.Workload("c", layout="contiguous", **base)
+    oz, lz = _ring_check(wz)
+    oc, lc = _ring_check(wc)
+    o1, l1 = _ring_check(wz, copy_stream=False)
+    assert torch.equal(oz, o1) and torch.equal(lz, l1)
+    assert (oz.float() - oc.float()).abs().max().item() <= 2e-2
+    assert (lz - lc).abs().max().item() <= 1e-3
+
+
+def test_ring_causality_perturbation_bitexact():
+    w = workloads.Workload("perturb", B=1, Hq=2, Hkv=1, D=128, S=2048, dtype="bf16", seed=41,
+                           causal=True, N=4, layout="zigzag")
+    q, k, v = (t.to(DEV) for t in workloads.make_inputs(w))
+    o1, l1 = ra.ring_attention_sim(q, k, v, N=w.N, layout=w.layout)
+    i = 1000
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, i + 1:] = _rnd(k2[:, :, i + 1:].shape, 99, torch.bfloat16).to(DEV)
+    v2[:, :, i + 1:] = _rnd(v2[:, :, i + 1:].shape, 98, torch.bfloat16).to(DEV)
+    o2, l2 = ra.ring_attention_sim(q, k2, v2, N=w.N, layout=w.layout)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, :, :i + 1], o2[:, :, :i + 1])
+    assert torch.equal(l1[:, :, :i + 1], l2[:, :, :i + 1])
+    assert not torch.equal(o1[:, :, i + 1:], o2[:, :, i + 1:])
+
+
+def test_ring_deterministic_under_copy_delay():
+    """Delaying the copy stream before the call must not change a single bit:
+    every compute step waits for its block to land."""
+    w = workloads.Workload("delay", B=1, Hq=8, Hkv=2, D=128, S=8192, dtype="bf16", seed=51,
+                           causal=True, N=8, layout="zigzag")
+    q, k, v = (t.to(DEV) for t in workloads.make_inputs(w))
+    r = ra.RingRunner(1, 8, 2, w.S, 128, torch.bfloat16, w.N, "zigzag", True, device=DEV)
+    out1 = torch.empty_like(q)
+    lse1 = torch.empty(1, 8, w.S, device=DEV)
+    r(q, k, v, out1, lse1)
+    torch.cuda.synchronize()
+    out2, lse2 = torch.empty_like(out1), torch.empty_like(lse1)
+    qr, kr, vr = r.permute_inputs(q, k, v)
+    with torch.cuda.stream(r.copy_stream):
+        torch.cuda._sleep(50_000_000)
+    r.ring(qr, kr, vr)
+    r.unpermute_outputs(out2, lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
