@@ -1,0 +1,219 @@
+"""Benchmark: ring-attention forward on one MI355X, the 128k GQA causal zigzag workload.
+
+One step is the whole hot path on one batch of synthetic input already resident
+in HBM: zigzag permute of q, k, v into rank-major order, the simulated 8-rank
+ring (every rank's query block against all 8 KV blocks, with the double-buffered
+block copies), and the inverse permute of out and lse. ``value`` is useful
+TFLOP/s: 4*D flops per (query, key) pair the causal mask allows, over the
+wall-clock time of the K timed steps.
+
+The JSON line also carries the attention kernel's roofline (its summed launch
+time from HIP events recorded on its own stream during the timed steps, against
+the bf16 dense MFMA peak) and the fp64 CPU oracle timed on a bounded sample of
+the same workload (a baseline, not the target).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ring-attn fwd useful TFLOP/s & % bf16 MFMA peak, S=131072 GQA causal zigzag"
+# MI355X published figures: 256 CUs x 2.4 GHz x 4096 dense bf16 flops/CU/clk, HBM3E 8 TB/s.
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def useful_pairs(S: int, causal: bool) -> int:
+    """Allowed (query, key) pairs of one head over the whole sequence."""
+    return S * (S + 1) // 2 if causal else S * S
+
+
+def useful_flops(w) -> float:
+    return 4.0 * w.D * w.B * w.Hq * useful_pairs(w.S, w.causal)
+
+
+def cpu_baseline(w, q, k, v, out_gpu, lse_gpu, budget_s: float, rows_per_head: int):
+    """Time the unmodified fp64 oracle on seeded random rows, head by head, until
+    the time budget is spent; also compare those rows with the GPU result."""
+    import numpy as np
+    import oracle
+    from workloads import sample_rows
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    useful = 0.0
+    heads = 0
+    err_out = 0.0
+    err_lse = 0.0
+    t0 = time.perf_counter()
+    group = w.Hq // w.Hkv
+    for h in range(w.Hq):
+        rows = sample_rows(w.S, rows_per_head, w.seed + 1000, h)
+        g = h // group
+        o, l_ = oracle.attention(q[:, h:h + 1, rows], k[:, g:g + 1], v[:, g:g + 1],
+                                 causal=w.causal, q_pos=rows)
+        heads += 1
+        useful += 4.0 * w.D * float(np.sum(rows + 1) if w.causal else len(rows) * w.S)
+        go = out_gpu[0, h, rows].double().numpy()
+        gl = lse_gpu[0, h, rows].double().numpy()
+        err_out = max(err_out, float(np.abs(go - o[0, 0]).max()))
+        err_lse = max(err_lse, float(np.abs(gl - l_[0, 0]).max()))
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": useful / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{rows_per_head} seeded random query rows x {heads} of {w.Hq} heads of "
+                   f"{w.name}, numpy fp64 (BLAS threads={threads}); "
+                   f"{useful / 1e12:.3f} useful TFLOP in {dt:.1f} s"),
+        "parity_vs_gpu": {"rows": rows_per_head * heads, "out_max_abs": err_out,
+                          "lse_max_abs": err_lse},
+    }
+
+
+def main(argv=None) -> int:
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default=None, help="workload name (default: the 128k GQA one)")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--cpu-rows", type=int, default=8)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    args = p.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; the ring is simulated on a single "
+              "MI355X (use --gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+    import ring_context_parallelism_flash_amd as ra
+    import workloads
+
+    w = workloads.BY_NAME[args.workload] if args.workload else workloads.HEADLINE
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"bench: generating {w.name} inputs", file=sys.stderr, flush=True)
+    q_cpu, k_cpu, v_cpu = workloads.make_inputs(w)
+    q, k, v = (t.to(dev) for t in (q_cpu, k_cpu, v_cpu))
+    runner = ra.RingRunner(w.B, w.Hq, w.Hkv, w.S, w.D, q.dtype, w.N, w.layout, w.causal,
+                           device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
+
+    print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        runner(q, k, v, out, lse)
+    torch.cuda.synchronize()
+
+    ra.ra_kernel_timing_enable(True)
+    ra.ra_kernel_timing_read()  # clear
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        runner(q, k, v, out, lse)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    k_ms, launches, k_flops = ra.ra_kernel_timing_read()
+    ra.ra_kernel_timing_enable(False)
+    print(f"bench: timed {args.steps} steps in {t1 - t0:.3f} s", file=sys.stderr, flush=True)
+
+    flops_step = useful_flops(w)
+    lib_flops_step = k_flops / max(args.steps, 1)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    value = flops_step / (ms_step / 1e3) / 1e12
+
+    # ring alone (inputs already in rank-major order), for the record
+    qr, kr, vr = runner.permute_inputs(q, k, v)
+    torch.cuda.synchronize()
+    r0 = time.perf_counter()
+    for _ in range(args.steps):
+        runner.ring(qr, kr, vr)
+    torch.cuda.synchronize()
+    ring_ms = (time.perf_counter() - r0) * 1e3 / args.steps
+
+    # permute bandwidth: one q-sized permute timed with events
+    dst = torch.empty_like(q)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        ra.ra_zigzag_permute(q, dst, w.N)
+    e1.record()
+    torch.cuda.synchronize()
+    perm_gbs = 2 * q.numel() * q.element_size() * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    # lse-merge bandwidth on one rank's fp32 running state
+    rows = w.B * w.Hq * (w.S // w.N)
+    mo = torch.randn(rows, w.D, device=dev)
+    ml = torch.randn(rows, device=dev)
+    mob, mlb = torch.randn_like(mo), torch.randn_like(ml)
+    e0.record()
+    for _ in range(5):
+        ra.ra_lse_merge(mo, ml, mob, mlb)
+    e1.record()
+    torch.cuda.synchronize()
+    merge_gbs = (3 * rows * w.D + 4 * rows) * 4 * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del dst, mo, ml, mob, mlb
+
+    achieved = k_flops / (k_ms / 1e3) / 1e12 if k_ms > 0 else 0.0
+    bf16 = w.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_MFMA_TFLOPS
+    line = {
+        "metric": METRIC if w is workloads.HEADLINE else f"ring-attn fwd useful TFLOP/s, {w.name}",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic (seeded iid normal q/k/v, k x0.5, bf16)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "S": w.S,
+                   "virtual_ranks": w.N, "layout": w.layout, "causal": w.causal},
+        "pct_peak": round(100.0 * value / peak, 2),
+        "useful_flops_per_step": flops_step,
+        "roofline": {
+            "kernel": f"attn_fwd_{'bf16' if bf16 else 'f32'}<{w.D}>",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": round(peak, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "launches_per_step": launches // max(args.steps, 1),
+            "avg_launch_ms": round(k_ms / max(launches, 1), 4),
+            "flops_per_launch": k_flops / max(launches, 1),
+            "kernel_ms_per_step": round(k_ms / max(args.steps, 1), 3),
+        },
+        "ring_only_ms": round(ring_ms, 3),
+        "aux_kernels": {"zigzag_permute_GBs": round(perm_gbs, 1),
+                        "lse_merge_GBs": round(merge_gbs, 1), "hbm_peak_GBs": PEAK_HBM_GBS},
+        "flops_check": {"closed_form": flops_step, "library_count": lib_flops_step},
+    }
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, out.cpu(), lse.cpu(),
+                                            args.cpu_seconds, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
