@@ -95,6 +95,9 @@ def main(argv=None) -> int:
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--cpu-rows", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="finish with one plain device copy of this many MiB (a known-size "
+                        "reference for hardware byte counters)")
     args = p.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; the ring is simulated on a single "
@@ -212,6 +215,14 @@ def main(argv=None) -> int:
         line["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, out.cpu(), lse.cpu(),
                                             args.cpu_seconds, args.cpu_rows)
     print(json.dumps(line), flush=True)
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"bench: calibration copy of {n} bytes done", file=sys.stderr, flush=True)
     return 0
 
 

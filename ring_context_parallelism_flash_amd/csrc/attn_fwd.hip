@@ -200,17 +200,47 @@ __device__ __forceinline__ void epilogue(const AttnArgs& a, const WorkItem& it, 
 
 // ---------------------------------------------------------------------------
 // bf16 kernel: 64-key tiles, MFMA 32x32x16.
+//
+// Pipeline (one barrier per key tile): K is staged two tiles ahead and V^T one
+// tile ahead in two LDS buffers each. In iteration t every wave issues the
+// score MFMAs of tile t+1 and, independent of them, the softmax of tile t,
+// then the P*V MFMAs of tile t.
+//
+// Lazy rescale: the running max used as the exponent reference is only moved
+// when a row's tile max exceeds it by more than 2^kRescaleLog2 in probability,
+// so the O^T rescale (64 multiplies per lane) is skipped for almost every
+// tile. Probabilities are then bounded by 2^kRescaleLog2 and the result is
+// unchanged, since l and O share the same reference.
 // ---------------------------------------------------------------------------
+constexpr float kRescaleLog2 = 8.f;
+
+// One wave-wide direct global->LDS load: lane i's 16 bytes land at
+// lds_base + 16*i (lds_base must be the same for the whole wave).
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// Barrier that also publishes this wave's direct global->LDS loads. The
+// compiler does not count those loads as LDS writes a barrier must wait for
+// (it emitted a bare s_barrier inside the key loop), so the vector-memory
+// counter is drained explicitly first.
+__device__ __forceinline__ void lds_loads_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
   constexpr int KS = D / 16;    // MFMA k-steps of the score product
   constexpr int DT = D / 32;    // 32-wide d tiles of the output
-  constexpr int KLD = D + 8;    // LDS row of K (bf16), padded by 16 B
-  constexpr int VLD = 64 + 8;   // LDS row of V^T (bf16), padded by 16 B
-  constexpr int KCH = 64 * D / 8 / kThreads;  // 16-byte K chunks per thread
-  constexpr int VCH = D * 8 / kThreads;       // 16-byte V^T chunks per thread
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[64 * KLD];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[D * VLD];
+  constexpr int CPR = D / 8;    // 16-byte chunks per K row
+  constexpr int KI = 64 * CPR / 64 / kWaves;  // direct loads per wave for a K tile
+  constexpr int VI = D * 8 / 64 / kWaves;     // direct loads per wave for a V^T tile
+  constexpr int KBUF = 64 * D * 2, VBUF = D * 64 * 2;  // bytes per LDS tile
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  unsigned char* Ks = lds;             // [2][64 keys][D], chunk-swizzled
+  unsigned char* Vs = lds + 2 * KBUF;  // [2][D][64 keys], chunk-swizzled
 
   WorkItem it;
   if (!decode_item(a, it)) return;
@@ -224,6 +254,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
   const int wg_qmax = pos_of(a.qp, min(it.q0 + kQTile - 1, qlast));
   const int n_keys = a.causal ? allowed_prefix(a.kp, wg_qmax) : a.Ck;
   const int n_kt = (n_keys + 63) / 64;
+  const float c = a.scale_log2;
 
   const __bf16* qb = reinterpret_cast<const __bf16*>(a.q) + it.b * a.q_bs + it.h * a.q_hs;
   const __bf16* kbp = reinterpret_cast<const __bf16*>(a.k) + it.b * a.k_bs + it.g * a.k_hs;
@@ -245,99 +276,156 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
     for (int i = 0; i < 16; ++i) O[T][i] = 0.f;
   float m_run = -INFINITY, l_part = 0.f;
 
-  uint4 kreg[KCH], vreg[VCH];
-  auto load_tile = [&](int kt) {
+  // Swizzled layouts. K row r stores logical 16-byte chunk lc at physical
+  // chunk lc ^ (r % CPR); V^T row d stores lc at lc ^ ((d / 2) % 8). With
+  // these the 32 rows an MFMA operand read touches fall in distinct banks.
+  // Global side of the direct loads: this lane's row and logical chunk.
+  int k_row[KI], k_gofs[KI];
+#pragma unroll
+  for (int j = 0; j < KI; ++j) {
+    const int P = (wv * KI + j) * 64 + lane;
+    const int row = P / CPR, pc = P % CPR;
+    k_row[j] = row;
+    k_gofs[j] = row * D + (pc ^ (row % CPR)) * 8;
+  }
+  int v_gofs[VI];
+#pragma unroll
+  for (int j = 0; j < VI; ++j) {
+    const int P = (wv * VI + j) * 64 + lane;
+    const int d = P / 8, pc = P % 8;
+    v_gofs[j] = d * (int)a.v_ld + (pc ^ ((d >> 1) & 7)) * 8;
+  }
+  auto load_k = [&](int kt, int buf) {
     const int kb = kt * 64;
+    const __bf16* base = kbp + (int64_t)kb * D;
+    unsigned char* dst = Ks + buf * KBUF + wv * KI * 1024;
+    if (kb + 64 <= a.Ck) {
 #pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int c = tid + kThreads * r;
-      const int row = c / (D / 8), col = c % (D / 8);
-      const int key = kb + row;
-      if (key < a.Ck)
-        kreg[r] = *reinterpret_cast<const uint4*>(kbp + (int64_t)key * D + col * 8);
-      else
-        kreg[r] = make_uint4(0, 0, 0, 0);
-    }
+      for (int j = 0; j < KI; ++j) load_lds16(base + k_gofs[j], dst + j * 1024);
+    } else {  // ragged tile: rows past the block end re-read the last row (masked later)
 #pragma unroll
-    for (int r = 0; r < VCH; ++r) {
-      const int c = tid + kThreads * r;
-      const int d = c / 8, col = c % 8;
-      vreg[r] = *reinterpret_cast<const uint4*>(vtb + (int64_t)d * a.v_ld + kb + col * 8);
+      for (int j = 0; j < KI; ++j) {
+        const int over = max(kb + k_row[j] - (a.Ck - 1), 0);
+        load_lds16(base + k_gofs[j] - over * D, dst + j * 1024);
+      }
     }
   };
-  auto store_tile = [&]() {
+  auto load_v = [&](int kt, int buf) {
+    const __bf16* base = vtb + kt * 64;
+    unsigned char* dst = Vs + buf * VBUF + wv * VI * 1024;
 #pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int c = tid + kThreads * r;
-      const int row = c / (D / 8), col = c % (D / 8);
-      *reinterpret_cast<uint4*>(&Ks[row * KLD + col * 8]) = kreg[r];
-    }
-#pragma unroll
-    for (int r = 0; r < VCH; ++r) {
-      const int c = tid + kThreads * r;
-      const int d = c / 8, col = c % 8;
-      *reinterpret_cast<uint4*>(&Vs[d * VLD + col * 8]) = vreg[r];
-    }
+    for (int j = 0; j < VI; ++j) load_lds16(base + v_gofs[j], dst + j * 1024);
   };
 
-  if (n_kt > 0) load_tile(0);
+  // LDS read offsets of the MFMA operands (bytes, within one buffer).
   const int krow0 = kperm(n);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < n_kt) load_tile(kt + 1);
+  int k_rofs[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) k_rofs[s] = krow0 * D * 2 + (((2 * s + hh) ^ (krow0 % CPR)) * 16);
+  int v_rofs[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) v_rofs[u] = n * 128 + (((2 * u + hh) ^ ((n >> 1) & 7)) * 16);
 
-    // S^T = K Q^T for two 32-key halves.
-    floatx16 S[2];
+  auto scores = [&](int buf, floatx16 (&S)[2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) S[t][i] = 0.f;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(&Ks[(32 * t + krow0) * KLD + 16 * s + 8 * hh]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+            Ks + buf * KBUF + t * 32 * D * 2 + k_rofs[s]);
         S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[s], S[t], 0, 0, 0);
       }
     }
+  };
 
-    // Mask diagonal and ragged tiles (wave-uniform decision).
-    const int kb = kt * 64;
-    const bool ragged = kb + 64 > a.Ck;
-    const bool diag = a.causal && pos_of(a.kp, min(kb + 63, a.Ck - 1)) > wave_qmin;
-    if (ragged || diag) {
+  if (n_kt > 0) {
+    // prologue: K0, V0, K1 in LDS; scores of tile 0
+    load_k(0, 0);
+    load_v(0, 0);
+    if (n_kt > 1) load_k(1, 1);
+    lds_loads_barrier();
+    floatx16 S[2];
+    scores(0, S);
+
+    for (int kt = 0; kt < n_kt; ++kt) {
+      const int cur = kt & 1;
+      // K(kt+1) and V(kt) have landed; every wave is done with K(kt), V(kt-1)
+      lds_loads_barrier();
+      if (kt + 2 < n_kt) load_k(kt + 2, cur);
+      if (kt + 1 < n_kt) load_v(kt + 1, cur ^ 1);
+
+      floatx16 Sn[2];
+      if (kt + 1 < n_kt) scores(cur ^ 1, Sn);
+
+      // mask (diagonal / ragged tiles only; wave-uniform decision)
+      const int kb = kt * 64;
+      const bool ragged = kb + 64 > a.Ck;
+      const bool diag = a.causal && pos_of(a.kp, min(kb + 63, a.Ck - 1)) > wave_qmin;
+      if (ragged || diag) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kb + 32 * t + 16 * (i >> 3) + 8 * hh + (i & 7);
+            S[t][i] = masked(S[t][i], key, a.Ck, a.causal, a.kp, qpos);
+          }
+      }
+
+      // online softmax with lazy rescale
+      float mx = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb + 32 * t + 16 * (i >> 3) + 8 * hh + (i & 7);
-          S[t][i] = masked(S[t][i], key, a.Ck, a.causal, a.kp, qpos);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[t][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool grow = (mx - m_run) * c > kRescaleLog2;
+      if (__any(grow)) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.f;
+#pragma unroll
+        for (int T = 0; T < DT; ++T)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) O[T][i] *= alpha;
+        l_part *= alpha;
+        m_run = m_new;
+      }
+      const float moff = (m_run == -INFINITY ? 0.f : m_run) * c;
+      // probabilities: the row sum is taken over the fp32 values (two partial
+      // sums), the P*V product uses them rounded to bf16
+      bf16x8 P[4];
+      float rs[2] = {0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(S[u >> 1][8 * (u & 1) + j], c, -moff));
+          rs[u & 1] += p;
+          P[u][j] = (__bf16)p;
         }
-    }
+      l_part += rs[0] + rs[1];
 
-    const float alpha = softmax_tile<2>(S, m_run, l_part, a.scale_log2);
+      // O^T += V^T P^T over four 16-key groups
 #pragma unroll
-    for (int T = 0; T < DT; ++T)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) O[T][i] *= alpha;
-
-    // O^T += V^T P^T over four 16-key groups.
+        for (int T = 0; T < DT; ++T) {
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
+              Vs + cur * VBUF + T * 32 * 128 + v_rofs[u]);
+          O[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[u], O[T], 0, 0, 0);
+        }
+      if (kt + 1 < n_kt) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      bf16x8 pf;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pf[j] = (__bf16)S[u >> 1][8 * (u & 1) + j];
-#pragma unroll
-      for (int T = 0; T < DT; ++T) {
-        const bf16x8 vf =
-            *reinterpret_cast<const bf16x8*>(&Vs[(32 * T + n) * VLD + 16 * u + 8 * hh]);
-        O[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, O[T], 0, 0, 0);
+        for (int t = 0; t < 2; ++t) S[t] = Sn[t];
       }
     }
   }
   epilogue<DT, true>(a, it, qi, hh, O, m_run, l_part);
 }
+
+// LDS bytes of the bf16 kernel (two K and two V^T tiles of 64 keys).
+constexpr size_t bf16_lds_bytes(int D) { return (size_t)2 * (64 * D + D * 64) * 2; }
 
 // ---------------------------------------------------------------------------
 // fp32 kernel: 32-key tiles, MFMA 32x32x2 f32, V row-major.
@@ -462,10 +550,21 @@ hipError_t launch_attn(const AttnArgs& a, ra_dtype dt, int D, hipStream_t s) {
   if (a.n_items <= 0) return hipSuccess;
   const dim3 grid((unsigned)(a.per_xcd * kXcds)), block(kThreads);
   if (dt == RA_BF16) {
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute((const void*)attn_fwd_bf16<128>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)bf16_lds_bytes(128));
+      if (e != hipSuccess) return e;
+      e = hipFuncSetAttribute((const void*)attn_fwd_bf16<64>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bf16_lds_bytes(64));
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
     if (D == 128)
-      hipLaunchKernelGGL(attn_fwd_bf16<128>, grid, block, 0, s, a);
+      hipLaunchKernelGGL(attn_fwd_bf16<128>, grid, block, bf16_lds_bytes(128), s, a);
     else
-      hipLaunchKernelGGL(attn_fwd_bf16<64>, grid, block, 0, s, a);
+      hipLaunchKernelGGL(attn_fwd_bf16<64>, grid, block, bf16_lds_bytes(64), s, a);
   } else {
     if (D == 128)
       hipLaunchKernelGGL(attn_fwd_f32<128>, grid, block, 0, s, a);

@@ -328,3 +328,21 @@ def test_ring_deterministic_under_copy_delay():
     r.unpermute_outputs(out2, lse2)
     torch.cuda.synchronize()
     assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_ring_repeat_bitexact_noncausal_8k():
+    """Repeated runs are bit-identical. This workload (32 key tiles per
+    launch) exposed a missing wait on the direct global->LDS tile loads
+    before the key-loop barrier: results then varied from run to run."""
+    w = workloads.WORKLOADS[1]
+    q, k, v = (t.to(DEV) for t in workloads.make_inputs(w))
+    r = ra.RingRunner(w.B, w.Hq, w.Hkv, w.S, w.D, q.dtype, w.N, w.layout, w.causal, device=DEV)
+    outs = []
+    for _ in range(3):
+        out = torch.empty_like(q)
+        lse = torch.empty(w.B, w.Hq, w.S, device=DEV)
+        r(q, k, v, out, lse)
+        torch.cuda.synchronize()
+        outs.append((out, lse))
+    for out, lse in outs[1:]:
+        assert torch.equal(out, outs[0][0]) and torch.equal(lse, outs[0][1])
