@@ -200,8 +200,8 @@ ra_status check_common(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, ra_dtype d
   return RA_OK;
 }
 
-void fill_work(AttnArgs& a, int32_t B, int32_t Hq, int64_t Cq, const std::vector<uint8_t>& kv_of,
-               const std::vector<uint8_t>& order) {
+void fill_work(AttnArgs& a, ra_dtype dt, int32_t B, int32_t Hq, int64_t Cq,
+               const std::vector<uint8_t>& kv_of, const std::vector<uint8_t>& order) {
   memset(a.head_order, 0, sizeof a.head_order);
   memset(a.kv_of, 0, sizeof a.kv_of);
   for (int h = 0; h < Hq; ++h) {
@@ -210,7 +210,9 @@ void fill_work(AttnArgs& a, int32_t B, int32_t Hq, int64_t Cq, const std::vector
   }
   a.B = B;
   a.Hq = Hq;
-  const int32_t n_qt_all = (int32_t)((Cq + kQTile - 1) / kQTile);
+  const int32_t qtile = dt == RA_BF16 ? kQTileBf16 : kQTileF32;
+  a.q_tile = qtile;
+  const int32_t n_qt_all = (int32_t)((Cq + qtile - 1) / qtile);
   // With accumulate = 1, leading query tiles that see no key are skipped:
   // positions increase with the row index, so these are the rows whose
   // position is below the block's first key position. Not on the final step
@@ -227,7 +229,7 @@ void fill_work(AttnArgs& a, int32_t B, int32_t Hq, int64_t Cq, const std::vector
       else if (p.nseg == 2 && kmin <= (int64_t)p.start1 + p.seg - 1)
         row = p.seg + std::max<int64_t>(0, kmin - p.start1);
     }
-    lo = (int32_t)(row / kQTile);
+    lo = (int32_t)(row / qtile);
   }
   a.qt_lo = lo;
   a.n_qt = n_qt_all - lo;
@@ -336,7 +338,7 @@ ra_status ra_block_attn_fwd(const void* q, const void* k, const void* v, float* 
     a.v_hs = a.k_hs;
     a.v_ld = D;
   }
-  fill_work(a, B, Hq, Cq, kv_of, order);
+  fill_work(a, dtype, B, Hq, Cq, kv_of, order);
   const double flops = 4.0 * D * B * Hq * (double)(Ck > 0 ? pairs_between(qp, Cq, kp, Ck, causal) : 0);
   return timed_launch(a, dtype, D, s, flops);
 }
@@ -548,7 +550,7 @@ ra_status ra_ring_sim_fwd(const void* q, const void* k, const void* v, void* out
       a.accumulate = step > 0;
       a.scale = scale;
       a.scale_log2 = scale * 1.4426950408889634f;
-      fill_work(a, B, Hq, C, kv_of, order);
+      fill_work(a, dtype, B, Hq, C, kv_of, order);
       const double flops = 4.0 * D * B * Hq * (double)pairs_between(a.qp, C, a.kp, C, causal);
       if ((st = timed_launch(a, dtype, D, cs, flops)) != RA_OK) return st;
       if (step > 0 && xs != cs) RA_HIP(hipEventRecord(ev->freed[step & 1], cs));

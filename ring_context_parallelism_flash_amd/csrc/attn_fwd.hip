@@ -90,7 +90,7 @@ __device__ __forceinline__ bool decode_item(const AttnArgs& a, WorkItem& it) {
   it.h = a.head_order[hidx];
   it.g = a.kv_of[it.h];
   // heaviest (latest-position) query tiles first
-  it.q0 = (a.qt_lo + (a.n_qt - 1 - qt_rel)) * kQTile;
+  it.q0 = (a.qt_lo + (a.n_qt - 1 - qt_rel)) * a.q_tile;
   return true;
 }
 
@@ -206,13 +206,16 @@ __device__ __forceinline__ void epilogue(const AttnArgs& a, const WorkItem& it, 
 // score MFMAs of tile t+1 and, independent of them, the softmax of tile t,
 // then the P*V MFMAs of tile t.
 //
-// Lazy rescale: the running max used as the exponent reference is only moved
-// when a row's tile max exceeds it by more than 2^kRescaleLog2 in probability,
-// so the O^T rescale (64 multiplies per lane) is skipped for almost every
-// tile. Probabilities are then bounded by 2^kRescaleLog2 and the result is
-// unchanged, since l and O share the same reference.
+// Lazy rescale: the exponent reference m_run is not the running max. A tile's
+// probabilities are computed against the current reference first; only if a
+// lane's probabilities sum to more than 2^kRescaleLog2 (or it has no reference
+// yet) is the true row max taken and the reference moved up. Probabilities are
+// therefore bounded by 2^kRescaleLog2, the row max and the O^T rescale (64
+// multiplies per lane) are skipped on almost every tile, and the result is
+// unchanged, since l and O always share the same reference.
 // ---------------------------------------------------------------------------
 constexpr float kRescaleLog2 = 8.f;
+constexpr float kFastSum = 256.f;  // 2^kRescaleLog2
 
 // One wave-wide direct global->LDS load: lane i's 16 bytes land at
 // lds_base + 16*i (lds_base must be the same for the whole wave).
@@ -230,13 +233,21 @@ __device__ __forceinline__ void lds_loads_barrier() {
   __syncthreads();
 }
 
+// Ping-pong schedule. A workgroup is 8 waves: group A (waves 0-3) and group B
+// (waves 4-7), one wave of each on every SIMD. Each wave alternates an MFMA
+// phase -- P*V of tile t and the scores of tile t+1 -- and a softmax phase
+// for tile t+1. Group B runs one barrier behind group A, so on every SIMD one
+// wave issues MFMAs while the other issues VALU work, and the two overlap.
+// Group B also issues the direct K / V^T tile loads during its softmax phase,
+// two phases before the tiles are read; K and V^T each have two LDS buffers.
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
+__global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs a) {
   constexpr int KS = D / 16;    // MFMA k-steps of the score product
   constexpr int DT = D / 32;    // 32-wide d tiles of the output
   constexpr int CPR = D / 8;    // 16-byte chunks per K row
-  constexpr int KI = 64 * CPR / 64 / kWaves;  // direct loads per wave for a K tile
-  constexpr int VI = D * 8 / 64 / kWaves;     // direct loads per wave for a V^T tile
+  constexpr int LW = 4;         // waves that issue tile loads (group B)
+  constexpr int KI = 64 * CPR / 64 / LW;  // direct loads per loading wave, K tile
+  constexpr int VI = D * 8 / 64 / LW;     // direct loads per loading wave, V^T tile
   constexpr int KBUF = 64 * D * 2, VBUF = D * 64 * 2;  // bytes per LDS tile
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   unsigned char* Ks = lds;             // [2][64 keys][D], chunk-swizzled
@@ -245,13 +256,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
   WorkItem it;
   if (!decode_item(a, it)) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const bool grpB = wv >= 4;
+  const int lw = wv & 3;
   const int n = lane & 31, hh = lane >> 5;
   const int qw0 = it.q0 + 32 * wv;
   const int qi = qw0 + n;
   const int qlast = a.Cq - 1;
   const int qpos = pos_of(a.qp, min(qi, qlast));
   const int wave_qmin = pos_of(a.qp, min(qw0, qlast));
-  const int wg_qmax = pos_of(a.qp, min(it.q0 + kQTile - 1, qlast));
+  const int wg_qmax = pos_of(a.qp, min(it.q0 + a.q_tile - 1, qlast));
   const int n_keys = a.causal ? allowed_prefix(a.kp, wg_qmax) : a.Ck;
   const int n_kt = (n_keys + 63) / 64;
   const float c = a.scale_log2;
@@ -279,11 +292,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
   // Swizzled layouts. K row r stores logical 16-byte chunk lc at physical
   // chunk lc ^ (r % CPR); V^T row d stores lc at lc ^ ((d / 2) % 8). With
   // these the 32 rows an MFMA operand read touches fall in distinct banks.
-  // Global side of the direct loads: this lane's row and logical chunk.
+  // Global side of the direct loads (loading waves): row and logical chunk.
   int k_row[KI], k_gofs[KI];
 #pragma unroll
   for (int j = 0; j < KI; ++j) {
-    const int P = (wv * KI + j) * 64 + lane;
+    const int P = (lw * KI + j) * 64 + lane;
     const int row = P / CPR, pc = P % CPR;
     k_row[j] = row;
     k_gofs[j] = row * D + (pc ^ (row % CPR)) * 8;
@@ -291,14 +304,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
   int v_gofs[VI];
 #pragma unroll
   for (int j = 0; j < VI; ++j) {
-    const int P = (wv * VI + j) * 64 + lane;
+    const int P = (lw * VI + j) * 64 + lane;
     const int d = P / 8, pc = P % 8;
     v_gofs[j] = d * (int)a.v_ld + (pc ^ ((d >> 1) & 7)) * 8;
   }
   auto load_k = [&](int kt, int buf) {
     const int kb = kt * 64;
     const __bf16* base = kbp + (int64_t)kb * D;
-    unsigned char* dst = Ks + buf * KBUF + wv * KI * 1024;
+    unsigned char* dst = Ks + buf * KBUF + lw * KI * 1024;
     if (kb + 64 <= a.Ck) {
 #pragma unroll
       for (int j = 0; j < KI; ++j) load_lds16(base + k_gofs[j], dst + j * 1024);
@@ -312,7 +325,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
   };
   auto load_v = [&](int kt, int buf) {
     const __bf16* base = vtb + kt * 64;
-    unsigned char* dst = Vs + buf * VBUF + wv * VI * 1024;
+    unsigned char* dst = Vs + buf * VBUF + lw * VI * 1024;
 #pragma unroll
     for (int j = 0; j < VI; ++j) load_lds16(base + v_gofs[j], dst + j * 1024);
   };
@@ -339,48 +352,60 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
       }
     }
   };
-
-  if (n_kt > 0) {
-    // prologue: K0, V0, K1 in LDS; scores of tile 0
-    load_k(0, 0);
-    load_v(0, 0);
-    if (n_kt > 1) load_k(1, 1);
-    lds_loads_barrier();
-    floatx16 S[2];
-    scores(0, S);
-
-    for (int kt = 0; kt < n_kt; ++kt) {
-      const int cur = kt & 1;
-      // K(kt+1) and V(kt) have landed; every wave is done with K(kt), V(kt-1)
-      lds_loads_barrier();
-      if (kt + 2 < n_kt) load_k(kt + 2, cur);
-      if (kt + 1 < n_kt) load_v(kt + 1, cur ^ 1);
-
-      floatx16 Sn[2];
-      if (kt + 1 < n_kt) scores(cur ^ 1, Sn);
-
-      // mask (diagonal / ragged tiles only; wave-uniform decision)
-      const int kb = kt * 64;
-      const bool ragged = kb + 64 > a.Ck;
-      const bool diag = a.causal && pos_of(a.kp, min(kb + 63, a.Ck - 1)) > wave_qmin;
-      if (ragged || diag) {
+  auto pv = [&](int buf, const bf16x8 (&P)[4]) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb + 32 * t + 16 * (i >> 3) + 8 * hh + (i & 7);
-            S[t][i] = masked(S[t][i], key, a.Ck, a.causal, a.kp, qpos);
-          }
+      for (int T = 0; T < DT; ++T) {
+        const bf16x8 vf =
+            *reinterpret_cast<const bf16x8*>(Vs + buf * VBUF + T * 32 * 128 + v_rofs[u]);
+        O[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[u], O[T], 0, 0, 0);
       }
-
-      // online softmax with lazy rescale
+  };
+  // Mask (diagonal / ragged tiles only), then probabilities of tile kt from
+  // its scores Sc into P, updating the reference, O and the row sum.
+  auto softmax = [&](int kt, floatx16 (&Sc)[2], bf16x8 (&P)[4]) {
+    const int kb = kt * 64;
+    const bool ragged = kb + 64 > a.Ck;
+    const bool diag = a.causal && pos_of(a.kp, min(kb + 63, a.Ck - 1)) > wave_qmin;
+    if (ragged || diag) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb + 32 * t + 16 * (i >> 3) + 8 * hh + (i & 7);
+          Sc[t][i] = masked(Sc[t][i], key, a.Ck, a.causal, a.kp, qpos);
+        }
+    }
+    // Probabilities against the current reference m_run. The row sum is
+    // taken over the fp32 values; P*V uses them rounded to bf16.
+    float rsum;
+    auto probs = [&]() {
+      const float moff = (m_run == -INFINITY ? 0.f : m_run) * c;
+      float rs[2] = {0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(Sc[u >> 1][8 * (u & 1) + j], c, -moff));
+          rs[u & 1] += p;
+          P[u][j] = (__bf16)p;
+        }
+      rsum = rs[0] + rs[1];
+    };
+    probs();
+    // Fast path: a reference exists and this lane's probabilities sum to at
+    // most 2^kRescaleLog2, so none exceeds it -- no row max is needed.
+    // Otherwise take the row max and move the reference where it grew.
+    const bool slow = !(rsum <= kFastSum) || (m_run == -INFINITY);
+    if (__any(slow)) {
       float mx = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[t][i]);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, Sc[t][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool grow = (mx - m_run) * c > kRescaleLog2;
+      const bool grow = mx > m_run;
       if (__any(grow)) {
         const float m_new = grow ? mx : m_run;
         const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.f;
@@ -390,36 +415,46 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
           for (int i = 0; i < 16; ++i) O[T][i] *= alpha;
         l_part *= alpha;
         m_run = m_new;
-      }
-      const float moff = (m_run == -INFINITY ? 0.f : m_run) * c;
-      // probabilities: the row sum is taken over the fp32 values (two partial
-      // sums), the P*V product uses them rounded to bf16
-      bf16x8 P[4];
-      float rs[2] = {0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(S[u >> 1][8 * (u & 1) + j], c, -moff));
-          rs[u & 1] += p;
-          P[u][j] = (__bf16)p;
-        }
-      l_part += rs[0] + rs[1];
-
-      // O^T += V^T P^T over four 16-key groups
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int T = 0; T < DT; ++T) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
-              Vs + cur * VBUF + T * 32 * 128 + v_rofs[u]);
-          O[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[u], O[T], 0, 0, 0);
-        }
-      if (kt + 1 < n_kt) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) S[t] = Sn[t];
+        probs();
       }
     }
+    l_part += rsum;
+  };
+
+  if (n_kt > 0) {
+    floatx16 S[2];
+    bf16x8 P[4];
+    // prologue: group B loads K0, V0, K1; every wave takes tile 0 through
+    // the softmax; then group B loads K2, V1 and falls one barrier behind.
+    if (grpB) {
+      load_k(0, 0);
+      load_v(0, 0);
+      if (n_kt > 1) load_k(1, 1);
+    }
+    lds_loads_barrier();
+    scores(0, S);
+    softmax(0, S, P);
+    __syncthreads();  // every wave is done with K0
+    if (grpB) {
+      if (n_kt > 2) load_k(2, 0);
+      if (n_kt > 1) load_v(1, 1);
+      lds_loads_barrier();
+    }
+    for (int t = 0; t < n_kt; ++t) {
+      // MFMA phase: P*V of tile t, scores of tile t+1
+      pv(t & 1, P);
+      if (t + 1 < n_kt) scores((t + 1) & 1, S);
+      if (grpB) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads of the last softmax phase
+      __syncthreads();
+      // softmax phase for tile t+1; group B loads K(t+3) and V(t+2)
+      if (grpB) {
+        if (t + 3 < n_kt) load_k(t + 3, (t + 1) & 1);
+        if (t + 2 < n_kt) load_v(t + 2, t & 1);
+      }
+      if (t + 1 < n_kt) softmax(t + 1, S, P);
+      __syncthreads();
+    }
+    if (!grpB) __syncthreads();  // group A matches group B's extra barrier
   }
   epilogue<DT, true>(a, it, qi, hh, O, m_run, l_part);
 }
@@ -449,7 +484,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_f32(const AttnArgs a) {
   const int qlast = a.Cq - 1;
   const int qpos = pos_of(a.qp, min(qi, qlast));
   const int wave_qmin = pos_of(a.qp, min(qw0, qlast));
-  const int wg_qmax = pos_of(a.qp, min(it.q0 + kQTile - 1, qlast));
+  const int wg_qmax = pos_of(a.qp, min(it.q0 + a.q_tile - 1, qlast));
   const int n_keys = a.causal ? allowed_prefix(a.kp, wg_qmax) : a.Ck;
   const int n_kt = (n_keys + 31) / 32;
 
@@ -561,10 +596,11 @@ hipError_t launch_attn(const AttnArgs& a, ra_dtype dt, int D, hipStream_t s) {
       if (e != hipSuccess) return e;
       attr_set = true;
     }
+    const dim3 block8(kThreadsBf16);
     if (D == 128)
-      hipLaunchKernelGGL(attn_fwd_bf16<128>, grid, block, bf16_lds_bytes(128), s, a);
+      hipLaunchKernelGGL(attn_fwd_bf16<128>, grid, block8, bf16_lds_bytes(128), s, a);
     else
-      hipLaunchKernelGGL(attn_fwd_bf16<64>, grid, block, bf16_lds_bytes(64), s, a);
+      hipLaunchKernelGGL(attn_fwd_bf16<64>, grid, block8, bf16_lds_bytes(64), s, a);
   } else {
     if (D == 128)
       hipLaunchKernelGGL(attn_fwd_f32<128>, grid, block, 0, s, a);

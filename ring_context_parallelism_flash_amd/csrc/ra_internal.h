@@ -9,10 +9,15 @@
 
 namespace ra {
 
-// One attention workgroup: 4 wave64s, each owning 32 query rows.
+// Attention workgroups: every wave64 owns 32 query rows. The bf16 kernel runs
+// 8 waves (two groups of 4 that alternate MFMA and softmax phases), the fp32
+// kernel 4 waves.
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQTile = 32 * kWaves;  // query rows per workgroup
+constexpr int kWavesBf16 = 8;
+constexpr int kThreadsBf16 = 64 * kWavesBf16;
+constexpr int kQTileF32 = 32 * kWaves;       // query rows per fp32 workgroup
+constexpr int kQTileBf16 = 32 * kWavesBf16;  // query rows per bf16 workgroup
 constexpr int kKTileBf16 = 64;       // keys per LDS tile, bf16 kernel
 constexpr int kKTileF32 = 32;        // keys per LDS tile, fp32 kernel
 constexpr int kVtAlign = 64;         // V^T rows are padded to a multiple of this
@@ -47,6 +52,7 @@ struct AttnArgs {
   int32_t causal, accumulate;
   float scale;       // natural-units softmax scale
   float scale_log2;  // scale * log2(e)
+  int32_t q_tile;    // query rows per workgroup (depends on the kernel)
   int32_t qt_lo;     // first query tile launched
   int32_t n_qt;      // query tiles launched per (b, head)
   int32_t n_items;   // B * Hq * n_qt
