@@ -8,7 +8,9 @@
 // and "Causal Masking and Load Balancing" (j <= i on global positions).
 //
 // gfx950 design
-//  * A workgroup is 4 wave64s; each wave owns 32 query rows (128 per WG).
+//  * Each wave64 owns 32 query rows. The bf16 kernel runs 8 waves (256 rows)
+//    per workgroup in two groups that alternate matrix and softmax phases;
+//    the fp32 kernel runs 4 waves (128 rows).
 //  * Scores are computed transposed, S^T = K * Q^T, with
 //    v_mfma_f32_32x32x16_bf16: a lane then holds 16 keys of ONE query, so the
 //    row max and row sum of the online softmax are in-lane reductions plus a
@@ -201,10 +203,10 @@ __device__ __forceinline__ void epilogue(const AttnArgs& a, const WorkItem& it, 
 // ---------------------------------------------------------------------------
 // bf16 kernel: 64-key tiles, MFMA 32x32x16.
 //
-// Pipeline (one barrier per key tile): K is staged two tiles ahead and V^T one
-// tile ahead in two LDS buffers each. In iteration t every wave issues the
-// score MFMAs of tile t+1 and, independent of them, the softmax of tile t,
-// then the P*V MFMAs of tile t.
+// Pipeline: K and V^T tiles are staged in two LDS buffers each by direct
+// global->LDS loads. In iteration t a wave issues the score MFMAs of tile t+1
+// with the softmax of tile t interleaved between them, then the P*V MFMAs of
+// tile t (the two-group schedule below).
 //
 // Lazy rescale: the exponent reference m_run is not the running max. A tile's
 // probabilities are computed against the current reference first; only if a
@@ -233,25 +235,32 @@ __device__ __forceinline__ void lds_loads_barrier() {
   __syncthreads();
 }
 
-// Ping-pong schedule. A workgroup is 8 waves: group A (waves 0-3) and group B
-// (waves 4-7), one wave of each on every SIMD. Each wave alternates an MFMA
-// phase -- P*V of tile t and the scores of tile t+1 -- and a softmax phase
-// for tile t+1. Group B runs one barrier behind group A, so on every SIMD one
-// wave issues MFMAs while the other issues VALU work, and the two overlap.
-// Group B also issues the direct K / V^T tile loads during its softmax phase,
-// two phases before the tiles are read; K and V^T each have two LDS buffers.
+// Two-group schedule. A workgroup is 8 waves: group A (waves 0-3) and group B
+// (waves 4-7), one wave of each on every SIMD. Each wave alternates
+//   S-phase(t): softmax of tile t (VALU) and the score MFMAs of tile t+1,
+//   P-phase(t): the P*V MFMAs of tile t,
+// with a workgroup barrier after every phase; group B runs one barrier behind
+// group A. On every SIMD both waves therefore issue LDS-fed MFMAs in every
+// interval (a single wave streaming one LDS operand per MFMA runs at about
+// half the MFMA rate; two waves come close to it), and one of them also
+// issues the softmax. The direct tile loads are issued in the P-phases --
+// group A loads V^T, group B loads K -- and drained before the barrier that
+// ends the same wave's next S-phase; K and V^T each have two LDS buffers.
 template <int D>
 __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs a) {
   constexpr int KS = D / 16;    // MFMA k-steps of the score product
   constexpr int DT = D / 32;    // 32-wide d tiles of the output
-  constexpr int CPR = D / 8;    // 16-byte chunks per K row
-  constexpr int LW = 4;         // waves that issue tile loads (group B)
-  constexpr int KI = 64 * CPR / 64 / LW;  // direct loads per loading wave, K tile
-  constexpr int VI = D * 8 / 64 / LW;     // direct loads per loading wave, V^T tile
-  constexpr int KBUF = 64 * D * 2, VBUF = D * 64 * 2;  // bytes per LDS tile
+  constexpr int CPR = D / 8;             // 16-byte data chunks per K row
+  constexpr int KCPR = CPR + 1;          // with the pad chunk
+  constexpr int KROW = KCPR * 16;        // bytes per padded K row
+  constexpr int VROW = 9 * 16;           // bytes per padded V^T row (64 keys + pad)
+  constexpr int KBUF = 64 * KROW, VBUF = D * VROW;  // bytes per LDS tile
+  constexpr int KINS = KBUF / 1024, VINS = VBUF / 1024;  // 1 KiB direct loads per tile
+  constexpr int LW = 4;                  // waves that issue tile loads (group B)
+  constexpr int KI = (KINS + LW - 1) / LW, VI = (VINS + LW - 1) / LW;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  unsigned char* Ks = lds;             // [2][64 keys][D], chunk-swizzled
-  unsigned char* Vs = lds + 2 * KBUF;  // [2][D][64 keys], chunk-swizzled
+  unsigned char* Ks = lds;             // [2][64 keys][D + 8]
+  unsigned char* Vs = lds + 2 * KBUF;  // [2][D][64 + 8]
 
   WorkItem it;
   if (!decode_item(a, it)) return;
@@ -289,114 +298,121 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs 
     for (int i = 0; i < 16; ++i) O[T][i] = 0.f;
   float m_run = -INFINITY, l_part = 0.f;
 
-  // Swizzled layouts. K row r stores logical 16-byte chunk lc at physical
-  // chunk lc ^ (r % CPR); V^T row d stores lc at lc ^ ((d / 2) % 8). With
-  // these the 32 rows an MFMA operand read touches fall in distinct banks.
-  // Global side of the direct loads (loading waves): row and logical chunk.
-  int k_row[KI], k_gofs[KI];
-#pragma unroll
-  for (int j = 0; j < KI; ++j) {
-    const int P = (lw * KI + j) * 64 + lane;
-    const int row = P / CPR, pc = P % CPR;
-    k_row[j] = row;
-    k_gofs[j] = row * D + (pc ^ (row % CPR)) * 8;
-  }
-  int v_gofs[VI];
-#pragma unroll
-  for (int j = 0; j < VI; ++j) {
-    const int P = (lw * VI + j) * 64 + lane;
-    const int d = P / 8, pc = P % 8;
-    v_gofs[j] = d * (int)a.v_ld + (pc ^ ((d >> 1) & 7)) * 8;
-  }
+  // Padded layouts: a K row is D+8 bf16 (CPR+1 chunks of 16 bytes), a V^T row
+  // 64+8 bf16 (9 chunks). The 32 rows an MFMA operand read touches then fall
+  // in distinct banks, and every operand offset is an immediate. A direct
+  // load fills 64 consecutive chunks; lanes that land on a pad chunk re-read
+  // a chunk of the same row.
+  // Direct loads (group B): instruction j of loading wave lw fills chunks
+  // P = (lw + LW*j)*64 + lane of the tile; offsets are computed at issue time
+  // (the softmax phase that issues them has VALU to spare).
   auto load_k = [&](int kt, int buf) {
     const int kb = kt * 64;
+    const int rows_left = a.Ck - 1 - kb;  // last valid row of this tile
     const __bf16* base = kbp + (int64_t)kb * D;
-    unsigned char* dst = Ks + buf * KBUF + lw * KI * 1024;
-    if (kb + 64 <= a.Ck) {
+    unsigned char* dst = Ks + buf * KBUF + lw * 1024;
 #pragma unroll
-      for (int j = 0; j < KI; ++j) load_lds16(base + k_gofs[j], dst + j * 1024);
-    } else {  // ragged tile: rows past the block end re-read the last row (masked later)
-#pragma unroll
-      for (int j = 0; j < KI; ++j) {
-        const int over = max(kb + k_row[j] - (a.Ck - 1), 0);
-        load_lds16(base + k_gofs[j] - over * D, dst + j * 1024);
+    for (int j = 0; j < KI; ++j)
+      if (lw + LW * j < KINS) {
+        const int P = (lw + LW * j) * 64 + lane;
+        const int cch = P % KCPR;
+        // rows past the block end re-read its last row (their scores are masked)
+        const int row = min(P / KCPR, rows_left);
+        load_lds16(base + row * D + (cch < CPR ? cch : 0) * 8, dst + j * LW * 1024);
       }
-    }
   };
   auto load_v = [&](int kt, int buf) {
     const __bf16* base = vtb + kt * 64;
-    unsigned char* dst = Vs + buf * VBUF + lw * VI * 1024;
+    unsigned char* dst = Vs + buf * VBUF + lw * 1024;
 #pragma unroll
-    for (int j = 0; j < VI; ++j) load_lds16(base + v_gofs[j], dst + j * 1024);
+    for (int j = 0; j < VI; ++j)
+      if (lw + LW * j < VINS) {
+        const int P = (lw + LW * j) * 64 + lane;
+        const int cch = P % 9;
+        load_lds16(base + (P / 9) * (int)a.v_ld + (cch < 8 ? cch : 0) * 8,
+                   dst + j * LW * 1024);
+      }
   };
 
   // LDS read offsets of the MFMA operands (bytes, within one buffer).
-  const int krow0 = kperm(n);
-  int k_rofs[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) k_rofs[s] = krow0 * D * 2 + (((2 * s + hh) ^ (krow0 % CPR)) * 16);
-  int v_rofs[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) v_rofs[u] = n * 128 + (((2 * u + hh) ^ ((n >> 1) & 7)) * 16);
+  const int k_rbase = kperm(n) * KROW + hh * 16;  // + t*32*KROW + s*32
+  const int v_rbase = n * VROW + hh * 16;         // + T*32*VROW + u*32
 
-  auto scores = [&](int buf, floatx16 (&S)[2]) {
+  // The two 32-key accumulators alternate, so consecutive MFMAs are
+  // independent (a dependent MFMA waits for its predecessor's result).
+  auto scores = [&](int kbuf, floatx16 (&S)[2]) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) S[t][i] = 0.f;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
+    for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-            Ks + buf * KBUF + t * 32 * D * 2 + k_rofs[s]);
-        S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[s], S[t], 0, 0, 0);
+            Ks + kbuf * KBUF + k_rbase + t * 32 * KROW + s2 * 32);
+        S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[s2], S[t], 0, 0, 0);
       }
-    }
   };
-  auto pv = [&](int buf, const bf16x8 (&P)[4]) {
+  // P*V of the tile in V buffer vbuf: 16 MFMAs, each with one 16-byte LDS
+  // operand read, scheduled as a pipeline with PF reads in flight.
+  auto pv_phase = [&](int vbuf, const bf16x8 (&P)[4]) {
+    constexpr int NPV = 4 * DT;
+    constexpr int PF = 4;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int T = 0; T < DT; ++T) {
-        const bf16x8 vf =
-            *reinterpret_cast<const bf16x8*>(Vs + buf * VBUF + T * 32 * 128 + v_rofs[u]);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vs + vbuf * VBUF + v_rbase +
+                                                           T * 32 * VROW + u * 32);
         O[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[u], O[T], 0, 0, 0);
       }
-  };
-  // Mask (diagonal / ragged tiles only), then probabilities of tile kt from
-  // its scores Sc into P, updating the reference, O and the row sum.
-  auto softmax = [&](int kt, floatx16 (&Sc)[2], bf16x8 (&P)[4]) {
-    const int kb = kt * 64;
-    const bool ragged = kb + 64 > a.Ck;
-    const bool diag = a.causal && pos_of(a.kp, min(kb + 63, a.Ck - 1)) > wave_qmin;
-    if (ragged || diag) {
+    // scheduling pattern (0x100: LDS read, 0x008: MFMA)
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb + 32 * t + 16 * (i >> 3) + 8 * hh + (i & 7);
-          Sc[t][i] = masked(Sc[t][i], key, a.Ck, a.causal, a.kp, qpos);
-        }
+    for (int i = 0; i < NPV - PF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    // Probabilities against the current reference m_run. The row sum is
-    // taken over the fp32 values; P*V uses them rounded to bf16.
-    float rsum;
-    auto probs = [&]() {
-      const float moff = (m_run == -INFINITY ? 0.f : m_run) * c;
-      float rs[2] = {0.f, 0.f};
+    __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+  };
+  // Tiles that cross the causal diagonal or the ragged end of the block.
+  auto needs_mask = [&](int kt) -> bool {
+    const int kb = kt * 64;
+    return kb + 64 > a.Ck || (a.causal && pos_of(a.kp, min(kb + 63, a.Ck - 1)) > wave_qmin);
+  };
+  auto apply_mask = [&](int kt, floatx16 (&Sc)[2]) {
+    const int kb = kt * 64;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(Sc[u >> 1][8 * (u & 1) + j], c, -moff));
-          rs[u & 1] += p;
-          P[u][j] = (__bf16)p;
-        }
-      rsum = rs[0] + rs[1];
-    };
-    probs();
-    // Fast path: a reference exists and this lane's probabilities sum to at
-    // most 2^kRescaleLog2, so none exceeds it -- no row max is needed.
-    // Otherwise take the row max and move the reference where it grew.
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb + 32 * t + 16 * (i >> 3) + 8 * hh + (i & 7);
+        Sc[t][i] = masked(Sc[t][i], key, a.Ck, a.causal, a.kp, qpos);
+      }
+  };
+  // Probabilities of scores Sc against the current reference m_run, into P
+  // (bf16); returns this lane's fp32 sum of them. Branch free, so that it can
+  // share a scheduling region with the next tile's score MFMAs.
+  auto probs = [&](const floatx16 (&Sc)[2], bf16x8 (&P)[4]) -> float {
+    const float moff = (m_run == -INFINITY ? 0.f : m_run) * c;
+    float rs[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      rs[u] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(Sc[u >> 1][8 * (u & 1) + j], c, -moff));
+        rs[u] += p;
+        P[u][j] = (__bf16)p;
+      }
+    }
+    return (rs[0] + rs[1]) + (rs[2] + rs[3]);
+  };
+  // Fast path: a reference exists and this lane's probabilities sum to at
+  // most 2^kRescaleLog2, so none exceeds it -- no row max is needed.
+  // Otherwise take the row max and move the reference where it grew.
+  auto finish = [&](const floatx16 (&Sc)[2], bf16x8 (&P)[4], float rsum) {
     const bool slow = !(rsum <= kFastSum) || (m_run == -INFINITY);
     if (__any(slow)) {
       float mx = -INFINITY;
@@ -415,52 +431,88 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs 
           for (int i = 0; i < 16; ++i) O[T][i] *= alpha;
         l_part *= alpha;
         m_run = m_new;
-        probs();
+        rsum = probs(Sc, P);
       }
     }
     l_part += rsum;
   };
+  // Scores of the next tile (K buffer kbuf) into Sn, interleaved with the
+  // probabilities of the current unmasked tile Sc: each QK MFMA is followed
+  // by a slice of the softmax arithmetic, so the exp/fma/add stream runs
+  // under this wave's own matrix work.
+  auto scores_probs = [&](int kbuf, floatx16 (&Sn)[2], const floatx16 (&Sc)[2],
+                          bf16x8 (&P)[4]) -> float {
+    scores(kbuf, Sn);
+    const float rsum = probs(Sc, P);
+    // pattern (0x100: LDS read, 0x008: MFMA, 0x002: VALU): two K reads in
+    // flight, five VALU instructions after each MFMA (measured best among
+    // 5, 7 and 9; deeper read prefetch was slower)
+    constexpr int NQK = 2 * KS;
+    constexpr int PF = 2;
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      if (i < NQK - PF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    return rsum;
+  };
 
   if (n_kt > 0) {
-    floatx16 S[2];
+    floatx16 SA[2], SB[2];
     bf16x8 P[4];
-    // prologue: group B loads K0, V0, K1; every wave takes tile 0 through
-    // the softmax; then group B loads K2, V1 and falls one barrier behind.
+    // prologue: K0, K1 (group B) and V0 (group A) in LDS; every wave takes
+    // the scores of tile 0; group B then loads K2 and falls one barrier behind.
     if (grpB) {
       load_k(0, 0);
-      load_v(0, 0);
       if (n_kt > 1) load_k(1, 1);
+    } else {
+      load_v(0, 0);
     }
     lds_loads_barrier();
-    scores(0, S);
-    softmax(0, S, P);
+    scores(0, SA);
     __syncthreads();  // every wave is done with K0
     if (grpB) {
       if (n_kt > 2) load_k(2, 0);
-      if (n_kt > 1) load_v(1, 1);
       lds_loads_barrier();
     }
-    for (int t = 0; t < n_kt; ++t) {
-      // MFMA phase: P*V of tile t, scores of tile t+1
-      pv(t & 1, P);
-      if (t + 1 < n_kt) scores((t + 1) & 1, S);
-      if (grpB) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads of the last softmax phase
+    // S-phase(t) / P-phase(t); Sc holds the scores of tile t, Sn receives
+    // those of tile t+1.
+    auto tile = [&](int t, floatx16 (&Sc)[2], floatx16 (&Sn)[2]) {
+      float rsum;
+      if (t + 1 < n_kt && !needs_mask(t)) {
+        rsum = scores_probs((t + 1) & 1, Sn, Sc, P);
+      } else {
+        if (t + 1 < n_kt) scores((t + 1) & 1, Sn);
+        if (needs_mask(t)) apply_mask(t, Sc);
+        rsum = probs(Sc, P);
+      }
+      finish(Sc, P, rsum);
+      // this wave's loads from its last P-phase land before the barrier
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      // softmax phase for tile t+1; group B loads K(t+3) and V(t+2)
       if (grpB) {
         if (t + 3 < n_kt) load_k(t + 3, (t + 1) & 1);
-        if (t + 2 < n_kt) load_v(t + 2, t & 1);
+      } else {
+        if (t + 1 < n_kt) load_v(t + 1, (t + 1) & 1);
       }
-      if (t + 1 < n_kt) softmax(t + 1, S, P);
+      pv_phase(t & 1, P);
       __syncthreads();
+    };
+    int t = 0;
+    for (; t + 1 < n_kt; t += 2) {
+      tile(t, SA, SB);
+      tile(t + 1, SB, SA);
     }
+    if (t < n_kt) tile(t, SA, SB);
     if (!grpB) __syncthreads();  // group A matches group B's extra barrier
   }
   epilogue<DT, true>(a, it, qi, hh, O, m_run, l_part);
 }
 
-// LDS bytes of the bf16 kernel (two K and two V^T tiles of 64 keys).
-constexpr size_t bf16_lds_bytes(int D) { return (size_t)2 * (64 * D + D * 64) * 2; }
+// LDS bytes of the bf16 kernel (two padded K and two padded V^T tiles).
+constexpr size_t bf16_lds_bytes(int D) { return (size_t)2 * (64 * (D / 8 + 1) * 16 + D * 9 * 16); }
 
 // ---------------------------------------------------------------------------
 // fp32 kernel: 32-key tiles, MFMA 32x32x2 f32, V row-major.
