@@ -235,15 +235,66 @@ __device__ __forceinline__ void lds_loads_barrier() {
   __syncthreads();
 }
 
+// 32-bit LDS address of a pointer into this workgroup's LDS.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Explicitly ordered LDS operand stream. The compiler keeps at most one or
+// two operand reads in flight ahead of the MFMAs (it recycles one register
+// set and drains the LDS counter); issuing the reads here, into a ring of
+// registers, with an explicit wait before each use keeps several in flight.
+// The wait names the register it guards, so its consumer cannot be moved
+// above it.
+template <int OFF>
+__device__ __forceinline__ bf16x8 ds_read16(unsigned addr) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(bf16x8& r) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N) : "memory");
+}
+
+// P*V operand stream of one 64-key tile: MFMA i (i = 0 .. 4*DT-1) takes
+// u = i / DT (16-key step) and d tile T = i % DT; its V^T operand sits at
+// byte offset T*32*VROW + u*32 from the lane's base address. Reads run PF
+// ahead of the MFMAs in a ring of PF registers.
+template <int D, int VROW>
+struct PvStream {
+  static constexpr int DT = D / 32, N = 4 * DT, PF = 4;
+  static_assert(N >= PF, "fewer operands than reads in flight");
+  static constexpr int off(int i) { return (i % DT) * 32 * VROW + (i / DT) * 32; }
+  template <int I>
+  static __device__ __forceinline__ void step(unsigned va, bf16x8 (&vr)[PF], floatx16 (&O)[DT],
+                                              const bf16x8 (&P)[4]) {
+    // reads issued after read I at this point: min(PF - 1, N - 1 - I)
+    lds_wait<(N - 1 - I < PF - 1) ? (N - 1 - I) : (PF - 1)>(vr[I % PF]);
+    O[I % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[I % PF], P[I / DT], O[I % DT], 0, 0, 0);
+    if constexpr (I + PF < N) vr[I % PF] = ds_read16<off(I + PF)>(va);
+    if constexpr (I + 1 < N) step<I + 1>(va, vr, O, P);
+  }
+  template <int I>
+  static __device__ __forceinline__ void prefetch(unsigned va, bf16x8 (&vr)[PF]) {
+    vr[I] = ds_read16<off(I)>(va);
+    if constexpr (I + 1 < PF) prefetch<I + 1>(va, vr);
+  }
+  static __device__ __forceinline__ void run(unsigned va, floatx16 (&O)[DT], const bf16x8 (&P)[4]) {
+    bf16x8 vr[PF];
+    prefetch<0>(va, vr);
+    step<0>(va, vr, O, P);
+  }
+};
+
 // Two-group schedule. A workgroup is 8 waves: group A (waves 0-3) and group B
 // (waves 4-7), one wave of each on every SIMD. Each wave alternates
 //   S-phase(t): softmax of tile t (VALU) and the score MFMAs of tile t+1,
 //   P-phase(t): the P*V MFMAs of tile t,
 // with a workgroup barrier after every phase; group B runs one barrier behind
 // group A. On every SIMD both waves therefore issue LDS-fed MFMAs in every
-// interval (a single wave streaming one LDS operand per MFMA runs at about
-// half the MFMA rate; two waves come close to it), and one of them also
-// issues the softmax. The direct tile loads are issued in the P-phases --
+// interval, and one of them also issues the softmax; that wave runs at raised
+// issue priority. The direct tile loads are issued in the P-phases --
 // group A loads V^T, group B loads K -- and drained before the barrier that
 // ends the same wave's next S-phase; K and V^T each have two LDS buffers.
 template <int D>
@@ -354,27 +405,11 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs 
         S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[s2], S[t], 0, 0, 0);
       }
   };
-  // P*V of the tile in V buffer vbuf: 16 MFMAs, each with one 16-byte LDS
-  // operand read, scheduled as a pipeline with PF reads in flight.
+  // P*V of the tile in V buffer vbuf: 4*DT MFMAs (u-major, so the DT
+  // accumulators alternate), each fed by one 16-byte V^T read, with reads kept
+  // in flight in a register ring.
   auto pv_phase = [&](int vbuf, const bf16x8 (&P)[4]) {
-    constexpr int NPV = 4 * DT;
-    constexpr int PF = 4;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int T = 0; T < DT; ++T) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vs + vbuf * VBUF + v_rbase +
-                                                           T * 32 * VROW + u * 32);
-        O[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[u], O[T], 0, 0, 0);
-      }
-    // scheduling pattern (0x100: LDS read, 0x008: MFMA)
-    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
-#pragma unroll
-    for (int i = 0; i < NPV - PF; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+    PvStream<D, VROW>::run(lds_addr(Vs) + vbuf * VBUF + v_rbase, O, P);
   };
   // Tiles that cross the causal diagonal or the ragged end of the block.
   auto needs_mask = [&](int kt) -> bool {
@@ -480,6 +515,10 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs 
     // S-phase(t) / P-phase(t); Sc holds the scores of tile t, Sn receives
     // those of tile t+1.
     auto tile = [&](int t, floatx16 (&Sc)[2], floatx16 (&Sn)[2]) {
+      // The S-phase wave (MFMAs plus the softmax VALU stream) is the longer
+      // of the two on a SIMD; raising its issue priority lets the P-phase
+      // wave's MFMAs fill the matrix pipe around it instead of delaying it.
+      __builtin_amdgcn_s_setprio(1);
       float rsum;
       if (t + 1 < n_kt && !needs_mask(t)) {
         rsum = scores_probs((t + 1) & 1, Sn, Sc, P);
@@ -489,6 +528,7 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs 
         rsum = probs(Sc, P);
       }
       finish(Sc, P, rsum);
+      __builtin_amdgcn_s_setprio(0);
       // this wave's loads from its last P-phase land before the barrier
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
