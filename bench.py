@@ -33,6 +33,41 @@ PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
+# Hardware byte counts of the attention kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE
+# passes, scaled by a plain-copy calibration) live in this summary; they are
+# reported only while the kernel sources still hash to what was profiled.
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_bf16_gqa128k_pmc.txt")
+KERNEL_SOURCES = ("attn_fwd.hip", "ra_internal.h", "api.cpp")
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "ring_context_parallelism_flash_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per attention launch from the committed counter summary, or
+    (None, reason) when it does not describe this workload or these sources."""
+    try:
+        kv = {}
+        with open(PMC_SUMMARY) as f:
+            for line in f:
+                if line.startswith("@ ") and "=" in line:
+                    key, val = line[2:].split("=", 1)
+                    kv[key.strip()] = val.strip()
+        if kv.get("workload") != workload_name:
+            return None, "no counter summary for this workload"
+        if kv.get("sources_sha256") != kernel_sources_sha256():
+            return None, "kernel sources changed since the counters were taken"
+        return int(float(kv["traffic_bytes_per_launch"])), PMC_SUMMARY[len(ROOT) + 1:]
+    except (OSError, KeyError, ValueError) as e:
+        return None, f"counter summary unreadable: {e}"
+
+
 def useful_pairs(S: int, causal: bool) -> int:
     """Allowed (query, key) pairs of one head over the whole sequence."""
     return S * (S + 1) // 2 if causal else S * S
@@ -173,6 +208,7 @@ def main(argv=None) -> int:
     del dst, mo, ml, mob, mlb
 
     achieved = k_flops / (k_ms / 1e3) / 1e12 if k_ms > 0 else 0.0
+    traffic, traffic_src = measured_traffic(w.name)
     bf16 = w.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_MFMA_TFLOPS
     line = {
@@ -199,7 +235,9 @@ def main(argv=None) -> int:
             "peak": round(peak, 1),
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_unit": "HBM bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
+            "traffic_source": traffic_src,
             "launches_per_step": launches // max(args.steps, 1),
             "avg_launch_ms": round(k_ms / max(launches, 1), 4),
             "flops_per_launch": k_flops / max(launches, 1),

@@ -52,7 +52,7 @@ typedef enum {
   RA_ERR_UNSUPPORTED = 4, /* valid but not implemented (e.g. D not 64 or 128) */
   RA_ERR_ALIGN = 5,       /* pointer misaligned (16 B for tensors, 4 B lse)    */
   RA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required          */
-  RA_ERR_ARG = 7,         /* other invalid value (scale not finite, flags)    */
+  RA_ERR_ARG = 7,         /* other invalid value (scale not finite / <= 0)    */
   RA_ERR_HIP = 8          /* a HIP runtime call failed; see ra_last_error()   */
 } ra_status;
 
@@ -106,8 +106,9 @@ const char* ra_last_error(void);
  *
  * q: [B,Hq,Cq,D]; k, v: [B,Hkv,Ck,D], all of `dtype`, 16-byte aligned.
  * out: float32 [B,Hq,Cq,D] (16-byte aligned); lse: float32 [B,Hq,Cq].
- * D must be 64 or 128. scale must be finite (pass 1/sqrt(D) for standard
- * attention). workspace: device scratch of at least
+ * D must be 64 or 128. scale must be finite and > 0 (pass 1/sqrt(D) for
+ * standard attention; the kernels track the exponent reference on unscaled
+ * scores, which preserves their order only for a positive scale). workspace: device scratch of at least
  * ra_block_attn_workspace_bytes(...) bytes, 256-byte aligned (may be NULL
  * when that size is 0); it is clobbered. Cq = 0 or Ck = 0 are valid (a block
  * with no keys is the identity for accumulate = 1).
