@@ -6,5 +6,5 @@ package. It does not import the HIP library and the library does not import it.
 from .fp64 import (  # noqa: F401
     NEG_INF, attention, contiguous_order, layout_order, merge, pairs_per_rank_step,
     permute_rows, rank_positions, ring_attention, ring_schedule, ring_source,
-    to_f64, unpermute_rows, useful_flops, useful_pairs, zigzag_order,
+    striped_order, to_f64, unpermute_rows, useful_flops, useful_pairs, zigzag_order,
 )

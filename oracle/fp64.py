@@ -18,7 +18,8 @@ Sources (cited by page title and section):
         Parallelism" -- the 4-GPU ring-topology figure, "Algorithmic
         Mechanics" (partitioning into P blocks of s/P, source (i-k) mod P,
         the online-softmax equations for m_new, l_new, O_new) and "Causal
-        Masking and Load Balancing" (position i attends to j <= i).
+        Masking and Load Balancing" (position i attends to j <= i; striped
+        partitioning gives token t to rank t mod P).
   [SCP] "Sequence and Context Parallelism" (praveentn.live): section "What it
         does not change" (the result is identical to single-device attention).
 
@@ -32,7 +33,8 @@ Readings taken where the pages are silent or garbled:
     sum_j exp(s_j - m_block) v_j; that is the reading used in
     ``ring_attention`` and ``merge``;
   * GQA: query head h reads KV head h // (Hq / Hkv) unless a map is given;
-  * zigzag keeps a rank's early chunk first in its memory.
+  * zigzag keeps a rank's early chunk first in its memory;
+  * striped: rank r holds positions r, r+N, r+2N, ... in increasing order.
 """
 from __future__ import annotations
 
@@ -151,11 +153,29 @@ def zigzag_order(S: int, N: int) -> np.ndarray:
     return order
 
 
+def striped_order(S: int, N: int) -> np.ndarray:
+    """Sequence positions in rank-major memory order for the striped split
+    [SP "Causal Masking and Load Balancing"]: token t goes to rank t mod N, and
+    each rank keeps its tokens in sequence order."""
+    if S % N:
+        raise ValueError("S must be divisible by N")
+    order = np.empty(S, dtype=np.int64)
+    p = 0
+    for r in range(N):
+        for t in range(S):
+            if t % N == r:
+                order[p] = t
+                p += 1
+    return order
+
+
 def layout_order(S: int, N: int, layout: str) -> np.ndarray:
     if layout == "contiguous":
         return contiguous_order(S, N)
     if layout == "zigzag":
         return zigzag_order(S, N)
+    if layout == "striped":
+        return striped_order(S, N)
     raise ValueError(f"unknown layout {layout!r}")
 
 

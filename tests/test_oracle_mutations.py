@@ -66,6 +66,8 @@ def _check_layouts(m):
         assert list(m.rank_positions(16, 4, "zigzag", r)) == exp
     order = m.zigzag_order(64, 4)
     assert sorted(order.tolist()) == list(range(64))
+    for r, exp in enumerate(fx["striped_S16_N4_rank_positions"]):
+        assert list(m.rank_positions(16, 4, "striped", r)) == exp
 
 
 def _check_schedule(m):
@@ -77,7 +79,7 @@ def _check_schedule(m):
 
 def _check_ring_exact(m):
     q, k, v = _rand((1, 2, 32, 8), 4), _rand((1, 1, 32, 8), 5), _rand((1, 1, 32, 8), 6)
-    for layout in ("contiguous", "zigzag"):
+    for layout in ("contiguous", "zigzag", "striped"):
         ref = good.attention(q, k, v, causal=True)   # the pinned, unmutated definition
         out, lse = m.ring_attention(q, k, v, N=4, layout=layout, causal=True)
         np.testing.assert_allclose(out, ref[0], atol=1e-10)
@@ -112,6 +114,7 @@ MUTATIONS = {
     "zigzag_late_first": ("for chunk in (i, 2 * N - 1 - i):", "for chunk in (2 * N - 1 - i, i):"),
     "zigzag_wrong_pair": ("for chunk in (i, 2 * N - 1 - i):", "for chunk in (i, 2 * N - 2 - i):"),
     "ring_direction": ("return (rank - step) % N", "return (rank + step) % N"),
+    "striped_rank_offset": ("if t % N == r:", "if (t + 1) % N == r:"),
     "update_drops_rescale": ("l_new = l_prev * a + l_blk * b", "l_new = l_prev * a + l_blk"),
     "update_sign": ("a = np.where(m_prev > NEG_INF, np.exp(m_prev - m_ref), 0.0)",
                     "a = np.where(m_prev > NEG_INF, np.exp(m_ref - m_prev), 0.0)"),

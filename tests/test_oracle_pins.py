@@ -7,7 +7,7 @@ Each test names the pin it implements:
   closed   -- closed forms (equal keys, zero queries, single key)
   exact    -- the fp64 ring equals full attention (the pages' exactness claim)
   causal   -- perturbing keys after position i leaves row i unchanged
-  layout   -- zigzag / contiguous assignment, with the pages' examples
+  layout   -- zigzag / contiguous / striped assignment, with the pages' examples
   work     -- masked-in work per rank: brute force vs closed form
   merge    -- merge algebra against attention over the union of key sets
   schedule -- the 4-GPU ring figure
@@ -170,7 +170,7 @@ def test_closed_scale_shift():
 
 
 # ------------------------------------------------------------------- exact
-@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag", "striped"])
 @pytest.mark.parametrize("N,S,causal,Hq,Hkv", [
     (4, 64, True, 2, 2), (4, 64, False, 2, 2), (2, 24, True, 4, 1),
     (8, 128, True, 4, 2), (1, 16, True, 1, 1), (3, 36, True, 3, 3),
@@ -246,6 +246,8 @@ def test_layout_examples_from_page():
     for N, S, key in ((2, 8, "zigzag_S8_N2_rank_positions"), (4, 16, "zigzag_S16_N4_rank_positions")):
         for r, expected in enumerate(fx[key]):
             assert list(oracle.rank_positions(S, N, "zigzag", r)) == expected
+    for r, expected in enumerate(fx["striped_S16_N4_rank_positions"]):
+        assert list(oracle.rank_positions(16, 4, "striped", r)) == expected
     first, last = fx["contiguous_S8192_N8_rank0_first_last"]
     p = oracle.rank_positions(8192, 8, "contiguous", 0)
     assert p[0] == first and p[-1] == last and len(p) == 1024
@@ -268,6 +270,19 @@ def test_layout_zigzag_properties(S, N):
     assert np.array_equal(oracle.unpermute_rows(oracle.permute_rows(x, order, 1), order, 1), x)
 
 
+@pytest.mark.parametrize("S,N", [(64, 4), (96, 3), (40, 8), (32, 32), (12, 1)])
+def test_layout_striped_properties(S, N):
+    """Brute force from the page's rule: token t lives on rank t mod N."""
+    order = oracle.striped_order(S, N)
+    assert sorted(order.tolist()) == list(range(S))
+    C = S // N
+    for r in range(N):
+        pos = order[r * C:(r + 1) * C]
+        assert pos.tolist() == [t for t in range(S) if t % N == r]
+    x = _rand((2, S, 3), 35)
+    assert np.array_equal(oracle.unpermute_rows(oracle.permute_rows(x, order, 1), order, 1), x)
+
+
 # -------------------------------------------------------------------- work
 @pytest.mark.parametrize("S,N", [(64, 4), (128, 8), (48, 2), (96, 3)])
 def test_work_per_rank_closed_forms(S, N):
@@ -281,6 +296,20 @@ def test_work_per_rank_closed_forms(S, N):
     assert zz.sum() == co.sum() == S * (S + 1) // 2
     nc = oracle.pairs_per_rank_step(S, N, "zigzag", False)
     assert np.all(nc == C * C)
+
+
+@pytest.mark.parametrize("S,N", [(64, 4), (128, 8), (48, 2), (96, 3)])
+def test_work_striped_closed_forms(S, N):
+    """Striped: rank r against source s holds C(C+1)/2 allowed pairs per head if
+    s <= r, else C(C-1)/2; rank r's total is C(r+1) + N C(C-1)/2."""
+    C = S // N
+    st = oracle.pairs_per_rank_step(S, N, "striped", True)
+    for r in range(N):
+        for k in range(N):
+            s_ = oracle.ring_source(r, k, N)
+            assert st[r, k] == (C * (C + 1) // 2 if s_ <= r else C * (C - 1) // 2)
+    assert list(st.sum(1)) == [C * (r + 1) + N * C * (C - 1) // 2 for r in range(N)]
+    assert st.sum() == S * (S + 1) // 2
 
 
 def test_work_counts_s64_n4():
