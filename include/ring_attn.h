@@ -59,22 +59,27 @@ typedef enum {
 typedef enum { RA_BF16 = 0, RA_F32 = 1 } ra_dtype;
 
 /* Sequence layouts [SP "Algorithmic Mechanics" item 1; CP "The causal
- * imbalance"]. CONTIGUOUS: rank r holds tokens [r*C, (r+1)*C), C = S/N.
- * ZIGZAG: the sequence is cut into 2N chunks of c = S/(2N); rank r holds
- * chunks r and 2N-1-r, the early chunk first in its memory. */
-typedef enum { RA_CONTIGUOUS = 0, RA_ZIGZAG = 1 } ra_layout;
+ * imbalance"; SP "Causal Masking and Load Balancing"]. CONTIGUOUS: rank r
+ * holds tokens [r*C, (r+1)*C), C = S/N. ZIGZAG: the sequence is cut into 2N
+ * chunks of c = S/(2N); rank r holds chunks r and 2N-1-r, the early chunk
+ * first in its memory. STRIPED: token t goes to rank t mod N; rank r holds
+ * tokens r, r+N, r+2N, ... in sequence order. */
+typedef enum { RA_CONTIGUOUS = 0, RA_ZIGZAG = 1, RA_STRIPED = 2 } ra_layout;
 
 /* Global sequence positions of the rows of one block: row t (0 <= t < rows)
- * sits at position start[t / seg_len] + (t % seg_len). nseg is 1 or 2 and
- * nseg * seg_len must equal the block's row count. With nseg = 2,
- * start[1] >= start[0] + seg_len (positions increase with t). This is the
- * "source" of the pages' flash_block call generalised to any block: a
- * contiguous rank is {1, C, {r*C}}, a zigzag rank is
- * {2, c, {r*c, (2N-1-r)*c}}. A NULL ra_pos means {1, rows, {0}}. */
+ * sits at position start[t / seg_len] + (t % seg_len) * stride. nseg is 1 or
+ * 2 and nseg * seg_len must equal the block's row count; stride >= 1 (0 is
+ * read as 1, so a zero-initialised field keeps the unit-stride meaning).
+ * With nseg = 2, start[1] > start[0] + (seg_len - 1) * stride (positions
+ * increase with t). All positions must be below 2^31. This is the "source"
+ * of the pages' flash_block call generalised to any block: a contiguous rank
+ * is {1, C, {r*C}, 1}, a zigzag rank is {2, c, {r*c, (2N-1-r)*c}, 1}, a
+ * striped rank is {1, C, {r}, N}. A NULL ra_pos means {1, rows, {0}, 1}. */
 typedef struct {
   int32_t nseg;
   int64_t seg_len;
   int64_t start[2];
+  int64_t stride;
 } ra_pos;
 
 /* Human-readable name of a status code (static string). */
@@ -163,6 +168,24 @@ ra_status ra_zigzag_permute(const void* src, void* dst, int64_t outer, int64_t S
                             int64_t row_bytes, int32_t N, int32_t inverse, void* stream);
 
 /* ------------------------------------------------------------------------
+ * ra_striped_permute -- sequence order <-> striped rank-major order.
+ *
+ * [SP "Causal Masking and Load Balancing": striped partitioning assigns
+ *  token t to rank t mod N.]
+ *
+ * src and dst are [outer, S, row_bytes] byte arrays as for ra_zigzag_permute.
+ * With C = S/N, the rank-major index p = r*C + i holds sequence position
+ * i*N + r (rank r's tokens in sequence order).
+ * inverse = 0: dst[rank-major p] = src[sequence position of p] (gather).
+ * inverse = 1: dst[sequence position of p] = src[rank-major p] (scatter).
+ * The copy is bit-exact. S must be divisible by N; src and dst must not
+ * overlap. Any alignment is accepted; 16-byte aligned rows are copied with
+ * 16-byte accesses.
+ * ---------------------------------------------------------------------- */
+ra_status ra_striped_permute(const void* src, void* dst, int64_t outer, int64_t S,
+                             int64_t row_bytes, int32_t N, int32_t inverse, void* stream);
+
+/* ------------------------------------------------------------------------
  * ra_ring_sim_fwd -- the whole N-rank ring, simulated on one GPU.
  *
  * [CP listing ring_attention(q, k, v, group) and "Ring attention"; SP figure
@@ -174,8 +197,9 @@ ra_status ra_zigzag_permute(const void* src, void* dst, int64_t outer, int64_t S
  * q: [B,Hq,S,D], k, v: [B,Hkv,S,D] of `dtype`; out: [B,Hq,S,D] of `dtype`;
  * lse: float32 [B,Hq,S]. The sequence axis is in RANK-MAJOR order: rank r's
  * C = S/N rows are rows [r*C, (r+1)*C). For RA_CONTIGUOUS that is sequence
- * order; for RA_ZIGZAG apply ra_zigzag_permute(inverse=0) to q, k, v before
- * and ra_zigzag_permute(inverse=1) to out and lse after.
+ * order; for RA_ZIGZAG (RA_STRIPED) apply ra_zigzag_permute
+ * (ra_striped_permute) with inverse=0 to q, k, v before and with inverse=1
+ * to out and lse after.
  *
  * For every virtual rank r = 0..N-1 and step k = 0..N-1 the driver attends
  * rank r's queries to the KV block of rank (r - k) mod N, masked by global

@@ -17,23 +17,25 @@ import torch
 __all__ = [
     "RAError", "lib", "library_path", "RA_BF16", "RA_F32", "RA_CONTIGUOUS", "RA_ZIGZAG",
     "ra_pos", "ra_status_str", "ra_last_error", "ra_block_attn_workspace_bytes",
-    "ra_block_attn_fwd", "ra_lse_merge", "ra_zigzag_permute", "ra_ring_sim_workspace_bytes",
+    "ra_block_attn_fwd", "ra_lse_merge", "ra_zigzag_permute", "ra_striped_permute",
+    "ra_ring_sim_workspace_bytes",
     "ra_ring_sim_fwd", "ra_kernel_timing_enable", "ra_kernel_timing_read", "zigzag_pos",
-    "contiguous_pos", "ring_attention_sim", "EXPORTS",
+    "contiguous_pos", "striped_pos", "ring_attention_sim", "EXPORTS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libringattn.so")
 
 RA_BF16, RA_F32 = 0, 1
-RA_CONTIGUOUS, RA_ZIGZAG = 0, 1
+RA_CONTIGUOUS, RA_ZIGZAG, RA_STRIPED = 0, 1, 2
 _DTYPES = {torch.bfloat16: RA_BF16, torch.float32: RA_F32}
-_LAYOUTS = {"contiguous": RA_CONTIGUOUS, "zigzag": RA_ZIGZAG}
+_LAYOUTS = {"contiguous": RA_CONTIGUOUS, "zigzag": RA_ZIGZAG, "striped": RA_STRIPED}
 
 # Every symbol include/ring_attn.h declares.
 EXPORTS = (
     "ra_status_str", "ra_last_error", "ra_block_attn_workspace_bytes", "ra_block_attn_fwd",
-    "ra_lse_merge", "ra_zigzag_permute", "ra_ring_sim_workspace_bytes", "ra_ring_sim_fwd",
+    "ra_lse_merge", "ra_zigzag_permute", "ra_striped_permute", "ra_ring_sim_workspace_bytes",
+    "ra_ring_sim_fwd",
     "ra_kernel_timing_enable", "ra_kernel_timing_read",
 )
 
@@ -46,7 +48,7 @@ class RAError(RuntimeError):
 
 class ra_pos(ctypes.Structure):
     _fields_ = [("nseg", ctypes.c_int32), ("seg_len", ctypes.c_int64),
-                ("start", ctypes.c_int64 * 2)]
+                ("start", ctypes.c_int64 * 2), ("stride", ctypes.c_int64)]
 
 
 _lib = None
@@ -77,6 +79,8 @@ def lib() -> ctypes.CDLL:
                                    c_void_p]),
         "ra_zigzag_permute": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int32,
                                         c_int32, c_void_p]),
+        "ra_striped_permute": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int32,
+                                         c_int32, c_void_p]),
         "ra_ring_sim_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int64, c_int32,
                                                    c_int32, c_int32]),
         "ra_ring_sim_fwd": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -121,12 +125,13 @@ def _stream(s):
 
 
 def _pos(p):
-    """None, an ra_pos, or a tuple (nseg, seg_len, start0[, start1])."""
+    """None, an ra_pos, or a tuple (nseg, seg_len, start0[, start1[, stride]])."""
     if p is None or isinstance(p, ra_pos):
         return p
-    nseg, seg_len, *starts = p
-    starts = list(starts) + [0] * (2 - len(starts))
-    return ra_pos(nseg, seg_len, (ctypes.c_int64 * 2)(*starts))
+    nseg, seg_len, *rest = p
+    rest = list(rest) + [0] * (3 - len(rest))
+    start0, start1, stride = rest[:3]
+    return ra_pos(nseg, seg_len, (ctypes.c_int64 * 2)(start0, start1), stride or 1)
 
 
 def _kvmap(m, Hq):
@@ -152,6 +157,10 @@ def contiguous_pos(S: int, N: int, rank: int):
 def zigzag_pos(S: int, N: int, rank: int):
     c = S // (2 * N)
     return (2, c, rank * c, (2 * N - 1 - rank) * c)
+
+
+def striped_pos(S: int, N: int, rank: int):
+    return (1, S // N, rank, 0, N)
 
 
 # ------------------------------------------------------------------ entry points
@@ -201,6 +210,20 @@ def ra_zigzag_permute(src, dst, N, inverse=False, seq_dim=-2, stream=None):
     _check(lib().ra_zigzag_permute(_ptr(src), _ptr(dst), outer, S, row_bytes, N,
                                    int(bool(inverse)), _stream(stream)))
     return dst
+
+
+def ra_striped_permute(src, dst, N, inverse=False, seq_dim=-2, stream=None):
+    """Striped permute along ``seq_dim`` (-2 for [..., S, D], -1 for lse [..., S])."""
+    seq_dim = seq_dim % src.dim()
+    S = src.shape[seq_dim]
+    outer = math.prod(src.shape[:seq_dim])
+    row_bytes = math.prod(src.shape[seq_dim + 1:]) * src.element_size()
+    _check(lib().ra_striped_permute(_ptr(src), _ptr(dst), outer, S, row_bytes, N,
+                                    int(bool(inverse)), _stream(stream)))
+    return dst
+
+
+_PERMUTES = {"zigzag": ra_zigzag_permute, "striped": ra_striped_permute}
 
 
 def ra_ring_sim_workspace_bytes(B, Hq, Hkv, S, D, dtype, N) -> int:
@@ -257,17 +280,18 @@ class RingRunner:
         self.out_rm = torch.empty((B, Hq, S, D), dtype=dtype, device=dev)
         self.lse_rm = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
         self.copy_stream = torch.cuda.Stream(device=dev) if copy_stream else None
-        if layout == "zigzag":
+        if layout in _PERMUTES:
             self.q_rm = torch.empty((B, Hq, S, D), dtype=dtype, device=dev)
             self.k_rm = torch.empty((B, Hkv, S, D), dtype=dtype, device=dev)
             self.v_rm = torch.empty((B, Hkv, S, D), dtype=dtype, device=dev)
 
     def permute_inputs(self, q, k, v):
-        if self.layout != "zigzag":
+        perm = _PERMUTES.get(self.layout)
+        if perm is None:
             return q, k, v
-        ra_zigzag_permute(q, self.q_rm, self.N)
-        ra_zigzag_permute(k, self.k_rm, self.N)
-        ra_zigzag_permute(v, self.v_rm, self.N)
+        perm(q, self.q_rm, self.N)
+        perm(k, self.k_rm, self.N)
+        perm(v, self.v_rm, self.N)
         return self.q_rm, self.k_rm, self.v_rm
 
     def ring(self, q_rm, k_rm, v_rm):
@@ -277,12 +301,13 @@ class RingRunner:
                                copy_stream=self.copy_stream)
 
     def unpermute_outputs(self, out, lse):
-        if self.layout != "zigzag":
+        perm = _PERMUTES.get(self.layout)
+        if perm is None:
             out.copy_(self.out_rm)
             lse.copy_(self.lse_rm)
             return out, lse
-        ra_zigzag_permute(self.out_rm, out, self.N, inverse=True)
-        ra_zigzag_permute(self.lse_rm, lse, self.N, inverse=True, seq_dim=-1)
+        perm(self.out_rm, out, self.N, inverse=True)
+        perm(self.lse_rm, lse, self.N, inverse=True, seq_dim=-1)
         return out, lse
 
     def __call__(self, q, k, v, out, lse):

@@ -50,7 +50,7 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // Block positions as a PosDesc, with the validation rules of ra_pos.
 ra_status make_pos(const ra_pos* p, int64_t rows, const char* name, PosDesc& out) {
   if (p == nullptr) {
-    out = PosDesc{1, (int32_t)rows, 0, 0};
+    out = PosDesc{1, (int32_t)rows, 0, 0, 1};
     return RA_OK;
   }
   if (p->nseg != 1 && p->nseg != 2)
@@ -58,19 +58,25 @@ ra_status make_pos(const ra_pos* p, int64_t rows, const char* name, PosDesc& out
   if (p->seg_len < 1 || p->nseg * p->seg_len != rows)
     return fail(RA_ERR_SHAPE, "%s: nseg*seg_len (%d*%lld) must equal the row count %lld", name,
                 p->nseg, (long long)p->seg_len, (long long)rows);
+  const int64_t stride = p->stride == 0 ? 1 : p->stride;
+  if (stride < 1 || stride > INT32_MAX)
+    return fail(RA_ERR_SHAPE, "%s.stride must be in [1, 2^31-1] (got %lld)", name,
+                (long long)p->stride);
   if (p->start[0] < 0) return fail(RA_ERR_SHAPE, "%s.start[0] must be >= 0", name);
-  if (p->nseg == 2 && p->start[1] < p->start[0] + p->seg_len)
-    return fail(RA_ERR_SHAPE, "%s: start[1] must be >= start[0] + seg_len", name);
-  const int64_t last = p->start[p->nseg - 1] + p->seg_len - 1;
+  const int64_t span = (p->seg_len - 1) * stride;  // seg_len < 2^31 here (row count check)
+  if (p->start[0] > INT32_MAX || span > INT32_MAX)
+    return fail(RA_ERR_UNSUPPORTED, "%s: positions beyond 2^31-1", name);
+  if (p->nseg == 2 && p->start[1] <= p->start[0] + span)
+    return fail(RA_ERR_SHAPE, "%s: start[1] must exceed start[0] + (seg_len-1)*stride", name);
+  const int64_t last = p->start[p->nseg - 1] + span;
   if (last > INT32_MAX) return fail(RA_ERR_UNSUPPORTED, "%s: positions beyond 2^31-1", name);
   out = PosDesc{p->nseg, (int32_t)p->seg_len, (int32_t)p->start[0],
-                (int32_t)(p->nseg == 2 ? p->start[1] : 0)};
+                (int32_t)(p->nseg == 2 ? p->start[1] : 0), (int32_t)stride};
   return RA_OK;
 }
 
-int64_t pos_at(const PosDesc& p, int64_t t) {
-  return (p.nseg == 2 && t >= p.seg) ? p.start1 + (t - p.seg) : p.start0 + t;
-}
+// floor(a / b) for b > 0
+inline int64_t floordiv(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 
 // Allowed (query, key) pairs between two position descriptors (per head).
 int64_t pairs_segment(int64_t a, int64_t La, int64_t b, int64_t Lb) {
@@ -98,9 +104,25 @@ int64_t pairs_between(const PosDesc& q, int64_t Cq, const PosDesc& k, int64_t Ck
     for (int sk = 0; sk < k.nseg; ++sk) {
       const int64_t a = sq == 0 ? q.start0 : q.start1, La = q.nseg == 1 ? Cq : q.seg;
       const int64_t b = sk == 0 ? k.start0 : k.start1, Lb = k.nseg == 1 ? Ck : k.seg;
-      total += pairs_segment(a, La, b, Lb);
+      if (q.stride == k.stride) {
+        // key j <= query i  <=>  j <= i + floor((a - b) / stride)
+        total += pairs_segment(floordiv(a - b, q.stride), La, 0, Lb);
+      } else {
+        for (int64_t i = 0; i < La; ++i)
+          total += std::clamp<int64_t>(floordiv(a + i * q.stride - b, k.stride) + 1, 0, Lb);
+      }
     }
   return total;
+}
+
+// First row of a block whose position is >= P (rows if none).
+int64_t first_row_at_or_after(const PosDesc& p, int64_t rows, int64_t P) {
+  const int64_t seg0 = p.nseg == 2 ? p.seg : rows;
+  const int64_t last0 = (int64_t)p.start0 + (seg0 - 1) * p.stride;
+  if (P <= last0) return std::max<int64_t>(0, -floordiv(-(P - p.start0), p.stride));
+  if (p.nseg == 2 && P <= (int64_t)p.start1 + (int64_t)(p.seg - 1) * p.stride)
+    return p.seg + std::max<int64_t>(0, -floordiv(-(P - p.start1), p.stride));
+  return rows;
 }
 
 // ---------------------------------------------------------------- timing
@@ -219,16 +241,7 @@ void fill_work(AttnArgs& a, ra_dtype dt, int32_t B, int32_t Hq, int64_t Cq,
   // of the ring, where every row still has to be written out.
   int32_t lo = 0;
   if (a.causal && a.accumulate && a.fin_out == nullptr) {
-    int64_t row = Cq;
-    if (a.Ck > 0) {
-      const int64_t kmin = a.kp.start0;
-      const PosDesc& p = a.qp;
-      const int64_t seg0 = p.nseg == 2 ? p.seg : Cq;
-      if (kmin <= (int64_t)p.start0 + seg0 - 1)
-        row = std::max<int64_t>(0, kmin - p.start0);
-      else if (p.nseg == 2 && kmin <= (int64_t)p.start1 + p.seg - 1)
-        row = p.seg + std::max<int64_t>(0, kmin - p.start1);
-    }
+    const int64_t row = a.Ck > 0 ? first_row_at_or_after(a.qp, Cq, a.kp.start0) : Cq;
     lo = (int32_t)(row / qtile);
   }
   a.qt_lo = lo;
@@ -291,7 +304,7 @@ ra_status ra_block_attn_fwd(const void* q, const void* k, const void* v, float* 
   if (Ck > 0) {
     if ((st = make_pos(k_pos, Ck, "k_pos", kp)) != RA_OK) return st;
   } else {
-    kp = PosDesc{1, 0, 0, 0};
+    kp = PosDesc{1, 0, 0, 0, 1};
   }
   const size_t need = ra_block_attn_workspace_bytes(B, Hkv, Ck, D, dtype);
   if (need > 0) {
@@ -374,6 +387,24 @@ ra_status ra_zigzag_permute(const void* src, void* dst, int64_t outer, int64_t S
   return RA_OK;
 }
 
+ra_status ra_striped_permute(const void* src, void* dst, int64_t outer, int64_t S, int64_t row_bytes,
+                             int32_t N, int32_t inverse, void* stream) {
+  g_err[0] = 0;
+  if (N < 1) return fail(RA_ERR_SHAPE, "N must be >= 1");
+  if (outer < 0 || S < 0 || row_bytes < 1) return fail(RA_ERR_SHAPE, "bad sizes");
+  if (S % N) return fail(RA_ERR_SHAPE, "S=%lld not divisible by N=%d", (long long)S, N);
+  if (inverse != 0 && inverse != 1) return fail(RA_ERR_ARG, "inverse must be 0 or 1");
+  if (outer == 0 || S == 0) return RA_OK;
+  if (!src || !dst) return fail(RA_ERR_NULL, "NULL pointer");
+  const uintptr_t bytes = (uintptr_t)outer * S * row_bytes;
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(RA_ERR_ARG, "src and dst overlap");
+  hipError_t e = launch_striped_permute(src, dst, outer, S, row_bytes, N, inverse,
+                                        reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "permute launch");
+  return RA_OK;
+}
+
 // Workspace of the ring: [V^T home blocks (bf16)] [2 KV slots] [fp32 running out]
 namespace {
 struct RingLayout {
@@ -413,7 +444,8 @@ ra_status ra_ring_sim_fwd(const void* q, const void* k, const void* v, void* out
   std::vector<uint8_t> kv_of, order;
   ra_status st = check_common(B, Hq, Hkv, D, dtype, kv_head_of_q, scale, kv_of, order);
   if (st != RA_OK) return st;
-  if (layout != RA_CONTIGUOUS && layout != RA_ZIGZAG) return fail(RA_ERR_ARG, "unknown layout");
+  if (layout != RA_CONTIGUOUS && layout != RA_ZIGZAG && layout != RA_STRIPED)
+    return fail(RA_ERR_ARG, "unknown layout");
   if (causal != 0 && causal != 1) return fail(RA_ERR_ARG, "causal must be 0 or 1");
   if (N < 1) return fail(RA_ERR_SHAPE, "N must be >= 1");
   if (S < 0) return fail(RA_ERR_SHAPE, "S must be >= 0");
@@ -456,9 +488,11 @@ ra_status ra_ring_sim_fwd(const void* q, const void* k, const void* v, void* out
     PosDesc p;
     if (layout == RA_ZIGZAG) {
       const int64_t c = S / (2 * N);
-      p = PosDesc{2, (int32_t)c, (int32_t)(r * c), (int32_t)((2 * N - 1 - r) * c)};
+      p = PosDesc{2, (int32_t)c, (int32_t)(r * c), (int32_t)((2 * N - 1 - r) * c), 1};
+    } else if (layout == RA_STRIPED) {
+      p = PosDesc{1, (int32_t)C, (int32_t)r, 0, (int32_t)N};
     } else {
-      p = PosDesc{1, (int32_t)C, (int32_t)(r * C), 0};
+      p = PosDesc{1, (int32_t)C, (int32_t)(r * C), 0, 1};
     }
     return p;
   };

@@ -45,7 +45,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ int pos_of(const PosDesc& p, int t) {
   const bool second = (p.nseg == 2) & (t >= p.seg);
-  return second ? p.start1 + (t - p.seg) : p.start0 + t;
+  return second ? p.start1 + (t - p.seg) * p.stride : p.start0 + t * p.stride;
 }
 
 // Score with the causal / ragged mask applied, as a select. The mask is
@@ -54,18 +54,18 @@ __device__ __forceinline__ int pos_of(const PosDesc& p, int t) {
 // accumulator vector was compiled into code that dropped the store.
 __device__ __forceinline__ float masked(float s, int key, int Ck, int causal, const PosDesc& kp,
                                         int qpos) {
-  const bool ok = (key < Ck) & ((causal == 0) | (pos_of(kp, key) <= qpos));
+  const bool ok = (key < Ck) & ((causal == 0) | (pos_of(kp, min(key, Ck - 1)) <= qpos));
   return ok ? s : -INFINITY;
 }
 
-__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // Number of keys whose position is <= P. Positions increase with the row
 // index, so these keys are a prefix of the block.
 __device__ __forceinline__ int allowed_prefix(const PosDesc& p, int P) {
-  int n = clampi(P - p.start0 + 1, 0, p.seg);
-  if (p.nseg == 2) n += clampi(P - p.start1 + 1, 0, p.seg);
-  return n;
+  // rows i < seg of a segment starting at s with s + i*stride <= P
+  const int n0 = P < p.start0 ? 0 : min((P - p.start0) / p.stride + 1, p.seg);
+  const int n1 = (p.nseg == 2 && P >= p.start1) ? min((P - p.start1) / p.stride + 1, p.seg) : 0;
+  return n0 + n1;
 }
 
 // Row of the K tile that feeds MFMA row m of a 32-key S^T tile (bf16 kernel).

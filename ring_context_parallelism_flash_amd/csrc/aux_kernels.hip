@@ -1,6 +1,6 @@
 // Memory-bound helper kernels: the V -> V^T block transpose that feeds the
 // bf16 attention kernel, the standalone log-sum-exp merge, and the zigzag
-// layout permute.
+// and striped layout permutes.
 #include <math.h>
 
 #include "ra_internal.h"
@@ -175,6 +175,76 @@ hipError_t launch_lse_merge(float* out, float* lse, const float* out_b, const fl
   const int64_t lblocks = (rows + 255) / 256;
   hipLaunchKernelGGL(lse_merge_lse_only, dim3((unsigned)(lblocks < 65536 ? lblocks : 65536)),
                      dim3(256), 0, s, lse, lse_b, rows);
+  return hipGetLastError();
+}
+
+// Striped permute [SP "Causal Masking and Load Balancing": token t on rank
+// t mod N]: rank-major row p = r*C + i of each [S]-row slab holds sequence row
+// i*N + r. Forward gathers (contiguous writes), inverse scatters (contiguous
+// reads). A block copies rpb whole rows at a time, one V-sized element per
+// thread when a row has at most 256 of them; longer rows are strided.
+template <typename V>
+__global__ __launch_bounds__(256) void striped_permute_kernel(const char* __restrict__ src,
+                                                              char* __restrict__ dst,
+                                                              int64_t rows_total, int64_t S, int N,
+                                                              int64_t C, int64_t row_vecs, int rpb,
+                                                              int inverse) {
+  const int t = threadIdx.x;
+  const int sub = rpb > 1 ? t / (int)row_vecs : 0;
+  const int e0 = rpb > 1 ? t - sub * (int)row_vecs : t;
+  if (sub >= rpb) return;  // no barriers below
+  for (int64_t g = (int64_t)blockIdx.x * rpb; g < rows_total; g += (int64_t)gridDim.x * rpb) {
+    const int64_t row = g + sub;
+    if (row >= rows_total) break;
+    const int64_t o = row / S, pr = row - o * S;
+    const int64_t r = pr / C, i = pr - r * C;
+    const int64_t seq = o * S + i * N + r;
+    const V* sp = reinterpret_cast<const V*>(src) + (inverse ? row : seq) * row_vecs;
+    V* dp = reinterpret_cast<V*>(dst) + (inverse ? seq : row) * row_vecs;
+    if (rpb > 1) {
+      dp[e0] = sp[e0];
+    } else {
+      for (int64_t e = e0; e < row_vecs; e += 256) dp[e] = sp[e];
+    }
+  }
+}
+
+hipError_t launch_striped_permute(const void* src, void* dst, int64_t outer, int64_t S,
+                                  int64_t row_bytes, int N, int inverse, hipStream_t s) {
+  const int64_t rows = outer * S;
+  if (rows == 0 || row_bytes == 0) return hipSuccess;
+  const uintptr_t al = (uintptr_t)src | (uintptr_t)dst | (uintptr_t)row_bytes;
+  int vb = 16;
+  while (vb > 1 && (al % vb)) vb >>= 1;
+  const int64_t row_vecs = row_bytes / vb;
+  const int rpb = row_vecs <= 256 ? (int)(256 / row_vecs) : 1;
+  const int64_t groups = (rows + rpb - 1) / rpb;
+  const dim3 grid((unsigned)(groups < 262144 ? groups : 262144));
+  const int64_t C = S / N;
+  const char* sp = reinterpret_cast<const char*>(src);
+  char* dp = reinterpret_cast<char*>(dst);
+  switch (vb) {
+    case 16:
+      hipLaunchKernelGGL(striped_permute_kernel<uint4>, grid, dim3(256), 0, s, sp, dp, rows, S, N,
+                         C, row_vecs, rpb, inverse);
+      break;
+    case 8:
+      hipLaunchKernelGGL(striped_permute_kernel<uint2>, grid, dim3(256), 0, s, sp, dp, rows, S, N,
+                         C, row_vecs, rpb, inverse);
+      break;
+    case 4:
+      hipLaunchKernelGGL(striped_permute_kernel<uint32_t>, grid, dim3(256), 0, s, sp, dp, rows, S,
+                         N, C, row_vecs, rpb, inverse);
+      break;
+    case 2:
+      hipLaunchKernelGGL(striped_permute_kernel<uint16_t>, grid, dim3(256), 0, s, sp, dp, rows, S,
+                         N, C, row_vecs, rpb, inverse);
+      break;
+    default:
+      hipLaunchKernelGGL(striped_permute_kernel<uint8_t>, grid, dim3(256), 0, s, sp, dp, rows, S,
+                         N, C, row_vecs, rpb, inverse);
+      break;
+  }
   return hipGetLastError();
 }
 

@@ -25,9 +25,10 @@ constexpr int kMaxHeads = 256;       // head maps travel in the kernel arguments
 constexpr int kXcds = 8;             // MI355X: 8 XCDs, workgroups dealt round-robin
 
 // Global positions of a block's rows: row t sits at
-// start0 + t (t < seg or nseg == 1) or start1 + (t - seg) (nseg == 2).
+// start0 + t*stride (t < seg or nseg == 1) or start1 + (t - seg)*stride
+// (nseg == 2). Positions increase with t and stay below 2^31.
 struct PosDesc {
-  int32_t nseg, seg, start0, start1;
+  int32_t nseg, seg, start0, start1, stride;
 };
 
 // Everything one attention launch needs. Strides are in elements; rows are
@@ -73,5 +74,8 @@ hipError_t launch_lse_merge(float* out, float* lse, const float* out_b, const fl
 
 hipError_t launch_zigzag_permute(const void* src, void* dst, int64_t outer, int64_t S,
                                  int64_t row_bytes, int N, int inverse, hipStream_t s);
+
+hipError_t launch_striped_permute(const void* src, void* dst, int64_t outer, int64_t S,
+                                  int64_t row_bytes, int N, int inverse, hipStream_t s);
 
 }  // namespace ra

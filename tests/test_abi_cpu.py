@@ -91,9 +91,17 @@ def test_block_attn_rejects_bad_positions_and_map():
     bad = [ra.ra_pos(3, 128, (ctypes.c_int64 * 2)(0, 0)),        # nseg
            ra.ra_pos(2, 60, (ctypes.c_int64 * 2)(0, 100)),       # 2*60 != 128
            ra.ra_pos(2, 64, (ctypes.c_int64 * 2)(0, 10)),        # overlapping segments
-           ra.ra_pos(1, 128, (ctypes.c_int64 * 2)(-5, 0))]       # negative start
+           ra.ra_pos(1, 128, (ctypes.c_int64 * 2)(-5, 0)),       # negative start
+           ra.ra_pos(1, 128, (ctypes.c_int64 * 2)(0, 0), -2),    # negative stride
+           ra.ra_pos(2, 64, (ctypes.c_int64 * 2)(0, 120), 2)]    # stride-2 segment 0 ends at 126
     for p in bad:
         assert ra.ra_status_str(_block(qp=ctypes.byref(p))) == "RA_ERR_SHAPE"
+    far = ra.ra_pos(1, 128, (ctypes.c_int64 * 2)(0, 0), 1 << 25)    # last position 127 * 2^25
+    assert ra.ra_status_str(_block(kp=ctypes.byref(far))) == "RA_ERR_UNSUPPORTED"
+    ok = [ra.ra_pos(2, 64, (ctypes.c_int64 * 2)(0, 127), 2),         # segment 0 ends at 126
+          ra.ra_pos(1, 128, (ctypes.c_int64 * 2)(3, 0), 0)]         # stride 0 reads as 1
+    for p in ok:   # valid positions: the call gets as far as the workspace check
+        assert ra.ra_status_str(_block(qp=ctypes.byref(p), dt=BF16)) == "RA_ERR_WORKSPACE"
     m = (ctypes.c_int32 * 2)(0, 2)  # kv head 2 of 2
     assert ra.ra_status_str(_block(kvmap=m)) == "RA_ERR_SHAPE"
 
@@ -115,6 +123,7 @@ def test_ring_rejects():
     assert ring(S=1028, layout=0) == "RA_ERR_WORKSPACE"  # divisible by N: ok until workspace
     assert ring(N=0) == "RA_ERR_SHAPE"
     assert ring(layout=5) == "RA_ERR_ARG"
+    assert ring(S=1020, layout=2) == "RA_ERR_WORKSPACE"  # striped: divisible by N suffices
     assert ring() == "RA_ERR_WORKSPACE"
     assert ring(S=0) == "RA_OK"
 
@@ -125,6 +134,11 @@ def test_permute_and_merge_reject():
     assert ra.ra_status_str(L.ra_zigzag_permute(FAKE, FAKE, 1, 1024, 2, 8, 0, None)) == "RA_ERR_ARG"
     assert ra.ra_status_str(L.ra_zigzag_permute(None, FAKE, 1, 1024, 2, 8, 0, None)) == "RA_ERR_NULL"
     assert ra.ra_status_str(L.ra_zigzag_permute(FAKE, FAKE, 1, 1024, 2, 8, 3, None)) == "RA_ERR_ARG"
+    assert ra.ra_status_str(L.ra_striped_permute(FAKE, FAKE, 1, 1001, 2, 8, 0, None)) == "RA_ERR_SHAPE"
+    assert ra.ra_status_str(L.ra_striped_permute(FAKE, FAKE, 1, 1000, 2, 8, 0, None)) == "RA_ERR_ARG"
+    assert ra.ra_status_str(L.ra_striped_permute(None, FAKE, 1, 1000, 2, 8, 0, None)) == "RA_ERR_NULL"
+    assert ra.ra_status_str(L.ra_striped_permute(FAKE, FAKE, 1, 1000, 2, 0, 0, None)) == "RA_ERR_SHAPE"
+    assert L.ra_striped_permute(None, None, 0, 1000, 2, 8, 0, None) == 0
     assert ra.ra_status_str(L.ra_lse_merge(None, FAKE, FAKE, FAKE, 10, 4, None)) == "RA_ERR_NULL"
     assert ra.ra_status_str(L.ra_lse_merge(FAKE, FAKE, FAKE, FAKE, 10, 0, None)) == "RA_ERR_SHAPE"
     assert L.ra_lse_merge(None, None, None, None, 0, 4, None) == 0

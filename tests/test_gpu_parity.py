@@ -2,7 +2,8 @@
 
 Tolerances: bf16 inputs (fp32 accumulation) out max-abs <= 2e-2, mean-abs <=
 2e-3, lse max-abs <= 1e-3; fp32 inputs <= 1e-4; the zigzag permute and
-the masked-row / empty-block identities are bit-exact.
+the masked-row / empty-block identities are bit-exact. The striped layout
+(token t on rank t mod N) is covered by its own permute, block and ring cases.
 """
 import math
 import os
@@ -26,13 +27,16 @@ def _rnd(shape, seed, dtype, scale=1.0):
 
 
 def _pos_array(desc, rows):
+    """Positions of a (nseg, seg_len, start0[, start1[, stride]]) descriptor."""
     if desc is None:
         return np.arange(rows)
-    nseg, seg, *starts = desc
+    nseg, seg, *rest = desc
+    rest = list(rest) + [0] * (3 - len(rest))
+    s0, s1, stride = rest[0], rest[1], rest[2] or 1
     t = np.arange(rows)
     if nseg == 1:
-        return starts[0] + t
-    return np.where(t < seg, starts[0] + t, starts[1] + t - seg)
+        return s0 + t * stride
+    return np.where(t < seg, s0 + t * stride, s1 + (t - seg) * stride)
 
 
 def _np(t):
@@ -64,6 +68,30 @@ def test_zigzag_permute_bitexact(shape, N, dtype, seq_dim):
     assert np.array_equal(got, expect)
     assert torch.equal(back.cpu().view(torch.int16) if dtype == torch.bfloat16 else back.cpu(),
                        src.view(torch.int16) if dtype == torch.bfloat16 else src)
+
+
+@pytest.mark.parametrize("shape,N,dtype,seq_dim", [
+    ((2, 3, 64, 8), 4, torch.bfloat16, -2),
+    ((1, 2, 1024), 8, torch.float32, -1),
+    ((1, 5, 48, 3), 3, torch.int16, -2),      # 6-byte rows: 2-byte accesses
+    ((1, 1, 4096, 128), 16, torch.bfloat16, -2),
+    ((1, 2, 96, 300), 3, torch.float32, -2),   # 1200-byte rows: longer than one block
+])
+def test_striped_permute_bitexact(shape, N, dtype, seq_dim):
+    g = torch.Generator().manual_seed(6)
+    src = torch.randint(-30000, 30000, shape, generator=g, dtype=torch.int32).to(dtype)
+    S = shape[seq_dim]
+    order = oracle.striped_order(S, N)
+    as_np = (lambda t: t.view(torch.int16).numpy()) if dtype == torch.bfloat16 else (lambda t: t.numpy())
+    expect = np.take(as_np(src), order, axis=seq_dim % len(shape))
+    s_dev = src.to(DEV)
+    dst = torch.empty_like(s_dev)
+    ra.ra_striped_permute(s_dev, dst, N, inverse=False, seq_dim=seq_dim)
+    back = torch.empty_like(s_dev)
+    ra.ra_striped_permute(dst, back, N, inverse=True, seq_dim=seq_dim)
+    torch.cuda.synchronize()
+    assert np.array_equal(as_np(dst.cpu()), expect)
+    assert np.array_equal(as_np(back.cpu()), as_np(src))
 
 
 # ---------------------------------------------------------------- merge
@@ -130,6 +158,12 @@ BLOCK_CASES = [
     (200, 333, None, None, False),
     (1, 1, None, None, True),
     (5, 3, (1, 5, 2), None, True),
+    # strided positions (the striped split): rank 1 against rank 2 of 4 is a
+    # strictly lower triangle, rank 3 against rank 0 an inclusive one
+    (256, 256, (1, 256, 1, 0, 4), (1, 256, 2, 0, 4), True),
+    (300, 200, (1, 300, 3, 0, 4), (1, 200, 0, 0, 4), True),
+    (256, 192, (2, 128, 0, 700, 3), (1, 192, 1, 0, 5), True),   # unequal strides
+    (130, 70, (1, 130, 0, 0, 7), (1, 70, 5, 0, 7), False),
 ]
 
 
@@ -238,6 +272,12 @@ SMALL_RINGS = [
                        seed=25, causal=True, N=4, layout="zigzag"),
     workloads.Workload("contig_s8192_n8_rank0_0_1023", B=1, Hq=2, Hkv=2, D=128, S=8192,
                        dtype="bf16", seed=26, causal=True, N=8, layout="contiguous"),
+    workloads.Workload("striped_gqa", B=1, Hq=4, Hkv=2, D=128, S=1024, dtype="bf16", seed=27,
+                       causal=True, N=4, layout="striped"),
+    workloads.Workload("striped_ragged_n8", B=1, Hq=2, Hkv=1, D=128, S=1000, dtype="bf16",
+                       seed=28, causal=True, N=8, layout="striped"),
+    workloads.Workload("striped_f32_d64", B=2, Hq=2, Hkv=1, D=64, S=600, dtype="f32", seed=29,
+                       causal=True, N=3, layout="striped"),
 ]
 
 
@@ -291,6 +331,14 @@ def test_ring_zigzag_equals_contiguous_and_no_copy_stream():
     assert torch.equal(oz, o1) and torch.equal(lz, l1)
     assert (oz.float() - oc.float()).abs().max().item() <= 2e-2
     assert (lz - lc).abs().max().item() <= 1e-3
+
+
+def test_ring_striped_equals_contiguous():
+    base = dict(B=1, Hq=4, Hkv=2, D=128, S=4096, dtype="bf16", seed=32, causal=True, N=8)
+    os_, ls_ = _ring_check(workloads.Workload("s", layout="striped", **base))
+    oc, lc = _ring_check(workloads.Workload("c", layout="contiguous", **base))
+    assert (os_.float() - oc.float()).abs().max().item() <= 2e-2
+    assert (ls_ - lc).abs().max().item() <= 1e-3
 
 
 def test_ring_causality_perturbation_bitexact():

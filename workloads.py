@@ -32,7 +32,7 @@ class Workload:
     seed: int
     causal: bool
     N: int              # virtual ring size
-    layout: str         # "contiguous" or "zigzag"
+    layout: str         # "contiguous", "zigzag" or "striped"
     k_scale: float = 1.0
     note: str = ""
 
