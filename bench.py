@@ -185,12 +185,13 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     ring_ms = (time.perf_counter() - r0) * 1e3 / args.steps
 
-    # permute bandwidth: one q-sized permute timed with events
+    # permute bandwidth: one q-sized permute of the workload's layout, timed with events
+    permute = ra.ra_striped_permute if w.layout == "striped" else ra.ra_zigzag_permute
     dst = torch.empty_like(q)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(5):
-        ra.ra_zigzag_permute(q, dst, w.N)
+        permute(q, dst, w.N)
     e1.record()
     torch.cuda.synchronize()
     perm_gbs = 2 * q.numel() * q.element_size() * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
@@ -244,7 +245,8 @@ def main(argv=None) -> int:
             "kernel_ms_per_step": round(k_ms / max(args.steps, 1), 3),
         },
         "ring_only_ms": round(ring_ms, 3),
-        "aux_kernels": {"zigzag_permute_GBs": round(perm_gbs, 1),
+        "aux_kernels": {f"{'striped' if w.layout == 'striped' else 'zigzag'}_permute_GBs":
+                        round(perm_gbs, 1),
                         "lse_merge_GBs": round(merge_gbs, 1), "hbm_peak_GBs": PEAK_HBM_GBS},
         "flops_check": {"closed_form": flops_step, "library_count": lib_flops_step},
     }

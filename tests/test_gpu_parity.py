@@ -315,6 +315,21 @@ def test_ring_headline_gqa_128k_sampled():
     _ring_check(w, rows=check_rows(w.S, w.Hq, n, w.seed, 2 * w.N))
 
 
+def test_ring_striped_gqa_128k_sampled():
+    """Seeded rows plus each striped rank's first and last rows (positions
+    0..N-1 and S-N..S-1) and the 2N chunk boundaries, the same count per head."""
+    from parity_util import boundary_rows
+    w = workloads.STRIPED_128K
+    n = int(os.environ.get("RA_ORACLE_ROWS", "32"))
+    fixed = np.union1d(boundary_rows(w.S, 2 * w.N),
+                       np.concatenate([np.arange(w.N), w.S - w.N + np.arange(w.N)]))
+    rest = np.setdiff1d(np.arange(w.S), fixed)
+    rows = np.stack([np.sort(np.concatenate(
+        [fixed, np.random.default_rng([w.seed, h]).choice(rest, n, replace=False)]))
+        for h in range(w.Hq)])
+    _ring_check(w, rows=rows)
+
+
 def test_ring_million_token_mqa_sampled():
     w = workloads.WORKLOADS[4]
     n = int(os.environ.get("RA_ORACLE_ROWS", "16"))

@@ -66,7 +66,13 @@ WORKLOADS = (
              note="32 chunks of 32768"),
 )
 
-BY_NAME = {w.name: w for w in WORKLOADS}
+# The same 128k GQA inputs on the striped split (token t on rank t mod N): a
+# parity case and a measurement of that layout, not one of the five configs.
+STRIPED_128K = Workload("gqa_causal_striped_s128k", B=1, Hq=64, Hkv=8, D=128, S=131072,
+                        dtype="bf16", seed=3, causal=True, N=8, layout="striped",
+                        k_scale=0.5, note="rank r holds tokens r, r+8, ...")
+
+BY_NAME = {w.name: w for w in WORKLOADS + (STRIPED_128K,)}
 HEADLINE = WORKLOADS[3]
 
 
