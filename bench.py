@@ -121,6 +121,80 @@ def cpu_baseline(w, q, k, v, out_gpu, lse_gpu, budget_s: float, rows_per_head: i
     }
 
 
+def bench_backward(args, w, q, k, v, runner, out, lse) -> int:
+    """One step = permute q, k, v, out, dout, lse into rank-major order, the ring
+    backward (all N ranks x N steps, fp32 accumulation, bf16 gradients), and the
+    inverse permute of dq, dk, dv. The forward runs once, untimed, for out/lse.
+    Useful work: 10*D flops per allowed pair (scores recomputed + four products)."""
+    import torch
+    import ring_context_parallelism_flash_amd as ra
+    import workloads
+    dev = q.device
+    runner(q, k, v, out, lse)
+    dout = workloads.make_random(q.shape, w.seed + 500, q.dtype).to(dev)
+    B, Hq, S, D = q.shape
+    ws = torch.empty(ra.ra_ring_sim_bwd_workspace_bytes(B, Hq, w.Hkv, S, D, q.dtype, w.N),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        return ra.ring_attention_sim_backward(q, k, v, out, lse, dout, N=w.N, layout=w.layout,
+                                              causal=w.causal, workspace=ws)
+
+    print(f"bench: backward warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ra.ra_kernel_timing_enable(True)
+    ra.ra_kernel_timing_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    k_ms, launches, k_flops = ra.ra_kernel_timing_read()
+    ra.ra_kernel_timing_enable(False)
+    print(f"bench: timed {args.steps} backward steps in {t1 - t0:.3f} s", file=sys.stderr, flush=True)
+    flops_step = 2.5 * useful_flops(w)   # 10*D per pair against the forward's 4*D
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    value = flops_step / (ms_step / 1e3) / 1e12
+    achieved = k_flops / (k_ms / 1e3) / 1e12 if k_ms > 0 else 0.0
+    line = {
+        "metric": f"ring-attn bwd useful TFLOP/s, {w.name}",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid normal q/k/v/dout, k x0.5, bf16)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "S": w.S,
+                   "virtual_ranks": w.N, "layout": w.layout, "causal": w.causal,
+                   "pass": "backward"},
+        "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "useful_flops_per_step": flops_step,
+        "roofline": {
+            "kernel": f"attn_bwd_dkdv<{w.D}> + attn_bwd_dq<{w.D}>",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": round(PEAK_BF16_TFLOPS, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "traffic_source": "no counter summary for the backward kernels",
+            "launches_per_step": launches // max(args.steps, 1),
+            "kernel_ms_per_step": round(k_ms / max(args.steps, 1), 3),
+        },
+        "flops_check": {"closed_form": flops_step, "library_count": k_flops / max(args.steps, 1)},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -130,6 +204,8 @@ def main(argv=None) -> int:
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--cpu-rows", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--backward", action="store_true",
+                   help="time the ring backward (dq, dk, dv of a seeded dout) instead of the forward")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="finish with one plain device copy of this many MiB (a known-size "
                         "reference for hardware byte counters)")
@@ -154,6 +230,8 @@ def main(argv=None) -> int:
     out = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
 
+    if args.backward:
+        return bench_backward(args, w, q, k, v, runner, out, lse)
     print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         runner(q, k, v, out, lse)

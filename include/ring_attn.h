@@ -226,15 +226,78 @@ ra_status ra_ring_sim_fwd(const void* q, const void* k, const void* v, void* out
                           void* compute_stream, void* copy_stream);
 
 /* ------------------------------------------------------------------------
+ * ra_block_attn_bwd -- gradients of one query block against one KV block.
+ *
+ * [SCP "What it does not change": the gradients under context parallelism
+ *  are those of single-device attention; SP "The Activation Memory Wall":
+ *  the attention probabilities are recomputed in the backward pass.]
+ *
+ * For query head h of batch b, kv head g = map(h), query row i and allowed
+ * key row j (the causal rule and positions of ra_block_attn_fwd):
+ *   p_ij    = exp(scale*<q_i,k_j> - lse_i)      (lse: the forward's final lse)
+ *   delta_i = <dout_i, out_i>                   (out: the forward's output)
+ *   ds_ij   = p_ij * (<dout_i, v_j> - delta_i)
+ *   dq_i   += scale * sum_j ds_ij k_j
+ *   dk_j   += scale * sum_{h, i} ds_ij q_i      (summed over the heads of g)
+ *   dv_j   += sum_{h, i} p_ij dout_i
+ * q, out, dout: [B,Hq,Cq,D]; k, v: [B,Hkv,Ck,D], bf16 (RA_F32 returns
+ * RA_ERR_UNSUPPORTED), 16-byte aligned. lse: float32 [B,Hq,Cq] (-inf marks a
+ * row with no key: it contributes nothing). dq: float32 [B,Hq,Cq,D]; dk, dv:
+ * float32 [B,Hkv,Ck,D], 16-byte aligned; the gradients are ADDED to them, so
+ * the contributions of several key blocks (a ring) accumulate. workspace: at
+ * least ra_block_attn_bwd_workspace_bytes(...) bytes, 256-byte aligned,
+ * clobbered (transposed copies of q, dout and k, per-row delta and lse).
+ * ---------------------------------------------------------------------- */
+size_t ra_block_attn_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t Cq,
+                                         int64_t Ck, int32_t D, ra_dtype dtype);
+
+ra_status ra_block_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                            const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                            int32_t B, int32_t Hq, int32_t Hkv, int64_t Cq, int64_t Ck, int32_t D,
+                            ra_dtype dtype, const ra_pos* q_pos, const ra_pos* k_pos,
+                            const int32_t* kv_head_of_q, int32_t causal, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * ra_ring_sim_bwd -- the backward of the N-rank ring, simulated on one GPU.
+ *
+ * [SCP "What it does not change"; SP "Algorithmic Mechanics" item 2: at step
+ *  k rank i holds the KV block of source (i - k) mod N.]
+ *
+ * Inputs as for ra_ring_sim_fwd (rank-major sequence order), plus out and lse
+ * (that call's results) and dout: [B,Hq,S,D] of `dtype`. Outputs dq
+ * [B,Hq,S,D] and dk, dv [B,Hkv,S,D] of `dtype`, rank-major. For every rank r
+ * and step k the driver adds the block pair (rank r's queries, the KV block
+ * of rank (r - k) mod N) to fp32 accumulators -- dq at rank r, dk and dv at
+ * the source block (in a real ring they travel with the block and return to
+ * its owner) -- and finally rounds them to `dtype`. The KV blocks are read in
+ * place (no copy stream). bf16 only; D 64 or 128; S divisible by N (by 2N for
+ * RA_ZIGZAG). workspace: ra_ring_sim_bwd_workspace_bytes(...) bytes, 256-byte
+ * aligned, clobbered. The result equals the gradients of full attention.
+ * ---------------------------------------------------------------------- */
+size_t ra_ring_sim_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D,
+                                       ra_dtype dtype, int32_t N);
+
+ra_status ra_ring_sim_bwd(const void* q, const void* k, const void* v, const void* out,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                          int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D,
+                          ra_dtype dtype, int32_t N, ra_layout layout, int32_t causal,
+                          float scale, const int32_t* kv_head_of_q, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Kernel timing for measurement (not part of the computation).
  *
- * While enabled, every attention-kernel launch made by ra_block_attn_fwd and
- * ra_ring_sim_fwd is bracketed by a pair of HIP events recorded on the
- * stream it is launched on, and the allowed (query, key) pairs it processes
- * are counted on the host. ra_kernel_timing_read waits for the recorded
- * events, returns the summed kernel time in milliseconds, the number of
- * launches and the useful flops (4*D per allowed pair), and clears the
- * record. Up to 65536 launches are recorded between reads; later ones are
+ * While enabled, every attention-kernel launch made by ra_block_attn_fwd,
+ * ra_ring_sim_fwd, ra_block_attn_bwd and ra_ring_sim_bwd is bracketed by a
+ * pair of HIP events recorded on the stream it is launched on, and the
+ * allowed (query, key) pairs it processes are counted on the host.
+ * ra_kernel_timing_read waits for the recorded events, returns the summed
+ * kernel time in milliseconds, the number of launches and the useful flops
+ * (per allowed pair: 4*D for a forward launch; for a backward pair 8*D for
+ * the dk/dv kernel and 2*D for the dq kernel, 10*D in all -- the recomputed
+ * scores and the four gradient products), and clears the record. Up to
+ * 65536 launches are recorded between reads; later ones are
  * not timed (launches still counts them; total_ms then covers only the
  * first 65536). Enabling creates the events once per process.
  * ---------------------------------------------------------------------- */

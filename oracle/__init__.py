@@ -9,5 +9,6 @@ from .fp64 import (  # noqa: F401
     striped_order, to_f64, unpermute_rows, useful_flops, useful_pairs, zigzag_order,
 )
 from .fp64_bwd import (  # noqa: F401
-    attention_backward, backward_flops, block_backward, ring_attention_backward,
+    attention_backward, attention_backward_dq_rows, backward_flops, block_backward,
+    ring_attention_backward,
 )

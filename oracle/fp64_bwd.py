@@ -80,6 +80,35 @@ def attention_backward(q, k, v, dout, *, causal: bool, scale: float | None = Non
     return dq, dk, dv
 
 
+def attention_backward_dq_rows(q, k, v, dout, rows, *, causal: bool, scale: float | None = None,
+                                kv_head_of_q=None):
+    """dq of selected query rows only, float64 (the same definition as
+    ``attention_backward``; each dq row needs only its own row's scores).
+    ``rows`` is [Hq, R] per-head row indices; returns [B, Hq, R, D]."""
+    q, k, v, dout = to_f64(q), to_f64(k), to_f64(v), to_f64(dout)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kv_map = _kv_map(Hq, Hkv, kv_head_of_q)
+    rows = np.asarray(rows, dtype=np.int64)
+    dq = np.zeros((B, Hq, rows.shape[1], D))
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_map[h]
+            for r, i in enumerate(rows[h]):
+                kk = k[b, g, :i + 1] if causal else k[b, g]
+                vv = v[b, g, :i + 1] if causal else v[b, g]
+                s = scale * (kk @ q[b, h, i])
+                p = np.exp(s - s.max())
+                p /= p.sum()
+                out = p @ vv
+                dp = vv @ dout[b, h, i]
+                ds = p * (dp - dout[b, h, i] @ out)
+                dq[b, h, r] = scale * (ds @ kk)
+    return dq
+
+
 def block_backward(q, k, v, dout, lse, delta, *, causal: bool, scale: float,
                    q_pos, k_pos):
     """One block pair's gradient contributions for one head, float64.

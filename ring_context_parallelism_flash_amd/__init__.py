@@ -18,7 +18,8 @@ __all__ = [
     "RAError", "lib", "library_path", "RA_BF16", "RA_F32", "RA_CONTIGUOUS", "RA_ZIGZAG",
     "ra_pos", "ra_status_str", "ra_last_error", "ra_block_attn_workspace_bytes",
     "ra_block_attn_fwd", "ra_lse_merge", "ra_zigzag_permute", "ra_striped_permute",
-    "ra_ring_sim_workspace_bytes",
+    "ra_ring_sim_workspace_bytes", "ra_block_attn_bwd_workspace_bytes", "ra_block_attn_bwd",
+    "ra_ring_sim_bwd_workspace_bytes", "ra_ring_sim_bwd", "ring_attention_sim_backward",
     "ra_ring_sim_fwd", "ra_kernel_timing_enable", "ra_kernel_timing_read", "zigzag_pos",
     "contiguous_pos", "striped_pos", "ring_attention_sim", "EXPORTS",
 ]
@@ -35,7 +36,8 @@ _LAYOUTS = {"contiguous": RA_CONTIGUOUS, "zigzag": RA_ZIGZAG, "striped": RA_STRI
 EXPORTS = (
     "ra_status_str", "ra_last_error", "ra_block_attn_workspace_bytes", "ra_block_attn_fwd",
     "ra_lse_merge", "ra_zigzag_permute", "ra_striped_permute", "ra_ring_sim_workspace_bytes",
-    "ra_ring_sim_fwd",
+    "ra_ring_sim_fwd", "ra_block_attn_bwd_workspace_bytes", "ra_block_attn_bwd",
+    "ra_ring_sim_bwd_workspace_bytes", "ra_ring_sim_bwd",
     "ra_kernel_timing_enable", "ra_kernel_timing_read",
 )
 
@@ -87,6 +89,18 @@ def lib() -> ctypes.CDLL:
                                       c_int32, c_int32, c_int32, c_int64, c_int32, c_int32,
                                       c_int32, c_int32, c_int32, c_float, P(c_int32),
                                       c_void_p, c_size_t, c_void_p, c_void_p]),
+        "ra_block_attn_bwd_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int64,
+                                                         c_int64, c_int32, c_int32]),
+        "ra_block_attn_bwd": (c_int32, [c_void_p] * 9 + [c_int32, c_int32, c_int32, c_int64,
+                                                         c_int64, c_int32, c_int32, P(ra_pos),
+                                                         P(ra_pos), P(c_int32), c_int32, c_float,
+                                                         c_void_p, c_size_t, c_void_p]),
+        "ra_ring_sim_bwd_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int64,
+                                                       c_int32, c_int32, c_int32]),
+        "ra_ring_sim_bwd": (c_int32, [c_void_p] * 9 + [c_int32, c_int32, c_int32, c_int64,
+                                                       c_int32, c_int32, c_int32, c_int32,
+                                                       c_int32, c_float, P(c_int32), c_void_p,
+                                                       c_size_t, c_void_p]),
         "ra_kernel_timing_enable": (c_int32, [c_int32]),
         "ra_kernel_timing_read": (c_int32, [P(ctypes.c_double), P(c_int64),
                                             P(ctypes.c_double)]),
@@ -252,6 +266,57 @@ def ra_ring_sim_fwd(q, k, v, out, lse, *, N, layout="zigzag", causal=True, scale
     return out, lse
 
 
+def ra_block_attn_bwd_workspace_bytes(B, Hq, Hkv, Cq, Ck, D, dtype) -> int:
+    dt = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib().ra_block_attn_bwd_workspace_bytes(B, Hq, Hkv, Cq, Ck, D, dt))
+
+
+def ra_block_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, *, q_pos=None, k_pos=None,
+                      kv_head_of_q=None, causal=True, scale=None, workspace=None, stream=None):
+    """Add one block pair's gradients to the fp32 dq, dk, dv (see include/ring_attn.h)."""
+    B, Hq, Cq, D = q.shape
+    Hkv, Ck = k.shape[1], k.shape[2]
+    dt = _dtype(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        n = ra_block_attn_bwd_workspace_bytes(B, Hq, Hkv, Cq, Ck, D, dt)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    qp, kp = _pos(q_pos), _pos(k_pos)
+    _check(lib().ra_block_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+        _ptr(dv), B, Hq, Hkv, Cq, Ck, D, dt,
+        None if qp is None else ctypes.byref(qp), None if kp is None else ctypes.byref(kp),
+        _kvmap(kv_head_of_q, Hq), int(bool(causal)), float(scale), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dq, dk, dv
+
+
+def ra_ring_sim_bwd_workspace_bytes(B, Hq, Hkv, S, D, dtype, N) -> int:
+    dt = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib().ra_ring_sim_bwd_workspace_bytes(B, Hq, Hkv, S, D, dt, N))
+
+
+def ra_ring_sim_bwd(q, k, v, out, dout, lse, dq, dk, dv, *, N, layout="zigzag", causal=True,
+                    scale=None, kv_head_of_q=None, workspace=None, stream=None):
+    """The simulated N-rank ring backward on rank-major tensors (see include/ring_attn.h)."""
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    dt = _dtype(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        workspace = torch.empty(max(ra_ring_sim_bwd_workspace_bytes(B, Hq, Hkv, S, D, dt, N), 1),
+                                dtype=torch.uint8, device=q.device)
+    _check(lib().ra_ring_sim_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+        _ptr(dv), B, Hq, Hkv, S, D, dt, N,
+        _LAYOUTS[layout] if isinstance(layout, str) else int(layout), int(bool(causal)),
+        float(scale), _kvmap(kv_head_of_q, Hq), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dq, dk, dv
+
+
 def ra_kernel_timing_enable(enable=True):
     _check(lib().ra_kernel_timing_enable(int(bool(enable))))
 
@@ -314,6 +379,33 @@ class RingRunner:
         """Whole step in sequence order: permute, ring, inverse permute."""
         self.ring(*self.permute_inputs(q, k, v))
         return self.unpermute_outputs(out, lse)
+
+
+def ring_attention_sim_backward(q, k, v, out, lse, dout, *, N, layout="zigzag", causal=True,
+                                scale=None, kv_head_of_q=None, workspace=None):
+    """Sequence-order tensors in (out, lse from the forward), sequence-order (dq, dk, dv) out."""
+    perm = _PERMUTES.get(layout)
+
+    def fwd(t, seq_dim=-2):
+        if perm is None:
+            return t
+        dst = torch.empty_like(t)
+        perm(t, dst, N, seq_dim=seq_dim)
+        return dst
+
+    def inv(t):
+        if perm is None:
+            return t
+        dst = torch.empty_like(t)
+        perm(t, dst, N, inverse=True)
+        return dst
+
+    qr, kr, vr, outr, doutr = (fwd(t) for t in (q, k, v, out, dout))
+    lser = fwd(lse, seq_dim=-1)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ra_ring_sim_bwd(qr, kr, vr, outr, doutr, lser, dq, dk, dv, N=N, layout=layout,
+                    causal=causal, scale=scale, kv_head_of_q=kv_head_of_q, workspace=workspace)
+    return inv(dq), inv(dk), inv(dv)
 
 
 def ring_attention_sim(q, k, v, *, N, layout="zigzag", causal=True, scale=None,

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libringattn.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["attn_fwd.hip", "aux_kernels.hip", "api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "aux_kernels.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

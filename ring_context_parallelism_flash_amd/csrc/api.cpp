@@ -137,8 +137,10 @@ struct Timing {
 Timing g_timing;
 constexpr size_t kMaxTimed = 65536;
 
-// Launch an attention kernel, bracketed by timing events when enabled.
-ra_status timed_launch(const AttnArgs& a, ra_dtype dt, int D, hipStream_t s, double flops) {
+// Launch an attention kernel (forward or backward), bracketed by timing events
+// when enabled; `flops` is its useful work.
+template <class F>
+ra_status timed(hipStream_t s, double flops, F&& launch) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
   {
     std::lock_guard<std::mutex> lk(g_timing.mu);
@@ -160,10 +162,14 @@ ra_status timed_launch(const AttnArgs& a, ra_dtype dt, int D, hipStream_t s, dou
     }
   }
   if (e0) RA_HIP(hipEventRecord(e0, s));
-  hipError_t e = launch_attn(a, dt, D, s);
+  hipError_t e = launch();
   if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   if (e1) RA_HIP(hipEventRecord(e1, s));
   return RA_OK;
+}
+
+ra_status timed_launch(const AttnArgs& a, ra_dtype dt, int D, hipStream_t s, double flops) {
+  return timed(s, flops, [&] { return launch_attn(a, dt, D, s); });
 }
 
 // ---------------------------------------------------------------- ring events
@@ -590,6 +596,262 @@ ra_status ra_ring_sim_fwd(const void* q, const void* k, const void* v, void* out
       if (step > 0 && xs != cs) RA_HIP(hipEventRecord(ev->freed[step & 1], cs));
     }
   }
+  return RA_OK;
+}
+
+// ---------------------------------------------------------------- backward
+namespace {
+struct BwdLayout {
+  int64_t Cqp, Ckp;
+  size_t qt, dot, kt, lse2, delta, total;  // byte offsets / total
+};
+// [Q^T][dO^T][K^T][lse2][delta] for nq query slabs of Cq rows and nk key slabs of Ck
+BwdLayout bwd_layout(int64_t BHq, int64_t BHkv, int64_t nblk, int64_t Cq, int64_t Ck, int32_t D) {
+  auto up = [](size_t x) { return (size_t)round_up((int64_t)x, 256); };
+  BwdLayout L{};
+  L.Cqp = round_up(Cq, kBwdRowPad);
+  L.Ckp = round_up(Ck, kBwdRowPad);
+  const size_t tq = up((size_t)BHq * nblk * D * L.Cqp * 2);
+  const size_t tk = up((size_t)BHkv * nblk * D * L.Ckp * 2);
+  const size_t rv = up((size_t)BHq * nblk * L.Cqp * 4);
+  L.qt = 0;
+  L.dot = tq;
+  L.kt = 2 * tq;
+  L.lse2 = 2 * tq + tk;
+  L.delta = L.lse2 + rv;
+  L.total = L.delta + rv;
+  return L;
+}
+
+ra_status check_bwd(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, ra_dtype dt,
+                    const int32_t* kv_map, float scale, std::vector<uint8_t>& kv_of,
+                    std::vector<uint8_t>& order) {
+  ra_status st = check_common(B, Hq, Hkv, D, dt, kv_map, scale, kv_of, order);
+  if (st != RA_OK) return st;
+  if (dt != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "the backward supports bf16 inputs only");
+  return RA_OK;
+}
+
+// Work decomposition and head tables of both backward kernels.
+void fill_bwd_heads(BwdArgs& a, int32_t Hq, int32_t Hkv, const std::vector<uint8_t>& kv_of,
+                    const std::vector<uint8_t>& order) {
+  memset(a.head_order, 0, sizeof a.head_order);
+  memset(a.kv_of, 0, sizeof a.kv_of);
+  memset(a.grp_off, 0, sizeof a.grp_off);
+  for (int h = 0; h < Hq; ++h) {
+    a.head_order[h] = order[h];
+    a.kv_of[h] = kv_of[h];
+  }
+  std::vector<int> count(Hkv + 1, 0);
+  for (int h = 0; h < Hq; ++h) count[kv_of[h] + 1]++;
+  for (int g = 0; g < Hkv; ++g) count[g + 1] += count[g];
+  for (int g = 0; g <= Hkv; ++g) a.grp_off[g] = (uint16_t)count[g];
+}
+
+// Both kernels for one block pair (dq, dk, dv fp32 accumulators added to).
+ra_status launch_bwd_pair(BwdArgs a, int32_t D, hipStream_t s) {
+  const double pairs = (double)(a.Ck > 0 ? pairs_between(a.qp, a.Cq, a.kp, a.Ck, a.causal) : 0);
+  if (a.Cq == 0 || a.Ck == 0) return RA_OK;
+  const double fl = (double)D * a.B * a.Hq * pairs;
+  a.n_tiles = (a.Ck + 127) / 128;
+  a.n_items = a.B * a.Hkv * a.n_tiles;
+  a.per_xcd = (a.n_items + kXcds - 1) / kXcds;
+  ra_status st = timed(s, 8.0 * fl, [&] { return launch_bwd_dkdv(a, D, s); });
+  if (st != RA_OK) return st;
+  a.n_tiles = (a.Cq + 127) / 128;
+  a.n_items = a.B * a.Hq * a.n_tiles;
+  a.per_xcd = (a.n_items + kXcds - 1) / kXcds;
+  return timed(s, 2.0 * fl, [&] { return launch_bwd_dq(a, D, s); });
+}
+}  // namespace
+
+size_t ra_block_attn_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t Cq,
+                                         int64_t Ck, int32_t D, ra_dtype dtype) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Cq < 0 || Ck < 0 || D < 1 || dtype != RA_BF16) return 0;
+  return bwd_layout((int64_t)B * Hq, (int64_t)B * Hkv, 1, Cq, Ck, D).total;
+}
+
+ra_status ra_block_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                            const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                            int32_t B, int32_t Hq, int32_t Hkv, int64_t Cq, int64_t Ck, int32_t D,
+                            ra_dtype dtype, const ra_pos* q_pos, const ra_pos* k_pos,
+                            const int32_t* kv_head_of_q, int32_t causal, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  std::vector<uint8_t> kv_of, order;
+  ra_status st = check_bwd(B, Hq, Hkv, D, dtype, kv_head_of_q, scale, kv_of, order);
+  if (st != RA_OK) return st;
+  if (Cq < 0 || Ck < 0) return fail(RA_ERR_SHAPE, "negative row count");
+  if (Cq > INT32_MAX || Ck > INT32_MAX) return fail(RA_ERR_UNSUPPORTED, "block rows beyond 2^31-1");
+  if (causal != 0 && causal != 1) return fail(RA_ERR_ARG, "causal must be 0 or 1");
+  if (Cq == 0 || Ck == 0) return RA_OK;
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
+    return fail(RA_ERR_NULL, "NULL tensor pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return fail(RA_ERR_ALIGN, "q, k, v, out, dout, dq, dk and dv must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(RA_ERR_ALIGN, "lse must be 4-byte aligned");
+  PosDesc qp, kp;
+  if ((st = make_pos(q_pos, Cq, "q_pos", qp)) != RA_OK) return st;
+  if ((st = make_pos(k_pos, Ck, "k_pos", kp)) != RA_OK) return st;
+  const BwdLayout L = bwd_layout((int64_t)B * Hq, (int64_t)B * Hkv, 1, Cq, Ck, D);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", L.total, workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(RA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  hipError_t e;
+  if ((e = launch_vt_transpose(q, ws + L.qt, (int64_t)B * Hq, 1, Cq, L.Cqp, D, Cq * D, s)) != hipSuccess ||
+      (e = launch_vt_transpose(dout, ws + L.dot, (int64_t)B * Hq, 1, Cq, L.Cqp, D, Cq * D, s)) != hipSuccess ||
+      (e = launch_vt_transpose(k, ws + L.kt, (int64_t)B * Hkv, 1, Ck, L.Ckp, D, Ck * D, s)) != hipSuccess ||
+      (e = launch_bwd_prep(out, dout, lse, (float*)(ws + L.lse2), (float*)(ws + L.delta),
+                           (int64_t)B * Hq, 1, Cq, L.Cqp, D, Cq * D, Cq, s)) != hipSuccess)
+    return hip_fail(e, "backward preparation launch");
+  BwdArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = q; a.k = k; a.v = v; a.dout = dout;
+  a.qt = ws + L.qt; a.dot = ws + L.dot; a.kt = ws + L.kt;
+  a.lse2 = (const float*)(ws + L.lse2); a.delta = (const float*)(ws + L.delta);
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.q_hs = Cq * D;            a.q_bs = (int64_t)Hq * a.q_hs;
+  a.k_hs = Ck * D;            a.k_bs = (int64_t)Hkv * a.k_hs;
+  a.qt_hs = (int64_t)D * L.Cqp; a.qt_bs = (int64_t)Hq * a.qt_hs;
+  a.kt_hs = (int64_t)D * L.Ckp; a.kt_bs = (int64_t)Hkv * a.kt_hs;
+  a.l_hs = L.Cqp;             a.l_bs = (int64_t)Hq * a.l_hs;
+  a.dq_hs = a.q_hs;           a.dq_bs = a.q_bs;
+  a.dk_hs = a.k_hs;           a.dk_bs = a.k_bs;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv;
+  a.Cq = (int32_t)Cq; a.Ck = (int32_t)Ck;
+  a.Cqp = (int32_t)L.Cqp; a.Ckp = (int32_t)L.Ckp;
+  a.qp = qp; a.kp = kp;
+  a.causal = causal;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  fill_bwd_heads(a, Hq, Hkv, kv_of, order);
+  return launch_bwd_pair(a, D, s);
+}
+
+namespace {
+// [fp32 dq][fp32 dk][fp32 dv] [Q^T, dO^T, K^T, lse2, delta of all N blocks]
+struct RingBwdLayout {
+  int64_t C;
+  size_t dq, dk, dv, prep, total;
+  BwdLayout P;
+};
+RingBwdLayout ring_bwd_layout(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D,
+                              int32_t N) {
+  auto up = [](size_t x) { return (size_t)round_up((int64_t)x, 256); };
+  RingBwdLayout L{};
+  L.C = S / N;
+  L.dq = 0;
+  L.dk = up((size_t)B * Hq * S * D * 4);
+  L.dv = L.dk + up((size_t)B * Hkv * S * D * 4);
+  L.prep = L.dv + up((size_t)B * Hkv * S * D * 4);
+  L.P = bwd_layout((int64_t)B * Hq, (int64_t)B * Hkv, N, L.C, L.C, D);
+  L.total = L.prep + L.P.total;
+  return L;
+}
+}  // namespace
+
+size_t ra_ring_sim_bwd_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D,
+                                       ra_dtype dtype, int32_t N) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || N < 1 || D < 1 || S % N || dtype != RA_BF16) return 0;
+  return ring_bwd_layout(B, Hq, Hkv, S, D, N).total;
+}
+
+ra_status ra_ring_sim_bwd(const void* q, const void* k, const void* v, const void* out,
+                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                          int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D,
+                          ra_dtype dtype, int32_t N, ra_layout layout, int32_t causal,
+                          float scale, const int32_t* kv_head_of_q, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  std::vector<uint8_t> kv_of, order;
+  ra_status st = check_bwd(B, Hq, Hkv, D, dtype, kv_head_of_q, scale, kv_of, order);
+  if (st != RA_OK) return st;
+  if (layout != RA_CONTIGUOUS && layout != RA_ZIGZAG && layout != RA_STRIPED)
+    return fail(RA_ERR_ARG, "unknown layout");
+  if (causal != 0 && causal != 1) return fail(RA_ERR_ARG, "causal must be 0 or 1");
+  if (N < 1) return fail(RA_ERR_SHAPE, "N must be >= 1");
+  if (S < 0) return fail(RA_ERR_SHAPE, "S must be >= 0");
+  const int64_t div = layout == RA_ZIGZAG ? 2 * (int64_t)N : N;
+  if (S % div) return fail(RA_ERR_SHAPE, "S=%lld not divisible by %lld", (long long)S, (long long)div);
+  if (S == 0) return RA_OK;
+  if (S > INT32_MAX) return fail(RA_ERR_UNSUPPORTED, "S beyond 2^31-1");
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
+    return fail(RA_ERR_NULL, "NULL tensor pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return fail(RA_ERR_ALIGN, "q, k, v, out, dout, dq, dk and dv must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(RA_ERR_ALIGN, "lse must be 4-byte aligned");
+  const RingBwdLayout L = ring_bwd_layout(B, Hq, Hkv, S, D, N);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", L.total, workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(RA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  const int64_t C = L.C, Cp = L.P.Cqp;
+  float* dq_acc = reinterpret_cast<float*>(ws + L.dq);
+  float* dk_acc = reinterpret_cast<float*>(ws + L.dk);
+  float* dv_acc = reinterpret_cast<float*>(ws + L.dv);
+  char* pw = ws + L.prep;
+  RA_HIP(hipMemsetAsync(ws, 0, L.prep, s));
+  hipError_t e;
+  if ((e = launch_vt_transpose(q, pw + L.P.qt, (int64_t)B * Hq, N, C, Cp, D, S * D, s)) != hipSuccess ||
+      (e = launch_vt_transpose(dout, pw + L.P.dot, (int64_t)B * Hq, N, C, Cp, D, S * D, s)) != hipSuccess ||
+      (e = launch_vt_transpose(k, pw + L.P.kt, (int64_t)B * Hkv, N, C, Cp, D, S * D, s)) != hipSuccess ||
+      (e = launch_bwd_prep(out, dout, lse, (float*)(pw + L.P.lse2), (float*)(pw + L.P.delta),
+                           (int64_t)B * Hq, N, C, Cp, D, S * D, S, s)) != hipSuccess)
+    return hip_fail(e, "backward preparation launch");
+
+  auto pos_of_rank = [&](int r) {
+    if (layout == RA_ZIGZAG) {
+      const int64_t c = S / (2 * N);
+      return PosDesc{2, (int32_t)c, (int32_t)(r * c), (int32_t)((2 * N - 1 - r) * c), 1};
+    }
+    if (layout == RA_STRIPED) return PosDesc{1, (int32_t)C, (int32_t)r, 0, (int32_t)N};
+    return PosDesc{1, (int32_t)C, (int32_t)(r * C), 0, 1};
+  };
+  BwdArgs a;
+  memset(&a, 0, sizeof a);
+  a.q_hs = S * D;              a.q_bs = (int64_t)Hq * a.q_hs;
+  a.k_hs = S * D;              a.k_bs = (int64_t)Hkv * a.k_hs;
+  a.qt_hs = (int64_t)N * D * Cp; a.qt_bs = (int64_t)Hq * a.qt_hs;
+  a.kt_hs = (int64_t)N * D * Cp; a.kt_bs = (int64_t)Hkv * a.kt_hs;
+  a.l_hs = (int64_t)N * Cp;    a.l_bs = (int64_t)Hq * a.l_hs;
+  a.dq_hs = a.q_hs;            a.dq_bs = a.q_bs;
+  a.dk_hs = a.k_hs;            a.dk_bs = a.k_bs;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv;
+  a.Cq = a.Ck = (int32_t)C;
+  a.Cqp = a.Ckp = (int32_t)Cp;
+  a.causal = causal;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  fill_bwd_heads(a, Hq, Hkv, kv_of, order);
+  for (int r = 0; r < N; ++r) {
+    for (int step = 0; step < N; ++step) {
+      const int src = ((r - step) % N + N) % N;  // [SP "Algorithmic Mechanics" item 2]
+      a.q = (const char*)q + (size_t)r * C * D * 2;
+      a.dout = (const char*)dout + (size_t)r * C * D * 2;
+      a.k = (const char*)k + (size_t)src * C * D * 2;
+      a.v = (const char*)v + (size_t)src * C * D * 2;
+      a.qt = pw + L.P.qt + (size_t)r * D * Cp * 2;
+      a.dot = pw + L.P.dot + (size_t)r * D * Cp * 2;
+      a.kt = pw + L.P.kt + (size_t)src * D * Cp * 2;
+      a.lse2 = (const float*)(pw + L.P.lse2) + (size_t)r * Cp;
+      a.delta = (const float*)(pw + L.P.delta) + (size_t)r * Cp;
+      a.dq = dq_acc + (size_t)r * C * D;
+      a.dk = dk_acc + (size_t)src * C * D;
+      a.dv = dv_acc + (size_t)src * C * D;
+      a.qp = pos_of_rank(r);
+      a.kp = pos_of_rank(src);
+      if ((st = launch_bwd_pair(a, D, s)) != RA_OK) return st;
+    }
+  }
+  if ((e = launch_f32_to_bf16(dq_acc, dq, (int64_t)B * Hq * S * D, s)) != hipSuccess ||
+      (e = launch_f32_to_bf16(dk_acc, dk, (int64_t)B * Hkv * S * D, s)) != hipSuccess ||
+      (e = launch_f32_to_bf16(dv_acc, dv, (int64_t)B * Hkv * S * D, s)) != hipSuccess)
+    return hip_fail(e, "gradient cast launch");
   return RA_OK;
 }
 

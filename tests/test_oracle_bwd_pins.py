@@ -134,6 +134,17 @@ def test_invariants_sum_dv_and_dk():
         np.testing.assert_allclose(dk[0, g].sum(0), 0, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_dq_rows_equal_full_backward(causal):
+    q, k, v = _rand((1, 4, 30, 8), 29), _rand((1, 2, 30, 8), 30), _rand((1, 2, 30, 8), 31)
+    dout = _rand((1, 4, 30, 8), 32)
+    full = oracle.attention_backward(q, k, v, dout, causal=causal)[0]
+    rows = np.array([[0, 7, 29], [3, 4, 5], [29, 28, 0], [10, 20, 1]])
+    got = oracle.attention_backward_dq_rows(q, k, v, dout, rows, causal=causal)
+    for h in range(4):
+        np.testing.assert_allclose(got[0, h], full[0, h, rows[h]], atol=1e-12)
+
+
 def test_backward_flops_counts_ten_d_per_pair():
     assert oracle.backward_flops(1, 64, 128, 1000) == 10 * 128 * 64 * 1000
 
