@@ -144,6 +144,46 @@ def test_permute_and_merge_reject():
     assert L.ra_lse_merge(None, None, None, None, 0, 4, None) == 0
 
 
+def test_backward_workspace_sizes_and_rejects():
+    L = ra.lib()
+    assert ra.ra_block_attn_bwd_workspace_bytes(1, 8, 2, 300, 200, 128, F32) == 0   # bf16 only
+    n = ra.ra_block_attn_bwd_workspace_bytes(1, 8, 2, 300, 200, 128, BF16)
+    # Q^T, dO^T [8][128][384] bf16 + K^T [2][128][256] bf16 + two [8][384] fp32 rows
+    assert n == 2 * 8 * 128 * 384 * 2 + 2 * 128 * 256 * 2 + 2 * 8 * 384 * 4
+    assert ra.ra_ring_sim_bwd_workspace_bytes(1, 8, 2, 1000, 128, BF16, 3) == 0     # S % N
+    assert ra.ra_ring_sim_bwd_workspace_bytes(1, 8, 2, 1024, 128, BF16, 4) > 0
+
+    def block(**kw):
+        a = dict(dt=BF16, D=128, Hq=2, Hkv=2, Cq=64, Ck=64, q=FAKE, dq=FAKE, ws=None, wsb=0,
+                 causal=1)
+        a.update(kw)
+        return ra.ra_status_str(L.ra_block_attn_bwd(
+            a["q"], FAKE, FAKE, FAKE, FAKE, FAKE, a["dq"], FAKE, FAKE, 1, a["Hq"], a["Hkv"],
+            a["Cq"], a["Ck"], a["D"], a["dt"], None, None, None, a["causal"], 0.088, a["ws"],
+            a["wsb"], None))
+    assert block(dt=F32) == "RA_ERR_UNSUPPORTED"
+    assert block(D=96) == "RA_ERR_UNSUPPORTED"
+    assert block(Hq=3) == "RA_ERR_SHAPE"
+    assert block(q=None) == "RA_ERR_NULL"
+    assert block(dq=FAKE_ODD) == "RA_ERR_ALIGN"
+    assert block(causal=3) == "RA_ERR_ARG"
+    assert block() == "RA_ERR_WORKSPACE"
+    assert block(Cq=0) == "RA_OK" and block(Ck=0) == "RA_OK"
+
+    def ring(**kw):
+        a = dict(dt=BF16, S=1024, N=4, layout=1)
+        a.update(kw)
+        return ra.ra_status_str(L.ra_ring_sim_bwd(
+            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, a["S"], 128, a["dt"],
+            a["N"], a["layout"], 1, 0.088, None, None, 0, None))
+    assert ring(dt=F32) == "RA_ERR_UNSUPPORTED"
+    assert ring(S=1020) == "RA_ERR_SHAPE"
+    assert ring(layout=9) == "RA_ERR_ARG"
+    assert ring(S=1020, layout=2) == "RA_ERR_WORKSPACE"
+    assert ring() == "RA_ERR_WORKSPACE"
+    assert ring(S=0) == "RA_OK"
+
+
 def test_timing_read_without_launches():
     ra.ra_kernel_timing_enable(True)
     ms, n, fl = ra.ra_kernel_timing_read()
