@@ -1,4 +1,4 @@
-"""CPU fp64 oracle for ring-attention forward and backward (test infrastructure only).
+"""CPU fp64 oracle for ring attention (forward, backward) and Ulysses (test infrastructure only).
 
 Only tests, the smoke check and the benchmark's CPU-baseline leg import this
 package. It does not import the HIP library and the library does not import it.
@@ -11,4 +11,7 @@ from .fp64 import (  # noqa: F401
 from .fp64_bwd import (  # noqa: F401
     attention_backward, attention_backward_dq_rows, backward_flops, block_backward,
     ring_attention_backward,
+)
+from .fp64_ulysses import (  # noqa: F401
+    ulysses_all_to_all, ulysses_all_to_all_inverse, ulysses_attention, ulysses_volume,
 )
