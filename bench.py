@@ -37,7 +37,7 @@ PEAK_HBM_GBS = 8000.0
 # passes, scaled by a plain-copy calibration) live in this summary; they are
 # reported only while the kernel sources still hash to what was profiled.
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_bf16_gqa128k_pmc.txt")
-KERNEL_SOURCES = ("attn_fwd.hip", "ra_internal.h", "api.cpp")
+KERNEL_SOURCES = ("attn_fwd.hip", "attn_common.h", "attn_fwd_args.h")
 
 
 def kernel_sources_sha256() -> str:
@@ -195,6 +195,105 @@ def bench_backward(args, w, q, k, v, runner, out, lse) -> int:
     return 0
 
 
+def bench_ulysses(args, w, q_cpu, k_cpu, v_cpu, dev) -> int:
+    """One step = the Ulysses forward of P = w.N ranks on one GPU: the all-to-all
+    of q, k, v (sequence slices -> head slices), each rank's attention over the
+    whole sequence for its Hq/P heads (the cast to bf16 fused), and the
+    all-to-all of the output back. The inputs are the ranks' sequence slices
+    [P, B, S/P, H, D], laid out once before timing. Useful work as for the ring:
+    4*D flops per allowed pair."""
+    import torch
+    import ring_context_parallelism_flash_amd as ra
+    P = w.N
+
+    def shard(x):
+        B, H, S, D = x.shape
+        return x.permute(0, 2, 1, 3).reshape(B, P, S // P, H, D).permute(1, 0, 2, 3, 4).contiguous()
+
+    q, k, v = (shard(t).to(dev) for t in (q_cpu, k_cpu, v_cpu))
+    out = torch.empty_like(q)
+    lse = torch.empty((P, w.B, w.Hq // P, w.S), dtype=torch.float32, device=dev)
+    ws = torch.empty(ra.ra_ulysses_sim_workspace_bytes(w.B, w.Hq, w.Hkv, w.S, w.D, q.dtype, P),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        ra.ra_ulysses_sim_fwd(q, k, v, out, lse, P=P, causal=w.causal, workspace=ws)
+
+    print(f"bench: ulysses warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ra.ra_kernel_timing_enable(True)
+    ra.ra_kernel_timing_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    k_ms, launches, k_flops = ra.ra_kernel_timing_read()
+    ra.ra_kernel_timing_enable(False)
+    print(f"bench: timed {args.steps} ulysses steps in {t1 - t0:.3f} s", file=sys.stderr,
+          flush=True)
+    # all-to-all bandwidth: one q-sized first all-to-all, timed with events
+    dst = torch.empty((P, w.B, w.Hq // P, w.S, w.D), dtype=q.dtype, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        ra.ra_ulysses_all_to_all(q, dst, P)
+    e1.record()
+    torch.cuda.synchronize()
+    a2a_gbs = 2 * q.numel() * q.element_size() * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del dst
+
+    flops_step = useful_flops(w)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    value = flops_step / (ms_step / 1e3) / 1e12
+    achieved = k_flops / (k_ms / 1e3) / 1e12 if k_ms > 0 else 0.0
+    line = {
+        "metric": f"ulysses attn fwd useful TFLOP/s, {w.name}",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid normal q/k/v, k x0.5, bf16)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "S": w.S,
+                   "virtual_ranks": P, "layout": "ulysses", "causal": w.causal},
+        "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "useful_flops_per_step": flops_step,
+        "roofline": {
+            "kernel": f"attn_fwd_bf16<{w.D}>",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": round(PEAK_BF16_TFLOPS, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "traffic_source": "no counter summary for this workload",
+            "launches_per_step": launches // max(args.steps, 1),
+            "avg_launch_ms": round(k_ms / max(launches, 1), 4),
+            "flops_per_launch": k_flops / max(launches, 1),
+            "kernel_ms_per_step": round(k_ms / max(args.steps, 1), 3),
+        },
+        "aux_kernels": {"ulysses_all_to_all_GBs": round(a2a_gbs, 1), "hbm_peak_GBs": PEAK_HBM_GBS},
+        "flops_check": {"closed_form": flops_step, "library_count": k_flops / max(args.steps, 1)},
+    }
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        o = out.cpu().permute(1, 0, 2, 3, 4).reshape(w.B, w.S, w.Hq, w.D).permute(0, 2, 1, 3)
+        l_ = lse.cpu().permute(1, 0, 2, 3).reshape(w.B, w.Hq, w.S)
+        line["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, o, l_, args.cpu_seconds,
+                                            args.cpu_rows)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -202,7 +301,7 @@ def main(argv=None) -> int:
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default=None, help="workload name (default: the 128k GQA one)")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
-    p.add_argument("--cpu-rows", type=int, default=8)
+    p.add_argument("--cpu-rows", type=int, default=32)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--backward", action="store_true",
                    help="time the ring backward (dq, dk, dv of a seeded dout) instead of the forward")
@@ -224,6 +323,11 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     print(f"bench: generating {w.name} inputs", file=sys.stderr, flush=True)
     q_cpu, k_cpu, v_cpu = workloads.make_inputs(w)
+    if w.layout == "ulysses":
+        if args.backward:
+            print("bench.py: no backward for the Ulysses workload", file=sys.stderr)
+            return 2
+        return bench_ulysses(args, w, q_cpu, k_cpu, v_cpu, dev)
     q, k, v = (t.to(dev) for t in (q_cpu, k_cpu, v_cpu))
     runner = ra.RingRunner(w.B, w.Hq, w.Hkv, w.S, w.D, q.dtype, w.N, w.layout, w.causal,
                            device=dev)

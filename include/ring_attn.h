@@ -1,5 +1,5 @@
 /*
- * ring_attn.h -- C ABI of the MI355X (gfx950) ring-attention forward library.
+ * ring_attn.h -- C ABI of the MI355X (gfx950) ring-attention library.
  *
  * The library computes the per-device step of Ring Attention / Context
  * Parallelism: exact blockwise softmax attention of a resident query chunk
@@ -15,7 +15,10 @@
  *         (llms.blog): "RingAttention and Blockwise Context Parallelism" --
  *         the 4-GPU ring figure, "Algorithmic Mechanics" (online-softmax
  *         equations for m_new, l_new, O_new), "Overlapping Compute and
- *         Communication", "Causal Masking and Load Balancing".
+ *         Communication", "Causal Masking and Load Balancing"; and "DeepSpeed
+ *         Ulysses: Head-to-Sequence All-to-All Transposition".
+ *   [SCP] "Sequence and Context Parallelism" (praveentn.live): "What it does
+ *         not change".
  *
  * Conventions shared by every entry point
  *   - Device pointers are HIP device memory owned by the caller. The library
@@ -286,10 +289,66 @@ ra_status ra_ring_sim_bwd(const void* q, const void* k, const void* v, const voi
                           size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * ra_ulysses_all_to_all -- the Ulysses head<->sequence all-to-all of P ranks,
+ * simulated on one GPU as a layout transform.
+ *
+ * [SP "DeepSpeed Ulysses: Head-to-Sequence All-to-All Transposition": the
+ *  layout diagram and Execution Flow items 2 and 4 -- each rank's [B, S/P, H,
+ *  D] slice goes to [B, S, H/P, D]: rank j receives every rank's slice of
+ *  heads j*H/P .. (j+1)*H/P - 1; the second all-to-all reverses it.]
+ *
+ * Rows are row_bytes bytes (one token of one head, e.g. D*2 for bf16).
+ * Sequence-sharded: [P][B][S/P][H] rows; rank p's slice holds positions
+ * p*S/P .. (p+1)*S/P - 1 (its part of the page's [B, S/P, H, D]).
+ * Head-sharded: [P][B][H/P][S] rows; rank j's part holds heads j*H/P .. for
+ * positions 0..S-1, each head's S rows contiguous (the page's [B, S, H/P, D]
+ * with the local head and sequence axes swapped -- the layout the attention
+ * kernel reads, so no separate local transpose is needed).
+ * inverse = 0: src sequence-sharded -> dst head-sharded (first all-to-all);
+ * inverse = 1: src head-sharded -> dst sequence-sharded (second all-to-all).
+ * The copy is bit-exact. S and H must be divisible by P; S and (S/P)*H must
+ * be below 2^31; src and dst must not overlap. Any alignment is accepted;
+ * 16-byte aligned rows are copied with 16-byte accesses.
+ * ---------------------------------------------------------------------- */
+ra_status ra_ulysses_all_to_all(const void* src, void* dst, int32_t B, int64_t S, int32_t H,
+                                int64_t row_bytes, int32_t P, int32_t inverse, void* stream);
+
+/* ------------------------------------------------------------------------
+ * ra_ulysses_sim_fwd -- the Ulysses attention of P ranks, simulated on one GPU.
+ *
+ * [SP "DeepSpeed Ulysses", Execution Flow items 2-4: all-to-all of q, k, v;
+ *  local attention on the full sequence for H/P heads; all-to-all of the
+ *  output back. "Communication Cost and Constraints": H divisible by P, and
+ *  P <= H_KV under GQA. SCP "What it does not change": the result is that of
+ *  single-device attention.]
+ *
+ * q: [P][B][S/P][Hq][D], k, v: [P][B][S/P][Hkv][D] of `dtype` (rank p's
+ * slice holds positions p*S/P ..); out: the same layout as q, of `dtype`.
+ * lse: float32 [P][B][Hq/P][S] -- it stays on the rank that computed it,
+ * head-sharded (rank j, head j*Hq/P + h, position t). Each rank's attention
+ * over positions 0..S-1 is one launch of the forward attention kernel with
+ * the cast to `dtype` fused into its epilogue. Hq and Hkv must be divisible
+ * by P; kv_head_of_q (NULL: h / (Hq/Hkv)) must map every query head to a KV
+ * head of the same rank (kv_head_of_q[h] / (Hkv/P) == h / (Hq/P)). D 64 or
+ * 128; S divisible by P and below 2^31; scale > 0. workspace: at least
+ * ra_ulysses_sim_workspace_bytes(...) bytes, 256-byte aligned, clobbered
+ * (head-sharded q, k, v, out and, for bf16, V^T).
+ * ---------------------------------------------------------------------- */
+size_t ra_ulysses_sim_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D,
+                                      ra_dtype dtype, int32_t P);
+
+ra_status ra_ulysses_sim_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D,
+                             ra_dtype dtype, int32_t P, int32_t causal, float scale,
+                             const int32_t* kv_head_of_q, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* ------------------------------------------------------------------------
  * Kernel timing for measurement (not part of the computation).
  *
  * While enabled, every attention-kernel launch made by ra_block_attn_fwd,
- * ra_ring_sim_fwd, ra_block_attn_bwd and ra_ring_sim_bwd is bracketed by a
+ * ra_ring_sim_fwd, ra_ulysses_sim_fwd, ra_block_attn_bwd and ra_ring_sim_bwd
+ * is bracketed by a
  * pair of HIP events recorded on the stream it is launched on, and the
  * allowed (query, key) pairs it processes are counted on the host.
  * ra_kernel_timing_read waits for the recorded events, returns the summed

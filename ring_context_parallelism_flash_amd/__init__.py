@@ -21,7 +21,8 @@ __all__ = [
     "ra_ring_sim_workspace_bytes", "ra_block_attn_bwd_workspace_bytes", "ra_block_attn_bwd",
     "ra_ring_sim_bwd_workspace_bytes", "ra_ring_sim_bwd", "ring_attention_sim_backward",
     "ra_ring_sim_fwd", "ra_kernel_timing_enable", "ra_kernel_timing_read", "zigzag_pos",
-    "contiguous_pos", "striped_pos", "ring_attention_sim", "EXPORTS",
+    "contiguous_pos", "striped_pos", "ring_attention_sim", "ra_ulysses_all_to_all",
+    "ra_ulysses_sim_workspace_bytes", "ra_ulysses_sim_fwd", "EXPORTS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +38,8 @@ EXPORTS = (
     "ra_status_str", "ra_last_error", "ra_block_attn_workspace_bytes", "ra_block_attn_fwd",
     "ra_lse_merge", "ra_zigzag_permute", "ra_striped_permute", "ra_ring_sim_workspace_bytes",
     "ra_ring_sim_fwd", "ra_block_attn_bwd_workspace_bytes", "ra_block_attn_bwd",
-    "ra_ring_sim_bwd_workspace_bytes", "ra_ring_sim_bwd",
+    "ra_ring_sim_bwd_workspace_bytes", "ra_ring_sim_bwd", "ra_ulysses_all_to_all",
+    "ra_ulysses_sim_workspace_bytes", "ra_ulysses_sim_fwd",
     "ra_kernel_timing_enable", "ra_kernel_timing_read",
 )
 
@@ -101,6 +103,14 @@ def lib() -> ctypes.CDLL:
                                                        c_int32, c_int32, c_int32, c_int32,
                                                        c_int32, c_float, P(c_int32), c_void_p,
                                                        c_size_t, c_void_p]),
+        "ra_ulysses_all_to_all": (c_int32, [c_void_p, c_void_p, c_int32, c_int64, c_int32,
+                                            c_int64, c_int32, c_int32, c_void_p]),
+        "ra_ulysses_sim_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int64,
+                                                      c_int32, c_int32, c_int32]),
+        "ra_ulysses_sim_fwd": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_int32, c_int32, c_int32, c_int64, c_int32, c_int32,
+                                         c_int32, c_int32, c_float, P(c_int32), c_void_p,
+                                         c_size_t, c_void_p]),
         "ra_kernel_timing_enable": (c_int32, [c_int32]),
         "ra_kernel_timing_read": (c_int32, [P(ctypes.c_double), P(c_int64),
                                             P(ctypes.c_double)]),
@@ -315,6 +325,49 @@ def ra_ring_sim_bwd(q, k, v, out, dout, lse, dq, dk, dv, *, N, layout="zigzag", 
         float(scale), _kvmap(kv_head_of_q, Hq), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return dq, dk, dv
+
+
+def ra_ulysses_all_to_all(src, dst, P, inverse=False, stream=None):
+    """Ulysses all-to-all of P ranks (see include/ring_attn.h). Forward: src
+    [P, B, S/P, H, row...] -> dst [P, B, H/P, S, row...]; inverse the reverse."""
+    if not inverse:
+        _, B, Sp, H = src.shape[:4]
+        S = Sp * P
+        row = src.shape[4:]
+    else:
+        _, B, Hp, S = src.shape[:4]
+        H = Hp * P
+        row = src.shape[4:]
+    row_bytes = math.prod(row) * src.element_size()
+    _check(lib().ra_ulysses_all_to_all(_ptr(src), _ptr(dst), B, S, H, row_bytes, P,
+                                       int(bool(inverse)), _stream(stream)))
+    return dst
+
+
+def ra_ulysses_sim_workspace_bytes(B, Hq, Hkv, S, D, dtype, P) -> int:
+    dt = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib().ra_ulysses_sim_workspace_bytes(B, Hq, Hkv, S, D, dt, P))
+
+
+def ra_ulysses_sim_fwd(q, k, v, out, lse, *, P, causal=True, scale=None, kv_head_of_q=None,
+                       workspace=None, stream=None):
+    """Ulysses attention of P ranks on one GPU. q, out: [P, B, S/P, Hq, D];
+    k, v: [P, B, S/P, Hkv, D]; lse: float32 [P, B, Hq/P, S]."""
+    _, B, Sp, Hq, D = q.shape
+    Hkv = k.shape[3]
+    S = Sp * P
+    dt = _dtype(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        workspace = torch.empty(ra_ulysses_sim_workspace_bytes(B, Hq, Hkv, S, D, dt, P),
+                                dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(lib().ra_ulysses_sim_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, S, D, dt, P,
+        int(bool(causal)), float(scale), _kvmap(kv_head_of_q, Hq), _ptr(workspace), wbytes,
+        _stream(stream)))
+    return out, lse
 
 
 def ra_kernel_timing_enable(enable=True):

@@ -115,16 +115,6 @@ int64_t pairs_between(const PosDesc& q, int64_t Cq, const PosDesc& k, int64_t Ck
   return total;
 }
 
-// First row of a block whose position is >= P (rows if none).
-int64_t first_row_at_or_after(const PosDesc& p, int64_t rows, int64_t P) {
-  const int64_t seg0 = p.nseg == 2 ? p.seg : rows;
-  const int64_t last0 = (int64_t)p.start0 + (seg0 - 1) * p.stride;
-  if (P <= last0) return std::max<int64_t>(0, -floordiv(-(P - p.start0), p.stride));
-  if (p.nseg == 2 && P <= (int64_t)p.start1 + (int64_t)(p.seg - 1) * p.stride)
-    return p.seg + std::max<int64_t>(0, -floordiv(-(P - p.start1), p.stride));
-  return rows;
-}
-
 // ---------------------------------------------------------------- timing
 struct Timing {
   std::mutex mu;
@@ -228,35 +218,6 @@ ra_status check_common(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, ra_dtype d
   return RA_OK;
 }
 
-void fill_work(AttnArgs& a, ra_dtype dt, int32_t B, int32_t Hq, int64_t Cq,
-               const std::vector<uint8_t>& kv_of, const std::vector<uint8_t>& order) {
-  memset(a.head_order, 0, sizeof a.head_order);
-  memset(a.kv_of, 0, sizeof a.kv_of);
-  for (int h = 0; h < Hq; ++h) {
-    a.head_order[h] = order[h];
-    a.kv_of[h] = kv_of[h];
-  }
-  a.B = B;
-  a.Hq = Hq;
-  const int32_t qtile = dt == RA_BF16 ? kQTileBf16 : kQTileF32;
-  a.q_tile = qtile;
-  const int32_t n_qt_all = (int32_t)((Cq + qtile - 1) / qtile);
-  // With accumulate = 1, leading query tiles that see no key are skipped:
-  // positions increase with the row index, so these are the rows whose
-  // position is below the block's first key position. Not on the final step
-  // of the ring, where every row still has to be written out.
-  int32_t lo = 0;
-  if (a.causal && a.accumulate && a.fin_out == nullptr) {
-    const int64_t row = a.Ck > 0 ? first_row_at_or_after(a.qp, Cq, a.kp.start0) : Cq;
-    lo = (int32_t)(row / qtile);
-  }
-  a.qt_lo = lo;
-  a.n_qt = n_qt_all - lo;
-  const int64_t items = (int64_t)B * Hq * a.n_qt;
-  a.n_items = (int32_t)items;
-  a.per_xcd = (int32_t)((items + kXcds - 1) / kXcds);
-}
-
 }  // namespace
 
 // ============================================================================
@@ -357,7 +318,7 @@ ra_status ra_block_attn_fwd(const void* q, const void* k, const void* v, float* 
     a.v_hs = a.k_hs;
     a.v_ld = D;
   }
-  fill_work(a, dtype, B, Hq, Cq, kv_of, order);
+  fill_attn_work(a, dtype, B, Hq, Cq, kv_of, order);
   const double flops = 4.0 * D * B * Hq * (double)(Ck > 0 ? pairs_between(qp, Cq, kp, Ck, causal) : 0);
   return timed_launch(a, dtype, D, s, flops);
 }
@@ -590,7 +551,7 @@ ra_status ra_ring_sim_fwd(const void* q, const void* k, const void* v, void* out
       a.accumulate = step > 0;
       a.scale = scale;
       a.scale_log2 = scale * 1.4426950408889634f;
-      fill_work(a, dtype, B, Hq, C, kv_of, order);
+      fill_attn_work(a, dtype, B, Hq, C, kv_of, order);
       const double flops = 4.0 * D * B * Hq * (double)pairs_between(a.qp, C, a.kp, C, causal);
       if ((st = timed_launch(a, dtype, D, cs, flops)) != RA_OK) return st;
       if (step > 0 && xs != cs) RA_HIP(hipEventRecord(ev->freed[step & 1], cs));
@@ -852,6 +813,164 @@ ra_status ra_ring_sim_bwd(const void* q, const void* k, const void* v, const voi
       (e = launch_f32_to_bf16(dk_acc, dk, (int64_t)B * Hkv * S * D, s)) != hipSuccess ||
       (e = launch_f32_to_bf16(dv_acc, dv, (int64_t)B * Hkv * S * D, s)) != hipSuccess)
     return hip_fail(e, "gradient cast launch");
+  return RA_OK;
+}
+
+// ---------------------------------------------------------------- Ulysses
+ra_status ra_ulysses_all_to_all(const void* src, void* dst, int32_t B, int64_t S, int32_t H,
+                                int64_t row_bytes, int32_t P, int32_t inverse, void* stream) {
+  g_err[0] = 0;
+  if (P < 1) return fail(RA_ERR_SHAPE, "P must be >= 1");
+  if (B < 0 || S < 0 || H < 1 || row_bytes < 1) return fail(RA_ERR_SHAPE, "bad sizes");
+  if (S % P || H % P)
+    return fail(RA_ERR_SHAPE, "S=%lld and H=%d must be divisible by P=%d", (long long)S, H, P);
+  if (S > INT32_MAX || (S / P) * H > INT32_MAX)
+    return fail(RA_ERR_UNSUPPORTED, "S or (S/P)*H beyond 2^31-1");
+  if (inverse != 0 && inverse != 1) return fail(RA_ERR_ARG, "inverse must be 0 or 1");
+  if (B == 0 || S == 0) return RA_OK;
+  if (!src || !dst) return fail(RA_ERR_NULL, "NULL pointer");
+  const uintptr_t bytes = (uintptr_t)B * S * H * row_bytes;
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(RA_ERR_ARG, "src and dst overlap");
+  hipError_t e = launch_ulysses_a2a(src, dst, B, S, H, row_bytes, P, inverse,
+                                    reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "all-to-all launch");
+  return RA_OK;
+}
+
+namespace {
+// Workspace of the Ulysses simulation: head-sharded [q][k][v][out] in the
+// input dtype, then (bf16) V^T [P*B*Hkv/P][D][Spad].
+struct UlyssesLayout {
+  int64_t Spad;
+  size_t q, k, v, o, vt, total;
+};
+UlyssesLayout ulysses_layout(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D,
+                             ra_dtype dt) {
+  auto up = [](size_t x) { return (size_t)round_up((int64_t)x, 256); };
+  UlyssesLayout L{};
+  const size_t es = esize(dt);
+  L.Spad = round_up(S, kVtAlign);
+  const size_t qb = up((size_t)B * Hq * S * D * es), kb = up((size_t)B * Hkv * S * D * es);
+  L.q = 0;
+  L.k = qb;
+  L.v = qb + kb;
+  L.o = qb + 2 * kb;
+  L.vt = 2 * qb + 2 * kb;
+  L.total = L.vt + (dt == RA_BF16 ? up((size_t)B * Hkv * D * L.Spad * 2) : 0);
+  return L;
+}
+}  // namespace
+
+size_t ra_ulysses_sim_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D,
+                                      ra_dtype dtype, int32_t P) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || D < 1 || P < 1 || S % P) return 0;
+  if (dtype != RA_BF16 && dtype != RA_F32) return 0;
+  return ulysses_layout(B, Hq, Hkv, S, D, dtype).total;
+}
+
+ra_status ra_ulysses_sim_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D,
+                             ra_dtype dtype, int32_t P, int32_t causal, float scale,
+                             const int32_t* kv_head_of_q, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  g_err[0] = 0;
+  std::vector<uint8_t> kv_of, order;
+  ra_status st = check_common(B, Hq, Hkv, D, dtype, kv_head_of_q, scale, kv_of, order);
+  if (st != RA_OK) return st;
+  if (causal != 0 && causal != 1) return fail(RA_ERR_ARG, "causal must be 0 or 1");
+  if (P < 1) return fail(RA_ERR_SHAPE, "P must be >= 1");
+  if (Hq % P || Hkv % P)
+    return fail(RA_ERR_SHAPE, "Hq=%d and Hkv=%d must be divisible by P=%d (P <= H_KV)", Hq, Hkv, P);
+  const int32_t Hqp = Hq / P, Hkvp = Hkv / P;
+  for (int h = 0; h < Hq; ++h)
+    if (kv_of[h] / Hkvp != h / Hqp)
+      return fail(RA_ERR_SHAPE, "query head %d reads KV head %d, held by another rank", h,
+                  (int)kv_of[h]);
+  if (S < 0) return fail(RA_ERR_SHAPE, "S must be >= 0");
+  if (S % P) return fail(RA_ERR_SHAPE, "S=%lld not divisible by P=%d", (long long)S, P);
+  if (S == 0) return RA_OK;
+  if (S > INT32_MAX || (S / P) * Hq > INT32_MAX)
+    return fail(RA_ERR_UNSUPPORTED, "S or (S/P)*Hq beyond 2^31-1");
+  if (!q || !k || !v || !out || !lse) return fail(RA_ERR_NULL, "NULL tensor pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(RA_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(RA_ERR_ALIGN, "lse must be 4-byte aligned");
+  const UlyssesLayout L = ulysses_layout(B, Hq, Hkv, S, D, dtype);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", L.total,
+                workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(RA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t es = esize(dtype);
+  char* ws = reinterpret_cast<char*>(workspace);
+  char *qh = ws + L.q, *kh = ws + L.k, *vh = ws + L.v, *oh = ws + L.o, *vt = ws + L.vt;
+  const bool bf16 = dtype == RA_BF16;
+  const int64_t row = (int64_t)D * es;
+
+  // First all-to-all: every rank's q, k, v slices -> head-sharded [P][B][H/P][S][D].
+  hipError_t e;
+  if ((e = launch_ulysses_a2a(q, qh, B, S, Hq, row, P, 0, s)) != hipSuccess ||
+      (e = launch_ulysses_a2a(k, kh, B, S, Hkv, row, P, 0, s)) != hipSuccess ||
+      (e = launch_ulysses_a2a(v, vh, B, S, Hkv, row, P, 0, s)) != hipSuccess)
+    return hip_fail(e, "all-to-all launch");
+  if (bf16 && (e = launch_vt_transpose(vh, vt, (int64_t)B * Hkv, 1, S, L.Spad, D, S * D, s)) !=
+                  hipSuccess)
+    return hip_fail(e, "V transpose launch");
+
+  // Local attention of each rank: its Hq/P heads over the whole sequence.
+  const PosDesc all{1, (int32_t)S, 0, 0, 1};
+  const int64_t pairs = pairs_between(all, S, all, S, causal);
+  for (int j = 0; j < P; ++j) {
+    std::vector<uint8_t> lkv(Hqp), lorder;
+    for (int h = 0; h < Hqp; ++h) lkv[h] = (uint8_t)(kv_of[j * Hqp + h] - j * Hkvp);
+    lorder.resize(Hqp);
+    for (int h = 0; h < Hqp; ++h) lorder[h] = (uint8_t)h;
+    std::stable_sort(lorder.begin(), lorder.end(),
+                     [&](uint8_t x, uint8_t y) { return lkv[x] < lkv[y]; });
+    AttnArgs a;
+    memset(&a, 0, sizeof a);
+    const size_t qoff = (size_t)j * B * Hqp * S * D, koff = (size_t)j * B * Hkvp * S * D;
+    a.q = qh + qoff * es;
+    a.q_bs = (int64_t)Hqp * S * D;
+    a.q_hs = S * D;
+    a.k = kh + koff * es;
+    a.k_bs = (int64_t)Hkvp * S * D;
+    a.k_hs = S * D;
+    if (bf16) {
+      a.v = vt + (size_t)j * B * Hkvp * D * L.Spad * 2;
+      a.v_bs = (int64_t)Hkvp * D * L.Spad;
+      a.v_hs = (int64_t)D * L.Spad;
+      a.v_ld = L.Spad;
+    } else {
+      a.v = vh + koff * es;
+      a.v_bs = a.k_bs;
+      a.v_hs = a.k_hs;
+      a.v_ld = D;
+    }
+    // accumulate = 0 with a final output: the running state is never read.
+    a.fin_out = oh + qoff * es;
+    a.fo_bs = a.q_bs;
+    a.fo_hs = a.q_hs;
+    a.fin_lse = lse + (size_t)j * B * Hqp * S;
+    a.fl_bs = (int64_t)Hqp * S;
+    a.fl_hs = S;
+    a.Cq = (int32_t)S;
+    a.Ck = (int32_t)S;
+    a.qp = all;
+    a.kp = all;
+    a.causal = causal;
+    a.accumulate = 0;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    fill_attn_work(a, dtype, B, Hqp, S, lkv, lorder);
+    const double flops = 4.0 * D * B * Hqp * (double)pairs;
+    if ((st = timed_launch(a, dtype, D, s, flops)) != RA_OK) return st;
+  }
+
+  // Second all-to-all: head-sharded out -> every rank's sequence slice.
+  if ((e = launch_ulysses_a2a(oh, out, B, S, Hq, row, P, 1, s)) != hipSuccess)
+    return hip_fail(e, "all-to-all launch");
   return RA_OK;
 }
 

@@ -33,6 +33,9 @@
 //  * The fp32 kernel (v_mfma_f32_32x32x2_f32) keeps the same structure with
 //    one element per lane per operand, so V needs no transpose there.
 #include <math.h>
+#include <string.h>
+
+#include <algorithm>
 
 #include "attn_common.h"
 
@@ -596,6 +599,53 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_f32(const AttnArgs a) {
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Host-side work list.
+// ---------------------------------------------------------------------------
+namespace {
+inline int64_t floordiv_i64(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
+// First row of a block whose position is >= P (rows if none).
+int64_t first_row_at_or_after(const PosDesc& p, int64_t rows, int64_t P) {
+  const int64_t seg0 = p.nseg == 2 ? p.seg : rows;
+  const int64_t last0 = (int64_t)p.start0 + (seg0 - 1) * p.stride;
+  if (P <= last0) return std::max<int64_t>(0, -floordiv_i64(-(P - p.start0), p.stride));
+  if (p.nseg == 2 && P <= (int64_t)p.start1 + (int64_t)(p.seg - 1) * p.stride)
+    return p.seg + std::max<int64_t>(0, -floordiv_i64(-(P - p.start1), p.stride));
+  return rows;
+}
+
+}  // namespace
+
+void fill_attn_work(AttnArgs& a, ra_dtype dt, int32_t B, int32_t Hq, int64_t Cq,
+                    const std::vector<uint8_t>& kv_of, const std::vector<uint8_t>& order) {
+  memset(a.head_order, 0, sizeof a.head_order);
+  memset(a.kv_of, 0, sizeof a.kv_of);
+  for (int h = 0; h < Hq; ++h) {
+    a.head_order[h] = order[h];
+    a.kv_of[h] = kv_of[h];
+  }
+  a.B = B;
+  a.Hq = Hq;
+  const int32_t qtile = dt == RA_BF16 ? kQTileBf16 : kQTileF32;
+  a.q_tile = qtile;
+  const int32_t n_qt_all = (int32_t)((Cq + qtile - 1) / qtile);
+  // With accumulate = 1, leading query tiles that see no key are skipped:
+  // positions increase with the row index, so these are the rows whose
+  // position is below the block's first key position. Not on the final step
+  // of the ring, where every row still has to be written out.
+  int32_t lo = 0;
+  if (a.causal && a.accumulate && a.fin_out == nullptr) {
+    const int64_t row = a.Ck > 0 ? first_row_at_or_after(a.qp, Cq, a.kp.start0) : Cq;
+    lo = (int32_t)(row / qtile);
+  }
+  a.qt_lo = lo;
+  a.n_qt = n_qt_all - lo;
+  const int64_t items = (int64_t)B * Hq * a.n_qt;
+  a.n_items = (int32_t)items;
+  a.per_xcd = (int32_t)((items + kXcds - 1) / kXcds);
+}
 
 hipError_t launch_attn(const AttnArgs& a, ra_dtype dt, int D, hipStream_t s) {
   if (a.n_items <= 0) return hipSuccess;

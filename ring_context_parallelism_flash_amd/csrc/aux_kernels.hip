@@ -1,6 +1,6 @@
 // Memory-bound helper kernels: the V -> V^T block transpose that feeds the
-// bf16 attention kernel, the standalone log-sum-exp merge, and the zigzag
-// and striped layout permutes.
+// bf16 attention kernel, the standalone log-sum-exp merge, the zigzag and
+// striped layout permutes and the Ulysses all-to-all.
 #include <math.h>
 
 #include "ra_internal.h"
@@ -243,6 +243,95 @@ hipError_t launch_striped_permute(const void* src, void* dst, int64_t outer, int
     default:
       hipLaunchKernelGGL(striped_permute_kernel<uint8_t>, grid, dim3(256), 0, s, sp, dp, rows, S,
                          N, C, row_vecs, rpb, inverse);
+      break;
+  }
+  return hipGetLastError();
+}
+
+// Ulysses all-to-all on one GPU [SP "DeepSpeed Ulysses": the first
+// all-to-all gathers the sequence and scatters the heads, the second reverses
+// it]. The P ranks' sequence slices are [P][B][Sp][H] rows (rank p holds
+// positions p*Sp ..); their head slices are [P][B][Hp][S] rows (rank j holds
+// heads j*Hp .. over all S positions, each head's rows contiguous). Both
+// directions gather, so the writes are contiguous and every read is one whole
+// row. blockIdx.y walks destination planes -- (rank, batch, head) forward,
+// (rank, batch) inverse -- and a block copies rpb consecutive rows of one
+// plane, so the index arithmetic inside a plane is 32-bit.
+template <typename V>
+__global__ __launch_bounds__(256) void ulysses_a2a_kernel(const char* __restrict__ src,
+                                                          char* __restrict__ dst, int B, int S,
+                                                          int P, int H, int64_t row_vecs, int rpb,
+                                                          int inverse) {
+  const int Sp = S / P, Hp = H / P;
+  const int t = threadIdx.x;
+  const int sub = rpb > 1 ? t / (int)row_vecs : 0;
+  const int e0 = rpb > 1 ? t - sub * (int)row_vecs : t;
+  if (sub >= rpb) return;  // no barriers below
+  const int64_t planes = inverse ? (int64_t)P * B : (int64_t)P * B * Hp;
+  const int plane_rows = inverse ? Sp * H : S;
+  for (int64_t y = blockIdx.y; y < planes; y += gridDim.y) {
+    for (int64_t g = (int64_t)blockIdx.x * rpb; g < plane_rows; g += (int64_t)gridDim.x * rpb) {
+      const int r = (int)g + sub;
+      if (r >= plane_rows) break;
+      int64_t from;
+      if (!inverse) {  // plane (j, b, hh), row = position r
+        const int hh = (int)(y % Hp);
+        const int64_t jb = y / Hp;
+        const int b = (int)(jb % B), j = (int)(jb / B);
+        const int p = r / Sp, i = r - p * Sp;
+        from = (((int64_t)p * B + b) * Sp + i) * H + (int64_t)j * Hp + hh;
+      } else {  // plane (p, b), row = (i, h)
+        const int b = (int)(y % B), p = (int)(y / B);
+        const int i = r / H, h = r - i * H;
+        const int j = h / Hp, hh = h - j * Hp;
+        from = (((int64_t)j * B + b) * Hp + hh) * S + (int64_t)p * Sp + i;
+      }
+      const V* sp = reinterpret_cast<const V*>(src) + from * row_vecs;
+      V* dp = reinterpret_cast<V*>(dst) + (y * plane_rows + r) * row_vecs;
+      if (rpb > 1) {
+        dp[e0] = sp[e0];
+      } else {
+        for (int64_t e = e0; e < row_vecs; e += 256) dp[e] = sp[e];
+      }
+    }
+  }
+}
+
+hipError_t launch_ulysses_a2a(const void* src, void* dst, int32_t B, int64_t S, int32_t H,
+                              int64_t row_bytes, int32_t P, int inverse, hipStream_t s) {
+  if (B == 0 || S == 0 || row_bytes == 0) return hipSuccess;
+  const uintptr_t al = (uintptr_t)src | (uintptr_t)dst | (uintptr_t)row_bytes;
+  int vb = 16;
+  while (vb > 1 && (al % vb)) vb >>= 1;
+  const int64_t row_vecs = row_bytes / vb;
+  const int rpb = row_vecs <= 256 ? (int)(256 / row_vecs) : 1;
+  const int64_t planes = inverse ? (int64_t)P * B : (int64_t)P * B * (H / P);
+  const int64_t plane_rows = inverse ? (S / P) * H : S;
+  const int64_t gx = (plane_rows + rpb - 1) / rpb;
+  const dim3 grid((unsigned)(gx < 65536 ? gx : 65536), (unsigned)(planes < 65535 ? planes : 65535));
+  const char* sp = reinterpret_cast<const char*>(src);
+  char* dp = reinterpret_cast<char*>(dst);
+  const int Si = (int)S;
+  switch (vb) {
+    case 16:
+      hipLaunchKernelGGL(ulysses_a2a_kernel<uint4>, grid, dim3(256), 0, s, sp, dp, B, Si, P, H,
+                         row_vecs, rpb, inverse);
+      break;
+    case 8:
+      hipLaunchKernelGGL(ulysses_a2a_kernel<uint2>, grid, dim3(256), 0, s, sp, dp, B, Si, P, H,
+                         row_vecs, rpb, inverse);
+      break;
+    case 4:
+      hipLaunchKernelGGL(ulysses_a2a_kernel<uint32_t>, grid, dim3(256), 0, s, sp, dp, B, Si, P,
+                         H, row_vecs, rpb, inverse);
+      break;
+    case 2:
+      hipLaunchKernelGGL(ulysses_a2a_kernel<uint16_t>, grid, dim3(256), 0, s, sp, dp, B, Si, P,
+                         H, row_vecs, rpb, inverse);
+      break;
+    default:
+      hipLaunchKernelGGL(ulysses_a2a_kernel<uint8_t>, grid, dim3(256), 0, s, sp, dp, B, Si, P,
+                         H, row_vecs, rpb, inverse);
       break;
   }
   return hipGetLastError();

@@ -184,6 +184,45 @@ def test_backward_workspace_sizes_and_rejects():
     assert ring(S=0) == "RA_OK"
 
 
+def test_ulysses_workspace_sizes_and_rejects():
+    L = ra.lib()
+    # head-sharded q, out [8][1000][128] and k, v [4][1000][128], + V^T [4][128][1024] (bf16)
+    assert ra.ra_ulysses_sim_workspace_bytes(1, 8, 4, 1000, 128, BF16, 4) == \
+        2 * (8 * 1000 * 128 * 2) + 2 * (4 * 1000 * 128 * 2) + 4 * 128 * 1024 * 2
+    assert ra.ra_ulysses_sim_workspace_bytes(1, 8, 4, 1000, 128, F32, 4) == \
+        2 * (8 * 1000 * 128 * 4) + 2 * (4 * 1000 * 128 * 4)
+    assert ra.ra_ulysses_sim_workspace_bytes(1, 8, 4, 1001, 128, BF16, 4) == 0     # S % P
+
+    def sim(**kw):
+        a = dict(dt=BF16, D=128, Hq=8, Hkv=4, S=1024, P=4, q=FAKE, out=FAKE, causal=1, kv=None)
+        a.update(kw)
+        kv = None if a["kv"] is None else (ctypes.c_int32 * len(a["kv"]))(*a["kv"])
+        return ra.ra_status_str(L.ra_ulysses_sim_fwd(
+            a["q"], FAKE, FAKE, a["out"], FAKE, 1, a["Hq"], a["Hkv"], a["S"], a["D"], a["dt"],
+            a["P"], a["causal"], 0.088, kv, None, 0, None))
+    assert sim(D=96) == "RA_ERR_UNSUPPORTED"
+    assert sim(P=8) == "RA_ERR_SHAPE"                      # P > H_KV
+    assert sim(P=3) == "RA_ERR_SHAPE"                      # heads not divisible by P
+    assert sim(S=1022) == "RA_ERR_SHAPE"                   # S % P
+    assert sim(kv=[2, 2, 0, 0, 1, 1, 3, 3]) == "RA_ERR_SHAPE"   # head 0 reads rank 1's KV head
+    assert sim(kv=[1, 0, 1, 0, 3, 3, 2, 2], P=2) == "RA_ERR_WORKSPACE"  # rank-local map: fine
+    assert sim(causal=2) == "RA_ERR_ARG"
+    assert sim(q=None) == "RA_ERR_NULL"
+    assert sim(out=FAKE_ODD) == "RA_ERR_ALIGN"
+    assert sim() == "RA_ERR_WORKSPACE"
+    assert sim(S=0) == "RA_OK"
+
+    def a2a(src=FAKE, dst=ctypes.c_void_p(0x7000000), B=1, S=1024, H=8, P=4, inv=0):
+        return ra.ra_status_str(L.ra_ulysses_all_to_all(src, dst, B, S, H, 256, P, inv, None))
+    assert a2a(S=1022) == "RA_ERR_SHAPE"
+    assert a2a(H=6) == "RA_ERR_SHAPE"
+    assert a2a(P=0) == "RA_ERR_SHAPE"
+    assert a2a(inv=2) == "RA_ERR_ARG"
+    assert a2a(src=None) == "RA_ERR_NULL"
+    assert a2a(dst=ctypes.c_void_p(0x10000 + 4096)) == "RA_ERR_ARG"    # overlap
+    assert a2a(B=0) == "RA_OK" and a2a(S=0) == "RA_OK"
+
+
 def test_timing_read_without_launches():
     ra.ra_kernel_timing_enable(True)
     ms, n, fl = ra.ra_kernel_timing_read()

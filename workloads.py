@@ -32,7 +32,7 @@ class Workload:
     seed: int
     causal: bool
     N: int              # virtual ring size
-    layout: str         # "contiguous", "zigzag" or "striped"
+    layout: str         # "contiguous", "zigzag", "striped" or "ulysses"
     k_scale: float = 1.0
     note: str = ""
 
@@ -72,7 +72,14 @@ STRIPED_128K = Workload("gqa_causal_striped_s128k", B=1, Hq=64, Hkv=8, D=128, S=
                         dtype="bf16", seed=3, causal=True, N=8, layout="striped",
                         k_scale=0.5, note="rank r holds tokens r, r+8, ...")
 
-BY_NAME = {w.name: w for w in WORKLOADS + (STRIPED_128K,)}
+# The same inputs under DeepSpeed-Ulysses with 8 ranks: each rank starts with
+# a contiguous eighth of the sequence for all heads; the all-to-all gives it 8
+# query heads and 1 KV head over the whole sequence.
+ULYSSES_128K = Workload("gqa_causal_ulysses_s128k", B=1, Hq=64, Hkv=8, D=128, S=131072,
+                        dtype="bf16", seed=3, causal=True, N=8, layout="ulysses",
+                        k_scale=0.5, note="8 ranks: 8 query heads and 1 KV head each")
+
+BY_NAME = {w.name: w for w in WORKLOADS + (STRIPED_128K, ULYSSES_128K)}
 HEADLINE = WORKLOADS[3]
 
 
