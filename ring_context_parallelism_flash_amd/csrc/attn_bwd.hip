@@ -25,6 +25,8 @@
 //    (bank-conflict-free operand reads), double buffered, one barrier per
 //    tile. Both kernels add into fp32 accumulators, so the ring can sum the
 //    contributions of all block pairs.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace ra {
@@ -83,15 +85,176 @@ __device__ __forceinline__ int xcd_item(int n_items, int per_xcd) {
   return L < n_items ? L : -1;
 }
 
+// 16-byte LDS read of four floats, issued by inline asm like the operand
+// rings: the compiler waits for every outstanding direct global->LDS load
+// before an LDS read it issues itself (it cannot tell that the read does not
+// alias the loads' destination), which would drain the tile prefetch.
+template <int OFF>
+__device__ __forceinline__ float4 ds_read_f4(unsigned addr) {
+  float4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+
+// First row of a block whose position is >= P (rows if none); positions
+// increase with the row index.
+__device__ __forceinline__ int first_row_at(const PosDesc& p, int rows, int P) {
+  const int seg0 = p.nseg == 2 ? p.seg : rows;
+  const int last0 = p.start0 + (seg0 - 1) * p.stride;
+  if (P <= last0) return P <= p.start0 ? 0 : (P - p.start0 + p.stride - 1) / p.stride;
+  if (p.nseg == 2 && P <= p.start1 + (p.seg - 1) * p.stride)
+    return p.seg + (P <= p.start1 ? 0 : (P - p.start1 + p.stride - 1) / p.stride);
+  return rows;
+}
+
+// dV^T += dO^T P and dK^T += Q^T dS for one 32-query sub-tile: 4*DT MFMAs
+// whose A operands (rows d of the dO^T / Q^T tiles) stream from LDS through a
+// ring of PF registers with an explicit wait before each use. Operand i:
+// u = i / (2 DT) (16-query half), T = (i / 2) % DT (32-wide d tile), even i
+// feed dV from dO^T, odd i feed dK from Q^T.
+template <int D, int TROW, int TBUF>
+struct DkdvStream {
+  static constexpr int DT = D / 32, N = 4 * DT, PF = 4;
+  static_assert(N >= PF, "fewer operands than reads in flight");
+  static constexpr int off(int i) {
+    return ((i & 1) ? 0 : TBUF) + 32 * ((i >> 1) % DT) * TROW + 32 * (i / (2 * DT));
+  }
+  template <int I>
+  static __device__ __forceinline__ void step(unsigned ta, bf16x8 (&r)[PF], floatx16 (&dVt)[DT],
+                                              floatx16 (&dKt)[DT], const bf16x8 (&Pb)[2],
+                                              const bf16x8 (&dSb)[2]) {
+    lds_wait<(N - 1 - I < PF - 1) ? (N - 1 - I) : (PF - 1)>(r[I % PF]);
+    constexpr int T = (I >> 1) % DT, u = I / (2 * DT);
+    if constexpr ((I & 1) == 0)
+      dVt[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[I % PF], Pb[u], dVt[T], 0, 0, 0);
+    else
+      dKt[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[I % PF], dSb[u], dKt[T], 0, 0, 0);
+    if constexpr (I + PF < N) r[I % PF] = ds_read16<off(I + PF)>(ta);
+    if constexpr (I + 1 < N) step<I + 1>(ta, r, dVt, dKt, Pb, dSb);
+  }
+  template <int I>
+  static __device__ __forceinline__ void prefetch(unsigned ta, bf16x8 (&r)[PF]) {
+    r[I] = ds_read16<off(I)>(ta);
+    if constexpr (I + 1 < PF) prefetch<I + 1>(ta, r);
+  }
+  static __device__ __forceinline__ void run(unsigned ta, floatx16 (&dVt)[DT], floatx16 (&dKt)[DT],
+                                             const bf16x8 (&Pb)[2], const bf16x8 (&dSb)[2]) {
+    bf16x8 r[PF];
+    prefetch<0>(ta, r);
+    step<0>(ta, r, dVt, dKt, Pb, dSb);
+  }
+};
+
+// S = Q K^T and dP = dO V^T for one 32-query sub-tile: 2*KS MFMAs whose A
+// operands (kperm'd Q / dO rows) stream from LDS through a ring of PF
+// registers. Operand i: s = i / 2 (16-wide d step), even i = Q (S), odd i =
+// dO (dP). After MFMA i the functor `work` gets step i, so a caller can
+// spread independent arithmetic over the matrix work.
+template <int D, int ROW, int RBUF>
+struct SdpStream {
+  static constexpr int KS = D / 16, N = 2 * KS, PF = 4;
+  static constexpr int off(int i) { return ((i & 1) ? RBUF : 0) + 32 * (i >> 1); }
+  template <int I, class W>
+  static __device__ __forceinline__ void step(unsigned ra, bf16x8 (&r)[PF], const bf16x8 (&kreg)[KS],
+                                              const bf16x8 (&vreg)[KS], floatx16& S, floatx16& dP,
+                                              W& work) {
+    lds_wait<(N - 1 - I < PF - 1) ? (N - 1 - I) : (PF - 1)>(r[I % PF]);
+    if constexpr ((I & 1) == 0)
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[I % PF], kreg[I >> 1], S, 0, 0, 0);
+    else
+      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[I % PF], vreg[I >> 1], dP, 0, 0, 0);
+    if constexpr (I + PF < N) r[I % PF] = ds_read16<off(I + PF)>(ra);
+    work(std::integral_constant<int, I>{});
+    if constexpr (I + 1 < N) step<I + 1>(ra, r, kreg, vreg, S, dP, work);
+  }
+  template <int I>
+  static __device__ __forceinline__ void prefetch(unsigned ra, bf16x8 (&r)[PF]) {
+    r[I] = ds_read16<off(I)>(ra);
+    if constexpr (I + 1 < PF) prefetch<I + 1>(ra, r);
+  }
+  template <class W>
+  static __device__ __forceinline__ void run(unsigned ra, const bf16x8 (&kreg)[KS],
+                                             const bf16x8 (&vreg)[KS], floatx16& S, floatx16& dP,
+                                             W& work) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      S[i] = 0.f;
+      dP[i] = 0.f;
+    }
+    bf16x8 r[PF];
+    prefetch<0>(ra, r);
+    step<0>(ra, r, kreg, vreg, S, dP, work);
+  }
+};
+
+// P = exp2(S c - lse2) and dS = P (dP - delta) of a 32-query sub-tile,
+// rounded to bf16 (the B operands of the dV / dK products), PER elements per
+// step of the next sub-tile's S / dP stream. Element e = 8w + jj of a lane is
+// row offset 16w + jj of the sub-tile; causal: masked iff that offset is
+// below lim.
+template <int PER>
+struct DkdvProbs {
+  const floatx16& S;
+  const floatx16& dP;
+  const float (&l2)[16];
+  const float (&dl)[16];
+  float c;
+  int lim;
+  bf16x8 (&Pb)[2];
+  bf16x8 (&dSb)[2];
+  template <int I>
+  __device__ __forceinline__ void operator()(std::integral_constant<int, I>) {
+#pragma unroll
+    for (int e = I * PER; e < (I + 1) * PER; ++e) {
+      const int w = e >> 3, jj = e & 7;
+      float sc = fmaf(S[e], c, -l2[e]);
+      sc = (16 * w + jj < lim) ? -INFINITY : sc;
+      const float p = __builtin_amdgcn_exp2f(sc);
+      Pb[w][jj] = (__bf16)p;
+      dSb[w][jj] = (__bf16)(p * (dP[e] - dl[e]));
+    }
+  }
+};
+struct NoWork {
+  template <int I>
+  __device__ __forceinline__ void operator()(std::integral_constant<int, I>) {}
+};
+
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup = 4 waves x 32 keys of one KV head.
+// dK, dV: one workgroup = 4 waves x 32 keys of one KV head, one wave per SIMD.
+//
+// The 64-query tiles of every query head that reads the KV head form one
+// stream, walked in 32-query sub-tiles j = 0, 1, ... Iteration j issues the
+// S and dP MFMAs of sub-tile j+1 with the probability arithmetic of sub-tile
+// j spread between them (the VALU work runs under the wave's own matrix
+// work), then the dV and dK MFMAs of sub-tile j. Both MFMA streams read their
+// LDS operands through explicit register rings. LDS holds two buffers of
+// Q / dO rows (read by the S, dP products) and two of Q^T / dO^T plus the
+// rows' lse2 and delta (read by the dV, dK products and the arithmetic).
+// Rows of tile u+2 are loaded at the start of iteration 2u+1 and Q^T/dO^T of
+// tile u+2 at the start of iteration 2u+2: each load has two iterations to
+// land before the barrier that publishes it.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
   using L = BwdLds<D>;
   constexpr int KS = D / 16, DT = D / 32;
-  constexpr int OFF_DO = L::RBUF, OFF_QT = 2 * L::RBUF, OFF_DOT = 2 * L::RBUF + L::TBUF;
-  constexpr int OFF_L = 2 * L::RBUF + 2 * L::TBUF, OFF_DL = OFF_L + 256, BUF = OFF_DL + 256;
+  constexpr int ROWS_BUF = 2 * L::RBUF;  // Q rows, dO rows
+  // lse2 and delta get 1 KiB each: the wave that loads them uses all 64
+  // lanes (lanes 16..63 repeat lanes 0..15), so every counted load is a
+  // whole-wave instruction
+  constexpr int OFF_L = 2 * L::TBUF, OFF_DL = OFF_L + 1024;
+  constexpr int TRANS_BUF = 2 * L::TBUF + 2048;  // Q^T, dO^T, lse2, delta
+  constexpr int OFF_TRANS = 2 * ROWS_BUF;
+  constexpr int OFF_HTAB = OFF_TRANS + 2 * TRANS_BUF;  // kMaxHeads ints
+  using G1 = SdpStream<D, L::ROW, L::RBUF>;
+  using G2 = DkdvStream<D, L::TROW, L::TBUF>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
   const int item = xcd_item(a.n_items, a.per_xcd);
@@ -99,7 +262,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
   const int kt = item % a.n_tiles;
   const int rest = item / a.n_tiles;
   const int g = rest % a.Hkv, b = rest / a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: load branches are per wave
   const int n = lane & 31, hh = lane >> 5;
   const int k0 = kt * 128, kw0 = k0 + 32 * wv;
   const int keyc = min(kw0 + n, a.Ck - 1);
@@ -112,6 +276,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
   for (int s = 0; s < KS; ++s) {
     kreg[s] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)keyc * D + 16 * s + 8 * hh);
     vreg[s] = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)keyc * D + 16 * s + 8 * hh);
+    // K and V are only ever MFMA operands: keep them in AGPRs, which leaves
+    // the VGPRs to the probability arithmetic
+    asm volatile("" : "+a"(kreg[s]));
+    asm volatile("" : "+a"(vreg[s]));
   }
   floatx16 dKt[DT], dVt[DT];
 #pragma unroll
@@ -122,91 +290,140 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
       dVt[T][i] = 0.f;
     }
   const int kpos = pos_of(a.kp, keyc);
-  const int wave_kmax = pos_of(a.kp, min(kw0 + 31, a.Ck - 1));
+  // causal: this lane's key is seen by query rows >= row_min only
+  const int row_min = a.causal ? first_row_at(a.qp, a.Cq, kpos) : 0;
   const int wg_kmin = pos_of(a.kp, min(k0, a.Ck - 1));
   // query rows before the first one that sees a key of this workgroup
   const int q_lo = a.causal ? allowed_prefix(a.qp, wg_kmin - 1) : 0;
   const int t_lo = q_lo / 64;
   const int n_t = max(0, (a.Cq + 63) / 64 - t_lo);
+  const int g0 = a.grp_off[g], ng = a.grp_off[g + 1] - g0;
+  const int NT = ng * n_t;  // tiles in the stream
+  // The group's query heads go to an LDS table once: a runtime-indexed read
+  // of the kernel-argument array inside the loop would be a vector-memory
+  // load, and waiting for it would also drain the in-flight tile loads.
+  int* htab = reinterpret_cast<int*>(lds + OFF_HTAB);
+  if (tid < ng) htab[tid] = a.head_order[g0 + tid];
+  auto head_at = [&](int i) -> int {  // i wave-uniform; the table is published
+    int v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(v)
+                 : "v"(lds_addr(htab + i))
+                 : "memory");
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  const int NJ = 2 * NT;                         // sub-tiles (even)
   const int rbase = kperm(n) * L::ROW + hh * 16;  // A operand of S / dP (+32 rows per sub-tile)
+  // Direct loads per batch: the 1 KiB loads of a tile are dealt round-robin
+  // to the 4 waves, so a wave issues at least VM_MIN of them in either batch
+  // (rows: 2 tiles of RINS; transposed: 2 of TINS, plus lse2 / delta on
+  // waves 0 / 1). Loads complete in order, so waiting until at most VM_MIN
+  // are outstanding retires every older batch.
+  constexpr int VM_MIN = 2 * ((L::RINS < L::TINS ? L::RINS : L::TINS) / 4);
 
-  for (int gi = a.grp_off[g]; gi < a.grp_off[g + 1]; ++gi) {
-    const int h = a.head_order[gi];
-    const __bf16* qb = reinterpret_cast<const __bf16*>(a.q) + b * a.q_bs + h * a.q_hs;
-    const __bf16* db = reinterpret_cast<const __bf16*>(a.dout) + b * a.q_bs + h * a.q_hs;
-    const __bf16* qtb = reinterpret_cast<const __bf16*>(a.qt) + b * a.qt_bs + h * a.qt_hs;
-    const __bf16* dtb = reinterpret_cast<const __bf16*>(a.dot) + b * a.qt_bs + h * a.qt_hs;
-    const float* l2b = a.lse2 + b * a.l_bs + h * a.l_hs;
-    const float* dlb = a.delta + b * a.l_bs + h * a.l_hs;
-    auto load_tile = [&](int t, int buf) {
-      const int q0 = (t_lo + t) * 64;
-      unsigned char* B0 = lds + buf * BUF;
-      load_row_tile<D>(qb + (int64_t)q0 * D, a.Cq - 1 - q0, B0, wv, lane);
-      load_row_tile<D>(db + (int64_t)q0 * D, a.Cq - 1 - q0, B0 + OFF_DO, wv, lane);
-      load_trans_tile<D>(qtb + q0, a.Cqp, B0 + OFF_QT, wv, lane);
-      load_trans_tile<D>(dtb + q0, a.Cqp, B0 + OFF_DOT, wv, lane);
-      if (wv == 0 && lane < 16) load_lds16(l2b + q0 + 4 * lane, B0 + OFF_L);
-      if (wv == 1 && lane < 16) load_lds16(dlb + q0 + 4 * lane, B0 + OFF_DL);
-    };
-    if (n_t > 0) load_tile(0, 0);
-    for (int t = 0; t < n_t; ++t) {
-      lds_loads_barrier();  // tile t landed; every wave is done with tile t-1
-      if (t + 1 < n_t) load_tile(t + 1, (t + 1) & 1);
-      const unsigned char* B0 = lds + (t & 1) * BUF;
-      const int q0 = (t_lo + t) * 64;
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys;
-        // element i of a lane is query 32qs + 16(i/8) + 8hh + i%8 of the tile
-        floatx16 S, dP;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          S[i] = 0.f;
-          dP[i] = 0.f;
-        }
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(B0 + rbase + qs * 32 * L::ROW + s * 32);
-          const bf16x8 da =
-              *reinterpret_cast<const bf16x8*>(B0 + OFF_DO + rbase + qs * 32 * L::ROW + s * 32);
-          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[s], S, 0, 0, 0);
-          dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[s], dP, 0, 0, 0);
-        }
-        const int qrow0 = q0 + 32 * qs;
-        const bool need_mask = a.causal && pos_of(a.qp, min(qrow0, a.Cq - 1)) < wave_kmax;
-        bf16x8 Pb[2], dSb[2];
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const int r0 = 32 * qs + 16 * w + 8 * hh;  // first of this lane's 8 rows
-          const float* lp = reinterpret_cast<const float*>(B0 + OFF_L) + r0;
-          const float* dp_ = reinterpret_cast<const float*>(B0 + OFF_DL) + r0;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int i = 8 * w + j;
-            float sc = S[i] * c - lp[j];
-            if (need_mask) {
-              const int qp_ = pos_of(a.qp, min(q0 + r0 + j, a.Cq - 1));
-              sc = (kpos <= qp_) ? sc : -INFINITY;
-            }
-            const float p = __builtin_amdgcn_exp2f(sc);
-            Pb[w][j] = (__bf16)p;
-            dSb[w][j] = (__bf16)(p * (dP[i] - dp_[j]));
-          }
-        }
-        // dV^T += dO^T P, dK^T += Q^T dS (A: row d of the transposed tiles)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int T = 0; T < DT; ++T) {
-            const int toff = (32 * T + n) * L::TROW + (32 * qs + 16 * u + 8 * hh) * 2;
-            const bf16x8 doa = *reinterpret_cast<const bf16x8*>(B0 + OFF_DOT + toff);
-            const bf16x8 qta = *reinterpret_cast<const bf16x8*>(B0 + OFF_QT + toff);
-            dVt[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doa, Pb[u], dVt[T], 0, 0, 0);
-            dKt[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, dSb[u], dKt[T], 0, 0, 0);
-          }
-      }
+  struct TileSrc {
+    int h, q0;
+  };
+  auto tile_src = [&](int T) -> TileSrc {
+    const int hi = T / n_t;
+    return TileSrc{head_at(hi), (t_lo + (T - hi * n_t)) * 64};
+  };
+  auto load_rows = [&](int T) {
+    const TileSrc ts = tile_src(T);
+    const int64_t off = b * a.q_bs + ts.h * a.q_hs + (int64_t)ts.q0 * D;
+    unsigned char* B0 = lds + (T & 1) * ROWS_BUF;
+    load_row_tile<D>(reinterpret_cast<const __bf16*>(a.q) + off, a.Cq - 1 - ts.q0, B0, wv, lane);
+    load_row_tile<D>(reinterpret_cast<const __bf16*>(a.dout) + off, a.Cq - 1 - ts.q0,
+                     B0 + L::RBUF, wv, lane);
+  };
+  auto load_trans = [&](int T) {
+    const TileSrc ts = tile_src(T);
+    const int64_t toff = b * a.qt_bs + ts.h * a.qt_hs + ts.q0;
+    const int64_t loff = b * a.l_bs + ts.h * a.l_hs + ts.q0;
+    unsigned char* B0 = lds + OFF_TRANS + (T & 1) * TRANS_BUF;
+    load_trans_tile<D>(reinterpret_cast<const __bf16*>(a.qt) + toff, a.Cqp, B0, wv, lane);
+    load_trans_tile<D>(reinterpret_cast<const __bf16*>(a.dot) + toff, a.Cqp, B0 + L::TBUF, wv,
+                       lane);
+    if (wv == 0) load_lds16(a.lse2 + loff + 4 * (lane & 15), B0 + OFF_L);
+    if (wv == 1) load_lds16(a.delta + loff + 4 * (lane & 15), B0 + OFF_DL);
+  };
+  // LDS address of the A operands of S / dP for sub-tile jn: kperm'd rows, so
+  // element i of a lane's result is query 32(jn%2) + 16(i/8) + 8hh + i%8
+  auto g1_addr = [&](int jn) -> unsigned {
+    return lds_addr(lds + ((jn >> 1) & 1) * ROWS_BUF) + rbase + (jn & 1) * 32 * L::ROW;
+  };
+
+  bool issued = false;  // this wave issued a load batch at the start of the previous iteration
+  auto iter = [&](int j, const floatx16& Sc, const floatx16& dPc, floatx16& Sn, floatx16& dPn) {
+    if (j > 0) {
+      // the batch of two iterations ago has landed in this wave ...
+      if (issued)
+        vm_wait<VM_MIN>();
+      else
+        vm_wait<0>();
+      // ... and in every wave; every wave is done with iteration j-1 (its LDS
+      // reads were all waited for)
+      workgroup_barrier();
     }
-    __syncthreads();  // the next head's first tile reuses buffer 0
+    issued = false;
+    if (j & 1) {
+      if ((j >> 1) + 2 < NT) {
+        load_rows((j >> 1) + 2);
+        issued = true;
+      }
+    } else if (j >= 2 && (j >> 1) + 1 < NT) {
+      load_trans((j >> 1) + 1);
+      issued = true;
+    }
+    const unsigned char* TB = lds + OFF_TRANS + ((j >> 1) & 1) * TRANS_BUF;
+    const int r0 = 32 * (j & 1) + 8 * hh;  // rows r0 + 16w + jj of the tile
+    float l2[16], dl[16];
+    const unsigned la = lds_addr(TB) + r0 * 4;
+    const float4 lx[4] = {ds_read_f4<OFF_L>(la), ds_read_f4<OFF_L + 16>(la),
+                          ds_read_f4<OFF_L + 64>(la), ds_read_f4<OFF_L + 80>(la)};
+    const float4 dx[4] = {ds_read_f4<OFF_DL>(la), ds_read_f4<OFF_DL + 16>(la),
+                          ds_read_f4<OFF_DL + 64>(la), ds_read_f4<OFF_DL + 80>(la)};
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int w = 0; w < 2; ++w)
+#pragma unroll
+      for (int v4 = 0; v4 < 2; ++v4) {
+        const float4 x = lx[2 * w + v4];
+        const float4 y = dx[2 * w + v4];
+        l2[8 * w + 4 * v4 + 0] = x.x;
+        l2[8 * w + 4 * v4 + 1] = x.y;
+        l2[8 * w + 4 * v4 + 2] = x.z;
+        l2[8 * w + 4 * v4 + 3] = x.w;
+        dl[8 * w + 4 * v4 + 0] = y.x;
+        dl[8 * w + 4 * v4 + 1] = y.y;
+        dl[8 * w + 4 * v4 + 2] = y.z;
+        dl[8 * w + 4 * v4 + 3] = y.w;
+      }
+    bf16x8 Pb[2], dSb[2];
+    DkdvProbs<16 / G1::N> pr{Sc, dPc, l2, dl, c, row_min - (tile_src(j >> 1).q0 + r0), Pb, dSb};
+    // the S, dP MFMAs of sub-tile j+1 (past the end: a stale but valid
+    // buffer, result unused) with this sub-tile's arithmetic between them
+    G1::run(g1_addr(min(j + 1, NJ - 1)), kreg, vreg, Sn, dPn, pr);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    G2::run(lds_addr(TB) + n * L::TROW + r0 * 2, dVt, dKt, Pb, dSb);
+  };
+
+  __syncthreads();  // the head table
+  if (NT > 0) {
+    load_rows(0);
+    load_trans(0);
+    if (NT > 1) {
+      load_rows(1);
+      load_trans(1);
+    }
+    lds_loads_barrier();
+    floatx16 SA, dPA, SB, dPB;
+    NoWork nw;
+    G1::run(g1_addr(0), kreg, vreg, SA, dPA, nw);
+    for (int j = 0; j < NJ; j += 2) {  // NJ is even
+      iter(j, SA, dPA, SB, dPB);
+      iter(j + 1, SB, dPB, SA, dPA);
+    }
   }
 
   // epilogue: add into the fp32 accumulators; lane holds key kw0+n,
@@ -236,14 +453,76 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
   }
 }
 
+// dQ^T += K^T dS^T for one 32-key sub-tile: 2*DT MFMAs whose A operands
+// (rows d of the K^T tile, 16 keys each) stream from LDS through a ring of PF
+// registers. Operand i: u = i / DT (16-key half), T = i % DT (32-wide d tile).
+template <int D, int TROW>
+struct DqStream {
+  static constexpr int DT = D / 32, N = 2 * DT, PF = 4;
+  static_assert(N >= PF, "fewer operands than reads in flight");
+  static constexpr int off(int i) { return 32 * (i % DT) * TROW + 32 * (i / DT); }
+  template <int I>
+  static __device__ __forceinline__ void step(unsigned ka, bf16x8 (&r)[PF], floatx16 (&dQt)[DT],
+                                              const bf16x8 (&dSb)[2]) {
+    lds_wait<(N - 1 - I < PF - 1) ? (N - 1 - I) : (PF - 1)>(r[I % PF]);
+    dQt[I % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[I % PF], dSb[I / DT], dQt[I % DT], 0, 0, 0);
+    if constexpr (I + PF < N) r[I % PF] = ds_read16<off(I + PF)>(ka);
+    if constexpr (I + 1 < N) step<I + 1>(ka, r, dQt, dSb);
+  }
+  template <int I>
+  static __device__ __forceinline__ void prefetch(unsigned ka, bf16x8 (&r)[PF]) {
+    r[I] = ds_read16<off(I)>(ka);
+    if constexpr (I + 1 < PF) prefetch<I + 1>(ka, r);
+  }
+  static __device__ __forceinline__ void run(unsigned ka, floatx16 (&dQt)[DT], const bf16x8 (&dSb)[2]) {
+    bf16x8 r[PF];
+    prefetch<0>(ka, r);
+    step<0>(ka, r, dQt, dSb);
+  }
+};
+
+// dS^T = P^T (dP^T - delta) of a 32-key sub-tile for the lane's query,
+// rounded to bf16 (the B operands of the dQ product), PER elements per step of
+// the next sub-tile's S^T / dP^T stream. Element e of a lane is key offset
+// 16(e/8) + 8hh + e%8 of the sub-tile; it is masked iff 16(e/8) + e%8 >= lim
+// (keys at or past the lane's allowed prefix, or past the block end).
+template <int PER>
+struct DqProbs {
+  const floatx16& S;
+  const floatx16& dP;
+  float lse2, dlt, c;
+  int lim;
+  bf16x8 (&dSb)[2];
+  template <int I>
+  __device__ __forceinline__ void operator()(std::integral_constant<int, I>) {
+#pragma unroll
+    for (int e = I * PER; e < (I + 1) * PER; ++e) {
+      float sc = fmaf(S[e], c, -lse2);
+      sc = (16 * (e >> 3) + (e & 7) >= lim) ? -INFINITY : sc;
+      const float p = __builtin_amdgcn_exp2f(sc);
+      dSb[e >> 3][e & 7] = (__bf16)(p * (dP[e] - dlt));
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
-// dQ: one workgroup = 4 waves x 32 queries of one query head.
+// dQ: one workgroup = 4 waves x 32 queries of one query head, one wave per
+// SIMD. The 64-key tiles are walked in 32-key sub-tiles j: iteration j issues
+// the S^T and dP^T MFMAs of sub-tile j+1 with the arithmetic of sub-tile j
+// spread between them, then the dQ MFMAs of sub-tile j. K and V rows (read
+// by S^T, dP^T) and K^T (read by dQ) have two LDS buffers each; rows of tile
+// u+2 are loaded at the start of iteration 2u+1, K^T of tile u+2 at the start
+// of iteration 2u+2, as in the dK / dV kernel.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dq(const BwdArgs a) {
   using L = BwdLds<D>;
   constexpr int KS = D / 16, DT = D / 32;
-  constexpr int OFF_V = L::RBUF, OFF_KT = 2 * L::RBUF, BUF = 2 * L::RBUF + L::TBUF;
+  constexpr int ROWS_BUF = 2 * L::RBUF;  // K rows, V rows
+  constexpr int TRANS_BUF = L::TBUF;     // K^T
+  constexpr int OFF_TRANS = 2 * ROWS_BUF;
+  using G1 = SdpStream<D, L::ROW, L::RBUF>;
+  using G2 = DqStream<D, L::TROW>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
   const int item = xcd_item(a.n_items, a.per_xcd);
@@ -253,7 +532,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq(const BwdArgs a) {
   const int hidx = rest % a.Hq, b = rest / a.Hq;
   const int h = a.head_order[hidx], g = a.kv_of[h];
   const int q0 = (a.n_tiles - 1 - qt_rel) * 128;  // latest (heaviest) query tiles first
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: load branches are per wave
   const int n = lane & 31, hh = lane >> 5;
   const int qw0 = q0 + 32 * wv;
   const int qi = qw0 + n;
@@ -267,15 +547,20 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq(const BwdArgs a) {
   for (int s = 0; s < KS; ++s) {
     qreg[s] = *reinterpret_cast<const bf16x8*>(qb + (int64_t)qc * D + 16 * s + 8 * hh);
     dreg[s] = *reinterpret_cast<const bf16x8*>(db + (int64_t)qc * D + 16 * s + 8 * hh);
+    // only ever MFMA operands: keep them in AGPRs
+    asm volatile("" : "+a"(qreg[s]));
+    asm volatile("" : "+a"(dreg[s]));
   }
   // rows past Cq read the padding: lse2 = +inf, so their probabilities are 0
   const float lse2 = a.lse2[b * a.l_bs + h * a.l_hs + qi];
   const float dlt = a.delta[b * a.l_bs + h * a.l_hs + qi];
   const int qpos = pos_of(a.qp, qc);
-  const int wave_qmin = pos_of(a.qp, min(qw0, a.Cq - 1));
+  // keys this lane's query sees: a prefix of the block (positions increase)
+  const int n_allow = a.causal ? allowed_prefix(a.kp, qpos) : a.Ck;
   const int wg_qmax = pos_of(a.qp, min(q0 + 127, a.Cq - 1));
   const int n_keys = a.causal ? allowed_prefix(a.kp, wg_qmax) : a.Ck;
-  const int n_kt = (n_keys + 63) / 64;
+  const int NT = (n_keys + 63) / 64;  // key tiles
+  const int NJ = 2 * NT;              // 32-key sub-tiles (even)
 
   floatx16 dQt[DT];
 #pragma unroll
@@ -286,61 +571,75 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq(const BwdArgs a) {
   const __bf16* kb = reinterpret_cast<const __bf16*>(a.k) + b * a.k_bs + g * a.k_hs;
   const __bf16* vb = reinterpret_cast<const __bf16*>(a.v) + b * a.k_bs + g * a.k_hs;
   const __bf16* ktb = reinterpret_cast<const __bf16*>(a.kt) + b * a.kt_bs + g * a.kt_hs;
-  auto load_tile = [&](int t, int buf) {
-    const int kb0 = t * 64;
-    unsigned char* B0 = lds + buf * BUF;
+  auto load_rows = [&](int T) {
+    const int kb0 = T * 64;
+    unsigned char* B0 = lds + (T & 1) * ROWS_BUF;
     load_row_tile<D>(kb + (int64_t)kb0 * D, a.Ck - 1 - kb0, B0, wv, lane);
-    load_row_tile<D>(vb + (int64_t)kb0 * D, a.Ck - 1 - kb0, B0 + OFF_V, wv, lane);
-    load_trans_tile<D>(ktb + kb0, a.Ckp, B0 + OFF_KT, wv, lane);
+    load_row_tile<D>(vb + (int64_t)kb0 * D, a.Ck - 1 - kb0, B0 + L::RBUF, wv, lane);
+  };
+  auto load_trans = [&](int T) {
+    load_trans_tile<D>(ktb + T * 64, a.Ckp, lds + OFF_TRANS + (T & 1) * TRANS_BUF, wv, lane);
   };
   const int rbase = kperm(n) * L::ROW + hh * 16;
-  if (n_kt > 0) load_tile(0, 0);
-  for (int t = 0; t < n_kt; ++t) {
-    lds_loads_barrier();
-    if (t + 1 < n_kt) load_tile(t + 1, (t + 1) & 1);
-    const unsigned char* B0 = lds + (t & 1) * BUF;
-    const int kb0 = t * 64;
-    const bool need_mask =
-        kb0 + 64 > a.Ck || (a.causal && pos_of(a.kp, min(kb0 + 63, a.Ck - 1)) > wave_qmin);
-    bf16x8 dSb[4];
-#pragma unroll
-    for (int th = 0; th < 2; ++th) {
-      // S^T, dP^T for 32 keys (kperm rows) x this wave's 32 queries; element i
-      // of a lane is key 32th + 16(i/8) + 8hh + i%8 of the tile
-      floatx16 S, dP;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        S[i] = 0.f;
-        dP[i] = 0.f;
-      }
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(B0 + rbase + th * 32 * L::ROW + s * 32);
-        const bf16x8 va =
-            *reinterpret_cast<const bf16x8*>(B0 + OFF_V + rbase + th * 32 * L::ROW + s * 32);
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s], S, 0, 0, 0);
-        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, dreg[s], dP, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float sc = S[i] * c - lse2;
-        if (need_mask) {
-          const int key = kb0 + 32 * th + 16 * (i >> 3) + 8 * hh + (i & 7);
-          sc = masked(sc, key, a.Ck, a.causal, a.kp, qpos);
-        }
-        const float p = __builtin_amdgcn_exp2f(sc);
-        dSb[2 * th + (i >> 3)][i & 7] = (__bf16)(p * (dP[i] - dlt));
-      }
+  auto g1_addr = [&](int jn) -> unsigned {
+    return lds_addr(lds + ((jn >> 1) & 1) * ROWS_BUF) + rbase + (jn & 1) * 32 * L::ROW;
+  };
+  // Loads per batch: rows (K and V of one tile) at least RMIN per wave, K^T
+  // at least TMIN; loads complete in order, so waiting until at most that
+  // many of the latest batch are outstanding retires every older batch.
+  constexpr int RMIN = 2 * (L::RINS / 4), TMIN = L::TINS / 4;
+
+  bool issued = false;
+  auto iter = [&](int j, const floatx16& Sc, const floatx16& dPc, floatx16& Sn, floatx16& dPn) {
+    if (j > 0) {
+      // the batch issued two iterations ago has landed in this wave ...
+      if (!issued)
+        vm_wait<0>();
+      else if ((j - 1) & 1)
+        vm_wait<RMIN>();  // the previous iteration issued rows
+      else
+        vm_wait<TMIN>();  // ... or K^T
+      // ... and in every wave; every wave is done with iteration j-1 (its LDS
+      // reads were all waited for)
+      workgroup_barrier();
     }
-    // dQ^T += K^T dS^T (A: row d of the K^T tile, keys 16u + 8h ..)
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int T = 0; T < DT; ++T) {
-        const bf16x8 kta = *reinterpret_cast<const bf16x8*>(
-            B0 + OFF_KT + (32 * T + n) * L::TROW + (16 * u + 8 * hh) * 2);
-        dQt[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kta, dSb[u], dQt[T], 0, 0, 0);
+    issued = false;
+    if (j & 1) {
+      if ((j >> 1) + 2 < NT) {
+        load_rows((j >> 1) + 2);
+        issued = true;
       }
+    } else if (j >= 2 && (j >> 1) + 1 < NT) {
+      load_trans((j >> 1) + 1);
+      issued = true;
+    }
+    bf16x8 dSb[2];
+    const int lim = n_allow - ((j >> 1) * 64 + 32 * (j & 1) + 8 * hh);
+    DqProbs<16 / G1::N> pr{Sc, dPc, lse2, dlt, c, lim, dSb};
+    // the S^T, dP^T MFMAs of sub-tile j+1 (past the end: a stale but valid
+    // buffer, result unused) with this sub-tile's arithmetic between them
+    G1::run(g1_addr(min(j + 1, NJ - 1)), qreg, dreg, Sn, dPn, pr);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    G2::run(lds_addr(lds + OFF_TRANS + ((j >> 1) & 1) * TRANS_BUF) + n * L::TROW +
+                (32 * (j & 1) + 8 * hh) * 2,
+            dQt, dSb);
+  };
+
+  if (NT > 0) {
+    load_rows(0);
+    load_trans(0);
+    if (NT > 1) {
+      load_rows(1);
+      load_trans(1);
+    }
+    lds_loads_barrier();
+    floatx16 SA, dPA, SB, dPB;
+    NoWork nw;
+    G1::run(g1_addr(0), qreg, dreg, SA, dPA, nw);
+    for (int j = 0; j < NJ; j += 2) {  // NJ is even
+      iter(j, SA, dPA, SB, dPB);
+      iter(j + 1, SB, dPB, SA, dPA);
+    }
   }
 
   if (qi < a.Cq) {
@@ -426,7 +725,8 @@ __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float4* __restri
 
 template <int D>
 constexpr size_t dkdv_lds_bytes() {
-  return (size_t)2 * (2 * BwdLds<D>::RBUF + 2 * BwdLds<D>::TBUF + 512);
+  return (size_t)2 * (2 * BwdLds<D>::RBUF) + (size_t)2 * (2 * BwdLds<D>::TBUF + 2048) +
+         4 * kMaxHeads;
 }
 template <int D>
 constexpr size_t dq_lds_bytes() {

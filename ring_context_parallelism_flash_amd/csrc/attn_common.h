@@ -65,6 +65,24 @@ __device__ __forceinline__ void lds_loads_barrier() {
   __syncthreads();
 }
 
+// Workgroup barrier without the memory fence of __syncthreads(). That fence
+// makes the compiler wait for every outstanding vector-memory operation --
+// including direct global->LDS tile loads meant to stay in flight across the
+// barrier. Callers wait explicitly for what the barrier publishes: their own
+// tile loads (vmcnt) and their LDS reads (lgkmcnt, the operand rings wait for
+// every read they issue). The "memory" clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void workgroup_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// This lane's index in the wave, computed by volatile asm: an expression of
+// it cannot be hoisted out of a loop (a hoisted per-lane value stays live in
+// a register through the loop).
+__device__ __forceinline__ int lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // 32-bit LDS address of a pointer into this workgroup's LDS.
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(size_t)(const __attribute__((address_space(3))) void*)p;

@@ -283,8 +283,12 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs 
   // a chunk of the same row.
   // Direct loads (group B): instruction j of loading wave lw fills chunks
   // P = (lw + LW*j)*64 + lane of the tile; offsets are computed at issue time
-  // (the softmax phase that issues them has VALU to spare).
+  // (the softmax phase that issues them has VALU to spare). The lane index is
+  // re-read by volatile asm so that the per-lane row / chunk values are not
+  // hoisted out of the key loop: kept live, they were spilled to scratch, and
+  // the wait for a scratch reload also waited for the tile loads just issued.
   auto load_k = [&](int kt, int buf) {
+    const int lane = lane_id();
     const int kb = kt * 64;
     const int rows_left = a.Ck - 1 - kb;  // last valid row of this tile
     const __bf16* base = kbp + (int64_t)kb * D;
@@ -300,6 +304,7 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs 
       }
   };
   auto load_v = [&](int kt, int buf) {
+    const int lane = lane_id();
     const __bf16* base = vtb + kt * 64;
     unsigned char* dst = Vs + buf * VBUF + lw * 1024;
 #pragma unroll
@@ -458,14 +463,14 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs 
       __builtin_amdgcn_s_setprio(0);
       // this wave's loads from its last P-phase land before the barrier
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      workgroup_barrier();
       if (grpB) {
         if (t + 3 < n_kt) load_k(t + 3, (t + 1) & 1);
       } else {
         if (t + 1 < n_kt) load_v(t + 1, (t + 1) & 1);
       }
       pv_phase(t & 1, P);
-      __syncthreads();
+      workgroup_barrier();
     };
     int t = 0;
     for (; t + 1 < n_kt; t += 2) {
