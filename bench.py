@@ -38,32 +38,36 @@ PEAK_HBM_GBS = 8000.0
 # reported only while the kernel sources still hash to what was profiled.
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_bf16_gqa128k_pmc.txt")
 KERNEL_SOURCES = ("attn_fwd.hip", "attn_common.h", "attn_fwd_args.h")
+# The same for the backward kernels, per block pair (one dk/dv + one dq launch).
+BWD_PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_bwd_bf16_gqa128k_pmc.txt")
+BWD_KERNEL_SOURCES = ("attn_bwd.hip", "attn_common.h", "attn_bwd_args.h")
 
 
-def kernel_sources_sha256() -> str:
+def kernel_sources_sha256(sources=KERNEL_SOURCES) -> str:
     import hashlib
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in sources:
         with open(os.path.join(ROOT, "ring_context_parallelism_flash_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload_name: str):
-    """HBM bytes per attention launch from the committed counter summary, or
-    (None, reason) when it does not describe this workload or these sources."""
+def measured_traffic(workload_name: str, summary=PMC_SUMMARY, sources=KERNEL_SOURCES):
+    """HBM bytes per launch (per block pair for the backward) from a committed
+    counter summary, or (None, reason) when it does not describe this
+    workload or these sources."""
     try:
         kv = {}
-        with open(PMC_SUMMARY) as f:
+        with open(summary) as f:
             for line in f:
                 if line.startswith("@ ") and "=" in line:
                     key, val = line[2:].split("=", 1)
                     kv[key.strip()] = val.strip()
         if kv.get("workload") != workload_name:
             return None, "no counter summary for this workload"
-        if kv.get("sources_sha256") != kernel_sources_sha256():
+        if kv.get("sources_sha256") != kernel_sources_sha256(sources):
             return None, "kernel sources changed since the counters were taken"
-        return int(float(kv["traffic_bytes_per_launch"])), PMC_SUMMARY[len(ROOT) + 1:]
+        return int(float(kv["traffic_bytes_per_launch"])), summary[len(ROOT) + 1:]
     except (OSError, KeyError, ValueError) as e:
         return None, f"counter summary unreadable: {e}"
 
@@ -156,6 +160,7 @@ def bench_backward(args, w, q, k, v, runner, out, lse) -> int:
     ra.ra_kernel_timing_enable(False)
     print(f"bench: timed {args.steps} backward steps in {t1 - t0:.3f} s", file=sys.stderr, flush=True)
     flops_step = 2.5 * useful_flops(w)   # 10*D per pair against the forward's 4*D
+    traffic, traffic_src = measured_traffic(w.name, BWD_PMC_SUMMARY, BWD_KERNEL_SOURCES)
     ms_step = (t1 - t0) * 1e3 / args.steps
     value = flops_step / (ms_step / 1e3) / 1e12
     achieved = k_flops / (k_ms / 1e3) / 1e12 if k_ms > 0 else 0.0
@@ -184,15 +189,32 @@ def bench_backward(args, w, q, k, v, runner, out, lse) -> int:
             "peak": round(PEAK_BF16_TFLOPS, 1),
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
-            "traffic_source": "no counter summary for the backward kernels",
+            "traffic": traffic,
+            "traffic_unit": "HBM bytes per block pair, dk/dv + dq launch (FETCH_SIZE x2.0 + "
+                            "WRITE_SIZE x1.0)",
+            "traffic_source": traffic_src,
             "launches_per_step": launches // max(args.steps, 1),
             "kernel_ms_per_step": round(k_ms / max(args.steps, 1), 3),
         },
         "flops_check": {"closed_form": flops_step, "library_count": k_flops / max(args.steps, 1)},
     }
     print(json.dumps(line), flush=True)
+    calibration_copy(args, dev)
     return 0
+
+
+def calibration_copy(args, dev):
+    """One plain device copy of a known size, a reference for byte counters."""
+    import torch
+    if args.copy_calibration_mib <= 0:
+        return
+    n = args.copy_calibration_mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"bench: calibration copy of {n} bytes done", file=sys.stderr, flush=True)
 
 
 def bench_ulysses(args, w, q_cpu, k_cpu, v_cpu, dev) -> int:
@@ -437,14 +459,7 @@ def main(argv=None) -> int:
         line["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, out.cpu(), lse.cpu(),
                                             args.cpu_seconds, args.cpu_rows)
     print(json.dumps(line), flush=True)
-    if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"bench: calibration copy of {n} bytes done", file=sys.stderr, flush=True)
+    calibration_copy(args, dev)
     return 0
 
 

@@ -594,34 +594,12 @@ ra_status check_bwd(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, ra_dtype dt,
 }
 
 // Work decomposition and head tables of both backward kernels.
-void fill_bwd_heads(BwdArgs& a, int32_t Hq, int32_t Hkv, const std::vector<uint8_t>& kv_of,
-                    const std::vector<uint8_t>& order) {
-  memset(a.head_order, 0, sizeof a.head_order);
-  memset(a.kv_of, 0, sizeof a.kv_of);
-  memset(a.grp_off, 0, sizeof a.grp_off);
-  for (int h = 0; h < Hq; ++h) {
-    a.head_order[h] = order[h];
-    a.kv_of[h] = kv_of[h];
-  }
-  std::vector<int> count(Hkv + 1, 0);
-  for (int h = 0; h < Hq; ++h) count[kv_of[h] + 1]++;
-  for (int g = 0; g < Hkv; ++g) count[g + 1] += count[g];
-  for (int g = 0; g <= Hkv; ++g) a.grp_off[g] = (uint16_t)count[g];
-}
-
-// Both kernels for one block pair (dq, dk, dv fp32 accumulators added to).
 ra_status launch_bwd_pair(BwdArgs a, int32_t D, hipStream_t s) {
   const double pairs = (double)(a.Ck > 0 ? pairs_between(a.qp, a.Cq, a.kp, a.Ck, a.causal) : 0);
   if (a.Cq == 0 || a.Ck == 0) return RA_OK;
   const double fl = (double)D * a.B * a.Hq * pairs;
-  a.n_tiles = (a.Ck + 127) / 128;
-  a.n_items = a.B * a.Hkv * a.n_tiles;
-  a.per_xcd = (a.n_items + kXcds - 1) / kXcds;
   ra_status st = timed(s, 8.0 * fl, [&] { return launch_bwd_dkdv(a, D, s); });
   if (st != RA_OK) return st;
-  a.n_tiles = (a.Cq + 127) / 128;
-  a.n_items = a.B * a.Hq * a.n_tiles;
-  a.per_xcd = (a.n_items + kXcds - 1) / kXcds;
   return timed(s, 2.0 * fl, [&] { return launch_bwd_dq(a, D, s); });
 }
 }  // namespace

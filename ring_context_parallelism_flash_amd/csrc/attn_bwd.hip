@@ -25,7 +25,10 @@
 //    (bank-conflict-free operand reads), double buffered, one barrier per
 //    tile. Both kernels add into fp32 accumulators, so the ring can sum the
 //    contributions of all block pairs.
+#include <string.h>
+
 #include <type_traits>
+#include <vector>
 
 #include "attn_common.h"
 
@@ -230,7 +233,8 @@ struct NoWork {
 // dK, dV: one workgroup = 4 waves x 32 keys of one KV head, one wave per SIMD.
 //
 // The 64-query tiles of every query head that reads the KV head form one
-// stream, walked in 32-query sub-tiles j = 0, 1, ... Iteration j issues the
+// stream (tile-major, latest tile first), walked in 32-query sub-tiles j = 0,
+// 1, ... Iteration j issues the
 // S and dP MFMAs of sub-tile j+1 with the probability arithmetic of sub-tile
 // j spread between them (the VALU work runs under the wave's own matrix
 // work), then the dV and dK MFMAs of sub-tile j. Both MFMA streams read their
@@ -324,9 +328,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
   struct TileSrc {
     int h, q0;
   };
+  // Stream order: query tiles from the last down to t_lo, and for each tile
+  // every query head of the group. All workgroups of a KV head start on the
+  // block's last tile and move down together (where t_lo differs -- a causal
+  // diagonal block -- the shorter ranges just end earlier), so they read the
+  // same Q / dO tiles at about the same time and share them in L2.
   auto tile_src = [&](int T) -> TileSrc {
-    const int hi = T / n_t;
-    return TileSrc{head_at(hi), (t_lo + (T - hi * n_t)) * 64};
+    const int tr = T / ng;
+    return TileSrc{head_at(T - tr * ng), (t_lo + n_t - 1 - tr) * 64};
   };
   auto load_rows = [&](int T) {
     const TileSrc ts = tile_src(T);
@@ -745,14 +754,35 @@ hipError_t launch_big(K kern, size_t lds, int grid, const BwdArgs& a, hipStream_
 
 }  // namespace
 
-hipError_t launch_bwd_dkdv(const BwdArgs& a, int D, hipStream_t s) {
+void fill_bwd_heads(BwdArgs& a, int32_t Hq, int32_t Hkv, const std::vector<uint8_t>& kv_of,
+                    const std::vector<uint8_t>& order) {
+  memset(a.head_order, 0, sizeof a.head_order);
+  memset(a.kv_of, 0, sizeof a.kv_of);
+  memset(a.grp_off, 0, sizeof a.grp_off);
+  for (int h = 0; h < Hq; ++h) {
+    a.head_order[h] = order[h];
+    a.kv_of[h] = kv_of[h];
+  }
+  std::vector<int> count(Hkv + 1, 0);
+  for (int h = 0; h < Hq; ++h) count[kv_of[h] + 1]++;
+  for (int g = 0; g < Hkv; ++g) count[g + 1] += count[g];
+  for (int g = 0; g <= Hkv; ++g) a.grp_off[g] = (uint16_t)count[g];
+}
+
+hipError_t launch_bwd_dkdv(BwdArgs a, int D, hipStream_t s) {
+  a.n_tiles = (a.Ck + 127) / 128;  // 128-key workgroups, per (batch, KV head)
+  a.n_items = a.B * a.Hkv * a.n_tiles;
+  a.per_xcd = (a.n_items + kXcds - 1) / kXcds;
   if (a.n_items <= 0) return hipSuccess;
   const int grid = a.per_xcd * kXcds;
   if (D == 128) return launch_big(attn_bwd_dkdv<128>, dkdv_lds_bytes<128>(), grid, a, s);
   return launch_big(attn_bwd_dkdv<64>, dkdv_lds_bytes<64>(), grid, a, s);
 }
 
-hipError_t launch_bwd_dq(const BwdArgs& a, int D, hipStream_t s) {
+hipError_t launch_bwd_dq(BwdArgs a, int D, hipStream_t s) {
+  a.n_tiles = (a.Cq + 127) / 128;  // 128-query workgroups, per (batch, query head)
+  a.n_items = a.B * a.Hq * a.n_tiles;
+  a.per_xcd = (a.n_items + kXcds - 1) / kXcds;
   if (a.n_items <= 0) return hipSuccess;
   const int grid = a.per_xcd * kXcds;
   if (D == 128) return launch_big(attn_bwd_dq<128>, dq_lds_bytes<128>(), grid, a, s);

@@ -174,3 +174,47 @@ def test_ring_bwd_gqa_128k_invariants_and_sampled_dq():
           flush=True)
     assert e_dv <= 1e-2
     assert e_dk <= 1e-3
+
+
+# ------------------------------------------------------- head maps and groups
+@pytest.mark.parametrize("kv_map,Hkv", [([1, 0, 1, 0, 0, 1], 2), ([2, 0, 1, 1, 2, 0, 0, 2], 3)])
+def test_block_bwd_custom_head_map(kv_map, Hkv):
+    """Query heads that read their KV heads out of order (the dk/dv kernel
+    walks each KV head's query heads from a per-workgroup head table)."""
+    Hq, Cq, Ck, D = len(kv_map), 192, 160, 128
+    q, k, v = _rnd((1, Hq, Cq, D), 71), _rnd((1, Hkv, Ck, D), 72), _rnd((1, Hkv, Ck, D), 73)
+    dout = _rnd((1, Hq, Cq, D), 74)
+    qp, kp = (1, Cq, 100), (1, Ck, 0)
+    qpa, kpa = _pos_array(qp, Cq), _pos_array(kp, Ck)
+    out, lse = oracle.attention(q, k, v, causal=True, q_pos=qpa, k_pos=kpa, kv_head_of_q=kv_map)
+    ref = oracle.attention_backward(q, k, v, dout, causal=True, q_pos=qpa, k_pos=kpa,
+                                    kv_head_of_q=kv_map)
+    dq = torch.zeros(1, Hq, Cq, D, device=DEV)
+    dk = torch.zeros(1, Hkv, Ck, D, device=DEV)
+    dv = torch.zeros(1, Hkv, Ck, D, device=DEV)
+    ra.ra_block_attn_bwd(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(out).to(torch.bfloat16).to(DEV),
+                         dout.to(DEV), torch.from_numpy(lse).float().to(DEV), dq, dk, dv,
+                         q_pos=qp, k_pos=kp, causal=True, kv_head_of_q=kv_map)
+    torch.cuda.synchronize()
+    _check_grads([_np(dq), _np(dk), _np(dv)], ref, f"head map {kv_map}")
+
+
+def test_ring_bwd_large_group_and_map():
+    """16 query heads on one KV head (one long head stream per workgroup) and a
+    ring with a permuted head map."""
+    w = workloads.Workload("bwd_mqa16", B=1, Hq=16, Hkv=1, D=64, S=512, dtype="bf16", seed=81,
+                           causal=True, N=4, layout="zigzag")
+    (q, k, v, dout), got = _ring_fwd_bwd(w, 181)
+    _check_grads([_np(t) for t in got], oracle.attention_backward(q, k, v, dout, causal=True),
+                 "ring mqa16")
+    kv_map = [1, 1, 0, 1, 0, 0]
+    q, k, v = _rnd((1, 6, 384, 128), 82), _rnd((1, 2, 384, 128), 83), _rnd((1, 2, 384, 128), 84)
+    dout = _rnd((1, 6, 384, 128), 85)
+    qd, kd, vd, dd = (t.to(DEV) for t in (q, k, v, dout))
+    out, lse = ra.ring_attention_sim(qd, kd, vd, N=3, layout="striped", causal=True,
+                                     kv_head_of_q=kv_map)
+    grads = ra.ring_attention_sim_backward(qd, kd, vd, out, lse, dd, N=3, layout="striped",
+                                           causal=True, kv_head_of_q=kv_map)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(q, k, v, dout, causal=True, kv_head_of_q=kv_map)
+    _check_grads([_np(t) for t in grads], ref, "ring striped head map")
