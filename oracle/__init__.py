@@ -14,4 +14,5 @@ from .fp64_bwd import (  # noqa: F401
 )
 from .fp64_ulysses import (  # noqa: F401
     ulysses_all_to_all, ulysses_all_to_all_inverse, ulysses_attention, ulysses_volume,
+    usp_attention, usp_token_lists,
 )

@@ -113,3 +113,74 @@ def ulysses_volume(B: int, S: int, H: int, D: int, P: int) -> float:
     (P-1)/P * b*(s/P)*h is the one that stays constant when s and P grow
     together, as the page says."""
     return (P - 1) / P * B * S * H * D
+
+
+# ---------------------------------------------------------------------------
+# Unified sequence parallelism [SP "Unified Sequence Parallelism (USP / 2D
+# SP)": Ulysses all-to-all inside a node across heads, the ring across nodes
+# circulating (K, V)].
+#
+# Readings (the page gives the grid, not the token assignment):
+#   * the ring dimension assigns tokens to the P_r nodes as the ring layout
+#     does for P_r ranks (contiguous, zigzag or striped); node n's token list
+#     L_n is that rank's positions in memory order;
+#   * inside node n, device u of the P_u Ulysses devices holds the contiguous
+#     piece L_n[u*C/P_u : (u+1)*C/P_u] (C = S/P_r) for all heads;
+#   * the intra-node all-to-all gives device u of every node the node's whole
+#     list L_n for head group u; the ring then runs over the P_r nodes, once
+#     per head group, on those tokens; the reverse all-to-all returns the
+#     output to the device slices;
+#   * lse stays with the device that computed it: [P_u, B, H/P_u, S], its
+#     sequence axis in node-major order (L_0, then L_1, ...).
+# ---------------------------------------------------------------------------
+def usp_token_lists(S: int, P_r: int, layout: str) -> np.ndarray:
+    """[P_r, S/P_r] global positions of each node's tokens (the ring layout)."""
+    from .fp64 import layout_order
+    return layout_order(S, P_r, layout).reshape(P_r, S // P_r)
+
+
+def usp_attention(q, k, v, *, P_u: int, P_r: int, layout: str, causal: bool,
+                  scale: float | None = None, kv_head_of_q=None):
+    """USP forward in float64.
+
+    q: [P_r*P_u, B, S/(P_r*P_u), Hq, D], k, v: [.., Hkv, D]: the slice of
+    device d = n*P_u + u, holding positions usp_token_lists(...)[n][u-th
+    piece]. Returns (out in the same layout as q, lse [P_u, B, Hq/P_u, S]).
+    """
+    from .fp64 import ring_attention
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    P = P_r * P_u
+    _, B, Sp, Hq, D = q.shape
+    Hkv = k.shape[3]
+    C = Sp * P_u                     # tokens per node
+    S = C * P_r
+    _check(P_u, C, Hq)
+    _check(P_u, C, Hkv)
+    kv_map = _kv_map(Hq, Hkv, kv_head_of_q)
+    Hqp, Hkvp = Hq // P_u, Hkv // P_u
+    for h in range(Hq):
+        if kv_map[h] // Hkvp != h // Hqp:
+            raise ValueError(f"query head {h} reads KV head {kv_map[h]} held by another device")
+    lists = usp_token_lists(S, P_r, layout)
+    # intra-node all-to-all: node n's devices -> [P_u, B, C, H/P_u, D]
+    heads = [[ulysses_all_to_all(t[n * P_u:(n + 1) * P_u], P_u) for n in range(P_r)]
+             for t in (q, k, v)]
+    out_h = [np.zeros_like(heads[0][n]) for n in range(P_r)]
+    lse = np.zeros((P_u, B, Hqp, S))
+    order = lists.reshape(-1)        # node-major position list
+    inv = np.argsort(order)
+    for u in range(P_u):
+        local_map = [kv_map[u * Hqp + h] - u * Hkvp for h in range(Hqp)]
+        # head group u over the whole sequence, in sequence order: [B, heads, S, D]
+        seq = []
+        for t in range(3):
+            nm = np.concatenate([heads[t][n][u] for n in range(P_r)], axis=1)  # [B, S, H, D]
+            seq.append(nm.transpose(0, 2, 1, 3)[:, :, inv])
+        o, l = ring_attention(seq[0], seq[1], seq[2], N=P_r, layout=layout, causal=causal,
+                              scale=scale, kv_head_of_q=local_map)
+        o_nm, l_nm = o[:, :, order], l[:, :, order]      # back to node-major order
+        for n in range(P_r):
+            out_h[n][u] = o_nm[:, :, n * C:(n + 1) * C].transpose(0, 2, 1, 3)
+        lse[u] = l_nm
+    out = np.concatenate([ulysses_all_to_all_inverse(out_h[n], P_u) for n in range(P_r)], axis=0)
+    return out, lse

@@ -176,3 +176,104 @@ def test_ulysses_planted_mistake_is_caught(name):
     m = _mutant(*MUTATIONS[name])
     with pytest.raises(AssertionError):
         _battery(m)
+
+
+# ====================================================================== USP
+USP_GOLDEN = pathlib.Path(__file__).parent / "golden" / "usp_devices.json"
+
+
+def _usp_shard(x, P_u, P_r, layout):
+    """[B, H, S, D] sequence order -> device slices [P_r*P_u, B, S/(P_r*P_u), H, D]."""
+    B, H, S, D = x.shape
+    L = oracle.usp_token_lists(S, P_r, layout).reshape(-1)
+    xs = x[:, :, L].transpose(0, 2, 1, 3)
+    return xs.reshape(B, P_r * P_u, S // (P_r * P_u), H, D).transpose(1, 0, 2, 3, 4)
+
+
+def test_usp_golden_device_positions():
+    g = json.loads(USP_GOLDEN.read_text())
+    lists = oracle.usp_token_lists(g["S"], g["P_r"], g["layout"])
+    np.testing.assert_array_equal(lists, np.array(g["node_token_lists"]))
+    pos = np.arange(g["S"], dtype=float)[None, None, :, None]          # value = position
+    dev = _usp_shard(pos, g["P_u"], g["P_r"], g["layout"])[:, 0, :, 0, 0]
+    np.testing.assert_array_equal(dev, np.array(g["device_positions"]))
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag", "striped"])
+@pytest.mark.parametrize("P_u,P_r,Hq,Hkv,causal", [(2, 4, 4, 2, True), (4, 2, 8, 4, True),
+                                                   (2, 2, 4, 2, False), (1, 4, 2, 1, True),
+                                                   (4, 1, 4, 4, True)])
+def test_usp_exact_equals_single_device(layout, P_u, P_r, Hq, Hkv, causal):
+    S, D = 64, 8
+    q, k, v = _rand((1, Hq, S, D), 31), _rand((1, Hkv, S, D), 32), _rand((1, Hkv, S, D), 33)
+    out, lse = oracle.usp_attention(*(_usp_shard(t, P_u, P_r, layout) for t in (q, k, v)),
+                                    P_u=P_u, P_r=P_r, layout=layout, causal=causal)
+    ro, rl = oracle.attention(q, k, v, causal=causal)
+    L = oracle.usp_token_lists(S, P_r, layout).reshape(-1)
+    np.testing.assert_allclose(out, _usp_shard(ro, P_u, P_r, layout), atol=1e-12)
+    np.testing.assert_allclose(lse.transpose(1, 0, 2, 3).reshape(1, Hq, S), rl[:, :, L], atol=1e-12)
+
+
+def test_usp_reduces_to_ulysses_and_to_ring():
+    S, D, Hq, Hkv = 48, 8, 4, 2
+    q, k, v = _rand((1, Hq, S, D), 34), _rand((1, Hkv, S, D), 35), _rand((1, Hkv, S, D), 36)
+    # one node: USP is Ulysses over P_u devices
+    uo, ul = oracle.ulysses_attention(_shard(q, 4 // 2), _shard(k, 2), _shard(v, 2), P=2, causal=True)
+    so, sl = oracle.usp_attention(_shard(q, 2), _shard(k, 2), _shard(v, 2), P_u=2, P_r=1,
+                                  layout="contiguous", causal=True)
+    np.testing.assert_allclose(so, uo, atol=1e-12)
+    np.testing.assert_allclose(sl, ul, atol=1e-12)
+    # one device per node: USP is the ring over P_r ranks (lse in rank-major order)
+    ro, rl = oracle.ring_attention(q, k, v, N=4, layout="zigzag", causal=True)
+    so, sl = oracle.usp_attention(*(_usp_shard(t, 1, 4, "zigzag") for t in (q, k, v)), P_u=1,
+                                  P_r=4, layout="zigzag", causal=True)
+    L = oracle.usp_token_lists(S, 4, "zigzag").reshape(-1)
+    np.testing.assert_allclose(so, _usp_shard(ro, 1, 4, "zigzag"), atol=1e-12)
+    np.testing.assert_allclose(sl[0], rl[:, :, L], atol=1e-12)
+
+
+def test_usp_degree_limit():
+    """The Ulysses dimension is bounded by the KV heads: degree H_KV x nodes."""
+    z = lambda *s: np.zeros(s)
+    oracle.usp_attention(z(16, 1, 2, 8, 4), z(16, 1, 2, 8, 4), z(16, 1, 2, 8, 4), P_u=8, P_r=2,
+                         layout="contiguous", causal=True)
+    with pytest.raises(ValueError):
+        oracle.usp_attention(z(32, 1, 1, 16, 4), z(32, 1, 1, 8, 4), z(32, 1, 1, 8, 4), P_u=16,
+                             P_r=2, layout="contiguous", causal=True)
+
+
+def _usp_battery(m):
+    S, D, Hq, Hkv, P_u, P_r = 32, 8, 8, 4, 2, 2
+    kv_map = [1, 0, 1, 0, 3, 2, 2, 3]
+    q, k, v = _rand((1, Hq, S, D), 37), _rand((1, Hkv, S, D), 38), _rand((1, Hkv, S, D), 39)
+    for layout in ("zigzag", "striped"):
+        out, lse = m.usp_attention(*(_usp_shard(t, P_u, P_r, layout) for t in (q, k, v)), P_u=P_u,
+                                   P_r=P_r, layout=layout, causal=True, kv_head_of_q=kv_map)
+        ro, rl = oracle.attention(q, k, v, causal=True, kv_head_of_q=kv_map)
+        L = oracle.usp_token_lists(S, P_r, layout).reshape(-1)
+        np.testing.assert_allclose(out, _usp_shard(ro, P_u, P_r, layout), atol=1e-10)
+        np.testing.assert_allclose(lse.transpose(1, 0, 2, 3).reshape(1, Hq, S), rl[:, :, L],
+                                   atol=1e-10)
+
+
+USP_MUTATIONS = {
+    "a2a_across_nodes": ("ulysses_all_to_all(t[n * P_u:(n + 1) * P_u], P_u)",
+                         "ulysses_all_to_all(t[n::P_r], P_u)"),
+    "node_order_taken_as_sequence": ("order = lists.reshape(-1)        # node-major position list",
+                                     "order = np.arange(S)"),
+    "usp_local_map_not_shifted": (
+        "        local_map = [kv_map[u * Hqp + h] - u * Hkvp for h in range(Hqp)]\n        # head group u",
+        "        local_map = [kv_map[h] for h in range(Hqp)]\n        # head group u"),
+    "lse_in_sequence_order": ("lse[u] = l_nm", "lse[u] = l"),
+}
+
+
+def test_unmutated_usp_passes_battery():
+    _usp_battery(good)
+
+
+@pytest.mark.parametrize("name", sorted(USP_MUTATIONS))
+def test_usp_planted_mistake_is_caught(name):
+    m = _mutant(*USP_MUTATIONS[name])
+    with pytest.raises(AssertionError):
+        _usp_battery(m)
