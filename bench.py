@@ -316,6 +316,112 @@ def bench_ulysses(args, w, q_cpu, k_cpu, v_cpu, dev) -> int:
     return 0
 
 
+def bench_usp(args, w, q_cpu, k_cpu, v_cpu, dev) -> int:
+    """One step = unified sequence parallelism on P_r = N / P_u nodes of P_u
+    devices, simulated on one GPU: the intra-node all-to-all of q, k, v, the
+    ring across the nodes for every head group, and the reverse all-to-all.
+    Inputs are laid out once, before timing, as the devices' slices (the
+    node token lists of the ring layout, split across each node's devices).
+    Useful work as for the ring: 4*D flops per allowed pair."""
+    import torch
+    import ring_context_parallelism_flash_amd as ra
+    P_u, P_r = w.P_u, w.N // w.P_u
+    perm = {"zigzag": ra.ra_zigzag_permute, "striped": ra.ra_striped_permute}.get(w.ring_layout)
+
+    def shard(x):
+        x = x.to(dev)
+        if perm is not None:                      # sequence order -> node-major order
+            y = torch.empty_like(x)
+            perm(x, y, P_r)
+            x = y
+        B, H, S, D = x.shape
+        return (x.permute(0, 2, 1, 3).reshape(B, P_r * P_u, S // (P_r * P_u), H, D)
+                .permute(1, 0, 2, 3, 4).contiguous())
+
+    q, k, v = (shard(t) for t in (q_cpu, k_cpu, v_cpu))
+    out = torch.empty_like(q)
+    lse = torch.empty((P_u, w.B, w.Hq // P_u, w.S), dtype=torch.float32, device=dev)
+    ws = torch.empty(ra.ra_usp_sim_workspace_bytes(w.B, w.Hq, w.Hkv, w.S, w.D, q.dtype, P_u, P_r),
+                     dtype=torch.uint8, device=dev)
+    copy = torch.cuda.Stream(device=dev)
+
+    def step():
+        ra.ra_usp_sim_fwd(q, k, v, out, lse, P_u=P_u, P_r=P_r, layout=w.ring_layout,
+                          causal=w.causal, workspace=ws, copy_stream=copy)
+
+    print(f"bench: usp warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ra.ra_kernel_timing_enable(True)
+    ra.ra_kernel_timing_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    k_ms, launches, k_flops = ra.ra_kernel_timing_read()
+    ra.ra_kernel_timing_enable(False)
+    print(f"bench: timed {args.steps} usp steps in {t1 - t0:.3f} s", file=sys.stderr, flush=True)
+    flops_step = useful_flops(w)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    value = flops_step / (ms_step / 1e3) / 1e12
+    achieved = k_flops / (k_ms / 1e3) / 1e12 if k_ms > 0 else 0.0
+    line = {
+        "metric": f"usp attn fwd useful TFLOP/s, {w.name}",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid normal q/k/v, k x0.5, bf16)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "S": w.S,
+                   "virtual_devices": w.N, "nodes": P_r, "devices_per_node": P_u,
+                   "ring_layout": w.ring_layout, "causal": w.causal},
+        "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "useful_flops_per_step": flops_step,
+        "roofline": {
+            "kernel": f"attn_fwd_bf16<{w.D}>",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": round(PEAK_BF16_TFLOPS, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "traffic_source": "no counter summary for this workload",
+            "launches_per_step": launches // max(args.steps, 1),
+            "avg_launch_ms": round(k_ms / max(launches, 1), 4),
+            "flops_per_launch": k_flops / max(launches, 1),
+            "kernel_ms_per_step": round(k_ms / max(args.steps, 1), 3),
+        },
+        "flops_check": {"closed_form": flops_step, "library_count": k_flops / max(args.steps, 1)},
+    }
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        node_major = torch.empty(w.S, dtype=torch.long)
+        pos = torch.arange(w.S, dtype=torch.float32, device=dev)[None, None, :, None]
+        if perm is not None:
+            y = torch.empty_like(pos)
+            perm(pos, y, P_r)
+            pos = y
+        node_major = pos[0, 0, :, 0].long().cpu()              # node-major -> position
+        inv = torch.empty_like(node_major)
+        inv[node_major] = torch.arange(w.S)
+        o = out.cpu().permute(1, 0, 2, 3, 4).reshape(w.B, w.S, w.Hq, w.D)[:, inv]
+        o = o.permute(0, 2, 1, 3)
+        l_ = lse.cpu().permute(1, 0, 2, 3).reshape(w.B, w.Hq, w.S)[:, :, inv]
+        line["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, o, l_, args.cpu_seconds,
+                                            args.cpu_rows)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -350,6 +456,11 @@ def main(argv=None) -> int:
             print("bench.py: no backward for the Ulysses workload", file=sys.stderr)
             return 2
         return bench_ulysses(args, w, q_cpu, k_cpu, v_cpu, dev)
+    if w.layout == "usp":
+        if args.backward:
+            print("bench.py: no backward for the USP workload", file=sys.stderr)
+            return 2
+        return bench_usp(args, w, q_cpu, k_cpu, v_cpu, dev)
     q, k, v = (t.to(dev) for t in (q_cpu, k_cpu, v_cpu))
     runner = ra.RingRunner(w.B, w.Hq, w.Hkv, w.S, w.D, q.dtype, w.N, w.layout, w.causal,
                            device=dev)

@@ -16,7 +16,8 @@
  *         the 4-GPU ring figure, "Algorithmic Mechanics" (online-softmax
  *         equations for m_new, l_new, O_new), "Overlapping Compute and
  *         Communication", "Causal Masking and Load Balancing"; and "DeepSpeed
- *         Ulysses: Head-to-Sequence All-to-All Transposition".
+ *         Ulysses: Head-to-Sequence All-to-All Transposition" and "Unified
+ *         Sequence Parallelism (USP / 2D SP)".
  *   [SCP] "Sequence and Context Parallelism" (praveentn.live): "What it does
  *         not change".
  *
@@ -344,11 +345,44 @@ ra_status ra_ulysses_sim_fwd(const void* q, const void* k, const void* v, void* 
                              void* stream);
 
 /* ------------------------------------------------------------------------
+ * ra_usp_sim_fwd -- unified sequence parallelism on a P_r x P_u device grid,
+ * simulated on one GPU.
+ *
+ * [SP "Unified Sequence Parallelism (USP / 2D SP)": Ulysses all-to-all across
+ *  heads inside a node, the ring circulating (K, V) across nodes; SP
+ *  "DeepSpeed Ulysses" for the all-to-all; CP listing / SP "Algorithmic
+ *  Mechanics" for the ring.]
+ *
+ * Device d = n*P_u + u is device u of node n. Node n holds the C = S/P_r
+ * positions the ring layout gives ring rank n (contiguous, zigzag or
+ * striped), in that rank's memory order; device u holds the contiguous piece
+ * u of that list, all heads: q [P_r*P_u][B][S/(P_r*P_u)][Hq][D], k, v
+ * [..][Hkv][D] of `dtype`; out: the same layout as q, of `dtype`. The call
+ * runs, per node, the all-to-all of q, k, v among its P_u devices (device u
+ * then holds the node's C positions for heads u*Hq/P_u ..), the ring across
+ * the P_r nodes for every head group (as ra_ring_sim_fwd), and the reverse
+ * all-to-all of the output. lse: float32 [P_u][B][Hq/P_u][S] -- head group
+ * u, sequence axis in ring rank-major order (node 0's positions, then node
+ * 1's, ...). Hq and Hkv divisible by P_u, and kv_head_of_q (NULL: h /
+ * (Hq/Hkv)) rank-local as for ra_ulysses_sim_fwd; S divisible by P_r*P_u
+ * (and by 2*P_r for RA_ZIGZAG). workspace: ra_usp_sim_workspace_bytes(...)
+ * bytes, 256-byte aligned, clobbered. copy_stream as for ra_ring_sim_fwd.
+ * ---------------------------------------------------------------------- */
+size_t ra_usp_sim_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D,
+                                  ra_dtype dtype, int32_t P_u, int32_t P_r);
+
+ra_status ra_usp_sim_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                         int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D, ra_dtype dtype,
+                         int32_t P_u, int32_t P_r, ra_layout layout, int32_t causal, float scale,
+                         const int32_t* kv_head_of_q, void* workspace, size_t workspace_bytes,
+                         void* compute_stream, void* copy_stream);
+
+/* ------------------------------------------------------------------------
  * Kernel timing for measurement (not part of the computation).
  *
  * While enabled, every attention-kernel launch made by ra_block_attn_fwd,
- * ra_ring_sim_fwd, ra_ulysses_sim_fwd, ra_block_attn_bwd and ra_ring_sim_bwd
- * is bracketed by a
+ * ra_ring_sim_fwd, ra_ulysses_sim_fwd, ra_usp_sim_fwd, ra_block_attn_bwd and
+ * ra_ring_sim_bwd is bracketed by a
  * pair of HIP events recorded on the stream it is launched on, and the
  * allowed (query, key) pairs it processes are counted on the host.
  * ra_kernel_timing_read waits for the recorded events, returns the summed

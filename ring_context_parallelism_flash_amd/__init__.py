@@ -22,7 +22,8 @@ __all__ = [
     "ra_ring_sim_bwd_workspace_bytes", "ra_ring_sim_bwd", "ring_attention_sim_backward",
     "ra_ring_sim_fwd", "ra_kernel_timing_enable", "ra_kernel_timing_read", "zigzag_pos",
     "contiguous_pos", "striped_pos", "ring_attention_sim", "ra_ulysses_all_to_all",
-    "ra_ulysses_sim_workspace_bytes", "ra_ulysses_sim_fwd", "EXPORTS",
+    "ra_ulysses_sim_workspace_bytes", "ra_ulysses_sim_fwd", "ra_usp_sim_workspace_bytes",
+    "ra_usp_sim_fwd", "EXPORTS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -39,8 +40,8 @@ EXPORTS = (
     "ra_lse_merge", "ra_zigzag_permute", "ra_striped_permute", "ra_ring_sim_workspace_bytes",
     "ra_ring_sim_fwd", "ra_block_attn_bwd_workspace_bytes", "ra_block_attn_bwd",
     "ra_ring_sim_bwd_workspace_bytes", "ra_ring_sim_bwd", "ra_ulysses_all_to_all",
-    "ra_ulysses_sim_workspace_bytes", "ra_ulysses_sim_fwd",
-    "ra_kernel_timing_enable", "ra_kernel_timing_read",
+    "ra_ulysses_sim_workspace_bytes", "ra_ulysses_sim_fwd", "ra_usp_sim_workspace_bytes",
+    "ra_usp_sim_fwd", "ra_kernel_timing_enable", "ra_kernel_timing_read",
 )
 
 
@@ -111,6 +112,12 @@ def lib() -> ctypes.CDLL:
                                          c_int32, c_int32, c_int32, c_int64, c_int32, c_int32,
                                          c_int32, c_int32, c_float, P(c_int32), c_void_p,
                                          c_size_t, c_void_p]),
+        "ra_usp_sim_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int64, c_int32,
+                                                  c_int32, c_int32, c_int32]),
+        "ra_usp_sim_fwd": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_int32, c_int32, c_int32, c_int64, c_int32, c_int32,
+                                     c_int32, c_int32, c_int32, c_int32, c_float, P(c_int32),
+                                     c_void_p, c_size_t, c_void_p, c_void_p]),
         "ra_kernel_timing_enable": (c_int32, [c_int32]),
         "ra_kernel_timing_read": (c_int32, [P(ctypes.c_double), P(c_int64),
                                             P(ctypes.c_double)]),
@@ -367,6 +374,34 @@ def ra_ulysses_sim_fwd(q, k, v, out, lse, *, P, causal=True, scale=None, kv_head
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, S, D, dt, P,
         int(bool(causal)), float(scale), _kvmap(kv_head_of_q, Hq), _ptr(workspace), wbytes,
         _stream(stream)))
+    return out, lse
+
+
+def ra_usp_sim_workspace_bytes(B, Hq, Hkv, S, D, dtype, P_u, P_r) -> int:
+    dt = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib().ra_usp_sim_workspace_bytes(B, Hq, Hkv, S, D, dt, P_u, P_r))
+
+
+def ra_usp_sim_fwd(q, k, v, out, lse, *, P_u, P_r, layout="zigzag", causal=True, scale=None,
+                   kv_head_of_q=None, workspace=None, compute_stream=None, copy_stream=None):
+    """USP on a P_r x P_u grid on one GPU. q, out: [P_r*P_u, B, S/(P_r*P_u), Hq, D];
+    k, v: [.., Hkv, D]; lse: float32 [P_u, B, Hq/P_u, S] (see include/ring_attn.h)."""
+    _, B, Sp, Hq, D = q.shape
+    Hkv = k.shape[3]
+    S = Sp * P_u * P_r
+    dt = _dtype(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        workspace = torch.empty(ra_usp_sim_workspace_bytes(B, Hq, Hkv, S, D, dt, P_u, P_r),
+                                dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    xs = None if copy_stream is None else _stream(copy_stream)
+    _check(lib().ra_usp_sim_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, S, D, dt, P_u, P_r,
+        _LAYOUTS[layout] if isinstance(layout, str) else int(layout), int(bool(causal)),
+        float(scale), _kvmap(kv_head_of_q, Hq), _ptr(workspace), wbytes,
+        _stream(compute_stream), xs))
     return out, lse
 
 

@@ -952,6 +952,118 @@ ra_status ra_ulysses_sim_fwd(const void* q, const void* k, const void* v, void* 
   return RA_OK;
 }
 
+// ---------------------------------------------------------------- USP
+namespace {
+// Workspace of the USP simulation: head-sharded [q][k][v][out] (input dtype),
+// each [P_u][B][H/P_u][S][D] with the ring's rank-major sequence, then one
+// ring workspace (reused by the P_u head groups in turn).
+struct UspLayout {
+  size_t q, k, v, o, ring, ring_bytes, total;
+};
+UspLayout usp_layout(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D, ra_dtype dt,
+                     int32_t P_u, int32_t P_r) {
+  auto up = [](size_t x) { return (size_t)round_up((int64_t)x, 256); };
+  UspLayout L{};
+  const size_t es = esize(dt);
+  const size_t qb = up((size_t)B * Hq * S * D * es), kb = up((size_t)B * Hkv * S * D * es);
+  L.q = 0;
+  L.k = qb;
+  L.v = qb + kb;
+  L.o = qb + 2 * kb;
+  L.ring = 2 * qb + 2 * kb;
+  L.ring_bytes = up(ra_ring_sim_workspace_bytes(B, Hq / P_u, Hkv / P_u, S, D, dt, P_r));
+  L.total = L.ring + L.ring_bytes;
+  return L;
+}
+}  // namespace
+
+size_t ra_usp_sim_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D,
+                                  ra_dtype dtype, int32_t P_u, int32_t P_r) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || D < 1 || P_u < 1 || P_r < 1) return 0;
+  if (Hq % P_u || Hkv % P_u || S % ((int64_t)P_u * P_r)) return 0;
+  if (dtype != RA_BF16 && dtype != RA_F32) return 0;
+  return usp_layout(B, Hq, Hkv, S, D, dtype, P_u, P_r).total;
+}
+
+ra_status ra_usp_sim_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                         int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t D, ra_dtype dtype,
+                         int32_t P_u, int32_t P_r, ra_layout layout, int32_t causal, float scale,
+                         const int32_t* kv_head_of_q, void* workspace, size_t workspace_bytes,
+                         void* compute_stream, void* copy_stream) {
+  g_err[0] = 0;
+  std::vector<uint8_t> kv_of, order;
+  ra_status st = check_common(B, Hq, Hkv, D, dtype, kv_head_of_q, scale, kv_of, order);
+  if (st != RA_OK) return st;
+  if (layout != RA_CONTIGUOUS && layout != RA_ZIGZAG && layout != RA_STRIPED)
+    return fail(RA_ERR_ARG, "unknown layout");
+  if (causal != 0 && causal != 1) return fail(RA_ERR_ARG, "causal must be 0 or 1");
+  if (P_u < 1 || P_r < 1) return fail(RA_ERR_SHAPE, "P_u and P_r must be >= 1");
+  if (Hq % P_u || Hkv % P_u)
+    return fail(RA_ERR_SHAPE, "Hq=%d and Hkv=%d must be divisible by P_u=%d (P_u <= H_KV)", Hq,
+                Hkv, P_u);
+  const int32_t Hqp = Hq / P_u, Hkvp = Hkv / P_u;
+  for (int h = 0; h < Hq; ++h)
+    if (kv_of[h] / Hkvp != h / Hqp)
+      return fail(RA_ERR_SHAPE, "query head %d reads KV head %d, held by another device", h,
+                  (int)kv_of[h]);
+  if (S < 0) return fail(RA_ERR_SHAPE, "S must be >= 0");
+  const int64_t P = (int64_t)P_u * P_r;
+  if (S % P) return fail(RA_ERR_SHAPE, "S=%lld not divisible by P_u*P_r=%lld", (long long)S,
+                         (long long)P);
+  if (layout == RA_ZIGZAG && S % (2 * (int64_t)P_r))
+    return fail(RA_ERR_SHAPE, "S=%lld not divisible by 2*P_r=%d", (long long)S, 2 * P_r);
+  if (S == 0) return RA_OK;
+  const int64_t C = S / P_r;  // tokens per node
+  if (S > INT32_MAX || (S / P) * Hq > INT32_MAX)
+    return fail(RA_ERR_UNSUPPORTED, "S or (S/P)*Hq beyond 2^31-1");
+  if (!q || !k || !v || !out || !lse) return fail(RA_ERR_NULL, "NULL tensor pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(RA_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(RA_ERR_ALIGN, "lse must be 4-byte aligned");
+  const UspLayout L = usp_layout(B, Hq, Hkv, S, D, dtype, P_u, P_r);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", L.total,
+                workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(RA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  hipStream_t cs = reinterpret_cast<hipStream_t>(compute_stream);
+  const size_t es = esize(dtype);
+  char* ws = reinterpret_cast<char*>(workspace);
+  char *qh = ws + L.q, *kh = ws + L.k, *vh = ws + L.v, *oh = ws + L.o;
+  const int64_t row = (int64_t)D * es;
+  // device slices of node n: devices n*P_u .. n*P_u + P_u - 1, contiguous
+  const size_t node_q = (size_t)P_u * B * (S / P) * Hq * D * es;
+  const size_t node_kv = (size_t)P_u * B * (S / P) * Hkv * D * es;
+
+  // Intra-node all-to-all, node by node: the node's tokens land at rows
+  // [n*C, (n+1)*C) of every head plane -- rank n of the ring's rank-major order.
+  hipError_t e;
+  for (int n = 0; n < P_r; ++n) {
+    if ((e = launch_ulysses_a2a((const char*)q + n * node_q, qh, B, C, Hq, row, P_u, 0, cs, S,
+                                n * C)) != hipSuccess ||
+        (e = launch_ulysses_a2a((const char*)k + n * node_kv, kh, B, C, Hkv, row, P_u, 0, cs, S,
+                                n * C)) != hipSuccess ||
+        (e = launch_ulysses_a2a((const char*)v + n * node_kv, vh, B, C, Hkv, row, P_u, 0, cs, S,
+                                n * C)) != hipSuccess)
+      return hip_fail(e, "all-to-all launch");
+  }
+  // The ring across the nodes, once per head group (device u of every node).
+  for (int u = 0; u < P_u; ++u) {
+    std::vector<int32_t> lmap(Hqp);
+    for (int h = 0; h < Hqp; ++h) lmap[h] = kv_of[u * Hqp + h] - u * Hkvp;
+    const size_t qo = (size_t)u * B * Hqp * S * D * es, ko = (size_t)u * B * Hkvp * S * D * es;
+    st = ra_ring_sim_fwd(qh + qo, kh + ko, vh + ko, oh + qo, lse + (size_t)u * B * Hqp * S, B, Hqp,
+                         Hkvp, S, D, dtype, P_r, layout, causal, scale, lmap.data(), ws + L.ring,
+                         L.ring_bytes, compute_stream, copy_stream);
+    if (st != RA_OK) return st;
+  }
+  // Reverse all-to-all, node by node.
+  for (int n = 0; n < P_r; ++n)
+    if ((e = launch_ulysses_a2a(oh, (char*)out + n * node_q, B, C, Hq, row, P_u, 1, cs, S,
+                                n * C)) != hipSuccess)
+      return hip_fail(e, "all-to-all launch");
+  return RA_OK;
+}
+
 ra_status ra_kernel_timing_enable(int32_t enable) {
   g_err[0] = 0;
   std::lock_guard<std::mutex> lk(g_timing.mu);

@@ -252,16 +252,19 @@ hipError_t launch_striped_permute(const void* src, void* dst, int64_t outer, int
 // all-to-all gathers the sequence and scatters the heads, the second reverses
 // it]. The P ranks' sequence slices are [P][B][Sp][H] rows (rank p holds
 // positions p*Sp ..); their head slices are [P][B][Hp][S] rows (rank j holds
-// heads j*Hp .. over all S positions, each head's rows contiguous). Both
-// directions gather, so the writes are contiguous and every read is one whole
-// row. blockIdx.y walks destination planes -- (rank, batch, head) forward,
-// (rank, batch) inverse -- and a block copies rpb consecutive rows of one
-// plane, so the index arithmetic inside a plane is 32-bit.
+// heads j*Hp .. over all S positions, each head's rows contiguous; a head's
+// plane of S rows starts every hs_stride rows, at row hs_off, so several
+// calls can fill one longer sequence). Both directions gather, so the writes
+// are contiguous and every read is one whole row. blockIdx.y walks
+// destination planes -- (rank, batch, head) forward, (rank, batch) inverse --
+// and a block copies rpb consecutive rows of one plane, so the index
+// arithmetic inside a plane is 32-bit.
 template <typename V>
 __global__ __launch_bounds__(256) void ulysses_a2a_kernel(const char* __restrict__ src,
                                                           char* __restrict__ dst, int B, int S,
                                                           int P, int H, int64_t row_vecs, int rpb,
-                                                          int inverse) {
+                                                          int inverse, int64_t hs_stride,
+                                                          int64_t hs_off) {
   const int Sp = S / P, Hp = H / P;
   const int t = threadIdx.x;
   const int sub = rpb > 1 ? t / (int)row_vecs : 0;
@@ -284,10 +287,11 @@ __global__ __launch_bounds__(256) void ulysses_a2a_kernel(const char* __restrict
         const int b = (int)(y % B), p = (int)(y / B);
         const int i = r / H, h = r - i * H;
         const int j = h / Hp, hh = h - j * Hp;
-        from = (((int64_t)j * B + b) * Hp + hh) * S + (int64_t)p * Sp + i;
+        from = (((int64_t)j * B + b) * Hp + hh) * hs_stride + hs_off + (int64_t)p * Sp + i;
       }
+      const int64_t to = inverse ? y * plane_rows + r : y * hs_stride + hs_off + r;
       const V* sp = reinterpret_cast<const V*>(src) + from * row_vecs;
-      V* dp = reinterpret_cast<V*>(dst) + (y * plane_rows + r) * row_vecs;
+      V* dp = reinterpret_cast<V*>(dst) + to * row_vecs;
       if (rpb > 1) {
         dp[e0] = sp[e0];
       } else {
@@ -298,7 +302,9 @@ __global__ __launch_bounds__(256) void ulysses_a2a_kernel(const char* __restrict
 }
 
 hipError_t launch_ulysses_a2a(const void* src, void* dst, int32_t B, int64_t S, int32_t H,
-                              int64_t row_bytes, int32_t P, int inverse, hipStream_t s) {
+                              int64_t row_bytes, int32_t P, int inverse, hipStream_t s,
+                              int64_t hs_stride, int64_t hs_off) {
+  if (hs_stride <= 0) hs_stride = S;
   if (B == 0 || S == 0 || row_bytes == 0) return hipSuccess;
   const uintptr_t al = (uintptr_t)src | (uintptr_t)dst | (uintptr_t)row_bytes;
   int vb = 16;
@@ -315,23 +321,23 @@ hipError_t launch_ulysses_a2a(const void* src, void* dst, int32_t B, int64_t S, 
   switch (vb) {
     case 16:
       hipLaunchKernelGGL(ulysses_a2a_kernel<uint4>, grid, dim3(256), 0, s, sp, dp, B, Si, P, H,
-                         row_vecs, rpb, inverse);
+                         row_vecs, rpb, inverse, hs_stride, hs_off);
       break;
     case 8:
       hipLaunchKernelGGL(ulysses_a2a_kernel<uint2>, grid, dim3(256), 0, s, sp, dp, B, Si, P, H,
-                         row_vecs, rpb, inverse);
+                         row_vecs, rpb, inverse, hs_stride, hs_off);
       break;
     case 4:
       hipLaunchKernelGGL(ulysses_a2a_kernel<uint32_t>, grid, dim3(256), 0, s, sp, dp, B, Si, P,
-                         H, row_vecs, rpb, inverse);
+                         H, row_vecs, rpb, inverse, hs_stride, hs_off);
       break;
     case 2:
       hipLaunchKernelGGL(ulysses_a2a_kernel<uint16_t>, grid, dim3(256), 0, s, sp, dp, B, Si, P,
-                         H, row_vecs, rpb, inverse);
+                         H, row_vecs, rpb, inverse, hs_stride, hs_off);
       break;
     default:
       hipLaunchKernelGGL(ulysses_a2a_kernel<uint8_t>, grid, dim3(256), 0, s, sp, dp, B, Si, P,
-                         H, row_vecs, rpb, inverse);
+                         H, row_vecs, rpb, inverse, hs_stride, hs_off);
       break;
   }
   return hipGetLastError();

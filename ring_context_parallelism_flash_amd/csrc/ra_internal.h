@@ -40,7 +40,11 @@ hipError_t launch_zigzag_permute(const void* src, void* dst, int64_t outer, int6
 
 hipError_t launch_striped_permute(const void* src, void* dst, int64_t outer, int64_t S,
                                   int64_t row_bytes, int N, int inverse, hipStream_t s);
+// Ulysses all-to-all: [P][B][S/P][H] rows <-> [P][B][H/P][S] rows; the
+// head-sharded side's head planes start every hs_stride rows (<= 0: S) at
+// row offset hs_off.
 hipError_t launch_ulysses_a2a(const void* src, void* dst, int32_t B, int64_t S, int32_t H,
-                              int64_t row_bytes, int32_t P, int inverse, hipStream_t s);
+                              int64_t row_bytes, int32_t P, int inverse, hipStream_t s,
+                              int64_t hs_stride = 0, int64_t hs_off = 0);
 
 }  // namespace ra

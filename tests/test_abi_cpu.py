@@ -223,6 +223,31 @@ def test_ulysses_workspace_sizes_and_rejects():
     assert a2a(B=0) == "RA_OK" and a2a(S=0) == "RA_OK"
 
 
+def test_usp_workspace_sizes_and_rejects():
+    L = ra.lib()
+    ring = ra.ra_ring_sim_workspace_bytes(1, 4, 2, 1024, 128, BF16, 4)
+    up = lambda x: (x + 255) // 256 * 256
+    # head-sharded q, out [8][1024][128] and k, v [4][1024][128] bf16, + one ring workspace
+    assert ra.ra_usp_sim_workspace_bytes(1, 8, 4, 1024, 128, BF16, 2, 4) == \
+        2 * (8 * 1024 * 128 * 2) + 2 * (4 * 1024 * 128 * 2) + up(ring)
+    assert ra.ra_usp_sim_workspace_bytes(1, 8, 4, 1020, 128, BF16, 2, 4) == 0    # S % (P_u*P_r)
+
+    def usp(**kw):
+        a = dict(S=1024, P_u=2, P_r=4, layout=1, Hq=8, Hkv=4, kv=None)
+        a.update(kw)
+        kv = None if a["kv"] is None else (ctypes.c_int32 * len(a["kv"]))(*a["kv"])
+        return ra.ra_status_str(L.ra_usp_sim_fwd(
+            FAKE, FAKE, FAKE, FAKE, FAKE, 1, a["Hq"], a["Hkv"], a["S"], 128, BF16, a["P_u"],
+            a["P_r"], a["layout"], 1, 0.088, kv, None, 0, None, None))
+    assert usp(P_u=8) == "RA_ERR_SHAPE"                 # P_u > H_KV
+    assert usp(S=1004) == "RA_ERR_SHAPE"                # S % (P_u * P_r)
+    assert usp(S=1029, P_r=3, P_u=1) == "RA_ERR_SHAPE"  # zigzag: S % (2 P_r)
+    assert usp(layout=7) == "RA_ERR_ARG"
+    assert usp(kv=[2, 2, 0, 0, 1, 1, 3, 3]) == "RA_ERR_SHAPE"
+    assert usp() == "RA_ERR_WORKSPACE"
+    assert usp(S=0) == "RA_OK"
+
+
 def test_timing_read_without_launches():
     ra.ra_kernel_timing_enable(True)
     ms, n, fl = ra.ra_kernel_timing_read()

@@ -135,3 +135,69 @@ def test_ulysses_gqa_128k_sampled():
     got_out = np.stack([o[h, idx[h]].double().numpy() for h in range(w.Hq)])
     got_lse = np.stack([l_[h, idx[h]].double().numpy() for h in range(w.Hq)])
     compare(got_out, got_lse, ref_out, ref_lse, TOL_BF16, "ulysses 128k gqa")
+
+
+# ====================================================================== USP
+def _usp_shard(x, P_u, P_r, layout):
+    """[B, H, S, D] sequence order -> device slices [P_r*P_u, B, S/(P_r*P_u), H, D]."""
+    B, H, S, D = x.shape
+    L = torch.from_numpy(oracle.usp_token_lists(S, P_r, layout).reshape(-1))
+    xs = x[:, :, L].permute(0, 2, 1, 3)
+    return xs.reshape(B, P_r * P_u, S // (P_r * P_u), H, D).permute(1, 0, 2, 3, 4).contiguous()
+
+
+USP_SMALL = [
+    # name, P_u, P_r, ring layout, B, Hq, Hkv, S, D, dtype, causal, kv map
+    ("usp_2x4_zigzag", 2, 4, "zigzag", 1, 4, 2, 1024, 128, "bf16", True, None),
+    ("usp_2x2_striped_b2_d64", 2, 2, "striped", 2, 4, 2, 768, 64, "bf16", True, None),
+    ("usp_4x2_contig_f32", 4, 2, "contiguous", 1, 4, 4, 512, 128, "f32", True, None),
+    ("usp_2x2_noncausal", 2, 2, "zigzag", 1, 4, 2, 512, 128, "bf16", False, None),
+    ("usp_1x4_is_ring", 1, 4, "zigzag", 1, 2, 1, 1024, 128, "bf16", True, None),
+    ("usp_4x1_is_ulysses", 4, 1, "contiguous", 1, 8, 4, 512, 128, "bf16", True, None),
+    ("usp_2x2_head_map", 2, 2, "zigzag", 1, 8, 4, 512, 128, "bf16", True, [1, 0, 1, 0, 3, 2, 2, 3]),
+]
+
+
+@pytest.mark.parametrize("case", USP_SMALL, ids=[c[0] for c in USP_SMALL])
+def test_usp_small_vs_oracle(case):
+    name, P_u, P_r, lay, B, Hq, Hkv, S, D, dt, causal, kv_map = case
+    w = workloads.Workload(name, B=B, Hq=Hq, Hkv=Hkv, D=D, S=S, dtype=dt, seed=700 + len(name),
+                           causal=causal, N=P_u * P_r, layout="usp", P_u=P_u, ring_layout=lay)
+    q, k, v = (_usp_shard(t, P_u, P_r, lay) for t in workloads.make_inputs(w))
+    out = torch.empty(q.shape, dtype=q.dtype, device=DEV)
+    lse = torch.empty((P_u, B, Hq // P_u, S), dtype=torch.float32, device=DEV)
+    ra.ra_usp_sim_fwd(q.to(DEV), k.to(DEV), v.to(DEV), out, lse, P_u=P_u, P_r=P_r, layout=lay,
+                      causal=causal, kv_head_of_q=kv_map)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.usp_attention(q, k, v, P_u=P_u, P_r=P_r, layout=lay, causal=causal,
+                                            kv_head_of_q=kv_map)
+    compare(_np(out), _np(lse), ref_out, ref_lse, TOL_F32 if dt == "f32" else TOL_BF16,
+            f"usp {name}")
+
+
+def test_usp_gqa_128k_sampled():
+    """The 128k GQA causal inputs on 4 nodes x 8 devices (zigzag ring across
+    nodes): seeded rows plus every node's first and last positions against
+    exact attention."""
+    import os
+    w = workloads.USP_128K
+    P_u, P_r = w.P_u, w.N // w.P_u
+    q, k, v = workloads.make_inputs(w)
+    qs, ks, vs = (_usp_shard(t, P_u, P_r, w.ring_layout).to(DEV) for t in (q, k, v))
+    out = torch.empty(qs.shape, dtype=qs.dtype, device=DEV)
+    lse = torch.empty((P_u, 1, w.Hq // P_u, w.S), dtype=torch.float32, device=DEV)
+    ra.ra_usp_sim_fwd(qs, ks, vs, out, lse, P_u=P_u, P_r=P_r, layout=w.ring_layout, causal=True)
+    torch.cuda.synchronize()
+    del qs, ks, vs
+    L = oracle.usp_token_lists(w.S, P_r, w.ring_layout).reshape(-1)     # node-major positions
+    inv = torch.from_numpy(np.argsort(L))
+    n = int(os.environ.get("RA_ORACLE_ROWS", "32"))
+    rows = check_rows(w.S, w.Hq, n, w.seed, 2 * P_r)
+    ref_out, ref_lse = pooled_attention(q, k, v, causal=True, rows=rows)
+    # device slices -> node-major -> sequence order
+    o = out.cpu().permute(1, 0, 2, 3, 4).reshape(1, w.S, w.Hq, w.D)[0][inv]   # [S, Hq, D]
+    l_ = lse.cpu()[:, 0].reshape(w.Hq, w.S)[:, inv]                           # [Hq, S]
+    idx = torch.from_numpy(rows)
+    got_out = np.stack([o[idx[h], h].double().numpy() for h in range(w.Hq)])
+    got_lse = np.stack([l_[h, idx[h]].double().numpy() for h in range(w.Hq)])
+    compare(got_out, got_lse, ref_out, ref_lse, TOL_BF16, "usp 128k gqa")

@@ -32,9 +32,11 @@ class Workload:
     seed: int
     causal: bool
     N: int              # virtual ring size
-    layout: str         # "contiguous", "zigzag", "striped" or "ulysses"
+    layout: str         # "contiguous", "zigzag", "striped", "ulysses" or "usp"
     k_scale: float = 1.0
     note: str = ""
+    P_u: int = 1                # "usp": devices per node (Ulysses degree); N / P_u nodes
+    ring_layout: str = "zigzag"  # "usp": the ring's layout over the nodes
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -79,7 +81,14 @@ ULYSSES_128K = Workload("gqa_causal_ulysses_s128k", B=1, Hq=64, Hkv=8, D=128, S=
                         dtype="bf16", seed=3, causal=True, N=8, layout="ulysses",
                         k_scale=0.5, note="8 ranks: 8 query heads and 1 KV head each")
 
-BY_NAME = {w.name: w for w in WORKLOADS + (STRIPED_128K, ULYSSES_128K)}
+# The same inputs on the 2D grid of unified sequence parallelism: 4 nodes of 8
+# devices (Ulysses inside a node, the zigzag ring across nodes).
+USP_128K = Workload("gqa_causal_usp_s128k", B=1, Hq=64, Hkv=8, D=128, S=131072,
+                    dtype="bf16", seed=3, causal=True, N=32, layout="usp", k_scale=0.5,
+                    P_u=8, ring_layout="zigzag",
+                    note="4 nodes x 8 devices: 8 query heads / 1 KV head per device")
+
+BY_NAME = {w.name: w for w in WORKLOADS + (STRIPED_128K, ULYSSES_128K, USP_128K)}
 HEADLINE = WORKLOADS[3]
 
 
