@@ -428,8 +428,8 @@ def main(argv=None) -> int:
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default=None, help="workload name (default: the 128k GQA one)")
-    p.add_argument("--cpu-seconds", type=float, default=15.0)
-    p.add_argument("--cpu-rows", type=int, default=32)
+    p.add_argument("--cpu-seconds", type=float, default=25.0)
+    p.add_argument("--cpu-rows", type=int, default=64)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--backward", action="store_true",
                    help="time the ring backward (dq, dk, dv of a seeded dout) instead of the forward")
@@ -438,8 +438,9 @@ def main(argv=None) -> int:
                         "reference for hardware byte counters)")
     args = p.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; the ring is simulated on a single "
-              "MI355X (use --gpus 1).", file=sys.stderr)
+        print("bench.py: measures one GPU only -- the N ranks of the ring (and the devices "
+              "of the Ulysses / USP grids) are simulated on a single MI355X; run with --gpus 1.",
+              file=sys.stderr)
         return 2
 
     import torch
