@@ -242,7 +242,8 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs 
 
   WorkItem it;
   if (!decode_item(a, it)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool grpB = wv >= 4;
   const int lw = wv & 3;
   const int n = lane & 31, hh = lane >> 5;
@@ -281,39 +282,67 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs 
   // in distinct banks, and every operand offset is an immediate. A direct
   // load fills 64 consecutive chunks; lanes that land on a pad chunk re-read
   // a chunk of the same row.
-  // Direct loads (group B): instruction j of loading wave lw fills chunks
-  // P = (lw + LW*j)*64 + lane of the tile; offsets are computed at issue time
-  // (the softmax phase that issues them has VALU to spare). The lane index is
-  // re-read by volatile asm so that the per-lane row / chunk values are not
-  // hoisted out of the key loop: kept live, they were spilled to scratch, and
-  // the wait for a scratch reload also waited for the tile loads just issued.
+  // Direct loads: instruction j of loading wave lw fills chunks
+  // P = (lw + LW*j)*64 + lane of the tile (group B loads K, group A V^T).
+  // Per-lane byte offsets of this wave's loads within a tile (K rows for
+  // group B, V^T rows for group A), computed once: a full tile's load is then
+  // a wave-uniform tile base plus one of these 32-bit offsets.
+  constexpr int NL = KI > VI ? KI : VI;
+  uint32_t loff[NL];
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const int P = (lw + LW * j) * 64 + lane;
+    if (grpB) {
+      const int cch = P % KCPR;
+      loff[j] = (uint32_t)((P / KCPR) * D + (cch < CPR ? cch : 0) * 8) * 2u;
+    } else {
+      const int cch = P % 9;
+      loff[j] = ((uint32_t)(P / 9) * (uint32_t)a.v_ld + (uint32_t)(cch < 8 ? cch : 0) * 8u) * 2u;
+    }
+  }
+  // the V^T offsets fit in 32 bits while a tile's D rows span < 4 GiB
+  const bool v_off32 = (int64_t)D * a.v_ld * 2 <= (int64_t)UINT32_MAX;
   auto load_k = [&](int kt, int buf) {
-    const int lane = lane_id();
     const int kb = kt * 64;
+    unsigned char* dst = Ks + buf * KBUF + lw * 1024;
+    if (kb + 64 <= a.Ck) {
+      const unsigned char* base = reinterpret_cast<const unsigned char*>(kbp + (int64_t)kb * D);
+#pragma unroll
+      for (int j = 0; j < KI; ++j)
+        if (lw + LW * j < KINS) load_lds16(base + loff[j], dst + j * LW * 1024);
+      return;
+    }
+    // ragged last tile: rows past the block end re-read its last row (their
+    // scores are masked)
+    const int lane = lane_id();
     const int rows_left = a.Ck - 1 - kb;  // last valid row of this tile
     const __bf16* base = kbp + (int64_t)kb * D;
-    unsigned char* dst = Ks + buf * KBUF + lw * 1024;
 #pragma unroll
     for (int j = 0; j < KI; ++j)
       if (lw + LW * j < KINS) {
         const int P = (lw + LW * j) * 64 + lane;
         const int cch = P % KCPR;
-        // rows past the block end re-read its last row (their scores are masked)
         const int row = min(P / KCPR, rows_left);
         load_lds16(base + row * D + (cch < CPR ? cch : 0) * 8, dst + j * LW * 1024);
       }
   };
   auto load_v = [&](int kt, int buf) {
+    unsigned char* dst = Vs + buf * VBUF + lw * 1024;
+    if (v_off32) {
+      const unsigned char* base = reinterpret_cast<const unsigned char*>(vtb + kt * 64);
+#pragma unroll
+      for (int j = 0; j < VI; ++j)
+        if (lw + LW * j < VINS) load_lds16(base + loff[j], dst + j * LW * 1024);
+      return;
+    }
     const int lane = lane_id();
     const __bf16* base = vtb + kt * 64;
-    unsigned char* dst = Vs + buf * VBUF + lw * 1024;
 #pragma unroll
     for (int j = 0; j < VI; ++j)
       if (lw + LW * j < VINS) {
         const int P = (lw + LW * j) * 64 + lane;
         const int cch = P % 9;
-        load_lds16(base + (P / 9) * (int)a.v_ld + (cch < 8 ? cch : 0) * 8,
-                   dst + j * LW * 1024);
+        load_lds16(base + (int64_t)(P / 9) * a.v_ld + (cch < 8 ? cch : 0) * 8, dst + j * LW * 1024);
       }
   };
 

@@ -209,6 +209,42 @@ def test_block_hand_case():
         assert torch.all(o[0, 0, :, 1:] == 0)
 
 
+def test_block_vt_rows_past_4gib_closed_form():
+    """A bf16 key block so long that the transposed-V rows of one head start
+    more than 4 GiB apart (D = 64, Ck = 2^25 + 2^20: row 63 begins at
+    63 * Ck * 2 bytes > 2^32), so the tile loads take their 64-bit offset path.
+
+    Keys and values are zero except three needle rows, each with score 30
+    (q[:, 0] = 8, k[needle, 0] = 30, scale 1/8) and its values in its own
+    third of the d columns. Closed form: every background score is 0, so with
+    Z = 3 e^30 + (Ck - 3), out[d] = e^30 v_n[d] / Z and lse = ln Z (the
+    background adds ~1e-6 relative, below the tolerance)."""
+    D, Hq, Hkv, Cq = 64, 2, 1, 64
+    Ck = (1 << 25) + (1 << 20)
+    q = torch.zeros(1, Hq, Cq, D, dtype=torch.bfloat16, device=DEV)
+    q[..., 0] = 8.0
+    k = torch.zeros(1, Hkv, Ck, D, dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros_like(k)
+    rows = (100, (1 << 24) + 12345, Ck - 7)   # early, middle, last tile
+    cols = ((0, 21), (21, 42), (42, 64))
+    expect_v = np.zeros(D)
+    for n, (r, (c0, c1)) in enumerate(zip(rows, cols)):
+        k[0, 0, r, 0] = 30.0
+        vals = np.arange(c0, c1) * 0.25 - 4.0 + n   # exact in bf16
+        v[0, 0, r, c0:c1] = torch.tensor(vals, dtype=torch.bfloat16)
+        expect_v[c0:c1] = vals
+    out = torch.zeros(1, Hq, Cq, D, device=DEV)
+    lse = torch.zeros(1, Hq, Cq, device=DEV)
+    ra.ra_block_attn_fwd(q, k, v, out, lse, causal=False)
+    torch.cuda.synchronize()
+    del k, v
+    Z = 3.0 * math.exp(30.0) + (Ck - 3)
+    exp_out = expect_v * math.exp(30.0) / Z
+    o, l_ = _np(out), _np(lse)
+    assert np.abs(o - exp_out).max() <= 1e-4
+    assert np.abs(l_ - math.log(Z)).max() <= 1e-4
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_block_future_keys_identity(dtype):
     """A block entirely after the queries: accumulate leaves the state bit-identical,
