@@ -44,11 +44,16 @@ BWD_KERNEL_SOURCES = ("attn_bwd.hip", "attn_common.h", "attn_bwd_args.h")
 
 
 def kernel_sources_sha256(sources=KERNEL_SOURCES) -> str:
+    """SHA-256 of a kernel's source files and of the compiler flags its .hip
+    file is built with (a flag can change the kernel as much as an edit)."""
     import hashlib
+    from ring_context_parallelism_flash_amd import build as ra_build
     h = hashlib.sha256()
     for name in sources:
         with open(os.path.join(ROOT, "ring_context_parallelism_flash_amd", "csrc", name), "rb") as f:
             h.update(f.read())
+        if name.endswith(".hip"):
+            h.update(" ".join(ra_build.FLAGS + ra_build.EXTRA.get(name, [])).encode())
     return h.hexdigest()
 
 

@@ -17,6 +17,12 @@ LIB = os.path.join(PKG, "libringattn.so")
 OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "aux_kernels.hip", "api.cpp"]
+# Per-source extra flags. The backward kernels read their S and dP MFMA
+# results with the VALU; by default the backend gave those results AGPRs and
+# copied 32 of them to VGPRs at every loop iteration. The VGPR form of the
+# MFMA instructions writes them where the VALU reads them (bit-identical
+# results, no spills).
+EXTRA = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
@@ -48,7 +54,7 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"]
-        cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
