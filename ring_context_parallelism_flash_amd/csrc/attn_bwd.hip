@@ -92,9 +92,12 @@ __device__ __forceinline__ int xcd_item(int n_items, int per_xcd) {
 // rings: the compiler waits for every outstanding direct global->LDS load
 // before an LDS read it issues itself (it cannot tell that the read does not
 // alias the loads' destination), which would drain the tile prefetch.
+// The hardware writes the result register when the read returns; callers
+// wait with an s_waitcnt that names the register as an operand.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 template <int OFF>
-__device__ __forceinline__ float4 ds_read_f4(unsigned addr) {
-  float4 r;
+__device__ __forceinline__ f32x4 ds_read_f4(unsigned addr) {
+  f32x4 r;
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
   return r;
 }
@@ -201,7 +204,7 @@ struct SdpStream {
 // step of the next sub-tile's S / dP stream. Element e = 8w + jj of a lane is
 // row offset 16w + jj of the sub-tile; causal: masked iff that offset is
 // below lim.
-template <int PER>
+template <int PER, bool MASK>
 struct DkdvProbs {
   const floatx16& S;
   const floatx16& dP;
@@ -217,7 +220,7 @@ struct DkdvProbs {
     for (int e = I * PER; e < (I + 1) * PER; ++e) {
       const int w = e >> 3, jj = e & 7;
       float sc = fmaf(S[e], c, -l2[e]);
-      sc = (16 * w + jj < lim) ? -INFINITY : sc;
+      if constexpr (MASK) sc = (16 * w + jj < lim) ? -INFINITY : sc;
       const float p = __builtin_amdgcn_exp2f(sc);
       Pb[w][jj] = (__bf16)p;
       dSb[w][jj] = (__bf16)(p * (dP[e] - dl[e]));
@@ -363,7 +366,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
   };
 
   bool issued = false;  // this wave issued a load batch at the start of the previous iteration
-  auto iter = [&](int j, const floatx16& Sc, const floatx16& dPc, floatx16& Sn, floatx16& dPn) {
+  auto iter = [&](auto mask, int j, const floatx16& Sc, const floatx16& dPc, floatx16& Sn,
+                  floatx16& dPn) {
     if (j > 0) {
       // the batch of two iterations ago has landed in this wave ...
       if (issued)
@@ -388,28 +392,31 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
     const int r0 = 32 * (j & 1) + 8 * hh;  // rows r0 + 16w + jj of the tile
     float l2[16], dl[16];
     const unsigned la = lds_addr(TB) + r0 * 4;
-    const float4 lx[4] = {ds_read_f4<OFF_L>(la), ds_read_f4<OFF_L + 16>(la),
-                          ds_read_f4<OFF_L + 64>(la), ds_read_f4<OFF_L + 80>(la)};
-    const float4 dx[4] = {ds_read_f4<OFF_DL>(la), ds_read_f4<OFF_DL + 16>(la),
-                          ds_read_f4<OFF_DL + 64>(la), ds_read_f4<OFF_DL + 80>(la)};
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    f32x4 lx[4] = {ds_read_f4<OFF_L>(la), ds_read_f4<OFF_L + 16>(la),
+                   ds_read_f4<OFF_L + 64>(la), ds_read_f4<OFF_L + 80>(la)};
+    f32x4 dx[4] = {ds_read_f4<OFF_DL>(la), ds_read_f4<OFF_DL + 16>(la),
+                   ds_read_f4<OFF_DL + 64>(la), ds_read_f4<OFF_DL + 80>(la)};
+    // The hardware writes these registers when the reads return, but the
+    // compiler takes them as written by the read statements: the wait names
+    // them as operands, so no use can be scheduled above it.
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(lx[0]), "+v"(lx[1]), "+v"(lx[2]), "+v"(lx[3]), "+v"(dx[0]), "+v"(dx[1]),
+                   "+v"(dx[2]), "+v"(dx[3])
+                 :
+                 : "memory");
 #pragma unroll
     for (int w = 0; w < 2; ++w)
 #pragma unroll
       for (int v4 = 0; v4 < 2; ++v4) {
-        const float4 x = lx[2 * w + v4];
-        const float4 y = dx[2 * w + v4];
-        l2[8 * w + 4 * v4 + 0] = x.x;
-        l2[8 * w + 4 * v4 + 1] = x.y;
-        l2[8 * w + 4 * v4 + 2] = x.z;
-        l2[8 * w + 4 * v4 + 3] = x.w;
-        dl[8 * w + 4 * v4 + 0] = y.x;
-        dl[8 * w + 4 * v4 + 1] = y.y;
-        dl[8 * w + 4 * v4 + 2] = y.z;
-        dl[8 * w + 4 * v4 + 3] = y.w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          l2[8 * w + 4 * v4 + e] = lx[2 * w + v4][e];
+          dl[8 * w + 4 * v4 + e] = dx[2 * w + v4][e];
+        }
       }
     bf16x8 Pb[2], dSb[2];
-    DkdvProbs<16 / G1::N> pr{Sc, dPc, l2, dl, c, row_min - (tile_src(j >> 1).q0 + r0), Pb, dSb};
+    DkdvProbs<16 / G1::N, decltype(mask)::value> pr{
+        Sc, dPc, l2, dl, c, row_min - (tile_src(j >> 1).q0 + r0), Pb, dSb};
     // the S, dP MFMAs of sub-tile j+1 (past the end: a stale but valid
     // buffer, result unused) with this sub-tile's arithmetic between them
     G1::run(g1_addr(min(j + 1, NJ - 1)), kreg, vreg, Sn, dPn, pr);
@@ -429,9 +436,25 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
     floatx16 SA, dPA, SB, dPB;
     NoWork nw;
     G1::run(g1_addr(0), kreg, vreg, SA, dPA, nw);
-    for (int j = 0; j < NJ; j += 2) {  // NJ is even
-      iter(j, SA, dPA, SB, dPB);
-      iter(j + 1, SB, dPB, SA, dPA);
+    // Query tiles that start at or after every lane's first allowed row hold
+    // no masked pair. The stream walks tiles latest first, so they are its
+    // leading whole tiles (all heads of each): those sub-tiles run without
+    // the mask's compare and select, the rest with them.
+    // row_min grows with the key index (positions increase along a block),
+    // so the wave's largest is its last key's: a scalar, with no cross-lane
+    // shuffle -- a shuffle is an LDS-pipe instruction, and one placed among
+    // the operand reads would upset their counted lgkmcnt waits.
+    const int rmax =
+        a.causal ? first_row_at(a.qp, a.Cq, pos_of(a.kp, min(kw0 + 31, a.Ck - 1))) : 0;
+    const int j_free = 2 * ng * min(n_t, max(0, t_lo + n_t - (rmax + 63) / 64));
+    int j = 0;
+    for (; j < j_free; j += 2) {  // NJ and j_free are even
+      iter(std::false_type{}, j, SA, dPA, SB, dPB);
+      iter(std::false_type{}, j + 1, SB, dPB, SA, dPA);
+    }
+    for (; j < NJ; j += 2) {
+      iter(std::true_type{}, j, SA, dPA, SB, dPB);
+      iter(std::true_type{}, j + 1, SB, dPB, SA, dPA);
     }
   }
 
@@ -495,7 +518,7 @@ struct DqStream {
 // the next sub-tile's S^T / dP^T stream. Element e of a lane is key offset
 // 16(e/8) + 8hh + e%8 of the sub-tile; it is masked iff 16(e/8) + e%8 >= lim
 // (keys at or past the lane's allowed prefix, or past the block end).
-template <int PER>
+template <int PER, bool MASK>
 struct DqProbs {
   const floatx16& S;
   const floatx16& dP;
@@ -507,7 +530,7 @@ struct DqProbs {
 #pragma unroll
     for (int e = I * PER; e < (I + 1) * PER; ++e) {
       float sc = fmaf(S[e], c, -lse2);
-      sc = (16 * (e >> 3) + (e & 7) >= lim) ? -INFINITY : sc;
+      if constexpr (MASK) sc = (16 * (e >> 3) + (e & 7) >= lim) ? -INFINITY : sc;
       const float p = __builtin_amdgcn_exp2f(sc);
       dSb[e >> 3][e & 7] = (__bf16)(p * (dP[e] - dlt));
     }
@@ -599,7 +622,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq(const BwdArgs a) {
   constexpr int RMIN = 2 * (L::RINS / 4), TMIN = L::TINS / 4;
 
   bool issued = false;
-  auto iter = [&](int j, const floatx16& Sc, const floatx16& dPc, floatx16& Sn, floatx16& dPn) {
+  auto iter = [&](auto mask, int j, const floatx16& Sc, const floatx16& dPc, floatx16& Sn,
+                  floatx16& dPn) {
     if (j > 0) {
       // the batch issued two iterations ago has landed in this wave ...
       if (!issued)
@@ -624,7 +648,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq(const BwdArgs a) {
     }
     bf16x8 dSb[2];
     const int lim = n_allow - ((j >> 1) * 64 + 32 * (j & 1) + 8 * hh);
-    DqProbs<16 / G1::N> pr{Sc, dPc, lse2, dlt, c, lim, dSb};
+    DqProbs<16 / G1::N, decltype(mask)::value> pr{Sc, dPc, lse2, dlt, c, lim, dSb};
     // the S^T, dP^T MFMAs of sub-tile j+1 (past the end: a stale but valid
     // buffer, result unused) with this sub-tile's arithmetic between them
     G1::run(g1_addr(min(j + 1, NJ - 1)), qreg, dreg, Sn, dPn, pr);
@@ -645,9 +669,22 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq(const BwdArgs a) {
     floatx16 SA, dPA, SB, dPB;
     NoWork nw;
     G1::run(g1_addr(0), qreg, dreg, SA, dPA, nw);
-    for (int j = 0; j < NJ; j += 2) {  // NJ is even
-      iter(j, SA, dPA, SB, dPB);
-      iter(j + 1, SB, dPB, SA, dPA);
+    // Key tiles that end within every lane's allowed prefix hold no masked
+    // pair (nor a key past the block end); they lead the walk and run
+    // without the mask's compare and select.
+    // n_allow grows with the query index, so the wave's smallest is its
+    // first query's: a scalar, with no cross-lane shuffle (see the dK / dV
+    // kernel)
+    const int amin = a.causal ? allowed_prefix(a.kp, pos_of(a.qp, min(qw0, a.Cq - 1))) : a.Ck;
+    const int j_free = 2 * min(NT, max(0, amin) / 64);
+    int j = 0;
+    for (; j < j_free; j += 2) {  // NJ and j_free are even
+      iter(std::false_type{}, j, SA, dPA, SB, dPB);
+      iter(std::false_type{}, j + 1, SB, dPB, SA, dPA);
+    }
+    for (; j < NJ; j += 2) {
+      iter(std::true_type{}, j, SA, dPA, SB, dPB);
+      iter(std::true_type{}, j + 1, SB, dPB, SA, dPA);
     }
   }
 
