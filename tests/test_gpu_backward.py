@@ -72,6 +72,8 @@ BLOCK_CASES = [
     (5, 3, (1, 5, 2), None, True, 2, 2, 128),
     (130, 70, (1, 130, 0, 0, 7), (1, 70, 5, 0, 7), False, 2, 2, 64),
     (64, 96, (1, 64, 0), (1, 96, 40), True, 2, 2, 128),            # rows 0..39 see no key
+    (256, 256, None, None, True, 2, 1, 64),    # D=64 diagonal: mask-free and masked sub-tiles
+    (192, 192, None, None, True, 1, 1, 64),
 ]
 
 
