@@ -36,6 +36,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "attn_common.h"
 
@@ -214,6 +215,68 @@ struct PvStream {
   }
 };
 
+struct QkNoWork {
+  template <int I>
+  __device__ __forceinline__ void operator()(std::integral_constant<int, I>) {}
+};
+
+// Score operand stream of one 64-key tile: 2*KS MFMAs alternating the two
+// 32-key accumulators (MFMA i: key half i%2, k-step i/2; K operand at byte
+// offset (i%2)*32*KROW + (i/2)*32 from the lane's base), operands read PF
+// ahead through a register ring; after MFMA i the work functor gets step i.
+template <int D, int KROW, int PF>
+struct QkStream {
+  static constexpr int KS = D / 16, N = 2 * KS;
+  static constexpr int off(int i) { return (i % 2) * 32 * KROW + (i / 2) * 32; }
+  template <int I, class W>
+  static __device__ __forceinline__ void step(unsigned ka, bf16x8 (&r)[PF], const bf16x8 (&qreg)[KS],
+                                              floatx16 (&S)[2], W& work) {
+    lds_wait<(N - 1 - I < PF - 1) ? (N - 1 - I) : (PF - 1)>(r[I % PF]);
+    S[I % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[I % PF], qreg[I / 2], S[I % 2], 0, 0, 0);
+    if constexpr (I + PF < N) r[I % PF] = ds_read16<off(I + PF)>(ka);
+    work(std::integral_constant<int, I>{});
+    if constexpr (I + 1 < N) step<I + 1>(ka, r, qreg, S, work);
+  }
+  template <int I>
+  static __device__ __forceinline__ void prefetch(unsigned ka, bf16x8 (&r)[PF]) {
+    r[I] = ds_read16<off(I)>(ka);
+    if constexpr (I + 1 < PF) prefetch<I + 1>(ka, r);
+  }
+  template <class W>
+  static __device__ __forceinline__ void run(unsigned ka, const bf16x8 (&qreg)[KS], floatx16 (&S)[2],
+                                             W& work) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) S[t][i] = 0.f;
+    bf16x8 r[PF];
+    prefetch<0>(ka, r);
+    step<0>(ka, r, qreg, S, work);
+  }
+};
+
+// Probabilities of the current tile's 32 scores per lane, PER per score MFMA
+// of the next tile: element e = 8u + j of P[u] is score Sc[u/2][8(u%2) + j].
+template <int PER>
+struct ProbsWork {
+  const floatx16 (&Sc)[2];
+  float c, moff;
+  float (&rs)[4];
+  bf16x8 (&P)[4];
+  template <int I>
+  __device__ __forceinline__ void operator()(std::integral_constant<int, I>) {
+#pragma unroll
+    for (int e = I * PER; e < (I + 1) * PER; ++e) {
+      const int u = e >> 3, j = e & 7;
+      const float p = __builtin_amdgcn_exp2f(fmaf(Sc[u >> 1][8 * (u & 1) + j], c, -moff));
+      rs[u] += p;
+      P[u][j] = (__bf16)p;
+    }
+    constexpr int ul = ((I + 1) * PER - 1) >> 3;
+    asm volatile("" : "+v"(P[ul]), "+v"(rs[ul]));
+  }
+};
+
 // Two-group schedule. A workgroup is 8 waves: group A (waves 0-3) and group B
 // (waves 4-7), one wave of each on every SIMD. Each wave alternates
 //   S-phase(t): softmax of tile t (VALU) and the score MFMAs of tile t+1,
@@ -350,21 +413,13 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs 
   const int k_rbase = kperm(n) * KROW + hh * 16;  // + t*32*KROW + s*32
   const int v_rbase = n * VROW + hh * 16;         // + T*32*VROW + u*32
 
-  // The two 32-key accumulators alternate, so consecutive MFMAs are
-  // independent (a dependent MFMA waits for its predecessor's result).
+  // Score MFMAs of one tile through the K operand ring (four reads in
+  // flight; the compiler's own schedule kept one or two and waited right
+  // before the MFMA that needed it).
+  using QK = QkStream<D, KROW, 4>;
   auto scores = [&](int kbuf, floatx16 (&S)[2]) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) S[t][i] = 0.f;
-#pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-            Ks + kbuf * KBUF + k_rbase + t * 32 * KROW + s2 * 32);
-        S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[s2], S[t], 0, 0, 0);
-      }
+    QkNoWork nw;
+    QK::run(lds_addr(Ks) + kbuf * KBUF + k_rbase, qreg, S, nw);
   };
   // P*V of the tile in V buffer vbuf: 4*DT MFMAs (u-major, so the DT
   // accumulators alternate), each fed by one 16-byte V^T read, with reads kept
@@ -388,8 +443,8 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs 
       }
   };
   // Probabilities of scores Sc against the current reference m_run, into P
-  // (bf16); returns this lane's fp32 sum of them. Branch free, so that it can
-  // share a scheduling region with the next tile's score MFMAs.
+  // (bf16); returns this lane's fp32 sum of them (the unfused path: masked
+  // tiles, the last tile, a rescale).
   auto probs = [&](const floatx16 (&Sc)[2], bf16x8 (&P)[4]) -> float {
     const float moff = (m_run == -INFINITY ? 0.f : m_run) * c;
     float rs[4];
@@ -433,26 +488,16 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs 
     l_part += rsum;
   };
   // Scores of the next tile (K buffer kbuf) into Sn, interleaved with the
-  // probabilities of the current unmasked tile Sc: each QK MFMA is followed
-  // by a slice of the softmax arithmetic, so the exp/fma/add stream runs
-  // under this wave's own matrix work.
+  // probabilities of the current unmasked tile Sc: each score MFMA is
+  // followed by a slice of the softmax arithmetic (the stream's work
+  // functor), so the exp/fma/add stream runs under this wave's own matrix
+  // work.
   auto scores_probs = [&](int kbuf, floatx16 (&Sn)[2], const floatx16 (&Sc)[2],
                           bf16x8 (&P)[4]) -> float {
-    scores(kbuf, Sn);
-    const float rsum = probs(Sc, P);
-    // pattern (0x100: LDS read, 0x008: MFMA, 0x002: VALU): two K reads in
-    // flight, five VALU instructions after each MFMA (measured best among
-    // 5, 7 and 9; deeper read prefetch was slower)
-    constexpr int NQK = 2 * KS;
-    constexpr int PF = 2;
-    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
-#pragma unroll
-    for (int i = 0; i < NQK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-      if (i < NQK - PF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    return rsum;
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    ProbsWork<32 / QK::N> w{Sc, c, (m_run == -INFINITY ? 0.f : m_run) * c, rs, P};
+    QK::run(lds_addr(Ks) + kbuf * KBUF + k_rbase, qreg, Sn, w);
+    return (rs[0] + rs[1]) + (rs[2] + rs[3]);
   };
 
   if (n_kt > 0) {
