@@ -272,6 +272,8 @@ struct ProbsWork {
       rs[u] += p;
       P[u][j] = (__bf16)p;
     }
+    // the empty asm keeps this slice between its MFMAs: its values must
+    // exist here, and volatile asm statements keep their order
     constexpr int ul = ((I + 1) * PER - 1) >> 3;
     asm volatile("" : "+v"(P[ul]), "+v"(rs[ul]));
   }
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs 
   constexpr int VROW = 9 * 16;           // bytes per padded V^T row (64 keys + pad)
   constexpr int KBUF = 64 * KROW, VBUF = D * VROW;  // bytes per LDS tile
   constexpr int KINS = KBUF / 1024, VINS = VBUF / 1024;  // 1 KiB direct loads per tile
-  constexpr int LW = 4;                  // waves that issue tile loads (group B)
+  constexpr int LW = 4;                  // waves per loading group (A: V^T, B: K)
   constexpr int KI = (KINS + LW - 1) / LW, VI = (VINS + LW - 1) / LW;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   unsigned char* Ks = lds;             // [2][64 keys][D + 8]
