@@ -17,13 +17,12 @@
 //    computed with the query rows permuted (kperm), so a lane holds the 16
 //    queries of one key that the next MFMAs need as 8-query B operands:
 //    dV^T += dO^T P and dK^T += Q^T dS, with Q^T and dO^T tiles in LDS.
-//  * attn_bwd_dq: a workgroup owns 128 queries of one query head (Q and dO
-//    rows of a wave in registers, as in the forward) and walks the key tiles
-//    (64 keys): S^T = K Q^T and dP^T = V dO^T with kperm'd key rows, then
-//    dQ^T += K^T dS^T with a K^T tile in LDS.
+//  * attn_bwd_dq: a workgroup owns 256 queries of one query head, two waves
+//    per SIMD (Q and dO rows of a wave in registers, as in the forward) and
+//    walks the key tiles (64 keys): S^T = K Q^T and dP^T = V dO^T with
+//    kperm'd key rows, then dQ^T += K^T dS^T with a K^T tile in LDS.
 //  * All tiles move global->LDS with direct 16-byte loads into padded rows
-//    (bank-conflict-free operand reads), double buffered, one barrier per
-//    tile. Both kernels add into fp32 accumulators, so the ring can sum the
+//    (bank-conflict-free operand reads), double buffered. Both kernels add into fp32 accumulators, so the ring can sum the
 //    contributions of all block pairs.
 #include <string.h>
 
@@ -50,13 +49,13 @@ struct BwdLds {
 
 // Rows [0, 64) of a row-major [rows][D] tile into padded LDS rows; rows past
 // rows_left re-read row rows_left (their contributions are masked or unused).
-template <int D>
+template <int D, int NW = 4>
 __device__ __forceinline__ void load_row_tile(const __bf16* base, int rows_left, unsigned char* dst,
                                               int wv, int lane) {
   using L = BwdLds<D>;
 #pragma unroll
-  for (int j = 0; j < (L::RINS + 3) / 4; ++j) {
-    const int ins = wv + 4 * j;
+  for (int j = 0; j < (L::RINS + NW - 1) / NW; ++j) {
+    const int ins = wv + NW * j;
     if (ins < L::RINS) {
       const int P = ins * 64 + lane;
       const int cch = P % L::RCPR;
@@ -67,13 +66,13 @@ __device__ __forceinline__ void load_row_tile(const __bf16* base, int rows_left,
 }
 
 // Columns [0, 64) of a transposed [D][ld] array into padded LDS rows.
-template <int D>
+template <int D, int NW = 4>
 __device__ __forceinline__ void load_trans_tile(const __bf16* base, int64_t ld, unsigned char* dst,
                                                 int wv, int lane) {
   using L = BwdLds<D>;
 #pragma unroll
-  for (int j = 0; j < (L::TINS + 3) / 4; ++j) {
-    const int ins = wv + 4 * j;
+  for (int j = 0; j < (L::TINS + NW - 1) / NW; ++j) {
+    const int ins = wv + NW * j;
     if (ins < L::TINS) {
       const int P = ins * 64 + lane;
       const int cch = P % 9;
@@ -538,16 +537,20 @@ struct DqProbs {
 };
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup = 4 waves x 32 queries of one query head, one wave per
+// dQ: one workgroup = 8 waves x 32 queries of one query head, two waves per
 // SIMD. The 64-key tiles are walked in 32-key sub-tiles j: iteration j issues
-// the S^T and dP^T MFMAs of sub-tile j+1 with the arithmetic of sub-tile j
-// spread between them, then the dQ MFMAs of sub-tile j. K and V rows (read
-// by S^T, dP^T) and K^T (read by dQ) have two LDS buffers each; rows of tile
-// u+2 are loaded at the start of iteration 2u+1, K^T of tile u+2 at the start
-// of iteration 2u+2, as in the dK / dV kernel.
+// the S^T and dP^T MFMAs of sub-tile j, the dS^T arithmetic, then the dQ
+// MFMAs of sub-tile j, with no software pipelining inside a wave -- the
+// SIMD's other wave fills the matrix pipe during one wave's arithmetic, and
+// the registers a pipeline would hold (a second S^T / dP^T pair) are what
+// lets two waves fit. K and V rows (read by S^T, dP^T) and K^T (read by dQ)
+// have two LDS buffers each, shared by the 256 queries of the workgroup.
 // ---------------------------------------------------------------------------
+constexpr int kDqWaves = 8;  // waves per dq workgroup (32 queries each)
+
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dq(const BwdArgs a) {
+__global__ __launch_bounds__(64 * kDqWaves, 1) void attn_bwd_dq(const BwdArgs a) {
+  constexpr int NW = kDqWaves;
   using L = BwdLds<D>;
   constexpr int KS = D / 16, DT = D / 32;
   constexpr int ROWS_BUF = 2 * L::RBUF;  // K rows, V rows
@@ -563,7 +566,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq(const BwdArgs a) {
   const int rest = item / a.n_tiles;
   const int hidx = rest % a.Hq, b = rest / a.Hq;
   const int h = a.head_order[hidx], g = a.kv_of[h];
-  const int q0 = (a.n_tiles - 1 - qt_rel) * 128;  // latest (heaviest) query tiles first
+  const int q0 = (a.n_tiles - 1 - qt_rel) * (32 * NW);  // latest (heaviest) query tiles first
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: load branches are per wave
   const int n = lane & 31, hh = lane >> 5;
@@ -584,12 +587,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq(const BwdArgs a) {
     asm volatile("" : "+a"(dreg[s]));
   }
   // rows past Cq read the padding: lse2 = +inf, so their probabilities are 0
-  const float lse2 = a.lse2[b * a.l_bs + h * a.l_hs + qi];
-  const float dlt = a.delta[b * a.l_bs + h * a.l_hs + qi];
+  // (rows past the padded length -- a 256-row workgroup can reach them --
+  // read its last row; those rows' dq is never written)
+  const int ql = min(qi, a.Cqp - 1);
+  const float lse2 = a.lse2[b * a.l_bs + h * a.l_hs + ql];
+  const float dlt = a.delta[b * a.l_bs + h * a.l_hs + ql];
   const int qpos = pos_of(a.qp, qc);
   // keys this lane's query sees: a prefix of the block (positions increase)
   const int n_allow = a.causal ? allowed_prefix(a.kp, qpos) : a.Ck;
-  const int wg_qmax = pos_of(a.qp, min(q0 + 127, a.Cq - 1));
+  const int wg_qmax = pos_of(a.qp, min(q0 + 32 * NW - 1, a.Cq - 1));
   const int n_keys = a.causal ? allowed_prefix(a.kp, wg_qmax) : a.Ck;
   const int NT = (n_keys + 63) / 64;  // key tiles
   const int NJ = 2 * NT;              // 32-key sub-tiles (even)
@@ -606,58 +612,20 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq(const BwdArgs a) {
   auto load_rows = [&](int T) {
     const int kb0 = T * 64;
     unsigned char* B0 = lds + (T & 1) * ROWS_BUF;
-    load_row_tile<D>(kb + (int64_t)kb0 * D, a.Ck - 1 - kb0, B0, wv, lane);
-    load_row_tile<D>(vb + (int64_t)kb0 * D, a.Ck - 1 - kb0, B0 + L::RBUF, wv, lane);
+    load_row_tile<D, NW>(kb + (int64_t)kb0 * D, a.Ck - 1 - kb0, B0, wv, lane);
+    load_row_tile<D, NW>(vb + (int64_t)kb0 * D, a.Ck - 1 - kb0, B0 + L::RBUF, wv, lane);
   };
   auto load_trans = [&](int T) {
-    load_trans_tile<D>(ktb + T * 64, a.Ckp, lds + OFF_TRANS + (T & 1) * TRANS_BUF, wv, lane);
+    load_trans_tile<D, NW>(ktb + T * 64, a.Ckp, lds + OFF_TRANS + (T & 1) * TRANS_BUF, wv, lane);
   };
   const int rbase = kperm(n) * L::ROW + hh * 16;
   auto g1_addr = [&](int jn) -> unsigned {
     return lds_addr(lds + ((jn >> 1) & 1) * ROWS_BUF) + rbase + (jn & 1) * 32 * L::ROW;
   };
-  // Loads per batch: rows (K and V of one tile) at least RMIN per wave, K^T
-  // at least TMIN; loads complete in order, so waiting until at most that
-  // many of the latest batch are outstanding retires every older batch.
-  constexpr int RMIN = 2 * (L::RINS / 4), TMIN = L::TINS / 4;
-
-  bool issued = false;
-  auto iter = [&](auto mask, int j, const floatx16& Sc, const floatx16& dPc, floatx16& Sn,
-                  floatx16& dPn) {
-    if (j > 0) {
-      // the batch issued two iterations ago has landed in this wave ...
-      if (!issued)
-        vm_wait<0>();
-      else if ((j - 1) & 1)
-        vm_wait<RMIN>();  // the previous iteration issued rows
-      else
-        vm_wait<TMIN>();  // ... or K^T
-      // ... and in every wave; every wave is done with iteration j-1 (its LDS
-      // reads were all waited for)
-      workgroup_barrier();
-    }
-    issued = false;
-    if (j & 1) {
-      if ((j >> 1) + 2 < NT) {
-        load_rows((j >> 1) + 2);
-        issued = true;
-      }
-    } else if (j >= 2 && (j >> 1) + 1 < NT) {
-      load_trans((j >> 1) + 1);
-      issued = true;
-    }
-    bf16x8 dSb[2];
-    const int lim = n_allow - ((j >> 1) * 64 + 32 * (j & 1) + 8 * hh);
-    DqProbs<16 / G1::N, decltype(mask)::value> pr{Sc, dPc, lse2, dlt, c, lim, dSb};
-    // the S^T, dP^T MFMAs of sub-tile j+1 (past the end: a stale but valid
-    // buffer, result unused) with this sub-tile's arithmetic between them
-    G1::run(g1_addr(min(j + 1, NJ - 1)), qreg, dreg, Sn, dPn, pr);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    G2::run(lds_addr(lds + OFF_TRANS + ((j >> 1) & 1) * TRANS_BUF) + n * L::TROW +
-                (32 * (j & 1) + 8 * hh) * 2,
-            dQt, dSb);
-  };
-
+  // Tiles 0 and 1 are loaded up front; K, V rows and K^T of tile u+1 are
+  // loaded at iteration 2u (u >= 1) into the buffers of tile u-1, which
+  // every wave finished with in iteration 2u-1 (the barrier), and waited
+  // for at iteration 2u+2, their first use (two iterations to land).
   if (NT > 0) {
     load_rows(0);
     load_trans(0);
@@ -666,28 +634,38 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq(const BwdArgs a) {
       load_trans(1);
     }
     lds_loads_barrier();
-    floatx16 SA, dPA, SB, dPB;
-    NoWork nw;
-    G1::run(g1_addr(0), qreg, dreg, SA, dPA, nw);
     // Key tiles that end within every lane's allowed prefix hold no masked
     // pair (nor a key past the block end); they lead the walk and run
-    // without the mask's compare and select.
-    // n_allow grows with the query index, so the wave's smallest is its
-    // first query's: a scalar, with no cross-lane shuffle (see the dK / dV
-    // kernel)
+    // without the mask's compare and select. n_allow grows with the query
+    // index, so the wave's smallest is its first query's: a scalar, with no
+    // cross-lane shuffle (see the dK / dV kernel).
     const int amin = a.causal ? allowed_prefix(a.kp, pos_of(a.qp, min(qw0, a.Cq - 1))) : a.Ck;
     const int j_free = 2 * min(NT, max(0, amin) / 64);
+    auto iter = [&](auto mask, int j) {
+      if (j >= 2 && !(j & 1)) {
+        vm_wait<0>();
+        workgroup_barrier();
+        if ((j >> 1) + 1 < NT) {
+          load_rows((j >> 1) + 1);
+          load_trans((j >> 1) + 1);
+        }
+      }
+      floatx16 S, dP;
+      NoWork nw;
+      G1::run(g1_addr(j), qreg, dreg, S, dP, nw);
+      bf16x8 dSb[2];
+      const int lim = n_allow - ((j >> 1) * 64 + 32 * (j & 1) + 8 * hh);
+      DqProbs<16, decltype(mask)::value> pr{S, dP, lse2, dlt, c, lim, dSb};
+      pr(std::integral_constant<int, 0>{});
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      G2::run(lds_addr(lds + OFF_TRANS + ((j >> 1) & 1) * TRANS_BUF) + n * L::TROW +
+                  (32 * (j & 1) + 8 * hh) * 2,
+              dQt, dSb);
+    };
     int j = 0;
-    for (; j < j_free; j += 2) {  // NJ and j_free are even
-      iter(std::false_type{}, j, SA, dPA, SB, dPB);
-      iter(std::false_type{}, j + 1, SB, dPB, SA, dPA);
-    }
-    for (; j < NJ; j += 2) {
-      iter(std::true_type{}, j, SA, dPA, SB, dPB);
-      iter(std::true_type{}, j + 1, SB, dPB, SA, dPA);
-    }
+    for (; j < j_free; ++j) iter(std::false_type{}, j);
+    for (; j < NJ; ++j) iter(std::true_type{}, j);
   }
-
   if (qi < a.Cq) {
     float* dqr = a.dq + b * a.dq_bs + h * a.dq_hs + (int64_t)qi * D;
 #pragma unroll
@@ -780,12 +758,12 @@ constexpr size_t dq_lds_bytes() {
 }
 
 template <typename K>
-hipError_t launch_big(K kern, size_t lds, int grid, const BwdArgs& a, hipStream_t s) {
+hipError_t launch_big(K kern, size_t lds, int grid, const BwdArgs& a, hipStream_t s, int threads = 256) {
   static_assert(sizeof(BwdArgs) <= 4096, "kernel arguments");
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -817,13 +795,14 @@ hipError_t launch_bwd_dkdv(BwdArgs a, int D, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dq(BwdArgs a, int D, hipStream_t s) {
-  a.n_tiles = (a.Cq + 127) / 128;  // 128-query workgroups, per (batch, query head)
+  constexpr int NW = kDqWaves;
+  a.n_tiles = (a.Cq + 32 * NW - 1) / (32 * NW);  // 256-query workgroups, per (batch, query head)
   a.n_items = a.B * a.Hq * a.n_tiles;
   a.per_xcd = (a.n_items + kXcds - 1) / kXcds;
   if (a.n_items <= 0) return hipSuccess;
   const int grid = a.per_xcd * kXcds;
-  if (D == 128) return launch_big(attn_bwd_dq<128>, dq_lds_bytes<128>(), grid, a, s);
-  return launch_big(attn_bwd_dq<64>, dq_lds_bytes<64>(), grid, a, s);
+  if (D == 128) return launch_big(attn_bwd_dq<128>, dq_lds_bytes<128>(), grid, a, s, 64 * NW);
+  return launch_big(attn_bwd_dq<64>, dq_lds_bytes<64>(), grid, a, s, 64 * NW);
 }
 
 hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, float* lse2p,

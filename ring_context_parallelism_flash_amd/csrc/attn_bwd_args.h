@@ -57,7 +57,7 @@ void fill_bwd_heads(BwdArgs& a, int32_t Hq, int32_t Hkv, const std::vector<uint8
                     const std::vector<uint8_t>& order);
 
 // The dk/dv kernel (a workgroup per 128 keys of one KV head) and the dq kernel
-// (a workgroup per 128 queries of one query head); each sets its own work
+// (a workgroup per 256 queries of one query head); each sets its own work
 // list (n_tiles, n_items, per_xcd) in its copy of the arguments.
 hipError_t launch_bwd_dkdv(BwdArgs a, int D, hipStream_t s);
 hipError_t launch_bwd_dq(BwdArgs a, int D, hipStream_t s);
