@@ -53,7 +53,10 @@ def kernel_sources_sha256(sources=KERNEL_SOURCES) -> str:
         with open(os.path.join(ROOT, "ring_context_parallelism_flash_amd", "csrc", name), "rb") as f:
             h.update(f.read())
         if name.endswith(".hip"):
-            h.update(" ".join(ra_build.FLAGS + ra_build.EXTRA.get(name, [])).encode())
+            # include paths name the checkout's directory, which differs from
+            # machine to machine; hash them relative to the repository root
+            flags = [f.replace(ROOT, "<root>") for f in ra_build.FLAGS + ra_build.EXTRA.get(name, [])]
+            h.update(" ".join(flags).encode())
     return h.hexdigest()
 
 
