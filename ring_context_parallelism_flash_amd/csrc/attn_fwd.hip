@@ -732,22 +732,18 @@ hipError_t launch_attn(const AttnArgs& a, ra_dtype dt, int D, hipStream_t s) {
   if (a.n_items <= 0) return hipSuccess;
   const dim3 grid((unsigned)(a.per_xcd * kXcds)), block(kThreads);
   if (dt == RA_BF16) {
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)attn_fwd_bf16<128>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)bf16_lds_bytes(128));
-      if (e != hipSuccess) return e;
-      e = hipFuncSetAttribute((const void*)attn_fwd_bf16<64>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bf16_lds_bytes(64));
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    // The dynamic-LDS limit is a per-device property of the function: set it
+    // on every launch (a host-side call), so any device and any thread that
+    // launches through the library has it.
+    const void* fn = D == 128 ? (const void*)attn_fwd_bf16<128> : (const void*)attn_fwd_bf16<64>;
+    const size_t lds = bf16_lds_bytes(D);
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
     const dim3 block8(kThreadsBf16);
     if (D == 128)
-      hipLaunchKernelGGL(attn_fwd_bf16<128>, grid, block8, bf16_lds_bytes(128), s, a);
+      hipLaunchKernelGGL(attn_fwd_bf16<128>, grid, block8, lds, s, a);
     else
-      hipLaunchKernelGGL(attn_fwd_bf16<64>, grid, block8, bf16_lds_bytes(64), s, a);
+      hipLaunchKernelGGL(attn_fwd_bf16<64>, grid, block8, lds, s, a);
   } else {
     if (D == 128)
       hipLaunchKernelGGL(attn_fwd_f32<128>, grid, block, 0, s, a);

@@ -317,6 +317,24 @@ def test_work_counts_s64_n4():
     assert list(oracle.pairs_per_rank_step(64, 4, "contiguous", True).sum(1)) == [136, 392, 648, 904]
 
 
+def test_score_term_grows_256x_from_8k_to_128k():
+    """"Sequence and Context Parallelism", *The memory that data and tensor
+    parallelism cannot touch*: a head's score matrix is S x S, so a 16x longer
+    context (8k -> 128k) carries 256x the score term. The oracle's pair and
+    flop counters reproduce the factor without a mask; with the causal mask
+    the count is S(S+1)/2 (brute-forced at small S above), whose ratio tends
+    to the same factor."""
+    small, big = 8192, 131072
+    p_small = oracle.useful_pairs(np.arange(small), np.arange(small), False)
+    p_big = oracle.useful_pairs(np.arange(big), np.arange(big), False)
+    assert p_big == 256 * p_small
+    assert oracle.useful_flops(1, 64, 128, p_big) == 256 * oracle.useful_flops(1, 64, 128, p_small)
+    causal_ratio = (big * (big + 1) // 2) / (small * (small + 1) // 2)
+    assert abs(causal_ratio / 256 - 1) < 1e-3
+    # the headline count: 4 D flops per allowed pair, 64 query heads, causal S = 2^17
+    assert oracle.useful_flops(1, 64, 128, big * (big + 1) // 2) == 281477124194304
+
+
 # ------------------------------------------------------------------- merge
 def _partial(q, k, v, causal=False, q_pos=None, k_pos=None):
     return oracle.attention(q, k, v, causal=causal, q_pos=q_pos, k_pos=k_pos)
