@@ -126,6 +126,12 @@ RINGS = [
                        causal=False, N=4, layout="contiguous"),
     workloads.Workload("bwd_single_rank", B=1, Hq=2, Hkv=2, D=128, S=640, dtype="bf16", seed=55,
                        causal=True, N=1, layout="zigzag"),
+    # five query heads per KV head, five ranks, 101-token chunks (ragged tiles)
+    workloads.Workload("bwd_zigzag_gqa5_n5_ragged", B=1, Hq=5, Hkv=1, D=64, S=1010,
+                       dtype="bf16", seed=56, causal=True, N=5, layout="zigzag"),
+    # non-causal zigzag with two batches
+    workloads.Workload("bwd_noncausal_zigzag_b2", B=2, Hq=4, Hkv=2, D=64, S=600, dtype="bf16",
+                       seed=57, causal=False, N=3, layout="zigzag"),
 ]
 
 

@@ -314,6 +314,12 @@ SMALL_RINGS = [
                        seed=28, causal=True, N=8, layout="striped"),
     workloads.Workload("striped_f32_d64", B=2, Hq=2, Hkv=1, D=64, S=600, dtype="f32", seed=29,
                        causal=True, N=3, layout="striped"),
+    # non-causal zigzag with two batches and two query heads per KV head
+    workloads.Workload("noncausal_zigzag_b2_gqa2_d64", B=2, Hq=6, Hkv=3, D=64, S=1200,
+                       dtype="bf16", seed=30, causal=False, N=3, layout="zigzag"),
+    # five query heads per KV head, five ranks, 101-token chunks (ragged tiles)
+    workloads.Workload("causal_zigzag_gqa5_n5_ragged", B=1, Hq=5, Hkv=1, D=64, S=1010,
+                       dtype="bf16", seed=31, causal=True, N=5, layout="zigzag"),
 ]
 
 
