@@ -182,8 +182,8 @@ __device__ __forceinline__ void epilogue(const AttnArgs& a, const WorkItem& it, 
 // multiplies per lane) are skipped on almost every tile, and the result is
 // unchanged, since l and O always share the same reference.
 // ---------------------------------------------------------------------------
-constexpr float kRescaleLog2 = 8.f;
-constexpr float kFastSum = 256.f;  // 2^kRescaleLog2
+constexpr int kRescaleLog2 = 8;
+constexpr float kFastSum = (float)(1 << kRescaleLog2);
 
 // P*V operand stream of one 64-key tile: MFMA i (i = 0 .. 4*DT-1) takes
 // u = i / DT (16-key step) and d tile T = i % DT; its V^T operand sits at
