@@ -207,22 +207,31 @@ template <int PER, bool MASK>
 struct DkdvProbs {
   const floatx16& S;
   const floatx16& dP;
-  const float (&l2)[16];
-  const float (&dl)[16];
+  f32x4 (&lx)[4];  // lse2 of rows 16w + jj: lx[2w + jj/4][jj%4]
+  f32x4 (&dx)[4];  // delta, same layout
   float c;
   int lim;
   bf16x8 (&Pb)[2];
   bf16x8 (&dSb)[2];
   template <int I>
   __device__ __forceinline__ void operator()(std::integral_constant<int, I>) {
+    if constexpr (I == 0) {
+      // lx / dx are LDS reads issued before the stream; its first counted
+      // wait (just executed) retired them, since LDS reads return in order.
+      // Naming the registers here keeps every use below that wait.
+      asm volatile("" : "+v"(lx[0]), "+v"(lx[1]), "+v"(lx[2]), "+v"(lx[3]), "+v"(dx[0]),
+                   "+v"(dx[1]), "+v"(dx[2]), "+v"(dx[3]));
+    }
 #pragma unroll
     for (int e = I * PER; e < (I + 1) * PER; ++e) {
       const int w = e >> 3, jj = e & 7;
-      float sc = fmaf(S[e], c, -l2[e]);
+      const float l2 = lx[2 * w + (jj >> 2)][jj & 3];
+      const float dl = dx[2 * w + (jj >> 2)][jj & 3];
+      float sc = fmaf(S[e], c, -l2);
       if constexpr (MASK) sc = (16 * w + jj < lim) ? -INFINITY : sc;
       const float p = __builtin_amdgcn_exp2f(sc);
       Pb[w][jj] = (__bf16)p;
-      dSb[w][jj] = (__bf16)(p * (dP[e] - dl[e]));
+      dSb[w][jj] = (__bf16)(p * (dP[e] - dl));
     }
   }
 };
@@ -389,33 +398,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
     }
     const unsigned char* TB = lds + OFF_TRANS + ((j >> 1) & 1) * TRANS_BUF;
     const int r0 = 32 * (j & 1) + 8 * hh;  // rows r0 + 16w + jj of the tile
-    float l2[16], dl[16];
+    // (tile_src reads the head table with a wait of its own: before the
+    // uncounted lse2 / delta reads below)
+    const int lim = row_min - (tile_src(j >> 1).q0 + r0);
     const unsigned la = lds_addr(TB) + r0 * 4;
     f32x4 lx[4] = {ds_read_f4<OFF_L>(la), ds_read_f4<OFF_L + 16>(la),
                    ds_read_f4<OFF_L + 64>(la), ds_read_f4<OFF_L + 80>(la)};
     f32x4 dx[4] = {ds_read_f4<OFF_DL>(la), ds_read_f4<OFF_DL + 16>(la),
                    ds_read_f4<OFF_DL + 64>(la), ds_read_f4<OFF_DL + 80>(la)};
-    // The hardware writes these registers when the reads return, but the
-    // compiler takes them as written by the read statements: the wait names
-    // them as operands, so no use can be scheduled above it.
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(lx[0]), "+v"(lx[1]), "+v"(lx[2]), "+v"(lx[3]), "+v"(dx[0]), "+v"(dx[1]),
-                   "+v"(dx[2]), "+v"(dx[3])
-                 :
-                 : "memory");
-#pragma unroll
-    for (int w = 0; w < 2; ++w)
-#pragma unroll
-      for (int v4 = 0; v4 < 2; ++v4) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          l2[8 * w + 4 * v4 + e] = lx[2 * w + v4][e];
-          dl[8 * w + 4 * v4 + e] = dx[2 * w + v4][e];
-        }
-      }
     bf16x8 Pb[2], dSb[2];
-    DkdvProbs<16 / G1::N, decltype(mask)::value> pr{
-        Sc, dPc, l2, dl, c, row_min - (tile_src(j >> 1).q0 + r0), Pb, dSb};
+    DkdvProbs<16 / G1::N, decltype(mask)::value> pr{Sc, dPc, lx, dx, c, lim, Pb, dSb};
     // the S, dP MFMAs of sub-tile j+1 (past the end: a stale but valid
     // buffer, result unused) with this sub-tile's arithmetic between them
     G1::run(g1_addr(min(j + 1, NJ - 1)), kreg, vreg, Sn, dPn, pr);
