@@ -198,6 +198,70 @@ struct SdpStream {
   }
 };
 
+// The S, dP stream of the next sub-tile followed by the dV, dK stream of
+// this one, as ONE operand stream: N1 = 2*KS reads from the Q / dO rows (ra)
+// then N2 = 4*DT from the Q^T / dO^T tiles (ta), PF in flight through one
+// register ring with counted waits over the whole sequence. The last PF
+// steps of the first part issue the first reads of the second, so the dV /
+// dK MFMAs start without an LDS round trip of their own. `work` runs after
+// each of the first N1 MFMAs (it must finish P, dS by then).
+template <class G1, class G2>
+struct SdpDkdvStream {
+  static constexpr int N1 = G1::N, N2 = G2::N, N = N1 + N2, PF = 4;
+  static constexpr int KS = G1::KS, DT = G2::DT;
+  template <int I>
+  static __device__ __forceinline__ bf16x8 read(unsigned ra, unsigned ta) {
+    if constexpr (I < N1)
+      return ds_read16<G1::off(I)>(ra);
+    else
+      return ds_read16<G2::off(I - N1)>(ta);
+  }
+  template <int I, class W>
+  static __device__ __forceinline__ void step(unsigned ra, unsigned ta, bf16x8 (&r)[PF],
+                                              const bf16x8 (&kreg)[KS], const bf16x8 (&vreg)[KS],
+                                              floatx16& S, floatx16& dP, floatx16 (&dVt)[DT],
+                                              floatx16 (&dKt)[DT], const bf16x8 (&Pb)[2],
+                                              const bf16x8 (&dSb)[2], W& work) {
+    lds_wait<(N - 1 - I < PF - 1) ? (N - 1 - I) : (PF - 1)>(r[I % PF]);
+    if constexpr (I < N1) {
+      if constexpr ((I & 1) == 0)
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[I % PF], kreg[I >> 1], S, 0, 0, 0);
+      else
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[I % PF], vreg[I >> 1], dP, 0, 0, 0);
+    } else {
+      constexpr int i = I - N1, T = (i >> 1) % DT, u = i / (2 * DT);
+      if constexpr ((i & 1) == 0)
+        dVt[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[I % PF], Pb[u], dVt[T], 0, 0, 0);
+      else
+        dKt[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r[I % PF], dSb[u], dKt[T], 0, 0, 0);
+    }
+    if constexpr (I + PF < N) r[I % PF] = read<I + PF>(ra, ta);
+    if constexpr (I < N1) work(std::integral_constant<int, I>{});
+    if constexpr (I + 1 < N) step<I + 1>(ra, ta, r, kreg, vreg, S, dP, dVt, dKt, Pb, dSb, work);
+  }
+  template <int I>
+  static __device__ __forceinline__ void prefetch(unsigned ra, unsigned ta, bf16x8 (&r)[PF]) {
+    r[I] = read<I>(ra, ta);
+    if constexpr (I + 1 < PF) prefetch<I + 1>(ra, ta, r);
+  }
+  template <class W>
+  static __device__ __forceinline__ void run(unsigned ra, unsigned ta, const bf16x8 (&kreg)[KS],
+                                             const bf16x8 (&vreg)[KS], floatx16& S, floatx16& dP,
+                                             floatx16 (&dVt)[DT], floatx16 (&dKt)[DT],
+                                             const bf16x8 (&Pb)[2], const bf16x8 (&dSb)[2],
+                                             W& work) {
+    static_assert(N1 >= PF && N2 >= PF, "fewer operands than reads in flight");
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      S[i] = 0.f;
+      dP[i] = 0.f;
+    }
+    bf16x8 r[PF];
+    prefetch<0>(ra, ta, r);
+    step<0>(ra, ta, r, kreg, vreg, S, dP, dVt, dKt, Pb, dSb, work);
+  }
+};
+
 // P = exp2(S c - lse2) and dS = P (dP - delta) of a 32-query sub-tile,
 // rounded to bf16 (the B operands of the dV / dK products), PER elements per
 // step of the next sub-tile's S / dP stream. Element e = 8w + jj of a lane is
@@ -409,10 +473,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
     bf16x8 Pb[2], dSb[2];
     DkdvProbs<16 / G1::N, decltype(mask)::value> pr{Sc, dPc, lx, dx, c, lim, Pb, dSb};
     // the S, dP MFMAs of sub-tile j+1 (past the end: a stale but valid
-    // buffer, result unused) with this sub-tile's arithmetic between them
-    G1::run(g1_addr(min(j + 1, NJ - 1)), kreg, vreg, Sn, dPn, pr);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    G2::run(lds_addr(TB) + n * L::TROW + r0 * 2, dVt, dKt, Pb, dSb);
+    // buffer, result unused) with this sub-tile's arithmetic between them,
+    // then this sub-tile's dV, dK MFMAs, in one operand stream
+    SdpDkdvStream<G1, G2>::run(g1_addr(min(j + 1, NJ - 1)), lds_addr(TB) + n * L::TROW + r0 * 2,
+                               kreg, vreg, Sn, dPn, dVt, dKt, Pb, dSb, pr);
   };
 
   __syncthreads();  // the head table
