@@ -438,6 +438,24 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
   };
 
   bool issued = false;  // this wave issued a load batch at the start of the previous iteration
+  // lse2 / delta of sub-tile j (8 LDS reads into lx, dx). Sub-tiles 2m and
+  // 2m+1 read the same Q^T / dO^T tile, published by the barrier of
+  // iteration 2m and not overwritten before iteration 2m+2: the reads of the
+  // odd sub-tile go out at the end of the even iteration and land across the
+  // barrier (the head-table wait after it retires them).
+  auto lse_reads = [&](int j, f32x4 (&lx)[4], f32x4 (&dx)[4]) {
+    const unsigned char* TB = lds + OFF_TRANS + ((j >> 1) & 1) * TRANS_BUF;
+    const unsigned la = lds_addr(TB) + (32 * (j & 1) + 8 * hh) * 4;
+    lx[0] = ds_read_f4<OFF_L>(la);
+    lx[1] = ds_read_f4<OFF_L + 16>(la);
+    lx[2] = ds_read_f4<OFF_L + 64>(la);
+    lx[3] = ds_read_f4<OFF_L + 80>(la);
+    dx[0] = ds_read_f4<OFF_DL>(la);
+    dx[1] = ds_read_f4<OFF_DL + 16>(la);
+    dx[2] = ds_read_f4<OFF_DL + 64>(la);
+    dx[3] = ds_read_f4<OFF_DL + 80>(la);
+  };
+  f32x4 lx[4], dx[4];
   auto iter = [&](auto mask, int j, const floatx16& Sc, const floatx16& dPc, floatx16& Sn,
                   floatx16& dPn) {
     if (j > 0) {
@@ -465,11 +483,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
     // (tile_src reads the head table with a wait of its own: before the
     // uncounted lse2 / delta reads below)
     const int lim = row_min - (tile_src(j >> 1).q0 + r0);
-    const unsigned la = lds_addr(TB) + r0 * 4;
-    f32x4 lx[4] = {ds_read_f4<OFF_L>(la), ds_read_f4<OFF_L + 16>(la),
-                   ds_read_f4<OFF_L + 64>(la), ds_read_f4<OFF_L + 80>(la)};
-    f32x4 dx[4] = {ds_read_f4<OFF_DL>(la), ds_read_f4<OFF_DL + 16>(la),
-                   ds_read_f4<OFF_DL + 64>(la), ds_read_f4<OFF_DL + 80>(la)};
+    if (!(j & 1)) lse_reads(j, lx, dx);  // odd sub-tiles: issued by the even iteration
     bf16x8 Pb[2], dSb[2];
     DkdvProbs<16 / G1::N, decltype(mask)::value> pr{Sc, dPc, lx, dx, c, lim, Pb, dSb};
     // the S, dP MFMAs of sub-tile j+1 (past the end: a stale but valid
@@ -477,6 +491,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
     // then this sub-tile's dV, dK MFMAs, in one operand stream
     SdpDkdvStream<G1, G2>::run(g1_addr(min(j + 1, NJ - 1)), lds_addr(TB) + n * L::TROW + r0 * 2,
                                kreg, vreg, Sn, dPn, dVt, dKt, Pb, dSb, pr);
+    if (!(j & 1)) lse_reads(j + 1, lx, dx);  // NJ is even: an odd sub-tile follows
   };
 
   __syncthreads();  // the head table
