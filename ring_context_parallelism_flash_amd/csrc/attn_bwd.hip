@@ -383,7 +383,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
   // load, and waiting for it would also drain the in-flight tile loads.
   int* htab = reinterpret_cast<int*>(lds + OFF_HTAB);
   if (tid < ng) htab[tid] = a.head_order[g0 + tid];
+  // Up to 64 heads also sit one per lane of a register (loaded with the
+  // table, published by the same barrier): v_readlane returns head i with no
+  // memory access, where the table read leaves this wave -- the only one on
+  // its SIMD -- waiting for an LDS round trip.
+  const bool heads_in_lanes = ng <= 64;
+  const int vhead = (lane < ng) ? (int)a.head_order[g0 + lane] : 0;
   auto head_at = [&](int i) -> int {  // i wave-uniform; the table is published
+    if (heads_in_lanes) return __builtin_amdgcn_readlane(vhead, i);
     int v;
     asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
                  : "=v"(v)
@@ -442,7 +449,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
   // 2m+1 read the same Q^T / dO^T tile, published by the barrier of
   // iteration 2m and not overwritten before iteration 2m+2: the reads of the
   // odd sub-tile go out at the end of the even iteration and land across the
-  // barrier (the head-table wait after it retires them).
+  // barrier; they are older than the operand stream's first reads, so its
+  // first counted wait retires them.
   auto lse_reads = [&](int j, f32x4 (&lx)[4], f32x4 (&dx)[4]) {
     const unsigned char* TB = lds + OFF_TRANS + ((j >> 1) & 1) * TRANS_BUF;
     const unsigned la = lds_addr(TB) + (32 * (j & 1) + 8 * hh) * 4;

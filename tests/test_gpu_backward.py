@@ -185,10 +185,17 @@ def test_ring_bwd_gqa_128k_invariants_and_sampled_dq():
 
 
 # ------------------------------------------------------- head maps and groups
-@pytest.mark.parametrize("kv_map,Hkv", [([1, 0, 1, 0, 0, 1], 2), ([2, 0, 1, 1, 2, 0, 0, 2], 3)])
+@pytest.mark.parametrize("kv_map,Hkv", [
+    ([1, 0, 1, 0, 0, 1], 2),
+    ([2, 0, 1, 1, 2, 0, 0, 2], 3),
+    # 66 query heads on KV head 0: more than a wave's 64 lanes can hold, so
+    # the dk/dv kernel reads the group's heads from its LDS table
+    ([1 if i % 12 == 0 else 0 for i in range(72)], 2),
+], ids=["6q_2kv", "8q_3kv", "72q_group66"])
 def test_block_bwd_custom_head_map(kv_map, Hkv):
     """Query heads that read their KV heads out of order (the dk/dv kernel
-    walks each KV head's query heads from a per-workgroup head table)."""
+    walks each KV head's query heads from a per-workgroup head list: one head
+    per lane for groups of up to 64, an LDS table beyond)."""
     Hq, Cq, Ck, D = len(kv_map), 192, 160, 128
     q, k, v = _rnd((1, Hq, Cq, D), 71), _rnd((1, Hkv, Ck, D), 72), _rnd((1, Hkv, Ck, D), 73)
     dout = _rnd((1, Hq, Cq, D), 74)
