@@ -312,8 +312,11 @@ struct NoWork {
 // 1, ... Iteration j issues the
 // S and dP MFMAs of sub-tile j+1 with the probability arithmetic of sub-tile
 // j spread between them (the VALU work runs under the wave's own matrix
-// work), then the dV and dK MFMAs of sub-tile j. Both MFMA streams read their
-// LDS operands through explicit register rings. LDS holds two buffers of
+// work), then the dV and dK MFMAs of sub-tile j. The two MFMA groups read
+// their LDS operands through one explicit register ring (SdpDkdvStream), so
+// the dV / dK operands are in flight before the S / dP MFMAs end, and the
+// sub-tile's lse2 / delta reads are retired by that ring's first counted
+// wait (an odd sub-tile's already before the barrier). LDS holds two buffers of
 // Q / dO rows (read by the S, dP products) and two of Q^T / dO^T plus the
 // rows' lse2 and delta (read by the dV, dK products and the arithmetic).
 // Rows of tile u+2 are loaded at the start of iteration 2u+1 and Q^T/dO^T of
