@@ -98,8 +98,8 @@ def attention(q, k, v, *, causal: bool, scale: float | None = None,
     out = np.zeros((B, Hq, R, D))
     lse = np.full((B, Hq, R), NEG_INF)
     # Rows are independent; they are taken a few at a time only to bound the
-    # size of the [rows, Sk] score matrix.
-    row_block = max(1, min(256, (1 << 21) // max(Sk, 1)))
+    # size of the [rows, Sk] score matrix (at most 2^24 entries, 128 MiB).
+    row_block = max(1, min(256, (1 << 24) // max(Sk, 1)))
     for b in range(B):
         for h in range(Hq):
             g = kv_map[h]
