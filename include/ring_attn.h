@@ -35,8 +35,11 @@
  *     runs surfaces at the caller's next synchronization.
  *   - lse is the natural-log log-sum-exp of the scaled, allowed scores, in
  *     float32. The identity ("no key seen yet") state is out = 0, lse = -inf.
- *   - Entry points are thread-safe with respect to each other; calls that
- *     share output or workspace buffers must be ordered by the caller.
+ *   - Entry points are thread-safe with respect to each other: the library
+ *     keeps no state between calls apart from the kernel-timing record (its
+ *     own lock) and each thread's last error; a ring call creates its own
+ *     stream events. Calls that share output or workspace buffers must be
+ *     ordered by the caller.
  */
 #ifndef RING_ATTN_H
 #define RING_ATTN_H
@@ -396,6 +399,28 @@ ra_status ra_usp_sim_fwd(const void* q, const void* k, const void* v, void* out,
  * ---------------------------------------------------------------------- */
 ra_status ra_kernel_timing_enable(int32_t enable);
 ra_status ra_kernel_timing_read(double* total_ms, int64_t* launches, double* useful_flops);
+
+/* ------------------------------------------------------------------------
+ * Device figures behind the roofline (measurement, not computation).
+ *
+ * ra_device_info: the current device's compute-unit count and its maximum
+ * shader clock in kHz (hipDeviceGetAttribute), the two factors of the dense
+ * bf16 matrix peak CU x clock x flops/CU/clk. Host-only; enqueues nothing.
+ *
+ * ra_mfma_probe_bf16: launches one workgroup of 8 waves on every compute unit
+ * (two waves per SIMD); each wave issues 4*iters register-fed
+ * v_mfma_f32_32x32x16_bf16 (32768 flops each) and writes three int64 to
+ * `out` (device memory, caller-owned, 8-byte aligned, out_len >= 3 * waves):
+ * its elapsed shader-clock cycles, its elapsed ticks of the constant 100 MHz
+ * reference clock, and a liveness word. *waves (host) receives the wave count
+ * (8 x compute units). flops/CU/clk = 8 * 4 * iters * 32768 / cycles; the
+ * clock during the probe is cycles / (ticks / 100 MHz). iters in [1, 2^24].
+ * Errors: RA_ERR_NULL, RA_ERR_ARG, RA_ERR_ALIGN, RA_ERR_WORKSPACE (out too
+ * short), RA_ERR_HIP. Asynchronous on `stream`.
+ * ---------------------------------------------------------------------- */
+ra_status ra_device_info(int32_t* compute_units, int32_t* max_clock_khz);
+ra_status ra_mfma_probe_bf16(int32_t iters, int64_t* out, int64_t out_len, int32_t* waves,
+                             void* stream);
 
 #ifdef __cplusplus
 }

@@ -20,10 +20,9 @@ __all__ = [
     "ra_block_attn_fwd", "ra_lse_merge", "ra_zigzag_permute", "ra_striped_permute",
     "ra_ring_sim_workspace_bytes", "ra_block_attn_bwd_workspace_bytes", "ra_block_attn_bwd",
     "ra_ring_sim_bwd_workspace_bytes", "ra_ring_sim_bwd", "ring_attention_sim_backward",
-    "ra_ring_sim_fwd", "ra_kernel_timing_enable", "ra_kernel_timing_read", "zigzag_pos",
-    "contiguous_pos", "striped_pos", "ring_attention_sim", "ra_ulysses_all_to_all",
+    "ra_ring_sim_fwd", "ra_kernel_timing_enable", "ra_kernel_timing_read", "ring_attention_sim", "ra_ulysses_all_to_all",
     "ra_ulysses_sim_workspace_bytes", "ra_ulysses_sim_fwd", "ra_usp_sim_workspace_bytes",
-    "ra_usp_sim_fwd", "EXPORTS",
+    "ra_usp_sim_fwd", "ra_device_info", "ra_mfma_probe_bf16", "EXPORTS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -41,7 +40,8 @@ EXPORTS = (
     "ra_ring_sim_fwd", "ra_block_attn_bwd_workspace_bytes", "ra_block_attn_bwd",
     "ra_ring_sim_bwd_workspace_bytes", "ra_ring_sim_bwd", "ra_ulysses_all_to_all",
     "ra_ulysses_sim_workspace_bytes", "ra_ulysses_sim_fwd", "ra_usp_sim_workspace_bytes",
-    "ra_usp_sim_fwd", "ra_kernel_timing_enable", "ra_kernel_timing_read",
+    "ra_usp_sim_fwd", "ra_kernel_timing_enable", "ra_kernel_timing_read", "ra_device_info",
+    "ra_mfma_probe_bf16",
 )
 
 
@@ -118,6 +118,8 @@ def lib() -> ctypes.CDLL:
                                      c_int32, c_int32, c_int32, c_int64, c_int32, c_int32,
                                      c_int32, c_int32, c_int32, c_int32, c_float, P(c_int32),
                                      c_void_p, c_size_t, c_void_p, c_void_p]),
+        "ra_device_info": (c_int32, [P(c_int32), P(c_int32)]),
+        "ra_mfma_probe_bf16": (c_int32, [c_int32, c_void_p, c_int64, P(c_int32), c_void_p]),
         "ra_kernel_timing_enable": (c_int32, [c_int32]),
         "ra_kernel_timing_read": (c_int32, [P(ctypes.c_double), P(c_int64),
                                             P(ctypes.c_double)]),
@@ -178,20 +180,6 @@ def _dtype(t):
     if t.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return _DTYPES[t.dtype]
-
-
-def contiguous_pos(S: int, N: int, rank: int):
-    C = S // N
-    return (1, C, rank * C)
-
-
-def zigzag_pos(S: int, N: int, rank: int):
-    c = S // (2 * N)
-    return (2, c, rank * c, (2 * N - 1 - rank) * c)
-
-
-def striped_pos(S: int, N: int, rank: int):
-    return (1, S // N, rank, 0, N)
 
 
 # ------------------------------------------------------------------ entry points
@@ -403,6 +391,40 @@ def ra_usp_sim_fwd(q, k, v, out, lse, *, P_u, P_r, layout="zigzag", causal=True,
         float(scale), _kvmap(kv_head_of_q, Hq), _ptr(workspace), wbytes,
         _stream(compute_stream), xs))
     return out, lse
+
+
+def ra_device_info():
+    """(compute units, maximum shader clock in kHz) of the current device."""
+    cus, khz = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().ra_device_info(ctypes.byref(cus), ctypes.byref(khz)))
+    return cus.value, khz.value
+
+
+def ra_mfma_probe_bf16(iters=20000, device=None):
+    """Run the matrix-core probe once (after a short warm-up launch) and
+    return its figures: dense bf16 flops per compute unit per clock, the
+    shader clock during the probe (from the 100 MHz reference ticks) and the
+    chip rate it sustained."""
+    dev = torch.device(device) if device is not None else torch.device("cuda",
+                                                                       torch.cuda.current_device())
+    cus, _ = ra_device_info()
+    buf = torch.zeros(3 * 8 * cus, dtype=torch.int64, device=dev)
+    waves = ctypes.c_int32()
+    stream = _stream(None)
+    _check(lib().ra_mfma_probe_bf16(max(1, iters // 10), _ptr(buf), buf.numel(),
+                                    ctypes.byref(waves), stream))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    _check(lib().ra_mfma_probe_bf16(iters, _ptr(buf), buf.numel(), ctypes.byref(waves), stream))
+    e1.record()
+    torch.cuda.synchronize()
+    rec = buf.view(-1, 3)[:waves.value].double()
+    cycles, ticks = rec[:, 0].mean().item(), rec[:, 1].mean().item()
+    flops = 8 * 4 * iters * 32768.0
+    ms = e0.elapsed_time(e1)
+    return {"flops_per_cu_clk": flops / cycles, "clock_mhz": cycles / (ticks / 100.0),
+            "chip_tflops": flops * cus / (ms * 1e-3) / 1e12, "waves": waves.value,
+            "iters": iters}
 
 
 def ra_kernel_timing_enable(enable=True):

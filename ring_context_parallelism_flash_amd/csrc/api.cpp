@@ -163,29 +163,26 @@ ra_status timed_launch(const AttnArgs& a, ra_dtype dt, int D, hipStream_t s, dou
 }
 
 // ---------------------------------------------------------------- ring events
+// The ready / freed / V^T-done events of ONE ring call. Every call creates
+// its own set and destroys it after enqueueing (a destroyed event that work
+// still waits on completes normally), so calls from several host threads
+// never bind a wait to another call's record and the library keeps no
+// per-device state between calls.
 struct RingEvents {
-  hipEvent_t ready[2], freed[2], vt_done;
-};
-std::mutex g_ev_mu;
-RingEvents* g_ring_ev[64] = {nullptr};
-
-ra_status ring_events(RingEvents*& out) {
-  int dev = 0;
-  RA_HIP(hipGetDevice(&dev));
-  if (dev < 0 || dev >= 64) return fail(RA_ERR_UNSUPPORTED, "device index %d", dev);
-  std::lock_guard<std::mutex> lk(g_ev_mu);
-  if (!g_ring_ev[dev]) {
-    RingEvents* r = new RingEvents;
-    for (int i = 0; i < 2; ++i) {
-      RA_HIP(hipEventCreateWithFlags(&r->ready[i], hipEventDisableTiming));
-      RA_HIP(hipEventCreateWithFlags(&r->freed[i], hipEventDisableTiming));
-    }
-    RA_HIP(hipEventCreateWithFlags(&r->vt_done, hipEventDisableTiming));
-    g_ring_ev[dev] = r;
+  hipEvent_t ready[2] = {nullptr, nullptr}, freed[2] = {nullptr, nullptr}, vt_done = nullptr;
+  ~RingEvents() {
+    for (hipEvent_t e : {ready[0], ready[1], freed[0], freed[1], vt_done})
+      if (e) (void)hipEventDestroy(e);
   }
-  out = g_ring_ev[dev];
-  return RA_OK;
-}
+  ra_status create() {
+    for (int i = 0; i < 2; ++i) {
+      RA_HIP(hipEventCreateWithFlags(&ready[i], hipEventDisableTiming));
+      RA_HIP(hipEventCreateWithFlags(&freed[i], hipEventDisableTiming));
+    }
+    RA_HIP(hipEventCreateWithFlags(&vt_done, hipEventDisableTiming));
+    return RA_OK;
+  }
+};
 
 // ---------------------------------------------------------------- shared checks
 ra_status check_common(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, ra_dtype dt,
@@ -429,10 +426,11 @@ ra_status ra_ring_sim_fwd(const void* q, const void* k, const void* v, void* out
     return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", L.total, workspace_bytes);
   if (!aligned(workspace, 256)) return fail(RA_ERR_ALIGN, "workspace must be 256-byte aligned");
 
-  RingEvents* ev = nullptr;
-  if ((st = ring_events(ev)) != RA_OK) return st;
   hipStream_t cs = reinterpret_cast<hipStream_t>(compute_stream);
   hipStream_t xs = copy_stream ? reinterpret_cast<hipStream_t>(copy_stream) : cs;
+  RingEvents ring_ev;
+  RingEvents* ev = &ring_ev;
+  if (xs != cs && (st = ring_ev.create()) != RA_OK) return st;
   const size_t es = esize(dtype);
   const int64_t C = L.C, Cpad = L.Cpad;
   char* ws = reinterpret_cast<char*>(workspace);
@@ -734,8 +732,8 @@ ra_status ra_ring_sim_bwd(const void* q, const void* k, const void* v, const voi
   float* dk_acc = reinterpret_cast<float*>(ws + L.dk);
   float* dv_acc = reinterpret_cast<float*>(ws + L.dv);
   char* pw = ws + L.prep;
-  RA_HIP(hipMemsetAsync(ws, 0, L.prep, s));
   hipError_t e;
+  if ((e = launch_zero_fill(ws, L.prep, s)) != hipSuccess) return hip_fail(e, "accumulator clear");
   if ((e = launch_vt_transpose(q, pw + L.P.qt, (int64_t)B * Hq, N, C, Cp, D, S * D, s)) != hipSuccess ||
       (e = launch_vt_transpose(dout, pw + L.P.dot, (int64_t)B * Hq, N, C, Cp, D, S * D, s)) != hipSuccess ||
       (e = launch_vt_transpose(k, pw + L.P.kt, (int64_t)B * Hkv, N, C, Cp, D, S * D, s)) != hipSuccess ||
@@ -1061,6 +1059,37 @@ ra_status ra_usp_sim_fwd(const void* q, const void* k, const void* v, void* out,
     if ((e = launch_ulysses_a2a(oh, (char*)out + n * node_q, B, C, Hq, row, P_u, 1, cs, S,
                                 n * C)) != hipSuccess)
       return hip_fail(e, "all-to-all launch");
+  return RA_OK;
+}
+
+ra_status ra_device_info(int32_t* compute_units, int32_t* max_clock_khz) {
+  g_err[0] = 0;
+  if (!compute_units || !max_clock_khz) return fail(RA_ERR_NULL, "NULL output pointer");
+  int dev = 0, cus = 0, khz = 0;
+  RA_HIP(hipGetDevice(&dev));
+  RA_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+  RA_HIP(hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, dev));
+  *compute_units = cus;
+  *max_clock_khz = khz;
+  return RA_OK;
+}
+
+ra_status ra_mfma_probe_bf16(int32_t iters, int64_t* out, int64_t out_len, int32_t* waves,
+                             void* stream) {
+  g_err[0] = 0;
+  if (!out || !waves) return fail(RA_ERR_NULL, "NULL pointer");
+  if (iters < 1 || iters > (1 << 24)) return fail(RA_ERR_ARG, "iters must be in [1, 2^24]");
+  if (!aligned(out, 8)) return fail(RA_ERR_ALIGN, "out must be 8-byte aligned");
+  int dev = 0, cus = 0;
+  RA_HIP(hipGetDevice(&dev));
+  RA_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+  const int64_t n = (int64_t)cus * (kProbeThreads / 64);
+  if (out_len < 3 * n)
+    return fail(RA_ERR_WORKSPACE, "out needs %lld entries (got %lld)", (long long)(3 * n),
+                (long long)out_len);
+  hipError_t e = launch_mfma_probe(cus, iters, out, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  *waves = (int32_t)n;
   return RA_OK;
 }
 

@@ -90,6 +90,33 @@ __global__ __launch_bounds__(256) void lse_merge_vec4(float* __restrict__ out,
   }
 }
 
+// One pass: the D/4 threads of a row sit in one wave, read both lse values,
+// update the row's float4 groups, and the row's first thread writes the new
+// lse. The store is issued after the wave's loads of that lse have returned
+// (it depends on them), and no other wave touches the row. dq must divide 64.
+__global__ __launch_bounds__(256) void lse_merge_rows(float* __restrict__ out,
+                                                      float* __restrict__ lse,
+                                                      const float* __restrict__ out_b,
+                                                      const float* __restrict__ lse_b,
+                                                      int64_t rows, int dq) {
+  const int64_t total = rows * dq;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / dq;
+    float ln, ca, cb;
+    merge_weights(lse[r], lse_b[r], ln, ca, cb);
+    const float4 a = reinterpret_cast<const float4*>(out)[i];
+    const float4 b = reinterpret_cast<const float4*>(out_b)[i];
+    float4 o;
+    o.x = fmaf(a.x, ca, b.x * cb);
+    o.y = fmaf(a.y, ca, b.y * cb);
+    o.z = fmaf(a.z, ca, b.z * cb);
+    o.w = fmaf(a.w, ca, b.w * cb);
+    reinterpret_cast<float4*>(out)[i] = o;
+    if (i - r * dq == 0) lse[r] = ln;
+  }
+}
+
 __global__ __launch_bounds__(256) void lse_merge_scalar(float* __restrict__ out,
                                                         const float* __restrict__ lse,
                                                         const float* __restrict__ out_b,
@@ -134,13 +161,42 @@ __global__ __launch_bounds__(256) void zigzag_permute_kernel(const char* __restr
     const int64_t to = o * twoN + (inverse ? sc : pc);
     const V* s = reinterpret_cast<const V*>(src) + from * chunk_vecs;
     V* d = reinterpret_cast<V*>(dst) + to * chunk_vecs;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < chunk_vecs;
-         e += (int64_t)gridDim.x * blockDim.x)
-      d[e] = s[e];
+    // four loads in flight per thread before the stores
+    const int64_t T = (int64_t)gridDim.x * blockDim.x;
+    int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; e + 3 * T < chunk_vecs; e += 4 * T) {
+      const V v0 = s[e], v1 = s[e + T], v2 = s[e + 2 * T], v3 = s[e + 3 * T];
+      d[e] = v0;
+      d[e + T] = v1;
+      d[e + 2 * T] = v2;
+      d[e + 3 * T] = v3;
+    }
+    for (; e < chunk_vecs; e += T) d[e] = s[e];
   }
 }
 
+// ---------------------------------------------------------------------------
+// Zero fill of a 16-byte-aligned range whose size is a multiple of 16 bytes:
+// a plain kernel (not hipMemsetAsync) so the clear is an ordinary kernel node
+// when the caller captures the stream into a graph.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* __restrict__ p, int64_t n16) {
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = z;
+}
+
 }  // namespace
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const int64_t blocks = (n16 + 255) / 256;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256),
+                     0, s, reinterpret_cast<uint4*>(p), n16);
+  return hipGetLastError();
+}
 
 hipError_t launch_vt_transpose(const void* v, void* vt, int64_t BH, int64_t nblk, int64_t C,
                                int64_t Cpad, int D, int64_t v_bh, hipStream_t s) {
@@ -161,6 +217,12 @@ hipError_t launch_lse_merge(float* out, float* lse, const float* out_b, const fl
                             int64_t rows, int D, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const bool vec = (D % 4 == 0) && ((uintptr_t)out % 16 == 0) && ((uintptr_t)out_b % 16 == 0);
+  if (vec && D / 4 <= 64 && (64 % (D / 4)) == 0) {
+    const int64_t blocks = (rows * (D / 4) + 255) / 256;
+    hipLaunchKernelGGL(lse_merge_rows, dim3((unsigned)(blocks < 65536 ? blocks : 65536)),
+                       dim3(256), 0, s, out, lse, out_b, lse_b, rows, D / 4);
+    return hipGetLastError();
+  }
   const int64_t work = vec ? rows * (D / 4) : rows * D;
   const int64_t blocks = (work + 255) / 256;
   const unsigned grid = (unsigned)(blocks < 65536 ? blocks : 65536);
@@ -353,7 +415,7 @@ hipError_t launch_zigzag_permute(const void* src, void* dst, int64_t outer, int6
   while (vb > 1 && (al % vb)) vb >>= 1;
   const int64_t chunk_vecs = chunk_bytes / vb;
   const int64_t nchunks = outer * twoN;
-  const int64_t gx = (chunk_vecs + 255) / 256;
+  const int64_t gx = (chunk_vecs + 1023) / 1024;  // four vectors per thread
   const dim3 grid((unsigned)(gx < 1024 ? gx : 1024), (unsigned)(nchunks < 65535 ? nchunks : 65535));
   const char* sp = reinterpret_cast<const char*>(src);
   char* dp = reinterpret_cast<char*>(dst);

@@ -32,6 +32,10 @@ hipError_t launch_f32_to_bf16(const float* src, void* dst, int64_t n, hipStream_
 hipError_t launch_vt_transpose(const void* v, void* vt, int64_t BH, int64_t nblk, int64_t C,
                                int64_t Cpad, int D, int64_t v_bh, hipStream_t s);
 
+// Zero `bytes` bytes at p (16-byte aligned, bytes a multiple of 16) with a
+// kernel, so a captured stream records a kernel node rather than a memset.
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
+
 hipError_t launch_lse_merge(float* out, float* lse, const float* out_b, const float* lse_b,
                             int64_t rows, int D, hipStream_t s);
 
@@ -46,5 +50,12 @@ hipError_t launch_striped_permute(const void* src, void* dst, int64_t outer, int
 hipError_t launch_ulysses_a2a(const void* src, void* dst, int32_t B, int64_t S, int32_t H,
                               int64_t row_bytes, int32_t P, int inverse, hipStream_t s,
                               int64_t hs_stride = 0, int64_t hs_off = 0);
+
+// Matrix-core probe: one workgroup of kProbeThreads per compute unit (the
+// dynamic LDS request leaves room for one); writes 3 int64 per wave (shader
+// cycles, 100 MHz reference ticks, a liveness word) to out.
+constexpr int kProbeThreads = 512;
+constexpr size_t kProbeLdsBytes = 96 * 1024;
+hipError_t launch_mfma_probe(int32_t workgroups, int32_t iters, int64_t* out, hipStream_t s);
 
 }  // namespace ra

@@ -344,38 +344,51 @@ def test_ring_config_all_rows(idx):
     _ring_check(workloads.WORKLOADS[idx])
 
 
-def test_ring_config_causal_zigzag_32k_sampled():
+def _rows_or_all(w, default_random, fixed=None):
+    """Rows checked per head: every row when ``RA_ORACLE_ROWS`` (default
+    ``default_random``; "all" or a number >= S) covers the sequence, else that
+    many seeded rows per head plus every chunk's first and last row."""
+    n = os.environ.get("RA_ORACLE_ROWS", str(default_random))
+    n = w.S if n == "all" else int(n)
+    if n >= w.S:
+        rows = np.tile(np.arange(w.S), (w.Hq, 1))
+    else:
+        rows = check_rows(w.S, w.Hq, n, w.seed, 2 * w.N, fixed=fixed)
+    print(f"  {w.name}: {rows.shape[1]} oracle rows per head x {w.Hq} heads "
+          f"(S={w.S})", flush=True)
+    return rows
+
+
+def test_ring_config_causal_zigzag_32k_all_rows():
+    """The 32k MHA zigzag ring on every row of every head."""
     w = workloads.WORKLOADS[2]
-    n = int(os.environ.get("RA_ORACLE_ROWS", "256"))
-    rows = check_rows(w.S, w.Hq, n, w.seed, 2 * w.N) if n < w.S else np.tile(np.arange(w.S), (w.Hq, 1))
-    _ring_check(w, rows=rows)
+    _ring_check(w, rows=_rows_or_all(w, "all"))
 
 
 def test_ring_headline_gqa_128k_sampled():
+    """The 128k GQA zigzag ring: 4096 seeded rows per head plus every chunk's
+    first and last row (so row S-1, which sees every key, on every head)."""
     w = workloads.HEADLINE
-    n = int(os.environ.get("RA_ORACLE_ROWS", "32"))
-    _ring_check(w, rows=check_rows(w.S, w.Hq, n, w.seed, 2 * w.N))
+    rows = _rows_or_all(w, 4096)
+    assert np.all(rows[:, -1] == w.S - 1) and np.all(rows[:, 0] == 0)
+    _ring_check(w, rows=rows)
 
 
 def test_ring_striped_gqa_128k_sampled():
     """Seeded rows plus each striped rank's first and last rows (positions
     0..N-1 and S-N..S-1) and the 2N chunk boundaries, the same count per head."""
-    from parity_util import boundary_rows
     w = workloads.STRIPED_128K
-    n = int(os.environ.get("RA_ORACLE_ROWS", "32"))
-    fixed = np.union1d(boundary_rows(w.S, 2 * w.N),
-                       np.concatenate([np.arange(w.N), w.S - w.N + np.arange(w.N)]))
-    rest = np.setdiff1d(np.arange(w.S), fixed)
-    rows = np.stack([np.sort(np.concatenate(
-        [fixed, np.random.default_rng([w.seed, h]).choice(rest, n, replace=False)]))
-        for h in range(w.Hq)])
-    _ring_check(w, rows=rows)
+    fixed = np.concatenate([np.arange(w.N), w.S - w.N + np.arange(w.N)])
+    _ring_check(w, rows=_rows_or_all(w, 256, fixed=fixed))
 
 
 def test_ring_million_token_mqa_sampled():
+    """The 1M-token MQA zigzag ring: 4096 seeded rows per head plus every
+    chunk's first and last row."""
     w = workloads.WORKLOADS[4]
-    n = int(os.environ.get("RA_ORACLE_ROWS", "16"))
-    _ring_check(w, rows=check_rows(w.S, w.Hq, n, w.seed, 2 * w.N))
+    rows = _rows_or_all(w, 4096)
+    assert np.all(rows[:, -1] == w.S - 1)
+    _ring_check(w, rows=rows)
 
 
 def test_ring_zigzag_equals_contiguous_and_no_copy_stream():
@@ -433,6 +446,92 @@ def test_ring_deterministic_under_copy_delay():
     r.unpermute_outputs(out2, lse2)
     torch.cuda.synchronize()
     assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_ring_copy_ahead_of_compute_waits_for_freed_slot():
+    """The write-after-read side of the double buffer. With 64 query heads on
+    one KV head, a block copy moves 1 MiB while the attention step that reads
+    the other slot does ~7e10 flops, so the copy stream is always ahead of the
+    compute stream; the compute stream is also held back by a sleep before
+    the ring. A copy into a slot may start only after the step that last read
+    it has finished (its "freed" event); if it did not wait, later blocks
+    would overwrite slots still being read. The result must be bit-identical
+    to the same ring on a single stream, where no overlap exists."""
+    w = workloads.Workload("war", B=1, Hq=64, Hkv=1, D=128, S=16384, dtype="bf16", seed=52,
+                           causal=True, N=8, layout="zigzag")
+    q, k, v = (t.to(DEV) for t in workloads.make_inputs(w))
+    one = ra.RingRunner(1, 64, 1, w.S, 128, torch.bfloat16, w.N, "zigzag", True, device=DEV,
+                        copy_stream=False)
+    two = ra.RingRunner(1, 64, 1, w.S, 128, torch.bfloat16, w.N, "zigzag", True, device=DEV)
+    out1, lse1 = torch.empty_like(q), torch.empty(1, 64, w.S, device=DEV)
+    one(q, k, v, out1, lse1)
+    torch.cuda.synchronize()
+    qr, kr, vr = two.permute_inputs(q, k, v)
+    for _ in range(2):
+        torch.cuda._sleep(50_000_000)          # the compute (current) stream waits
+        two.ring(qr, kr, vr)
+        out2, lse2 = torch.empty_like(out1), torch.empty_like(lse1)
+        two.unpermute_outputs(out2, lse2)
+        torch.cuda.synchronize()
+        assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+RACE_RINGS = [
+    workloads.Workload("race_a_zigzag", B=1, Hq=8, Hkv=2, D=128, S=8192, dtype="bf16", seed=61,
+                       causal=True, N=8, layout="zigzag"),
+    workloads.Workload("race_b_contig", B=1, Hq=4, Hkv=4, D=64, S=4096, dtype="bf16", seed=62,
+                       causal=True, N=4, layout="contiguous"),
+]
+
+
+def test_ring_concurrent_host_threads_bitexact():
+    """Two host threads enqueue rings at the same time, each on its own compute
+    and copy streams with its own workspace (the binding's library calls
+    release the interpreter lock, so the two enqueue loops interleave in the
+    library). Every call creates its own ring events, so a wait cannot bind
+    to the other thread's record: each result is bit-identical to the same
+    ring run alone."""
+    import threading
+    runners, inputs, ref = [], [], []
+    for w in RACE_RINGS:
+        r = ra.RingRunner(w.B, w.Hq, w.Hkv, w.S, w.D, torch.bfloat16, w.N, w.layout, w.causal,
+                          device=DEV)
+        q, k, v = (t.to(DEV) for t in workloads.make_inputs(w))
+        out, lse = torch.empty_like(q), torch.empty(w.B, w.Hq, w.S, device=DEV)
+        r(q, k, v, out, lse)
+        torch.cuda.synchronize()
+        runners.append(r)
+        inputs.append((q, k, v))
+        ref.append((out, lse))
+    results = [[], []]
+    errors = []
+    start = threading.Barrier(2)
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream(device=DEV)
+            with torch.cuda.stream(s):
+                outs = [(torch.empty_like(ref[i][0]), torch.empty_like(ref[i][1]))
+                        for _ in range(4)]
+                start.wait()
+                for out, lse in outs:
+                    runners[i](*inputs[i], out, lse)
+            s.synchronize()
+            results[i] = outs
+        except Exception as e:  # reported in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a ring thread did not finish"
+    assert not errors, errors
+    for i in range(2):
+        assert len(results[i]) == 4
+        for out, lse in results[i]:
+            assert torch.equal(out, ref[i][0]) and torch.equal(lse, ref[i][1]), RACE_RINGS[i].name
 
 
 def test_ring_repeat_bitexact_noncausal_8k():
