@@ -28,7 +28,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "ring-attn fwd useful TFLOP/s & % bf16 MFMA peak, S=131072 GQA causal zigzag"
 # MI355X published figures: 256 CUs x 2.4 GHz x 4096 dense bf16 flops/CU/clk, HBM3E 8 TB/s.
-PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+# The bench re-reads the CU count and clock on the device (peak_derivation) and
+# confirms the flops/CU/clk with the matrix-core probe.
+BF16_FLOPS_PER_CU_CLK = 4096
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * BF16_FLOPS_PER_CU_CLK / 1e12
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
@@ -89,48 +92,145 @@ def useful_flops(w) -> float:
     return 4.0 * w.D * w.B * w.Hq * useful_pairs(w.S, w.causal)
 
 
-def cpu_baseline(w, q, k, v, out_gpu, lse_gpu, budget_s: float, rows_per_head: int):
-    """Time the unmodified fp64 oracle on seeded random rows, head by head, until
-    the time budget is spent; also compare those rows with the GPU result."""
+def baseline_rows(w, rows_per_head: int):
+    """[Hq, R] sorted rows per head: the first and last row of every chunk of
+    the 2N-chunk split, and ``rows_per_head`` rows drawn per head from the
+    rest with numpy.random.default_rng([seed, head])."""
     import numpy as np
-    import oracle
-    from workloads import sample_rows
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    useful = 0.0
-    heads = 0
-    err_out = 0.0
-    err_lse = 0.0
+    c = w.S // (2 * w.N)
+    fixed = np.unique(np.concatenate([np.arange(2 * w.N) * c, np.arange(1, 2 * w.N + 1) * c - 1]))
+    rest = np.setdiff1d(np.arange(w.S), fixed)
+    n = min(rows_per_head, len(rest))
+    return np.stack([np.sort(np.concatenate(
+        [fixed, np.random.default_rng([w.seed, h]).choice(rest, n, replace=False)]))
+        for h in range(w.Hq)])
+
+
+def cpu_baseline(w, q, k, v, out_gpu, lse_gpu, rows_per_head: int):
+    """Time the unmodified fp64 oracle on seeded rows of every head, run over
+    a process pool of the host's cores (oracle.pool: groups of sorted rows,
+    each against the keys its last row can see), and compare those rows with
+    the GPU result."""
+    import numpy as np
+    from oracle import pool
+    rows = baseline_rows(w, rows_per_head)
+    n_workers = pool.workers()
     t0 = time.perf_counter()
-    group = w.Hq // w.Hkv
-    for h in range(w.Hq):
-        rows = sample_rows(w.S, rows_per_head, w.seed + 1000, h)
-        g = h // group
-        o, l_ = oracle.attention(q[:, h:h + 1, rows], k[:, g:g + 1], v[:, g:g + 1],
-                                 causal=w.causal, q_pos=rows)
-        heads += 1
-        useful += 4.0 * w.D * float(np.sum(rows + 1) if w.causal else len(rows) * w.S)
-        go = out_gpu[0, h, rows].double().numpy()
-        gl = lse_gpu[0, h, rows].double().numpy()
-        err_out = max(err_out, float(np.abs(go - o[0, 0]).max()))
-        err_lse = max(err_lse, float(np.abs(gl - l_[0, 0]).max()))
-        if time.perf_counter() - t0 >= budget_s:
-            break
+    ref_out, ref_lse = pool.pooled_attention(q, k, v, causal=w.causal, rows=rows,
+                                             n_workers=n_workers)
     dt = time.perf_counter() - t0
+    pairs = float(np.sum(rows + 1)) if w.causal else float(rows.size) * w.S
+    useful = 4.0 * w.D * w.B * pairs
+    idx = [np.asarray(r) for r in rows]
+    go = np.stack([out_gpu[0, h, idx[h]].double().numpy() for h in range(w.Hq)])
+    gl = np.stack([lse_gpu[0, h, idx[h]].double().numpy() for h in range(w.Hq)])
+    err = np.abs(go - ref_out)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
     return {
         "value": useful / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": threads,
+        "cores": n_workers,
         "kind": "oracle",
-        "sample": (f"{rows_per_head} seeded random query rows x {heads} of {w.Hq} heads of "
-                   f"{w.name}, numpy fp64 (BLAS threads={threads}); "
-                   f"{useful / 1e12:.3f} useful TFLOP in {dt:.1f} s"),
-        "parity_vs_gpu": {"rows": rows_per_head * heads, "out_max_abs": err_out,
-                          "lse_max_abs": err_lse},
+        "sample": (f"{rows.shape[1]} rows per head ({rows_per_head} seeded random + every "
+                   f"chunk's first and last row) x {w.Hq} heads of {w.name}, numpy fp64, "
+                   f"{n_workers} single-threaded worker processes ({affinity} CPUs in the "
+                   f"affinity mask); {useful / 1e12:.3f} useful TFLOP in {dt:.1f} s"),
+        "parity_vs_gpu": {"rows": int(rows.size), "out_max_abs": float(err.max()),
+                          "out_mean_abs": float(err.mean()),
+                          "lse_max_abs": float(np.abs(gl - ref_lse).max())},
     }
+
+
+def peak_derivation(dev):
+    """The bf16 dense peak from the device's own figures: compute units x
+    maximum shader clock x flops per CU per clock, the last confirmed by the
+    library's matrix-core probe (register-fed MFMAs, two waves per SIMD)."""
+    import ring_context_parallelism_flash_amd as ra
+    cus, khz = ra.ra_device_info()
+    probe = ra.ra_mfma_probe_bf16(iters=100000, device=dev)
+    derived = cus * khz * 1e3 * BF16_FLOPS_PER_CU_CLK / 1e12
+    return {
+        "compute_units": cus,
+        "max_clock_mhz": khz / 1e3,
+        "flops_per_cu_clk": BF16_FLOPS_PER_CU_CLK,
+        "derived_tflops": round(derived, 1),
+        "published_tflops": round(PEAK_BF16_TFLOPS, 1),
+        "probe": {"flops_per_cu_clk": round(probe["flops_per_cu_clk"], 1),
+                  "clock_mhz": round(probe["clock_mhz"], 1),
+                  "chip_tflops": round(probe["chip_tflops"], 1),
+                  "mfma_per_wave": 4 * probe["iters"]},
+    }
+
+
+def copy_overlap(kernel_trace_csv: str) -> dict:
+    """From a rocprofv3 kernel trace (csv): the ring's block copies (the
+    runtime's copyBuffer kernels) and how much of their time passes while an
+    attention kernel runs."""
+    import csv
+    att, cp = [], []
+    with open(kernel_trace_csv) as f:
+        for r in csv.DictReader(f):
+            iv = (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+            name = r["Kernel_Name"]
+            if "attn_fwd" in name or "attn_bwd" in name:
+                att.append(iv)
+            elif "copyBuffer" in name:
+                cp.append(iv)
+    att.sort()
+    merged = []
+    for a, b in att:
+        if merged and a <= merged[-1][1]:
+            merged[-1][1] = max(merged[-1][1], b)
+        else:
+            merged.append([a, b])
+    import bisect
+    starts = [m[0] for m in merged]
+    total = covered = 0
+    for a, b in cp:
+        total += b - a
+        i = max(0, bisect.bisect_right(starts, a) - 1)
+        while i < len(merged) and merged[i][0] < b:
+            covered += max(0, min(b, merged[i][1]) - max(a, merged[i][0]))
+            i += 1
+    return {"copies": len(cp), "copy_ms": total / 1e6, "copy_ms_under_attention": covered / 1e6,
+            "overlap_frac": covered / total if total else None,
+            "attention_launches": len(att)}
+
+
+def aux_bandwidth(w, q, dev):
+    """HBM rates of the layout permute (one q-sized permute, read + write) and
+    of the lse merge (one rank's fp32 running state), timed with events."""
+    import torch
+    import ring_context_parallelism_flash_amd as ra
+    permute = ra.ra_striped_permute if w.layout == "striped" else ra.ra_zigzag_permute
+    dst = torch.empty_like(q)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    permute(q, dst, w.N)
+    e0.record()
+    for _ in range(5):
+        permute(q, dst, w.N)
+    e1.record()
+    torch.cuda.synchronize()
+    perm_gbs = 2 * q.numel() * q.element_size() * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del dst
+    rows = w.B * w.Hq * (w.S // w.N)
+    mo = torch.randn(rows, w.D, device=dev)
+    ml = torch.randn(rows, device=dev)
+    mob, mlb = torch.randn_like(mo), torch.randn_like(ml)
+    ra.ra_lse_merge(mo, ml, mob, mlb)
+    e0.record()
+    for _ in range(5):
+        ra.ra_lse_merge(mo, ml, mob, mlb)
+    e1.record()
+    torch.cuda.synchronize()
+    merge_gbs = (3 * rows * w.D + 3 * rows) * 4 * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    return {f"{'striped' if w.layout == 'striped' else 'zigzag'}_permute_GBs": round(perm_gbs, 1),
+            "lse_merge_GBs": round(merge_gbs, 1), "hbm_peak_GBs": PEAK_HBM_GBS,
+            "permute_bytes": 2 * q.numel() * q.element_size(),
+            "lse_merge_bytes": (3 * rows * w.D + 3 * rows) * 4}
 
 
 def bench_backward(args, w, q, k, v, runner, out, lse) -> int:
@@ -318,8 +418,7 @@ def bench_ulysses(args, w, q_cpu, k_cpu, v_cpu, dev) -> int:
         print("bench: cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         o = out.cpu().permute(1, 0, 2, 3, 4).reshape(w.B, w.S, w.Hq, w.D).permute(0, 2, 1, 3)
         l_ = lse.cpu().permute(1, 0, 2, 3).reshape(w.B, w.Hq, w.S)
-        line["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, o, l_, args.cpu_seconds,
-                                            args.cpu_rows)
+        line["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, o, l_, args.cpu_rows)
     print(json.dumps(line), flush=True)
     return 0
 
@@ -424,8 +523,7 @@ def bench_usp(args, w, q_cpu, k_cpu, v_cpu, dev) -> int:
         o = out.cpu().permute(1, 0, 2, 3, 4).reshape(w.B, w.S, w.Hq, w.D)[:, inv]
         o = o.permute(0, 2, 1, 3)
         l_ = lse.cpu().permute(1, 0, 2, 3).reshape(w.B, w.Hq, w.S)[:, :, inv]
-        line["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, o, l_, args.cpu_seconds,
-                                            args.cpu_rows)
+        line["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, o, l_, args.cpu_rows)
     print(json.dumps(line), flush=True)
     return 0
 
@@ -436,15 +534,23 @@ def main(argv=None) -> int:
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default=None, help="workload name (default: the 128k GQA one)")
-    p.add_argument("--cpu-seconds", type=float, default=25.0)
-    p.add_argument("--cpu-rows", type=int, default=64)
+    p.add_argument("--cpu-rows", type=int, default=4096,
+                   help="seeded random rows per head for the CPU oracle (plus chunk boundaries)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--backward", action="store_true",
                    help="time the ring backward (dq, dk, dv of a seeded dout) instead of the forward")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="finish with one plain device copy of this many MiB (a known-size "
                         "reference for hardware byte counters)")
+    p.add_argument("--aux-only", action="store_true",
+                   help="only the permute and lse-merge kernels (for hardware-counter runs)")
+    p.add_argument("--trace-overlap", metavar="KERNEL_TRACE_CSV", default=None,
+                   help="print the block copies' overlap with attention kernels in a "
+                        "rocprofv3 kernel trace and exit (no GPU use)")
     args = p.parse_args(argv)
+    if args.trace_overlap:
+        print(json.dumps(copy_overlap(args.trace_overlap)), flush=True)
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: measures one GPU only -- the N ranks of the ring (and the devices "
               "of the Ulysses / USP grids) are simulated on a single MI355X; run with --gpus 1.",
@@ -471,6 +577,11 @@ def main(argv=None) -> int:
             return 2
         return bench_usp(args, w, q_cpu, k_cpu, v_cpu, dev)
     q, k, v = (t.to(dev) for t in (q_cpu, k_cpu, v_cpu))
+    if args.aux_only:
+        print(json.dumps({"workload": w.name, "aux_kernels": aux_bandwidth(w, q, dev)}),
+              flush=True)
+        calibration_copy(args, dev)
+        return 0
     runner = ra.RingRunner(w.B, w.Hq, w.Hkv, w.S, w.D, q.dtype, w.N, w.layout, w.causal,
                            device=dev)
     out = torch.empty_like(q)
@@ -509,28 +620,8 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     ring_ms = (time.perf_counter() - r0) * 1e3 / args.steps
 
-    # permute bandwidth: one q-sized permute of the workload's layout, timed with events
-    permute = ra.ra_striped_permute if w.layout == "striped" else ra.ra_zigzag_permute
-    dst = torch.empty_like(q)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
-        permute(q, dst, w.N)
-    e1.record()
-    torch.cuda.synchronize()
-    perm_gbs = 2 * q.numel() * q.element_size() * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
-    # lse-merge bandwidth on one rank's fp32 running state
-    rows = w.B * w.Hq * (w.S // w.N)
-    mo = torch.randn(rows, w.D, device=dev)
-    ml = torch.randn(rows, device=dev)
-    mob, mlb = torch.randn_like(mo), torch.randn_like(ml)
-    e0.record()
-    for _ in range(5):
-        ra.ra_lse_merge(mo, ml, mob, mlb)
-    e1.record()
-    torch.cuda.synchronize()
-    merge_gbs = (3 * rows * w.D + 4 * rows) * 4 * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
-    del dst, mo, ml, mob, mlb
+    aux = aux_bandwidth(w, q, dev)
+    peak_info = peak_derivation(dev) if w.dtype == "bf16" else None
 
     achieved = k_flops / (k_ms / 1e3) / 1e12 if k_ms > 0 else 0.0
     traffic, traffic_src = measured_traffic(w.name)
@@ -569,15 +660,15 @@ def main(argv=None) -> int:
             "kernel_ms_per_step": round(k_ms / max(args.steps, 1), 3),
         },
         "ring_only_ms": round(ring_ms, 3),
-        "aux_kernels": {f"{'striped' if w.layout == 'striped' else 'zigzag'}_permute_GBs":
-                        round(perm_gbs, 1),
-                        "lse_merge_GBs": round(merge_gbs, 1), "hbm_peak_GBs": PEAK_HBM_GBS},
+        "aux_kernels": aux,
         "flops_check": {"closed_form": flops_step, "library_count": lib_flops_step},
     }
+    if peak_info is not None:
+        line["peak_derivation"] = peak_info
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, out.cpu(), lse.cpu(),
-                                            args.cpu_seconds, args.cpu_rows)
+                                            args.cpu_rows)
     print(json.dumps(line), flush=True)
     calibration_copy(args, dev)
     return 0

@@ -407,14 +407,17 @@ ra_status ra_kernel_timing_read(double* total_ms, int64_t* launches, double* use
  * shader clock in kHz (hipDeviceGetAttribute), the two factors of the dense
  * bf16 matrix peak CU x clock x flops/CU/clk. Host-only; enqueues nothing.
  *
- * ra_mfma_probe_bf16: launches one workgroup of 8 waves on every compute unit
- * (two waves per SIMD); each wave issues 4*iters register-fed
- * v_mfma_f32_32x32x16_bf16 (32768 flops each) and writes three int64 to
- * `out` (device memory, caller-owned, 8-byte aligned, out_len >= 3 * waves):
- * its elapsed shader-clock cycles, its elapsed ticks of the constant 100 MHz
- * reference clock, and a liveness word. *waves (host) receives the wave count
- * (8 x compute units). flops/CU/clk = 8 * 4 * iters * 32768 / cycles; the
- * clock during the probe is cycles / (ticks / 100 MHz). iters in [1, 2^24].
+ * ra_mfma_probe_bf16: launches as many workgroups of 8 waves as there are
+ * compute units, one resident per compute unit (two waves per SIMD); each
+ * wave issues 4*iters register-fed v_mfma_f32_32x32x16_bf16 (32768 flops
+ * each) and writes five int64 to out[5*w ...] (device memory, caller-owned,
+ * 8-byte aligned, out_len >= 5 * waves; wave w belongs to workgroup w / 8):
+ * the shader-clock counter (s_memtime) at its start and end, the constant
+ * 100 MHz reference counter (s_memrealtime) at its start and end, and a
+ * liveness word. *waves (host) receives the wave count (8 x compute units).
+ * Over a workgroup's span (earliest start to latest end of its waves),
+ * flops/CU/clk = 8 * 4 * iters * 32768 / cycles and the shader clock is
+ * cycles / (ticks / 100 MHz). iters in [1, 2^24].
  * Errors: RA_ERR_NULL, RA_ERR_ARG, RA_ERR_ALIGN, RA_ERR_WORKSPACE (out too
  * short), RA_ERR_HIP. Asynchronous on `stream`.
  * ---------------------------------------------------------------------- */

@@ -400,15 +400,17 @@ def ra_device_info():
     return cus.value, khz.value
 
 
-def ra_mfma_probe_bf16(iters=20000, device=None):
+def ra_mfma_probe_bf16(iters=100000, device=None):
     """Run the matrix-core probe once (after a short warm-up launch) and
-    return its figures: dense bf16 flops per compute unit per clock, the
-    shader clock during the probe (from the 100 MHz reference ticks) and the
-    chip rate it sustained."""
+    return its figures: dense bf16 flops per compute unit per clock and the
+    shader clock (median over workgroups, each over its own span from the
+    earliest start to the latest end of its 8 waves), and the chip rate over
+    the whole launch (HIP events)."""
     dev = torch.device(device) if device is not None else torch.device("cuda",
                                                                        torch.cuda.current_device())
     cus, _ = ra_device_info()
-    buf = torch.zeros(3 * 8 * cus, dtype=torch.int64, device=dev)
+    words = 5
+    buf = torch.zeros(words * 8 * cus, dtype=torch.int64, device=dev)
     waves = ctypes.c_int32()
     stream = _stream(None)
     _check(lib().ra_mfma_probe_bf16(max(1, iters // 10), _ptr(buf), buf.numel(),
@@ -418,13 +420,15 @@ def ra_mfma_probe_bf16(iters=20000, device=None):
     _check(lib().ra_mfma_probe_bf16(iters, _ptr(buf), buf.numel(), ctypes.byref(waves), stream))
     e1.record()
     torch.cuda.synchronize()
-    rec = buf.view(-1, 3)[:waves.value].double()
-    cycles, ticks = rec[:, 0].mean().item(), rec[:, 1].mean().item()
-    flops = 8 * 4 * iters * 32768.0
+    rec = buf.view(-1, 8, words)[:waves.value // 8].cpu()
+    cycles = (rec[:, :, 1].max(dim=1).values - rec[:, :, 0].min(dim=1).values).double()
+    ticks = (rec[:, :, 3].max(dim=1).values - rec[:, :, 2].min(dim=1).values).double()
+    flops_wg = 8 * 4 * iters * 32768.0
     ms = e0.elapsed_time(e1)
-    return {"flops_per_cu_clk": flops / cycles, "clock_mhz": cycles / (ticks / 100.0),
-            "chip_tflops": flops * cus / (ms * 1e-3) / 1e12, "waves": waves.value,
-            "iters": iters}
+    return {"flops_per_cu_clk": (flops_wg / cycles).median().item(),
+            "clock_mhz": (cycles / (ticks / 100.0)).median().item(),
+            "chip_tflops": flops_wg * (waves.value // 8) / (ms * 1e-3) / 1e12,
+            "waves": waves.value, "iters": iters}
 
 
 def ra_kernel_timing_enable(enable=True):

@@ -1084,9 +1084,9 @@ ra_status ra_mfma_probe_bf16(int32_t iters, int64_t* out, int64_t out_len, int32
   RA_HIP(hipGetDevice(&dev));
   RA_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
   const int64_t n = (int64_t)cus * (kProbeThreads / 64);
-  if (out_len < 3 * n)
-    return fail(RA_ERR_WORKSPACE, "out needs %lld entries (got %lld)", (long long)(3 * n),
-                (long long)out_len);
+  if (out_len < kProbeWords * n)
+    return fail(RA_ERR_WORKSPACE, "out needs %lld entries (got %lld)",
+                (long long)(kProbeWords * n), (long long)out_len);
   hipError_t e = launch_mfma_probe(cus, iters, out, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "probe launch");
   *waves = (int32_t)n;

@@ -2,10 +2,12 @@
 // per compute unit per clock that the attention kernels' roofline is priced
 // against. Every wave issues register-fed v_mfma_f32_32x32x16_bf16 on four
 // independent accumulators (no operand loads, no dependency stalls) and
-// records its own elapsed shader-clock cycles (s_memtime) and constant
-// 100 MHz reference ticks (s_memrealtime). One workgroup of 8 waves runs on
-// every compute unit (the dynamic LDS request leaves room for one), so each
-// SIMD holds two waves and its matrix pipe never waits for an issue slot.
+// records the shader-clock counter (s_memtime) and the constant 100 MHz
+// reference counter (s_memrealtime) at its start and end. One workgroup of 8
+// waves runs on a compute unit at a time (the dynamic LDS request leaves room
+// for one), so each SIMD holds two waves and its matrix pipe never waits for
+// an issue slot; the host takes a workgroup's span from its earliest start
+// to its latest end, so waves that start late do not inflate the rate.
 #include <hip/hip_runtime.h>
 
 #include "ra_internal.h"
@@ -33,6 +35,10 @@ __global__ __launch_bounds__(kProbeThreads, 1) void mfma_bf16_probe(int32_t iter
     for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
   const int64_t c0 = __builtin_amdgcn_s_memtime();
   const int64_t r0 = __builtin_amdgcn_s_memrealtime();
+  if (lane == 0) {
+    out[kProbeWords * wave + 0] = c0;
+    out[kProbeWords * wave + 2] = r0;
+  }
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
@@ -45,10 +51,10 @@ __global__ __launch_bounds__(kProbeThreads, 1) void mfma_bf16_probe(int32_t iter
   const int64_t c1 = __builtin_amdgcn_s_memtime();
   const int64_t r1 = __builtin_amdgcn_s_memrealtime();
   if (lane == 0) {
-    out[3 * wave + 0] = c1 - c0;
-    out[3 * wave + 1] = r1 - r0;
+    out[kProbeWords * wave + 1] = c1;
+    out[kProbeWords * wave + 3] = r1;
   }
-  if (lane == 1) out[3 * wave + 2] = (int64_t)(sum != sum);  // keeps the products live
+  if (lane == 1) out[kProbeWords * wave + 4] = (int64_t)(sum != sum);  // keeps the products live
 }
 
 }  // namespace

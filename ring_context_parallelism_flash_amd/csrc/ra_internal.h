@@ -52,9 +52,11 @@ hipError_t launch_ulysses_a2a(const void* src, void* dst, int32_t B, int64_t S, 
                               int64_t hs_stride = 0, int64_t hs_off = 0);
 
 // Matrix-core probe: one workgroup of kProbeThreads per compute unit (the
-// dynamic LDS request leaves room for one); writes 3 int64 per wave (shader
-// cycles, 100 MHz reference ticks, a liveness word) to out.
+// dynamic LDS request leaves room for one); writes kProbeWords int64 per wave
+// (shader-clock counter at start and end, 100 MHz reference counter at start
+// and end, a liveness word) to out.
 constexpr int kProbeThreads = 512;
+constexpr int kProbeWords = 5;
 constexpr size_t kProbeLdsBytes = 96 * 1024;
 hipError_t launch_mfma_probe(int32_t workgroups, int32_t iters, int64_t* out, hipStream_t s);
 
