@@ -138,6 +138,29 @@ ra_status ra_block_attn_fwd(const void* q, const void* k, const void* v,
                             void* stream);
 
 /* ------------------------------------------------------------------------
+ * ra_block_attn_fwd_noalloc -- ra_block_attn_fwd for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *
+ * Same arguments, semantics and kernels as ra_block_attn_fwd, without
+ * `workspace`: the transposed V block (bf16) lives in a 64 MiB array in the
+ * library's code object, one per device, looked up once per device and never
+ * allocated or freed by the call. Limit: B * Hkv * D * round_up(Ck, 64) * 2
+ * bytes must not exceed 64 MiB (e.g. Hkv = 8, D = 128, Ck <= 32768), else
+ * RA_ERR_WORKSPACE and nothing is enqueued; fp32 inputs use no scratch.
+ * Every call on one device shares that device's array and overwrites it
+ * completely before reading it: calls that overlap on one device (other
+ * streams, other threads) race and must be ordered by the caller.
+ * ---------------------------------------------------------------------- */
+ra_status ra_block_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                                    float* out, float* lse,
+                                    int32_t B, int32_t Hq, int32_t Hkv,
+                                    int64_t Cq, int64_t Ck, int32_t D, ra_dtype dtype,
+                                    const ra_pos* q_pos, const ra_pos* k_pos,
+                                    const int32_t* kv_head_of_q, int32_t causal, float scale,
+                                    int32_t accumulate, void* stream);
+
+/* ------------------------------------------------------------------------
  * ra_lse_merge -- fold one normalised partial into a running one, in place.
  *
  * [SP "Algorithmic Mechanics": m_new = max(m_prev, m_block), l_new, O_new.

@@ -17,8 +17,8 @@ import torch
 __all__ = [
     "RAError", "lib", "library_path", "RA_BF16", "RA_F32", "RA_CONTIGUOUS", "RA_ZIGZAG",
     "ra_pos", "ra_status_str", "ra_last_error", "ra_block_attn_workspace_bytes",
-    "ra_block_attn_fwd", "ra_lse_merge", "ra_zigzag_permute", "ra_striped_permute",
-    "ra_ring_sim_workspace_bytes", "ra_block_attn_bwd_workspace_bytes", "ra_block_attn_bwd",
+    "ra_block_attn_fwd", "ra_block_attn_fwd_noalloc", "ra_lse_merge", "ra_zigzag_permute",
+    "ra_striped_permute", "ra_ring_sim_workspace_bytes", "ra_block_attn_bwd_workspace_bytes", "ra_block_attn_bwd",
     "ra_ring_sim_bwd_workspace_bytes", "ra_ring_sim_bwd", "ring_attention_sim_backward",
     "ra_ring_sim_fwd", "ra_kernel_timing_enable", "ra_kernel_timing_read", "ring_attention_sim", "ra_ulysses_all_to_all",
     "ra_ulysses_sim_workspace_bytes", "ra_ulysses_sim_fwd", "ra_usp_sim_workspace_bytes",
@@ -36,7 +36,7 @@ _LAYOUTS = {"contiguous": RA_CONTIGUOUS, "zigzag": RA_ZIGZAG, "striped": RA_STRI
 # Every symbol include/ring_attn.h declares.
 EXPORTS = (
     "ra_status_str", "ra_last_error", "ra_block_attn_workspace_bytes", "ra_block_attn_fwd",
-    "ra_lse_merge", "ra_zigzag_permute", "ra_striped_permute", "ra_ring_sim_workspace_bytes",
+    "ra_block_attn_fwd_noalloc", "ra_lse_merge", "ra_zigzag_permute", "ra_striped_permute", "ra_ring_sim_workspace_bytes",
     "ra_ring_sim_fwd", "ra_block_attn_bwd_workspace_bytes", "ra_block_attn_bwd",
     "ra_ring_sim_bwd_workspace_bytes", "ra_ring_sim_bwd", "ra_ulysses_all_to_all",
     "ra_ulysses_sim_workspace_bytes", "ra_ulysses_sim_fwd", "ra_usp_sim_workspace_bytes",
@@ -80,6 +80,10 @@ def lib() -> ctypes.CDLL:
                                         c_int32, c_int32, c_int32, c_int64, c_int64, c_int32,
                                         c_int32, P(ra_pos), P(ra_pos), P(c_int32), c_int32,
                                         c_float, c_int32, c_void_p, c_size_t, c_void_p]),
+        "ra_block_attn_fwd_noalloc": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                c_int32, c_int32, c_int32, c_int64, c_int64,
+                                                c_int32, c_int32, P(ra_pos), P(ra_pos),
+                                                P(c_int32), c_int32, c_float, c_int32, c_void_p]),
         "ra_lse_merge": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32,
                                    c_void_p]),
         "ra_zigzag_permute": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int32,
@@ -208,6 +212,25 @@ def ra_block_attn_fwd(q, k, v, out, lse, *, q_pos=None, k_pos=None, kv_head_of_q
         ctypes.byref(kp) if kp is not None else None,
         _kvmap(kv_head_of_q, Hq), int(bool(causal)), float(scale), int(bool(accumulate)),
         _ptr(workspace), wbytes, _stream(stream)))
+    return out, lse
+
+
+def ra_block_attn_fwd_noalloc(q, k, v, out, lse, *, q_pos=None, k_pos=None, kv_head_of_q=None,
+                              causal=True, scale=None, accumulate=False, stream=None):
+    """ra_block_attn_fwd without a workspace: the transposed V block lives in
+    the library's static per-device scratch (see include/ring_attn.h)."""
+    B, Hq, Cq, D = q.shape
+    Hkv, Ck = k.shape[1], k.shape[2]
+    dt = _dtype(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    qp, kp = _pos(q_pos), _pos(k_pos)
+    _check(lib().ra_block_attn_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Cq, Ck, D, dt,
+        ctypes.byref(qp) if qp is not None else None,
+        ctypes.byref(kp) if kp is not None else None,
+        _kvmap(kv_head_of_q, Hq), int(bool(causal)), float(scale), int(bool(accumulate)),
+        _stream(stream)))
     return out, lse
 
 

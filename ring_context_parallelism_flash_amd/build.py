@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libringattn.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "aux_kernels.hip", "probe.hip", "api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "aux_kernels.hip", "probe.hip", "noalloc.hip",
+           "api.cpp"]
 # Per-source extra flags. The backward kernels read their S and dP MFMA
 # results with the VALU; by default the backend gave those results AGPRs and
 # copied 32 of them to VGPRs at every loop iteration. The VGPR form of the

@@ -320,6 +320,29 @@ ra_status ra_block_attn_fwd(const void* q, const void* k, const void* v, float* 
   return timed_launch(a, dtype, D, s, flops);
 }
 
+ra_status ra_block_attn_fwd_noalloc(const void* q, const void* k, const void* v, float* out,
+                                    float* lse, int32_t B, int32_t Hq, int32_t Hkv, int64_t Cq,
+                                    int64_t Ck, int32_t D, ra_dtype dtype, const ra_pos* q_pos,
+                                    const ra_pos* k_pos, const int32_t* kv_head_of_q,
+                                    int32_t causal, float scale, int32_t accumulate,
+                                    void* stream) {
+  g_err[0] = 0;
+  const size_t need = ra_block_attn_workspace_bytes(B, Hkv, Ck, D, dtype);
+  if (need > kNoAllocScratchBytes)
+    return fail(RA_ERR_WORKSPACE,
+                "the transposed V block needs %zu bytes, beyond the %zu-byte static scratch "
+                "(B*Hkv*D*round_up(Ck, 64)*2 must not exceed it)",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "static scratch address");
+  }
+  return ra_block_attn_fwd(q, k, v, out, lse, B, Hq, Hkv, Cq, Ck, D, dtype, q_pos, k_pos,
+                           kv_head_of_q, causal, scale, accumulate, ws,
+                           need > 0 ? kNoAllocScratchBytes : 0, stream);
+}
+
 ra_status ra_lse_merge(float* out, float* lse, const float* out_b, const float* lse_b,
                        int64_t rows, int32_t D, void* stream) {
   g_err[0] = 0;

@@ -60,4 +60,10 @@ constexpr int kProbeWords = 5;
 constexpr size_t kProbeLdsBytes = 96 * 1024;
 hipError_t launch_mfma_probe(int32_t workgroups, int32_t iters, int64_t* out, hipStream_t s);
 
+// Static device scratch of ra_block_attn_fwd_noalloc (64 MiB per device):
+// *ptr receives the current device's address of the array, looked up once
+// per device.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace ra
