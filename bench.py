@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0
 # passes, scaled by a plain-copy calibration) live in this summary; they are
 # reported only while the kernel sources still hash to what was profiled.
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_bf16_gqa128k_pmc.txt")
-KERNEL_SOURCES = ("attn_fwd.hip", "attn_common.h", "attn_fwd_args.h")
+KERNEL_SOURCES = ("attn_fwd.hip", "attn_fwd_w64_phases.h", "attn_common.h", "attn_fwd_args.h")
 # The same for the backward kernels, per block pair (one dk/dv + one dq launch).
 BWD_PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_bwd_bf16_gqa128k_pmc.txt")
 BWD_KERNEL_SOURCES = ("attn_bwd.hip", "attn_common.h", "attn_bwd_args.h")

@@ -8,9 +8,15 @@
 // and "Causal Masking and Load Balancing" (j <= i on global positions).
 //
 // gfx950 design
-//  * Each wave64 owns 32 query rows. The bf16 kernel runs 8 waves (256 rows)
-//    per workgroup in two groups that alternate matrix and softmax phases;
-//    the fp32 kernel runs 4 waves (128 rows).
+//  * D = 128 bf16 blocks of whole 64-key tiles run attn_fwd_bf16_w64: one
+//    wave per SIMD owns 64 query rows (two 32-row blocks), so every K or V^T
+//    operand read from LDS feeds two MFMAs; its key loop is one generated
+//    inline-asm statement (attn_fwd_w64_phases.h, gen_fwd_w64.py) that
+//    interleaves each block's softmax with the other MFMA phase.
+//  * Other bf16 blocks (D = 64, ragged blocks) run attn_fwd_bf16: each wave64
+//    owns 32 query rows, 8 waves (256 rows) per workgroup in two groups that
+//    alternate matrix and softmax phases; the fp32 kernel runs 4 waves (128
+//    rows).
 //  * Scores are computed transposed, S^T = K * Q^T, with
 //    v_mfma_f32_32x32x16_bf16: a lane then holds 16 keys of ONE query, so the
 //    row max and row sum of the online softmax are in-lane reductions plus a
@@ -39,6 +45,7 @@
 #include <type_traits>
 
 #include "attn_common.h"
+#include "attn_fwd_w64_phases.h"
 
 namespace ra {
 namespace {
@@ -563,6 +570,152 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs 
 constexpr size_t bf16_lds_bytes(int D) { return (size_t)2 * (64 * (D / 8 + 1) * 16 + D * 9 * 16); }
 
 // ---------------------------------------------------------------------------
+// bf16 kernel for D = 128, one wave per SIMD: 4 waves x 64 query rows (two
+// 32-row blocks per wave). Every K or V^T operand read from LDS feeds two
+// MFMAs, one per row block, and the wave's own instruction stream overlaps
+// its matrix and vector work:
+//   phase A(t): score MFMAs of tile t+1 (both blocks) with the softmax of
+//               block 1 of tile t between them;
+//   phase B(t): P*V MFMAs of tile t (both blocks) with the softmax of
+//               block 0 of tile t+1 between them.
+// Both phases are inline-asm blocks with a fixed schedule and fixed
+// registers (attn_fwd_w64_phases.h, written by gen_fwd_w64.py); the masks,
+// the lazy-rescale check and the tile loads stay in C++ between them. K and
+// V^T tiles have two LDS buffers each; all four waves load both, and one
+// barrier per tile publishes the loads and frees the buffers they refill.
+// ---------------------------------------------------------------------------
+constexpr int kWavesW64 = 4;
+constexpr int kThreadsW64 = 64 * kWavesW64;
+
+__global__ __launch_bounds__(kThreadsW64, 1) void attn_fwd_bf16_w64(const AttnArgs a) {
+  constexpr int D = 128;
+  constexpr int KS = D / 16;             // MFMA k-steps of the score product
+  constexpr int DT = D / 32;             // 32-wide d tiles of the output
+  constexpr int CPR = D / 8;             // 16-byte data chunks per K row
+  constexpr int KCPR = CPR + 1;          // with the pad chunk
+  constexpr int KROW = KCPR * 16;        // bytes per padded K row
+  constexpr int VROW = 9 * 16;           // bytes per padded V^T row (64 keys + pad)
+  constexpr int KBUF = 64 * KROW, VBUF = D * VROW;  // bytes per LDS tile
+  constexpr int KINS = KBUF / 1024, VINS = VBUF / 1024;  // 1 KiB direct loads per tile
+  constexpr int NW = kWavesW64;
+  constexpr int KI = (KINS + NW - 1) / NW, VI = (VINS + NW - 1) / NW;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  unsigned char* Ks = lds;             // [2][64 keys][D + 8]
+  unsigned char* Vs = lds + 2 * KBUF;  // [2][D][64 + 8]
+
+  WorkItem it;
+  if (!decode_item(a, it)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hh = lane >> 5;
+  const int qlast = a.Cq - 1;
+  const int qw0 = it.q0 + 64 * wv;                 // first row of the wave
+  const int qi0 = qw0 + n, qi1 = qw0 + 32 + n;     // this lane's row in block 0 / 1
+  const int qpos0 = pos_of(a.qp, min(qi0, qlast));
+  const int qpos1 = pos_of(a.qp, min(qi1, qlast));
+  const int wave_qmin = pos_of(a.qp, min(qw0, qlast));
+  const int wg_qmax = pos_of(a.qp, min(it.q0 + a.q_tile - 1, qlast));
+  const int n_keys = a.causal ? allowed_prefix(a.kp, wg_qmax) : a.Ck;
+  const int n_kt = (n_keys + 63) / 64;
+  const float c = a.scale_log2;
+
+  const __bf16* qb = reinterpret_cast<const __bf16*>(a.q) + it.b * a.q_bs + it.h * a.q_hs;
+  const __bf16* kbp = reinterpret_cast<const __bf16*>(a.k) + it.b * a.k_bs + it.g * a.k_hs;
+  const __bf16* vtb = reinterpret_cast<const __bf16*>(a.v) + it.b * a.v_bs + it.g * a.v_hs;
+
+  bf16x8 q0[KS], q1[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (qi0 < a.Cq)
+      q0[s] = *reinterpret_cast<const bf16x8*>(qb + (int64_t)qi0 * D + 16 * s + 8 * hh);
+    else
+      for (int j = 0; j < 8; ++j) q0[s][j] = (__bf16)0.f;
+    if (qi1 < a.Cq)
+      q1[s] = *reinterpret_cast<const bf16x8*>(qb + (int64_t)qi1 * D + 16 * s + 8 * hh);
+    else
+      for (int j = 0; j < 8; ++j) q1[s][j] = (__bf16)0.f;
+  }
+
+  floatx16 O0[DT], O1[DT];
+  float m0 = -INFINITY, l0 = 0.f, m1 = -INFINITY, l1 = 0.f;
+
+  // Per-lane byte offsets of this wave's direct loads within a K tile and a
+  // V^T tile (instruction j fills 1 KiB chunk wv + NW*j of the tile).
+  uint32_t koff[KI], voff[VI];
+#pragma unroll
+  for (int j = 0; j < KI; ++j) {
+    const int P = (wv + NW * j) * 64 + lane;
+    const int cch = P % KCPR;
+    koff[j] = (uint32_t)((P / KCPR) * D + (cch < CPR ? cch : 0) * 8) * 2u;
+  }
+#pragma unroll
+  for (int j = 0; j < VI; ++j) {
+    const int P = (wv + NW * j) * 64 + lane;
+    const int cch = P % 9;
+    voff[j] = ((uint32_t)(P / 9) * (uint32_t)a.v_ld + (uint32_t)(cch < 8 ? cch : 0) * 8u) * 2u;
+  }
+  // Whole tiles only (the block is a multiple of 64 keys and the V^T rows of
+  // a tile lie within 4 GiB: the launch dispatches other blocks to the
+  // 8-wave kernel), so every load is a tile base plus a 32-bit offset.
+  auto load_k = [&](int kt, int buf) {
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(kbp + (int64_t)kt * 64 * D);
+    unsigned char* dst = Ks + buf * KBUF + wv * 1024;
+#pragma unroll
+    for (int j = 0; j < KI; ++j)
+      if (wv + NW * j < KINS) load_lds16(base + koff[j], dst + j * NW * 1024);
+  };
+  auto load_v = [&](int kt, int buf) {
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(vtb + kt * 64);
+    unsigned char* dst = Vs + buf * VBUF + wv * 1024;
+#pragma unroll
+    for (int j = 0; j < VI; ++j)
+      if (wv + NW * j < VINS) load_lds16(base + voff[j], dst + j * NW * 1024);
+  };
+
+  // Keys of the block each row may see (a prefix: positions increase along
+  // the block); tiles before first_mask are fully visible to every row of
+  // the wave, later ones are masked per lane.
+  const int nal0 = a.causal ? allowed_prefix(a.kp, qpos0) : a.Ck;
+  const int nal1 = a.causal ? allowed_prefix(a.kp, qpos1) : a.Ck;
+  const int first_mask = a.causal ? allowed_prefix(a.kp, wave_qmin) / 64 : n_kt;
+
+  if (n_kt > 0) {
+    // prologue: K0, K1, V0 in LDS, then the whole key loop in one asm block
+    load_k(0, 0);
+    if (n_kt > 1) load_k(1, 1);
+    load_v(0, 0);
+    lds_loads_barrier();
+    // wave-uniform values the loop keeps in SGPRs (the compiler cannot tell
+    // that pointers derived from the head tables are uniform)
+    auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+    auto uni_ptr = [](const void* p) {
+      const uint64_t v = (uint64_t)(size_t)p;
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+      return (const void*)(size_t)(((uint64_t)hi << 32) | lo);
+    };
+    w64::attn_loop(uni(n_kt), uni(first_mask), uni(lds_addr(Ks) + wv * 1024),
+                   uni(lds_addr(Vs) + wv * 1024), uni((wv + NW * (KI - 1)) < KINS),
+                   uni((wv + NW * (VI - 1)) < VINS), c,
+                   lds_addr(Ks) + kperm(n) * KROW + hh * 16, lds_addr(Vs) + n * VROW + hh * 16,
+                   nal0 - 8 * hh, nal1 - 8 * hh, (unsigned)((lane ^ 32) * 4),
+                   uni_ptr(kbp + (int64_t)2 * 64 * D), uni_ptr(vtb + 64), koff, voff, q0, q1, O0,
+                   O1, m0, l0, m1, l1);
+  } else {
+#pragma unroll
+    for (int T = 0; T < DT; ++T)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        O0[T][i] = 0.f;
+        O1[T][i] = 0.f;
+      }
+  }
+  epilogue<DT, true>(a, it, qi0, hh, O0, m0, l0);
+  epilogue<DT, true>(a, it, qi1, hh, O1, m1, l1);
+}
+
+
+// ---------------------------------------------------------------------------
 // fp32 kernel: 32-key tiles, MFMA 32x32x2 f32, V row-major.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -735,15 +888,21 @@ hipError_t launch_attn(const AttnArgs& a, ra_dtype dt, int D, hipStream_t s) {
     // The dynamic-LDS limit is a per-device property of the function: set it
     // on every launch (a host-side call), so any device and any thread that
     // launches through the library has it.
-    const void* fn = D == 128 ? (const void*)attn_fwd_bf16<128> : (const void*)attn_fwd_bf16<64>;
+    // D = 128 blocks of whole 64-key tiles run on the one-wave-per-SIMD
+    // kernel; ragged blocks, V^T rows more than 4 GiB apart and D = 64 on
+    // the 8-wave kernel.
+    const bool w64 = D == 128 && a.Ck % 64 == 0 && (int64_t)D * a.v_ld * 2 <= (int64_t)UINT32_MAX;
+    const void* fn = w64 ? (const void*)attn_fwd_bf16_w64
+                         : (D == 128 ? (const void*)attn_fwd_bf16<128> : (const void*)attn_fwd_bf16<64>);
     const size_t lds = bf16_lds_bytes(D);
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    const dim3 block8(kThreadsBf16);
-    if (D == 128)
-      hipLaunchKernelGGL(attn_fwd_bf16<128>, grid, block8, lds, s, a);
+    if (w64)
+      hipLaunchKernelGGL(attn_fwd_bf16_w64, grid, dim3(kThreadsW64), lds, s, a);
+    else if (D == 128)
+      hipLaunchKernelGGL(attn_fwd_bf16<128>, grid, dim3(kThreadsBf16), lds, s, a);
     else
-      hipLaunchKernelGGL(attn_fwd_bf16<64>, grid, block8, lds, s, a);
+      hipLaunchKernelGGL(attn_fwd_bf16<64>, grid, dim3(kThreadsBf16), lds, s, a);
   } else {
     if (D == 128)
       hipLaunchKernelGGL(attn_fwd_f32<128>, grid, block, 0, s, a);

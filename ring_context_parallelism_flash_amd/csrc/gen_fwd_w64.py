@@ -1,0 +1,417 @@
+"""Writes attn_fwd_w64_phases.h: the key-tile loop of the one-wave-per-SIMD
+bf16 forward kernel (D = 128) as one inline-asm statement with a fixed
+instruction schedule and a fixed register plan.
+
+A wave owns 64 query rows in two 32-row blocks. Each iteration (key tile t)
+runs two phases. Phase A issues the 32 score MFMAs of tile t+1 (each K
+operand read from LDS feeds the MFMA of both blocks) with the softmax of
+block 1 of tile t between them; phase B issues the 32 P*V MFMAs of tile t
+(each V^T read feeds both blocks) with the softmax of block 0 of tile t+1
+between them. Every MFMA is followed by part of one step's vector work, so
+the wave's vector and LDS instructions issue while its matrix pipe runs.
+One barrier per tile publishes the next tiles' direct global->LDS loads
+(two LDS buffers each for K and V^T).
+
+Online softmax with a lazy reference (the pages' running max / sum /
+rescaled output, "Algorithmic Mechanics"): probabilities are taken against a
+per-row reference m that moves only when a lane's probabilities of one tile
+sum past 2^8 (or it has none yet); then the row max is taken, O and l are
+rescaled by exp2((m_old - m_new) * c) and the tile's probabilities redone.
+l and O always share the reference, so the result is the same. That slow
+path and the causal mask (tiles from the wave's first partly visible one)
+are placed out of line, so the common path has no taken branch but the
+loop's back edge.
+
+Register plan (one wave per SIMD: 256 VGPRs + 256 AGPRs):
+  a[0:63]    O of block 0, four 32-wide d tiles of 16 registers (O^T layout)
+  a[64:127]  O of block 1
+  a[128:159] Q of block 0, eight k-steps of 4 registers (bf16x8)
+  a[160:191] Q of block 1
+  v52 m0, v53 l0, v54 m1, v55 l1: reference and running sum of each block
+  v56 row sum, v57 LDS address, v58 minus the exponent offset, v[60:63]
+  temporaries
+  v[64:79]   LDS operand ring, four 16-byte reads in flight
+  v[80:95]   P0a  bf16 probabilities of block 0 (tile parity 0)
+  v[96:111]  P0b  (tile parity 1)
+  v[112:127] P1   bf16 probabilities of block 1
+  v[128:159] SA0  scores of block 0, two 32-key halves of 16 registers
+  v[160:191] SA1  scores of block 1
+  v[192:223] SB0, v[224:255] SB1: the other score buffer pair
+  s[80:81], s[82:83]: global addresses of the next K and V^T tiles
+The compiler keeps everything else (the load offsets, the lane addresses,
+its own values) in v[0:51], a[192:255] and the other SGPRs.
+
+Hazards the statement respects by construction: a transcendental result is
+read no earlier than the second instruction after it; every phase ends with
+24 wait states (s_nop 7 x 3) so no later vector instruction reads an MFMA
+result early; an MFMA accumulator is reused no sooner than three MFMAs
+later; an M0 write is followed by one wait state before the LDS-DMA load
+that reads it; LDS reads wait on counted lgkmcnt with no other LGKM
+operation in flight (every phase starts by draining the counter).
+
+Run: python gen_fwd_w64.py  (writes the header next to this file)
+"""
+import os
+
+D = 128
+KS = D // 16           # score k-steps
+DT = D // 32           # output d tiles
+KROW = (D // 8 + 1) * 16   # padded K row in LDS, bytes
+VROW = 9 * 16              # padded V^T row in LDS, bytes
+N = 16                 # operand reads per phase (2*KS score reads, 4*DT P*V reads)
+PF = 4                 # reads in flight
+assert 2 * KS == N and 4 * DT == N
+FAST_SUM = 256.0       # 2^8: the lazy-rescale bound on a lane's tile sum
+NEG_INF = "0xff800000"
+
+O_ = (0, 64)                     # O of block 0 / 1 (AGPR base)
+Q_ = (128, 160)                  # Q of block 0 / 1 (AGPR base)
+M_ = (52, 54)
+L_ = (53, 55)
+V_RS, V_ADDR, V_NMOFF, V_PERM = 56, 57, 58, 59
+T0, T1, T2, T3 = 60, 61, 62, 63
+RING = 64
+P0A, P0B, P1 = 80, 96, 112
+SA0, SA1, SB0, SB1 = 128, 160, 192, 224
+PAD = ["s_nop 7", "s_nop 7", "s_nop 7"]
+KG_S, VG_S = 80, 82              # SGPR pairs of the global K / V^T tile addresses
+
+
+def vr(base, n):
+    return f"v[{base}:{base + n - 1}]"
+
+
+def ar(base, n):
+    return f"a[{base}:{base + n - 1}]"
+
+
+def ring(i):
+    return vr(RING + 4 * (i % PF), 4)
+
+
+def elem(S, e):
+    """VGPR of probability element e (= 8u + j of P[u]) of a 32-score block."""
+    u, j = e >> 3, e & 7
+    return S + 16 * (u >> 1) + 8 * (u & 1) + j
+
+
+def nmoff_lines(m):
+    """v58 = -(m == -inf ? 0 : m) * c."""
+    return [f"v_mul_f32 v{V_NMOFF}, %[c], v{m}",
+            f"v_sub_f32 v{V_NMOFF}, 0, v{V_NMOFF}",
+            f"v_cmp_class_f32_e64 vcc, v{m}, 4",
+            f"v_cndmask_b32_e64 v{V_NMOFF}, v{V_NMOFF}, 0, vcc"]
+
+
+def softmax_pair(i, S, P):
+    """Vector work for scores e = 2i, 2i+1: two halves (after each MFMA)."""
+    s0 = elem(S, 2 * i)
+    u, j = (2 * i) >> 3, (2 * i) & 7
+    first = [f"v_fma_f32 v{T0}, v{s0}, %[c], v{V_NMOFF}",
+             f"v_fma_f32 v{T1}, v{s0 + 1}, %[c], v{V_NMOFF}",
+             f"v_exp_f32 v{T0}, v{T0}",
+             f"v_exp_f32 v{T1}, v{T1}"]
+    second = [f"v_add_f32 v{T2}, v{T2}, v{T0}",
+              f"v_add_f32 v{T3}, v{T3}, v{T1}",
+              f"v_cvt_pk_bf16_f32 v{P + 4 * u + j // 2}, v{T0}, v{T1}"]
+    return first, second
+
+
+def score_phase(S0, S1, work):
+    """Score MFMAs of a tile into (S0, S1) from the K tile at v57; with
+    `work` = (Scur, P, block) the softmax of Scur between them."""
+    off = lambda i: (i % 2) * 32 * KROW + (i // 2) * 32
+    lines = ["s_waitcnt lgkmcnt(0)"]
+    if work:
+        lines += nmoff_lines(M_[work[2]]) + [f"v_mov_b32 v{T2}, 0", f"v_mov_b32 v{T3}, 0"]
+    for i in range(PF):
+        lines.append(f"ds_read_b128 {ring(i)}, v{V_ADDR} offset:{off(i)}")
+    for i in range(N):
+        h, s = i % 2, i // 2
+        lines.append(f"s_waitcnt lgkmcnt({min(PF - 1, N - 1 - i)})")
+        c0 = "0" if s == 0 else vr(S0 + 16 * h, 16)
+        c1 = "0" if s == 0 else vr(S1 + 16 * h, 16)
+        first, second = softmax_pair(i, work[0], work[1]) if work else ([], [])
+        lines.append(f"v_mfma_f32_32x32x16_bf16 {vr(S0 + 16 * h, 16)}, {ring(i)}, "
+                     f"{ar(Q_[0] + 4 * s, 4)}, {c0}")
+        lines += first
+        lines.append(f"v_mfma_f32_32x32x16_bf16 {vr(S1 + 16 * h, 16)}, {ring(i)}, "
+                     f"{ar(Q_[1] + 4 * s, 4)}, {c1}")
+        if i + PF < N:
+            lines.append(f"ds_read_b128 {ring(i)}, v{V_ADDR} offset:{off(i + PF)}")
+        lines += second
+    return lines + PAD
+
+
+def pv_phase(P0, P1_, work):
+    """O += V^T P for both blocks from the V^T tile at v57; with `work` =
+    (Snext, Pnext, block) the softmax of Snext between the MFMAs."""
+    off = lambda i: (i % DT) * 32 * VROW + (i // DT) * 32
+    lines = ["s_waitcnt lgkmcnt(0)"]
+    if work:
+        lines += nmoff_lines(M_[work[2]]) + [f"v_mov_b32 v{T2}, 0", f"v_mov_b32 v{T3}, 0"]
+    for i in range(PF):
+        lines.append(f"ds_read_b128 {ring(i)}, v{V_ADDR} offset:{off(i)}")
+    for i in range(N):
+        u, T = i // DT, i % DT
+        lines.append(f"s_waitcnt lgkmcnt({min(PF - 1, N - 1 - i)})")
+        first, second = softmax_pair(i, work[0], work[1]) if work else ([], [])
+        lines.append(f"v_mfma_f32_32x32x16_bf16 {ar(O_[0] + 16 * T, 16)}, {ring(i)}, "
+                     f"{vr(P0 + 4 * u, 4)}, {ar(O_[0] + 16 * T, 16)}")
+        lines += first
+        lines.append(f"v_mfma_f32_32x32x16_bf16 {ar(O_[1] + 16 * T, 16)}, {ring(i)}, "
+                     f"{vr(P1_ + 4 * u, 4)}, {ar(O_[1] + 16 * T, 16)}")
+        if i + PF < N:
+            lines.append(f"ds_read_b128 {ring(i)}, v{V_ADDR} offset:{off(i + PF)}")
+        lines += second
+    return lines + PAD
+
+
+LOOP_CLOBBER = ([f'"v{r}"' for r in range(V_RS, 256)] +
+                ['"vcc"', '"scc"', '"m0"', '"exec"', '"memory"'])
+
+
+class Loop:
+    """The whole key-tile loop as one asm statement. Rarely taken code (the
+    slow path, the causal mask) is placed out of line after the loop, so the
+    common path runs without taken branches."""
+
+    def __init__(self):
+        self.lines = []
+        self.ool = []
+
+    def add(self, lines):
+        self.lines += lines
+
+    def lab(self, name):
+        return f".L{name}_%="
+
+    def place(self, name):
+        self.lines.append(f"{self.lab(name)}:")
+
+    def set_addr(self, reg_operand, const):
+        self.lines.append(f"v_add_u32 v{V_ADDR}, {const}, {reg_operand}")
+
+    def check_and_slow(self, b, S, P, site):
+        """Row sum check of block b; the fast path adds it to l, the slow
+        path (out of line) redoes the tile's softmax."""
+        m, l = M_[b], L_[b]
+        self.add([f"v_add_f32 v{V_RS}, v{T2}, v{T3}",
+                  f"v_cmp_ge_f32 vcc, {FAST_SUM}, v{V_RS}",
+                  f"v_cmp_class_f32_e64 %[stmp], v{m}, 4",
+                  "s_andn2_b64 vcc, vcc, %[stmp]",
+                  "s_cmp_eq_u64 vcc, exec",
+                  f"s_cbranch_scc0 {self.lab('slow' + site)}",
+                  f"v_add_f32 v{l}, v{l}, v{V_RS}"])
+        self.place("cont" + site)
+        self.ool += [f"{self.lab('slow' + site)}:"]
+        self.ool += slow_path_body(S, P, b, self.lab("keep" + site))
+        self.ool += [f"s_branch {self.lab('cont' + site)}"]
+
+    def mask(self, S0, S1, kt_sgpr, site, cond):
+        """Causal mask of the tile whose index is in kt_sgpr, on both blocks,
+        out of line; `cond` = instructions leaving SCC = 1 when it is needed."""
+        self.add(cond + [f"s_cbranch_scc1 {self.lab('mask' + site)}"])
+        self.place("mback" + site)
+        body = [f"{self.lab('mask' + site)}:",
+                f"s_lshl_b32 %[sx], {kt_sgpr}, 6",
+                f"v_subrev_u32 v{T1}, %[sx], %[nal0]",
+                f"v_subrev_u32 v{T2}, %[sx], %[nal1]",
+                f"v_mov_b32 v{T0}, {NEG_INF}"]
+        for S, lim in ((S0, T1), (S1, T2)):
+            for t in range(2):
+                for i in range(16):
+                    k = 32 * t + 16 * (i >> 3) + (i & 7)
+                    r = S + 16 * t + i
+                    body += [f"v_cmp_lt_i32 vcc, {k}, v{lim}",
+                             f"v_cndmask_b32 v{r}, v{T0}, v{r}, vcc"]
+        self.ool += body + [f"s_branch {self.lab('mback' + site)}"]
+
+
+def slow_path_body(S, P, b, keep_label):
+    """Row max of S; where it exceeds the reference, O and l of block b are
+    scaled by exp2((m - m_new) c) and m moves up; then P and the row sum are
+    redone from S against the reference and l += sum."""
+    m, l, Ob = M_[b], L_[b], O_[b]
+    regs = [elem(S, e) for e in range(32)]
+    lines = [f"v_max_f32 v{T0}, v{regs[0]}, v{regs[1]}",
+             f"v_max_f32 v{T1}, v{regs[2]}, v{regs[3]}"]
+    for k in range(4, 32, 2):
+        t = T0 if (k // 2) % 2 == 0 else T1
+        lines.append(f"v_max3_f32 v{t}, v{t}, v{regs[k]}, v{regs[k + 1]}")
+    lines += [f"v_max_f32 v{T0}, v{T0}, v{T1}",
+              f"ds_bpermute_b32 v{T1}, %[perm], v{T0}",
+              "s_waitcnt lgkmcnt(0)",
+              f"v_max_f32 v{T0}, v{T0}, v{T1}",            # row max (both lane halves)
+              f"v_cmp_gt_f32 vcc, v{T0}, v{m}",             # grow
+              "s_cmp_eq_u64 vcc, 0",
+              f"s_cbranch_scc1 {keep_label}",
+              f"v_cndmask_b32 v{T1}, v{m}, v{T0}, vcc",     # m_new
+              f"v_sub_f32 v{T2}, v{m}, v{T1}",
+              f"v_mul_f32 v{T2}, %[c], v{T2}",
+              f"v_exp_f32 v{T2}, v{T2}",
+              "s_nop 1",
+              f"v_cndmask_b32_e64 v{T2}, 1.0, v{T2}, vcc",   # alpha
+              f"v_mov_b32 v{m}, v{T1}",
+              f"v_mul_f32 v{l}, v{l}, v{T2}"]
+    for r in range(64):
+        t = RING + (r % 8)
+        lines += [f"v_accvgpr_read_b32 v{t}, a{Ob + r}",
+                  f"v_mul_f32 v{t}, v{t}, v{T2}",
+                  f"v_accvgpr_write_b32 a{Ob + r}, v{t}"]
+    lines.append(f"{keep_label}:")
+    lines += nmoff_lines(m) + [f"v_mov_b32 v{T2}, 0", f"v_mov_b32 v{T3}, 0"]
+    for i in range(16):
+        first, second = softmax_pair(i, S, P)
+        lines += first + second
+    lines += [f"v_add_f32 v{V_RS}, v{T2}, v{T3}", f"v_add_f32 v{l}, v{l}, v{V_RS}"]
+    return lines
+
+
+def loads(L, p):
+    """Barrier, then K(t+2) (if it exists) into K buffer t&1 = p and V(t+1)
+    into V buffer 1-p; advance the global tile addresses. A wave's fifth
+    load of a tile runs under %[x5k] / %[x5v] as its exec mask (all lanes or
+    none), so no wave branches around it."""
+    KBUF, VBUF = 64 * KROW, D * VROW
+    L.add(["s_waitcnt vmcnt(0)", "s_barrier",
+           "s_add_u32 %[sx], %[t], 2",
+           "s_cmp_lt_u32 %[sx], %[nkt]",
+           f"s_cbranch_scc0 {L.lab(f'nok{p}')}"])
+    for j in range(4):
+        L.add([f"s_add_u32 m0, %[kdst], {p * KBUF + j * 4096}", "s_nop 0",
+               f"global_load_lds_dwordx4 %[ko{j}], %[kg]"])
+    L.add([f"s_add_u32 m0, %[kdst], {p * KBUF + 16384}",
+           "s_mov_b64 exec, %[x5k]",
+           "global_load_lds_dwordx4 %[ko4], %[kg]",
+           "s_mov_b64 exec, -1"])
+    L.place(f"nok{p}")
+    for j in range(4):
+        L.add([f"s_add_u32 m0, %[vdst], {(1 - p) * VBUF + j * 4096}", "s_nop 0",
+               f"global_load_lds_dwordx4 %[vo{j}], %[vg]"])
+    L.add([f"s_add_u32 m0, %[vdst], {(1 - p) * VBUF + 16384}",
+           "s_mov_b64 exec, %[x5v]",
+           "global_load_lds_dwordx4 %[vo4], %[vg]",
+           "s_mov_b64 exec, -1"])
+    L.add([f"s_add_u32 s{KG_S}, s{KG_S}, {64 * D * 2}", f"s_addc_u32 s{KG_S + 1}, s{KG_S + 1}, 0",
+           f"s_add_u32 s{VG_S}, s{VG_S}, 128", f"s_addc_u32 s{VG_S + 1}, s{VG_S + 1}, 0"])
+
+
+def loop_asm():
+    KBUF, VBUF = 64 * KROW, D * VROW
+    S = {0: (SA0, SA1, SB0, SB1), 1: (SB0, SB1, SA0, SA1)}
+    P0 = {0: (P0A, P0B), 1: (P0B, P0A)}
+    L = Loop()
+    L.add([f"v_accvgpr_write_b32 a{O_[b] + r}, 0" for b in (0, 1) for r in range(64)])
+    # prologue: scores of tile 0 (K0 in buffer 0), mask, block 0 softmax
+    L.set_addr("%[krb]", 0)
+    L.add(score_phase(SA0, SA1, None))
+    L.add(["s_mov_b32 %[t], 0"])
+    L.mask(SA0, SA1, "%[t]", "pro", ["s_cmp_eq_u32 %[fmask], 0"])
+    L.add(["s_waitcnt lgkmcnt(0)"] + nmoff_lines(M_[0]) +
+          [f"v_mov_b32 v{T2}, 0", f"v_mov_b32 v{T3}, 0"])
+    for i in range(16):
+        first, second = softmax_pair(i, SA0, P0A)
+        L.add(first + second)
+    L.check_and_slow(0, SA0, P0A, "pro")
+    L.add(["s_mov_b32 %[t], 0"])
+    L.place("loop")
+    for p in (0, 1):
+        c0, c1, n0, n1 = S[p]
+        pc, pn = P0[p]
+        # t + 1 < n_kt, else the last tile of this parity
+        L.add(["s_add_u32 %[t1], %[t], 1", "s_cmp_ge_u32 %[t1], %[nkt]",
+               f"s_cbranch_scc1 {L.lab(f'last{p}')}"])
+        loads(L, p)
+        L.set_addr("%[krb]", (1 - p) * KBUF)
+        L.add(score_phase(n0, n1, (c1, P1, 1)))
+        L.check_and_slow(1, c1, P1, f"a{p}")
+        L.mask(n0, n1, "%[t1]", f"{p}", ["s_cmp_ge_u32 %[t1], %[fmask]"])
+        L.set_addr("%[vrb]", p * VBUF)
+        L.add(pv_phase(pc, P1, (n0, pn, 0)))
+        L.check_and_slow(0, n0, pn, f"b{p}")
+        L.add(["s_mov_b32 %[t], %[t1]"])
+    L.add([f"s_branch {L.lab('loop')}"])
+    for p in (0, 1):
+        c0, c1, n0, n1 = S[p]
+        pc, pn = P0[p]
+        L.place(f"last{p}")
+        L.add(["s_waitcnt vmcnt(0)", "s_barrier", "s_waitcnt lgkmcnt(0)"] + nmoff_lines(M_[1]) +
+              [f"v_mov_b32 v{T2}, 0", f"v_mov_b32 v{T3}, 0"])
+        for i in range(16):
+            first, second = softmax_pair(i, c1, P1)
+            L.add(first + second)
+        L.check_and_slow(1, c1, P1, f"l{p}")
+        L.set_addr("%[vrb]", p * VBUF)
+        L.add(pv_phase(pc, P1, None))
+        L.add([f"s_branch {L.lab('done')}"])
+    L.add(L.ool)
+    L.place("done")
+    return L.lines
+
+
+def main():
+    out = [f'''// Generated by gen_fwd_w64.py -- do not edit by hand.
+//
+// The key-tile loop of attn_fwd_bf16_w64 (D = {D}) as one inline-asm
+// statement with a fixed schedule and fixed registers; gen_fwd_w64.py
+// documents the register plan, the schedule and the hazards it respects.
+#pragma once
+
+namespace ra {{
+namespace w64 {{
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+''']
+    lines = loop_asm()
+    outs = ([f'"={{{ar(O_[b] + 16 * T, 16)}}}"(o{b}[{T}])' for b in (0, 1) for T in range(DT)] +
+            [f'"+{{v{M_[b]}}}"(m{b})' for b in (0, 1)] +
+            [f'"+{{v{L_[b]}}}"(l{b})' for b in (0, 1)] +
+            ['[t] "=&s"(t)', '[t1] "=&s"(t1)', '[sx] "=&s"(sx)', '[stmp] "=&s"(stmp)',
+             f'[kg] "+{{s[{KG_S}:{KG_S + 1}]}}"(kgv)', f'[vg] "+{{s[{VG_S}:{VG_S + 1}]}}"(vgv)'])
+    ins = (['[nkt] "s"(n_kt)', '[fmask] "s"(first_mask)', '[kdst] "s"(kdst)',
+            '[vdst] "s"(vdst)', '[x5k] "s"(x5k)', '[x5v] "s"(x5v)', '[c] "s"(c)',
+            '[krb] "v"(krb)', '[vrb] "v"(vrb)', '[nal0] "v"(nal0)', '[nal1] "v"(nal1)',
+            '[perm] "v"(perm)'] +
+           [f'[ko{j}] "v"(koff[{j}])' for j in range(5)] +
+           [f'[vo{j}] "v"(voff[{j}])' for j in range(5)] +
+           [f'"{{{ar(Q_[0] + 4 * s, 4)}}}"(q0[{s}])' for s in range(KS)] +
+           [f'"{{{ar(Q_[1] + 4 * s, 4)}}}"(q1[{s}])' for s in range(KS)])
+    body = "\n".join(f'      "{ln}\\n\\t"' for ln in lines)
+    out.append(f"""// The key-tile loop of one wave: n_kt >= 1 tiles; tiles 0 and 1 of K and
+// tile 0 of V^T are already in LDS (buffers 0, 1 and 0). krb / vrb: this
+// lane's operand read address in K buffer 0 / V^T buffer 0; kdst / vdst:
+// this wave's first load destination in K / V^T buffer 0; kg / vg: global
+// address of K tile 2 / V^T tile 1 (advanced by the loop); koff / voff: the
+// lane's load offsets; k5 / v5: whether the wave issues a fifth load per
+// tile; first_mask: first tile needing the causal mask; nal0 / nal1: keys
+// visible to the lane's row of block 0 / 1, minus 8 for the upper half of
+// the wave; perm: byte address of lane ^ 32. Returns O, m and l of both
+// blocks (O^T layout, exponent reference m, sum l).
+__device__ __forceinline__ void attn_loop(
+    int n_kt, int first_mask, unsigned kdst, unsigned vdst, int k5, int v5, float c,
+    unsigned krb, unsigned vrb, int nal0, int nal1, unsigned perm, const void* kg,
+    const void* vg, const unsigned (&koff)[5], const unsigned (&voff)[5],
+    const bf16x8 (&q0)[8], const bf16x8 (&q1)[8], floatx16 (&o0)[4], floatx16 (&o1)[4],
+    float& m0, float& l0, float& m1, float& l1) {{
+  int t, t1, sx;
+  long long stmp;
+  const long long x5k = k5 ? -1ll : 0ll, x5v = v5 ? -1ll : 0ll;
+  unsigned long long kgv = (unsigned long long)(size_t)kg, vgv = (unsigned long long)(size_t)vg;
+  asm volatile(
+{body}
+      : {", ".join(outs)}
+      : {", ".join(ins)}
+      : {", ".join(LOOP_CLOBBER)});
+}}
+""")
+    out.append("}  // namespace w64\n}  // namespace ra\n")
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "attn_fwd_w64_phases.h")
+    with open(path, "w") as f:
+        f.write("\n".join(out))
+    return path
+
+
+if __name__ == "__main__":
+    print(main())
