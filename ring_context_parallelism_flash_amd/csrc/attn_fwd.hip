@@ -62,8 +62,13 @@ __device__ __forceinline__ bool decode_item(const AttnArgs& a, WorkItem& it) {
   const int rest = L / a.n_qt;
   const int hidx = rest % a.Hq;
   it.b = rest / a.Hq;
-  it.h = a.head_order[hidx];
-  it.g = a.kv_of[it.h];
+  // The head tables are read as 32-bit words of the kernel arguments, and
+  // the results marked uniform, so the pointers derived from them stay in
+  // scalar registers.
+  const uint32_t* ho = reinterpret_cast<const uint32_t*>(a.head_order);
+  const uint32_t* ko = reinterpret_cast<const uint32_t*>(a.kv_of);
+  it.h = __builtin_amdgcn_readfirstlane((int)((ho[hidx >> 2] >> (8 * (hidx & 3))) & 255u));
+  it.g = __builtin_amdgcn_readfirstlane((int)((ko[it.h >> 2] >> (8 * (it.h & 3))) & 255u));
   // heaviest (latest-position) query tiles first
   it.q0 = (a.qt_lo + (a.n_qt - 1 - qt_rel)) * a.q_tile;
   return true;
@@ -172,6 +177,125 @@ __device__ __forceinline__ void epilogue(const AttnArgs& a, const WorkItem& it, 
       *rl = lse_new;
   }
 }
+
+// The same merge for the two 32-row blocks of a one-wave-per-SIMD wave (bf16
+// inputs, D = 128; ACC: fold into the running state, FIN: write the final
+// output), through the wave's own LDS staging area so that the running state
+// is read and written in whole rows (each 16-byte access of the MFMA layout
+// would otherwise touch 32 rows at once). The running output rows of both
+// blocks are loaded first, row-major; then per block the lanes of the MFMA
+// layout stage O * cb and each row's (ca, write) pair, and the row-major
+// lanes merge ca * old + staged and store. Rows whose previous lse is -inf
+// take none of the loaded output (a select, not a product).
+constexpr int kStageRow = 528;  // bytes per staged row: 128 floats + (ca, write) + pad
+
+template <bool ACC, bool FIN>
+__device__ __forceinline__ void epilogue_w64(const AttnArgs& a, const WorkItem& it, int qw0, int lane,
+                                             floatx16 (&O0)[4], floatx16 (&O1)[4],
+                                             const float (&m_run)[2], const float (&l_part)[2],
+                                             unsigned char* stage) {
+  constexpr int D = 128;
+  const int n = lane & 31, hh = lane >> 5;
+  if (qw0 >= a.Cq) return;  // the whole wave lies past the block
+  const int rmax = a.Cq - 1 - qw0;  // last row of the wave inside the block
+  // wave-uniform bases at the wave's first row; per-lane 32-bit byte offsets
+  unsigned char* ro = reinterpret_cast<unsigned char*>(a.run_out + it.b * a.ro_bs + it.h * a.ro_hs +
+                                                       (int64_t)qw0 * D);
+  float* rl = a.run_lse + it.b * a.rl_bs + it.h * a.rl_hs + qw0;
+  unsigned char* fo = FIN ? reinterpret_cast<unsigned char*>(reinterpret_cast<__bf16*>(a.fin_out) +
+                                                             it.b * a.fo_bs + it.h * a.fo_hs +
+                                                             (int64_t)qw0 * D)
+                          : nullptr;
+  float* fl = FIN ? a.fin_lse + it.b * a.fl_bs + it.h * a.fl_hs + qw0 : nullptr;
+  // row-major view: access i of block b is row 32b + 2i + hh, floats 4n .. 4n+3
+  float4 old[2][16];
+  float lse_old[2] = {-INFINITY, -INFINITY};
+  if (ACC) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      if (32 * b + n <= rmax) lse_old[b] = rl[32 * b + n];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = min(32 * b + 2 * i + hh, rmax);
+        old[b][i] = *reinterpret_cast<const float4*>(ro + (uint32_t)(r * D + 4 * n) * 4u);
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    floatx16(&O)[4] = b ? O1 : O0;
+    const float l = l_part[b] + __shfl_xor(l_part[b], 32);
+    const float m_use = (m_run[b] == -INFINITY) ? 0.f : m_run[b];
+    const float lse_blk = (l > 0.f) ? fmaf(m_use, a.scale, logf(l)) : -INFINITY;
+    const bool write = 32 * b + n <= rmax && !(ACC && !FIN && lse_blk == -INFINITY);
+    const float mx = fmaxf(lse_old[b], lse_blk);
+    float lse_new, ca, cb;
+    if (mx == -INFINITY) {
+      lse_new = -INFINITY;
+      ca = 0.f;
+      cb = 0.f;
+    } else {
+      const float mn = fminf(lse_old[b], lse_blk);
+      lse_new = mx + log1pf(expf(mn - mx));
+      ca = (lse_old[b] == -INFINITY) ? 0.f : expf(lse_old[b] - lse_new);
+      cb = (lse_blk == -INFINITY) ? 0.f : expf(lse_blk - lse_new) / l;
+    }
+    // MFMA layout: lane (n, hh) holds d = 32T + 8g + 4hh + (0..3) of row n
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        float4 r;
+        r.x = O[T][4 * g4 + 0] * cb;
+        r.y = O[T][4 * g4 + 1] * cb;
+        r.z = O[T][4 * g4 + 2] * cb;
+        r.w = O[T][4 * g4 + 3] * cb;
+        *reinterpret_cast<float4*>(stage + n * kStageRow + (32 * T + 8 * g4 + 4 * hh) * 4) = r;
+      }
+    if (hh == 0) {
+      *reinterpret_cast<float2*>(stage + n * kStageRow + 4 * D) = make_float2(ca, write ? 1.f : 0.f);
+      if (write) (FIN ? fl : rl)[32 * b + n] = lse_new;
+    }
+#pragma unroll
+    for (int i0 = 0; i0 < 16; i0 += 8) {
+      // all LDS reads of 8 rows first, so they are in flight together
+      float4 rs[8];
+      float2 fs[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r_loc = 2 * (i0 + k) + hh;
+        rs[k] = *reinterpret_cast<const float4*>(stage + r_loc * kStageRow + 16 * n);
+        fs[k] = *reinterpret_cast<const float2*>(stage + r_loc * kStageRow + 4 * D);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k;
+        const uint32_t e = (uint32_t)((32 * b + 2 * i + hh) * D + 4 * n);  // element offset
+        float4 r = rs[k];
+        if (ACC) {
+          const bool use_old = fs[k].x != 0.f;
+          r.x = use_old ? fmaf(old[b][i].x, fs[k].x, r.x) : r.x;
+          r.y = use_old ? fmaf(old[b][i].y, fs[k].x, r.y) : r.y;
+          r.z = use_old ? fmaf(old[b][i].z, fs[k].x, r.z) : r.z;
+          r.w = use_old ? fmaf(old[b][i].w, fs[k].x, r.w) : r.w;
+        }
+        if (fs[k].y != 0.f) {
+          if (FIN) {
+            bf16x4 pk;
+            pk[0] = (__bf16)r.x;
+            pk[1] = (__bf16)r.y;
+            pk[2] = (__bf16)r.z;
+            pk[3] = (__bf16)r.w;
+            *reinterpret_cast<bf16x4*>(fo + e * 2u) = pk;
+          } else {
+            *reinterpret_cast<float4*>(ro + e * 4u) = r;
+          }
+        }
+      }
+    }
+  }
+}
+
 
 // ---------------------------------------------------------------------------
 // bf16 kernel: 64-key tiles, MFMA 32x32x16.
@@ -568,6 +692,11 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16(const AttnArgs 
 
 // LDS bytes of the bf16 kernel (two padded K and two padded V^T tiles).
 constexpr size_t bf16_lds_bytes(int D) { return (size_t)2 * (64 * (D / 8 + 1) * 16 + D * 9 * 16); }
+// K tiles in w64::kKBufs buffers, V^T tiles in two, and a 64-row staging
+// area per wave (D = 128).
+constexpr size_t w64_lds_bytes() {
+  return (size_t)(w64::kKBufs + 4) * 64 * 17 * 16 + 2 * 128 * 9 * 16;
+}
 
 // ---------------------------------------------------------------------------
 // bf16 kernel for D = 128, one wave per SIMD: 4 waves x 64 query rows (two
@@ -578,11 +707,14 @@ constexpr size_t bf16_lds_bytes(int D) { return (size_t)2 * (64 * (D / 8 + 1) * 
 //               block 1 of tile t between them;
 //   phase B(t): P*V MFMAs of tile t (both blocks) with the softmax of
 //               block 0 of tile t+1 between them.
-// Both phases are inline-asm blocks with a fixed schedule and fixed
-// registers (attn_fwd_w64_phases.h, written by gen_fwd_w64.py); the masks,
-// the lazy-rescale check and the tile loads stay in C++ between them. K and
-// V^T tiles have two LDS buffers each; all four waves load both, and one
-// barrier per tile publishes the loads and frees the buffers they refill.
+// The whole key loop -- both phases, the masks, the lazy-rescale check and
+// the tile loads -- is one inline-asm statement with a fixed schedule and
+// fixed registers (attn_fwd_w64_phases.h, written by gen_fwd_w64.py). K tiles
+// rotate through three LDS buffers and V^T tiles through two; all four waves
+// load both, and one barrier per tile publishes the loads and frees the
+// buffers they refill. Around the loop, each wave stages its query rows and
+// its output rows through an LDS area of its own, so that the state in
+// global memory is read and written in whole rows.
 // ---------------------------------------------------------------------------
 constexpr int kWavesW64 = 4;
 constexpr int kThreadsW64 = 64 * kWavesW64;
@@ -600,8 +732,15 @@ __global__ __launch_bounds__(kThreadsW64, 1) void attn_fwd_bf16_w64(const AttnAr
   constexpr int NW = kWavesW64;
   constexpr int KI = (KINS + NW - 1) / NW, VI = (VINS + NW - 1) / NW;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  unsigned char* Ks = lds;             // [2][64 keys][D + 8]
-  unsigned char* Vs = lds + 2 * KBUF;  // [2][D][64 + 8]
+  unsigned char* Ks = lds;                           // [kKBufs][64 keys][D + 8]
+  unsigned char* Vs = lds + w64::kKBufs * KBUF;      // [2][D][64 + 8]
+  // per wave: its 64 query rows (padded like K) in the prologue, its output
+  // rows on the way out
+  unsigned char* Stage = Vs + 2 * VBUF;              // [NW][64 rows][D + 8]
+  static_assert(32 * kStageRow <= KBUF, "a staged 32-row block fits a wave's area");
+  static_assert(NW == 4 && w64_lds_bytes() == (size_t)(w64::kKBufs + NW) * KBUF + 2 * VBUF &&
+                    w64_lds_bytes() <= 160 * 1024,
+                "LDS layout of the one-wave-per-SIMD kernel");
 
   WorkItem it;
   if (!decode_item(a, it)) return;
@@ -611,33 +750,10 @@ __global__ __launch_bounds__(kThreadsW64, 1) void attn_fwd_bf16_w64(const AttnAr
   const int qlast = a.Cq - 1;
   const int qw0 = it.q0 + 64 * wv;                 // first row of the wave
   const int qi0 = qw0 + n, qi1 = qw0 + 32 + n;     // this lane's row in block 0 / 1
-  const int qpos0 = pos_of(a.qp, min(qi0, qlast));
-  const int qpos1 = pos_of(a.qp, min(qi1, qlast));
-  const int wave_qmin = pos_of(a.qp, min(qw0, qlast));
-  const int wg_qmax = pos_of(a.qp, min(it.q0 + a.q_tile - 1, qlast));
-  const int n_keys = a.causal ? allowed_prefix(a.kp, wg_qmax) : a.Ck;
-  const int n_kt = (n_keys + 63) / 64;
-  const float c = a.scale_log2;
 
   const __bf16* qb = reinterpret_cast<const __bf16*>(a.q) + it.b * a.q_bs + it.h * a.q_hs;
   const __bf16* kbp = reinterpret_cast<const __bf16*>(a.k) + it.b * a.k_bs + it.g * a.k_hs;
   const __bf16* vtb = reinterpret_cast<const __bf16*>(a.v) + it.b * a.v_bs + it.g * a.v_hs;
-
-  bf16x8 q0[KS], q1[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    if (qi0 < a.Cq)
-      q0[s] = *reinterpret_cast<const bf16x8*>(qb + (int64_t)qi0 * D + 16 * s + 8 * hh);
-    else
-      for (int j = 0; j < 8; ++j) q0[s][j] = (__bf16)0.f;
-    if (qi1 < a.Cq)
-      q1[s] = *reinterpret_cast<const bf16x8*>(qb + (int64_t)qi1 * D + 16 * s + 8 * hh);
-    else
-      for (int j = 0; j < 8; ++j) q1[s][j] = (__bf16)0.f;
-  }
-
-  floatx16 O0[DT], O1[DT];
-  float m0 = -INFINITY, l0 = 0.f, m1 = -INFINITY, l1 = 0.f;
 
   // Per-lane byte offsets of this wave's direct loads within a K tile and a
   // V^T tile (instruction j fills 1 KiB chunk wv + NW*j of the tile).
@@ -672,21 +788,56 @@ __global__ __launch_bounds__(kThreadsW64, 1) void attn_fwd_bf16_w64(const AttnAr
       if (wv + NW * j < VINS) load_lds16(base + voff[j], dst + j * NW * 1024);
   };
 
+  // Prologue loads, issued before anything else is worked out: the wave's
+  // query rows (whole-row loads into its staging area; the pad chunk repeats
+  // chunk 0, rows past the block repeat the last one), the first kKBufs K
+  // tiles of the block and V^T tile 0, of those the block has. Tiles the
+  // causal mask leaves unused are loaded all the same (they lie inside the
+  // block).
+  unsigned char* stage = Stage + wv * KBUF;
+  {
+    const unsigned char* qbytes = reinterpret_cast<const unsigned char*>(qb);
+#pragma unroll
+    for (int j = 0; j < KCPR; ++j) {
+      const int P = j * 64 + lane, cch = P % KCPR;
+      const int row = min(qw0 + P / KCPR, qlast);
+      load_lds16(qbytes + ((int64_t)row * D + (cch < CPR ? cch : 0) * 8) * 2, stage + j * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < w64::kKBufs; ++j)
+      if (64 * j < a.Ck) load_k(j, j);
+    if (a.Ck > 0) load_v(0, 0);  // an empty block has no V^T tile
+  }
+
   // Keys of the block each row may see (a prefix: positions increase along
   // the block); tiles before first_mask are fully visible to every row of
   // the wave, later ones are masked per lane.
+  const int qpos0 = pos_of(a.qp, min(qi0, qlast));
+  const int qpos1 = pos_of(a.qp, min(qi1, qlast));
+  const int wave_qmin = pos_of(a.qp, min(qw0, qlast));
+  const int wg_qmax = pos_of(a.qp, min(it.q0 + a.q_tile - 1, qlast));
+  const int n_keys = a.causal ? allowed_prefix(a.kp, wg_qmax) : a.Ck;
+  const int n_kt = (n_keys + 63) / 64;
   const int nal0 = a.causal ? allowed_prefix(a.kp, qpos0) : a.Ck;
   const int nal1 = a.causal ? allowed_prefix(a.kp, qpos1) : a.Ck;
   const int first_mask = a.causal ? allowed_prefix(a.kp, wave_qmin) / 64 : n_kt;
+  const float c = a.scale_log2;
 
+  floatx16 O0[DT], O1[DT];
+  float m0 = -INFINITY, l0 = 0.f, m1 = -INFINITY, l1 = 0.f;
+  lds_loads_barrier();  // also when no tile is needed: no load may outlive the workgroup
   if (n_kt > 0) {
-    // prologue: K0, K1, V0 in LDS, then the whole key loop in one asm block
-    load_k(0, 0);
-    if (n_kt > 1) load_k(1, 1);
-    load_v(0, 0);
-    lds_loads_barrier();
-    // wave-uniform values the loop keeps in SGPRs (the compiler cannot tell
-    // that pointers derived from the head tables are uniform)
+    bf16x8 q0[KS], q1[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      q0[s] = *reinterpret_cast<const bf16x8*>(stage + n * KROW + 32 * s + 16 * hh);
+      q1[s] = *reinterpret_cast<const bf16x8*>(stage + (n + 32) * KROW + 32 * s + 16 * hh);
+      if (qi0 >= a.Cq)
+        for (int j = 0; j < 8; ++j) q0[s][j] = (__bf16)0.f;
+      if (qi1 >= a.Cq)
+        for (int j = 0; j < 8; ++j) q1[s][j] = (__bf16)0.f;
+    }
+    // wave-uniform values the loop keeps in SGPRs
     auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
     auto uni_ptr = [](const void* p) {
       const uint64_t v = (uint64_t)(size_t)p;
@@ -699,8 +850,8 @@ __global__ __launch_bounds__(kThreadsW64, 1) void attn_fwd_bf16_w64(const AttnAr
                    uni((wv + NW * (VI - 1)) < VINS), c,
                    lds_addr(Ks) + kperm(n) * KROW + hh * 16, lds_addr(Vs) + n * VROW + hh * 16,
                    nal0 - 8 * hh, nal1 - 8 * hh, (unsigned)((lane ^ 32) * 4),
-                   uni_ptr(kbp + (int64_t)2 * 64 * D), uni_ptr(vtb + 64), koff, voff, q0, q1, O0,
-                   O1, m0, l0, m1, l1);
+                   uni_ptr(kbp + (int64_t)min(w64::kKBufs, n_kt - 1) * 64 * D), uni_ptr(vtb + 64), koff, voff,
+                   q0, q1, O0, O1, m0, l0, m1, l1);
   } else {
 #pragma unroll
     for (int T = 0; T < DT; ++T)
@@ -710,8 +861,18 @@ __global__ __launch_bounds__(kThreadsW64, 1) void attn_fwd_bf16_w64(const AttnAr
         O1[T][i] = 0.f;
       }
   }
-  epilogue<DT, true>(a, it, qi0, hh, O0, m0, l0);
-  epilogue<DT, true>(a, it, qi1, hh, O1, m1, l1);
+  const float ms[2] = {m0, m1}, ls[2] = {l0, l1};
+  if (a.fin_out) {
+    if (a.accumulate)
+      epilogue_w64<true, true>(a, it, qw0, lane, O0, O1, ms, ls, stage);
+    else
+      epilogue_w64<false, true>(a, it, qw0, lane, O0, O1, ms, ls, stage);
+  } else {
+    if (a.accumulate)
+      epilogue_w64<true, false>(a, it, qw0, lane, O0, O1, ms, ls, stage);
+    else
+      epilogue_w64<false, false>(a, it, qw0, lane, O0, O1, ms, ls, stage);
+  }
 }
 
 
@@ -894,7 +1055,7 @@ hipError_t launch_attn(const AttnArgs& a, ra_dtype dt, int D, hipStream_t s) {
     const bool w64 = D == 128 && a.Ck % 64 == 0 && (int64_t)D * a.v_ld * 2 <= (int64_t)UINT32_MAX;
     const void* fn = w64 ? (const void*)attn_fwd_bf16_w64
                          : (D == 128 ? (const void*)attn_fwd_bf16<128> : (const void*)attn_fwd_bf16<64>);
-    const size_t lds = bf16_lds_bytes(D);
+    const size_t lds = w64 ? w64_lds_bytes() : bf16_lds_bytes(D);
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     if (w64)

@@ -61,8 +61,8 @@ struct AttnArgs {
   int32_t n_qt;      // query tiles launched per (b, head)
   int32_t n_items;   // B * Hq * n_qt
   int32_t per_xcd;   // ceil(n_items / kXcds)
-  uint8_t head_order[kMaxHeads];  // query heads grouped by KV head
-  uint8_t kv_of[kMaxHeads];       // KV head of each query head
+  alignas(4) uint8_t head_order[kMaxHeads];  // query heads grouped by KV head
+  alignas(4) uint8_t kv_of[kMaxHeads];       // KV head of each query head
 };
 
 hipError_t launch_attn(const AttnArgs& a, ra_dtype dt, int D, hipStream_t s);

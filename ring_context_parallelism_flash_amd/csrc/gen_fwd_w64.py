@@ -8,9 +8,18 @@ operand read from LDS feeds the MFMA of both blocks) with the softmax of
 block 1 of tile t between them; phase B issues the 32 P*V MFMAs of tile t
 (each V^T read feeds both blocks) with the softmax of block 0 of tile t+1
 between them. Every MFMA is followed by part of one step's vector work, so
-the wave's vector and LDS instructions issue while its matrix pipe runs.
-One barrier per tile publishes the next tiles' direct global->LDS loads
-(two LDS buffers each for K and V^T).
+the wave's vector and LDS instructions issue while its matrix pipe runs, and
+the last pairs of each phase already issue the first operand reads of the
+next one, so no phase starts by waiting for LDS.
+
+Tiles reach LDS through direct global->LDS loads: K tiles rotate through
+three buffers, V^T tiles through two. One barrier per iteration publishes
+the loads of the previous iteration and frees the buffers it refills; the
+ten loads of a wave (K tile t+3, V^T tile t+1) are then spread over the
+first ten MFMA pairs of phase A, where their issue overlaps the matrix pipe
+instead of stalling all four waves at once behind the barrier. A K tile
+past the last one repeats the last one (into a buffer nobody reads), so no
+wave branches around its loads.
 
 Online softmax with a lazy reference (the pages' running max / sum /
 rescaled output, "Algorithmic Mechanics"): probabilities are taken against a
@@ -28,8 +37,8 @@ Register plan (one wave per SIMD: 256 VGPRs + 256 AGPRs):
   a[128:159] Q of block 0, eight k-steps of 4 registers (bf16x8)
   a[160:191] Q of block 1
   v52 m0, v53 l0, v54 m1, v55 l1: reference and running sum of each block
-  v56 row sum, v57 LDS address, v58 minus the exponent offset, v[60:63]
-  temporaries
+  v56 row sum, v57 K read address, v58 minus the exponent offset,
+  v59 V^T read address, v[60:63] temporaries
   v[64:79]   LDS operand ring, four 16-byte reads in flight
   v[80:95]   P0a  bf16 probabilities of block 0 (tile parity 0)
   v[96:111]  P0b  (tile parity 1)
@@ -42,12 +51,15 @@ The compiler keeps everything else (the load offsets, the lane addresses,
 its own values) in v[0:51], a[192:255] and the other SGPRs.
 
 Hazards the statement respects by construction: a transcendental result is
-read no earlier than the second instruction after it; every phase ends with
-24 wait states (s_nop 7 x 3) so no later vector instruction reads an MFMA
-result early; an MFMA accumulator is reused no sooner than three MFMAs
+read no earlier than the second instruction after it; an MFMA result is
+read by a vector instruction only after at least 24 wait states (phase A's
+scores are first read two MFMA pairs into phase B, or by the out-of-line
+mask, which starts with s_nop 7 x 3; O is read only by the out-of-line slow
+path, which starts the same way, and after the statement, which ends with
+the same pad); an MFMA accumulator is reused no sooner than three MFMAs
 later; an M0 write is followed by one wait state before the LDS-DMA load
-that reads it; LDS reads wait on counted lgkmcnt with no other LGKM
-operation in flight (every phase starts by draining the counter).
+that reads it; LDS reads wait on counted lgkmcnt and return in order, with
+no other LGKM operation in flight on the common path.
 
 Run: python gen_fwd_w64.py  (writes the header next to this file)
 """
@@ -58,6 +70,8 @@ KS = D // 16           # score k-steps
 DT = D // 32           # output d tiles
 KROW = (D // 8 + 1) * 16   # padded K row in LDS, bytes
 VROW = 9 * 16              # padded V^T row in LDS, bytes
+KBUF, VBUF = 64 * KROW, D * VROW   # bytes per K / V^T tile buffer
+KBUFS = 3              # K tile buffers (V^T: two)
 N = 16                 # operand reads per phase (2*KS score reads, 4*DT P*V reads)
 PF = 4                 # reads in flight
 assert 2 * KS == N and 4 * DT == N
@@ -68,12 +82,13 @@ O_ = (0, 64)                     # O of block 0 / 1 (AGPR base)
 Q_ = (128, 160)                  # Q of block 0 / 1 (AGPR base)
 M_ = (52, 54)
 L_ = (53, 55)
-V_RS, V_ADDR, V_NMOFF, V_PERM = 56, 57, 58, 59
+V_RS, V_KADDR, V_NMOFF, V_VADDR = 56, 57, 58, 59
 T0, T1, T2, T3 = 60, 61, 62, 63
 RING = 64
 P0A, P0B, P1 = 80, 96, 112
 SA0, SA1, SB0, SB1 = 128, 160, 192, 224
-PAD = ["s_nop 7", "s_nop 7", "s_nop 7"]
+PAD = ["s_nop 7", "s_nop 7", "s_nop 7"]   # 24 wait states after an MFMA
+ZERO_SUMS = [f"v_mov_b32 v{T2}, 0", f"v_mov_b32 v{T3}, 0"]
 KG_S, VG_S = 80, 82              # SGPR pairs of the global K / V^T tile addresses
 
 
@@ -104,7 +119,8 @@ def nmoff_lines(m):
 
 
 def softmax_pair(i, S, P):
-    """Vector work for scores e = 2i, 2i+1: two halves (after each MFMA)."""
+    """Vector work for scores e = 2i, 2i+1 in two parts, one after each MFMA
+    of a pair: the exponentials, then the row sums and the bf16 packing."""
     s0 = elem(S, 2 * i)
     u, j = (2 * i) >> 3, (2 * i) & 7
     first = [f"v_fma_f32 v{T0}, v{s0}, %[c], v{V_NMOFF}",
@@ -117,54 +133,65 @@ def softmax_pair(i, S, P):
     return first, second
 
 
-def score_phase(S0, S1, work):
-    """Score MFMAs of a tile into (S0, S1) from the K tile at v57; with
-    `work` = (Scur, P, block) the softmax of Scur between them."""
-    off = lambda i: (i % 2) * 32 * KROW + (i // 2) * 32
-    lines = ["s_waitcnt lgkmcnt(0)"]
+def score_off(i):
+    return (i % 2) * 32 * KROW + (i // 2) * 32
+
+
+def pv_off(i):
+    return (i % DT) * 32 * VROW + (i // DT) * 32
+
+
+def phase(mfmas, addr, off, work, pre_in=False, nxt=None, extra=()):
+    """16 MFMA pairs; pair i reads one LDS operand (address register `addr`,
+    byte offset off(i)) through the read ring. `work` = (S, P, block): the
+    softmax of S between the MFMAs. pre_in: the first PF reads were issued
+    by the previous phase; nxt = (addr, off): issue the first PF reads of
+    the next phase in the last PF pairs (LDS reads return in order, so every
+    pair waits until at most PF - 1 reads are outstanding); extra[i]: more
+    instructions after pair i."""
+    lines = [] if pre_in else ["s_waitcnt lgkmcnt(0)"]
     if work:
-        lines += nmoff_lines(M_[work[2]]) + [f"v_mov_b32 v{T2}, 0", f"v_mov_b32 v{T3}, 0"]
-    for i in range(PF):
-        lines.append(f"ds_read_b128 {ring(i)}, v{V_ADDR} offset:{off(i)}")
+        lines += nmoff_lines(M_[work[2]]) + ZERO_SUMS
+    if not pre_in:
+        for i in range(PF):
+            lines.append(f"ds_read_b128 {ring(i)}, v{addr} offset:{off(i)}")
     for i in range(N):
+        lines.append(f"s_waitcnt lgkmcnt({PF - 1 if nxt else min(PF - 1, N - 1 - i)})")
+        first, second = softmax_pair(i, work[0], work[1]) if work else ([], [])
+        ma, mb = mfmas(i)
+        lines += [ma] + first + [mb]
+        if i + PF < N:
+            lines.append(f"ds_read_b128 {ring(i)}, v{addr} offset:{off(i + PF)}")
+        elif nxt:
+            lines.append(f"ds_read_b128 {ring(i)}, v{nxt[0]} offset:{nxt[1](i + PF - N)}")
+        lines += second
+        if i < len(extra):
+            lines += extra[i]
+    return lines
+
+
+def score_mfmas(S0, S1):
+    """Pair i: half h = i % 2 (32 keys) at k-step s = i // 2, block 0 then 1."""
+    def f(i):
         h, s = i % 2, i // 2
-        lines.append(f"s_waitcnt lgkmcnt({min(PF - 1, N - 1 - i)})")
         c0 = "0" if s == 0 else vr(S0 + 16 * h, 16)
         c1 = "0" if s == 0 else vr(S1 + 16 * h, 16)
-        first, second = softmax_pair(i, work[0], work[1]) if work else ([], [])
-        lines.append(f"v_mfma_f32_32x32x16_bf16 {vr(S0 + 16 * h, 16)}, {ring(i)}, "
-                     f"{ar(Q_[0] + 4 * s, 4)}, {c0}")
-        lines += first
-        lines.append(f"v_mfma_f32_32x32x16_bf16 {vr(S1 + 16 * h, 16)}, {ring(i)}, "
-                     f"{ar(Q_[1] + 4 * s, 4)}, {c1}")
-        if i + PF < N:
-            lines.append(f"ds_read_b128 {ring(i)}, v{V_ADDR} offset:{off(i + PF)}")
-        lines += second
-    return lines + PAD
+        return (f"v_mfma_f32_32x32x16_bf16 {vr(S0 + 16 * h, 16)}, {ring(i)}, "
+                f"{ar(Q_[0] + 4 * s, 4)}, {c0}",
+                f"v_mfma_f32_32x32x16_bf16 {vr(S1 + 16 * h, 16)}, {ring(i)}, "
+                f"{ar(Q_[1] + 4 * s, 4)}, {c1}")
+    return f
 
 
-def pv_phase(P0, P1_, work):
-    """O += V^T P for both blocks from the V^T tile at v57; with `work` =
-    (Snext, Pnext, block) the softmax of Snext between the MFMAs."""
-    off = lambda i: (i % DT) * 32 * VROW + (i // DT) * 32
-    lines = ["s_waitcnt lgkmcnt(0)"]
-    if work:
-        lines += nmoff_lines(M_[work[2]]) + [f"v_mov_b32 v{T2}, 0", f"v_mov_b32 v{T3}, 0"]
-    for i in range(PF):
-        lines.append(f"ds_read_b128 {ring(i)}, v{V_ADDR} offset:{off(i)}")
-    for i in range(N):
+def pv_mfmas(P0, P1_):
+    """Pair i: d tile T = i % DT, probability k-step u = i // DT."""
+    def f(i):
         u, T = i // DT, i % DT
-        lines.append(f"s_waitcnt lgkmcnt({min(PF - 1, N - 1 - i)})")
-        first, second = softmax_pair(i, work[0], work[1]) if work else ([], [])
-        lines.append(f"v_mfma_f32_32x32x16_bf16 {ar(O_[0] + 16 * T, 16)}, {ring(i)}, "
-                     f"{vr(P0 + 4 * u, 4)}, {ar(O_[0] + 16 * T, 16)}")
-        lines += first
-        lines.append(f"v_mfma_f32_32x32x16_bf16 {ar(O_[1] + 16 * T, 16)}, {ring(i)}, "
-                     f"{vr(P1_ + 4 * u, 4)}, {ar(O_[1] + 16 * T, 16)}")
-        if i + PF < N:
-            lines.append(f"ds_read_b128 {ring(i)}, v{V_ADDR} offset:{off(i + PF)}")
-        lines += second
-    return lines + PAD
+        return (f"v_mfma_f32_32x32x16_bf16 {ar(O_[0] + 16 * T, 16)}, {ring(i)}, "
+                f"{vr(P0 + 4 * u, 4)}, {ar(O_[0] + 16 * T, 16)}",
+                f"v_mfma_f32_32x32x16_bf16 {ar(O_[1] + 16 * T, 16)}, {ring(i)}, "
+                f"{vr(P1_ + 4 * u, 4)}, {ar(O_[1] + 16 * T, 16)}")
+    return f
 
 
 LOOP_CLOBBER = ([f'"v{r}"' for r in range(V_RS, 256)] +
@@ -189,8 +216,8 @@ class Loop:
     def place(self, name):
         self.lines.append(f"{self.lab(name)}:")
 
-    def set_addr(self, reg_operand, const):
-        self.lines.append(f"v_add_u32 v{V_ADDR}, {const}, {reg_operand}")
+    def set_addr(self, reg, reg_operand, const):
+        self.lines.append(f"v_add_u32 v{reg}, {const}, {reg_operand}")
 
     def check_and_slow(self, b, S, P, site):
         """Row sum check of block b; the fast path adds it to l, the slow
@@ -204,7 +231,7 @@ class Loop:
                   f"s_cbranch_scc0 {self.lab('slow' + site)}",
                   f"v_add_f32 v{l}, v{l}, v{V_RS}"])
         self.place("cont" + site)
-        self.ool += [f"{self.lab('slow' + site)}:"]
+        self.ool += [f"{self.lab('slow' + site)}:"] + PAD
         self.ool += slow_path_body(S, P, b, self.lab("keep" + site))
         self.ool += [f"s_branch {self.lab('cont' + site)}"]
 
@@ -213,7 +240,7 @@ class Loop:
         out of line; `cond` = instructions leaving SCC = 1 when it is needed."""
         self.add(cond + [f"s_cbranch_scc1 {self.lab('mask' + site)}"])
         self.place("mback" + site)
-        body = [f"{self.lab('mask' + site)}:",
+        body = [f"{self.lab('mask' + site)}:"] + PAD + [
                 f"s_lshl_b32 %[sx], {kt_sgpr}, 6",
                 f"v_subrev_u32 v{T1}, %[sx], %[nal0]",
                 f"v_subrev_u32 v{T2}, %[sx], %[nal1]",
@@ -231,7 +258,9 @@ class Loop:
 def slow_path_body(S, P, b, keep_label):
     """Row max of S; where it exceeds the reference, O and l of block b are
     scaled by exp2((m - m_new) c) and m moves up; then P and the row sum are
-    redone from S against the reference and l += sum."""
+    redone from S against the reference and l += sum. The O rescale uses P
+    (about to be redone) as temporaries: the operand ring may hold reads of
+    the next phase."""
     m, l, Ob = M_[b], L_[b], O_[b]
     regs = [elem(S, e) for e in range(32)]
     lines = [f"v_max_f32 v{T0}, v{regs[0]}, v{regs[1]}",
@@ -255,12 +284,12 @@ def slow_path_body(S, P, b, keep_label):
               f"v_mov_b32 v{m}, v{T1}",
               f"v_mul_f32 v{l}, v{l}, v{T2}"]
     for r in range(64):
-        t = RING + (r % 8)
+        t = P + (r % 8)
         lines += [f"v_accvgpr_read_b32 v{t}, a{Ob + r}",
                   f"v_mul_f32 v{t}, v{t}, v{T2}",
                   f"v_accvgpr_write_b32 a{Ob + r}, v{t}"]
     lines.append(f"{keep_label}:")
-    lines += nmoff_lines(m) + [f"v_mov_b32 v{T2}, 0", f"v_mov_b32 v{T3}, 0"]
+    lines += nmoff_lines(m) + ZERO_SUMS
     for i in range(16):
         first, second = softmax_pair(i, S, P)
         lines += first + second
@@ -268,48 +297,54 @@ def slow_path_body(S, P, b, keep_label):
     return lines
 
 
+def rotate(sreg):
+    """Next K buffer offset: + KBUF, wrapping after the last buffer."""
+    return [f"s_add_u32 {sreg}, {sreg}, {KBUF}", f"s_cmp_eq_u32 {sreg}, {KBUFS * KBUF}",
+            f"s_cselect_b32 {sreg}, 0, {sreg}"]
+
+
 def loads(L, p):
-    """Barrier, then K(t+2) (if it exists) into K buffer t&1 = p and V(t+1)
-    into V buffer 1-p; advance the global tile addresses. A wave's fifth
-    load of a tile runs under %[x5k] / %[x5v] as its exec mask (all lanes or
-    none), so no wave branches around it."""
-    KBUF, VBUF = 64 * KROW, D * VROW
-    L.add(["s_waitcnt vmcnt(0)", "s_barrier",
-           "s_add_u32 %[sx], %[t], 2",
-           "s_cmp_lt_u32 %[sx], %[nkt]",
-           f"s_cbranch_scc0 {L.lab(f'nok{p}')}"])
+    """Barrier, then the tile loads of iteration t (parity p) as groups for
+    the MFMA pairs of phase A: K(min(t+3, n_kt-1)) into K buffer %[kw] and
+    V(t+1) into V^T buffer 1-p; the global tile addresses advance after them.
+    A wave's fifth load of a tile runs under %[x5k] / %[x5v] as its exec mask
+    (all lanes or none)."""
+    L.add(["s_waitcnt vmcnt(0)", "s_barrier", "s_add_u32 %[sx], %[kdst], %[kw]"] + rotate("%[kw]"))
+    groups = []
     for j in range(4):
-        L.add([f"s_add_u32 m0, %[kdst], {p * KBUF + j * 4096}", "s_nop 0",
-               f"global_load_lds_dwordx4 %[ko{j}], %[kg]"])
-    L.add([f"s_add_u32 m0, %[kdst], {p * KBUF + 16384}",
-           "s_mov_b64 exec, %[x5k]",
-           "global_load_lds_dwordx4 %[ko4], %[kg]",
-           "s_mov_b64 exec, -1"])
-    L.place(f"nok{p}")
+        groups.append([f"s_add_u32 m0, %[sx], {j * 4096}", "s_nop 0",
+                       f"global_load_lds_dwordx4 %[ko{j}], %[kg]"])
+    groups.append([f"s_add_u32 m0, %[sx], 16384", "s_mov_b64 exec, %[x5k]",
+                   "global_load_lds_dwordx4 %[ko4], %[kg]", "s_mov_b64 exec, -1"])
     for j in range(4):
-        L.add([f"s_add_u32 m0, %[vdst], {(1 - p) * VBUF + j * 4096}", "s_nop 0",
-               f"global_load_lds_dwordx4 %[vo{j}], %[vg]"])
-    L.add([f"s_add_u32 m0, %[vdst], {(1 - p) * VBUF + 16384}",
-           "s_mov_b64 exec, %[x5v]",
-           "global_load_lds_dwordx4 %[vo4], %[vg]",
-           "s_mov_b64 exec, -1"])
-    L.add([f"s_add_u32 s{KG_S}, s{KG_S}, {64 * D * 2}", f"s_addc_u32 s{KG_S + 1}, s{KG_S + 1}, 0",
-           f"s_add_u32 s{VG_S}, s{VG_S}, 128", f"s_addc_u32 s{VG_S + 1}, s{VG_S + 1}, 0"])
+        groups.append([f"s_add_u32 m0, %[vdst], {(1 - p) * VBUF + j * 4096}", "s_nop 0",
+                       f"global_load_lds_dwordx4 %[vo{j}], %[vg]"])
+    groups.append([f"s_add_u32 m0, %[vdst], {(1 - p) * VBUF + 16384}",
+                   "s_mov_b64 exec, %[x5v]",
+                   "global_load_lds_dwordx4 %[vo4], %[vg]",
+                   "s_mov_b64 exec, -1",
+                   # the next K tile, t+4, if it exists; else the last one again
+                   f"s_add_u32 %[sx], %[t], {KBUFS + 1}", "s_cmp_lt_u32 %[sx], %[nkt]",
+                   f"s_cselect_b32 %[sx], {64 * D * 2}, 0",
+                   f"s_add_u32 s{KG_S}, s{KG_S}, %[sx]", f"s_addc_u32 s{KG_S + 1}, s{KG_S + 1}, 0",
+                   f"s_add_u32 s{VG_S}, s{VG_S}, 128", f"s_addc_u32 s{VG_S + 1}, s{VG_S + 1}, 0"])
+    return groups
 
 
 def loop_asm():
-    KBUF, VBUF = 64 * KROW, D * VROW
     S = {0: (SA0, SA1, SB0, SB1), 1: (SB0, SB1, SA0, SA1)}
     P0 = {0: (P0A, P0B), 1: (P0B, P0A)}
     L = Loop()
     L.add([f"v_accvgpr_write_b32 a{O_[b] + r}, 0" for b in (0, 1) for r in range(64)])
-    # prologue: scores of tile 0 (K0 in buffer 0), mask, block 0 softmax
-    L.set_addr("%[krb]", 0)
-    L.add(score_phase(SA0, SA1, None))
+    # prologue: scores of tile 0 (K buffer 0), whose last pairs start the
+    # reads of tile 1 (K buffer 1); mask; block 0 softmax
+    L.set_addr(V_KADDR, "%[krb]", 0)
+    L.set_addr(V_VADDR, "%[krb]", KBUF)
+    L.add(phase(score_mfmas(SA0, SA1), V_KADDR, score_off, None, nxt=(V_VADDR, score_off)) + PAD)
+    L.set_addr(V_KADDR, "%[krb]", KBUF)
     L.add(["s_mov_b32 %[t], 0"])
     L.mask(SA0, SA1, "%[t]", "pro", ["s_cmp_eq_u32 %[fmask], 0"])
-    L.add(["s_waitcnt lgkmcnt(0)"] + nmoff_lines(M_[0]) +
-          [f"v_mov_b32 v{T2}, 0", f"v_mov_b32 v{T3}, 0"])
+    L.add(nmoff_lines(M_[0]) + ZERO_SUMS)
     for i in range(16):
         first, second = softmax_pair(i, SA0, P0A)
         L.add(first + second)
@@ -322,13 +357,16 @@ def loop_asm():
         # t + 1 < n_kt, else the last tile of this parity
         L.add(["s_add_u32 %[t1], %[t], 1", "s_cmp_ge_u32 %[t1], %[nkt]",
                f"s_cbranch_scc1 {L.lab(f'last{p}')}"])
-        loads(L, p)
-        L.set_addr("%[krb]", (1 - p) * KBUF)
-        L.add(score_phase(n0, n1, (c1, P1, 1)))
+        groups = loads(L, p)
+        L.set_addr(V_VADDR, "%[vrb]", p * VBUF)
+        L.add(phase(score_mfmas(n0, n1), V_KADDR, score_off, (c1, P1, 1), pre_in=True,
+                    nxt=(V_VADDR, pv_off), extra=groups))
         L.check_and_slow(1, c1, P1, f"a{p}")
         L.mask(n0, n1, "%[t1]", f"{p}", ["s_cmp_ge_u32 %[t1], %[fmask]"])
-        L.set_addr("%[vrb]", p * VBUF)
-        L.add(pv_phase(pc, P1, (n0, pn, 0)))
+        # K tile t+2 (buffer %[kr]) for the reads started at the end of phase B
+        L.add([f"v_add_u32 v{V_KADDR}, %[kr], %[krb]"] + rotate("%[kr]"))
+        L.add(phase(pv_mfmas(pc, P1), V_VADDR, pv_off, (n0, pn, 0), pre_in=True,
+                    nxt=(V_KADDR, score_off)))
         L.check_and_slow(0, n0, pn, f"b{p}")
         L.add(["s_mov_b32 %[t], %[t1]"])
     L.add([f"s_branch {L.lab('loop')}"])
@@ -337,16 +375,17 @@ def loop_asm():
         pc, pn = P0[p]
         L.place(f"last{p}")
         L.add(["s_waitcnt vmcnt(0)", "s_barrier", "s_waitcnt lgkmcnt(0)"] + nmoff_lines(M_[1]) +
-              [f"v_mov_b32 v{T2}, 0", f"v_mov_b32 v{T3}, 0"])
+              ZERO_SUMS)
         for i in range(16):
             first, second = softmax_pair(i, c1, P1)
             L.add(first + second)
         L.check_and_slow(1, c1, P1, f"l{p}")
-        L.set_addr("%[vrb]", p * VBUF)
-        L.add(pv_phase(pc, P1, None))
+        L.set_addr(V_VADDR, "%[vrb]", p * VBUF)
+        L.add(phase(pv_mfmas(pc, P1), V_VADDR, pv_off, None))
         L.add([f"s_branch {L.lab('done')}"])
     L.add(L.ool)
     L.place("done")
+    L.add(PAD)
     return L.lines
 
 
@@ -363,13 +402,17 @@ namespace w64 {{
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// LDS buffers of K tiles the loop rotates through.
+constexpr int kKBufs = {KBUFS};
 ''']
     lines = loop_asm()
     outs = ([f'"={{{ar(O_[b] + 16 * T, 16)}}}"(o{b}[{T}])' for b in (0, 1) for T in range(DT)] +
             [f'"+{{v{M_[b]}}}"(m{b})' for b in (0, 1)] +
             [f'"+{{v{L_[b]}}}"(l{b})' for b in (0, 1)] +
             ['[t] "=&s"(t)', '[t1] "=&s"(t1)', '[sx] "=&s"(sx)', '[stmp] "=&s"(stmp)',
-             f'[kg] "+{{s[{KG_S}:{KG_S + 1}]}}"(kgv)', f'[vg] "+{{s[{VG_S}:{VG_S + 1}]}}"(vgv)'])
+             f'[kg] "+{{s[{KG_S}:{KG_S + 1}]}}"(kgv)', f'[vg] "+{{s[{VG_S}:{VG_S + 1}]}}"(vgv)',
+             '[kw] "+s"(kw)', '[kr] "+s"(kr)'])
     ins = (['[nkt] "s"(n_kt)', '[fmask] "s"(first_mask)', '[kdst] "s"(kdst)',
             '[vdst] "s"(vdst)', '[x5k] "s"(x5k)', '[x5v] "s"(x5v)', '[c] "s"(c)',
             '[krb] "v"(krb)', '[vrb] "v"(vrb)', '[nal0] "v"(nal0)', '[nal1] "v"(nal1)',
@@ -379,16 +422,17 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
            [f'"{{{ar(Q_[0] + 4 * s, 4)}}}"(q0[{s}])' for s in range(KS)] +
            [f'"{{{ar(Q_[1] + 4 * s, 4)}}}"(q1[{s}])' for s in range(KS)])
     body = "\n".join(f'      "{ln}\\n\\t"' for ln in lines)
-    out.append(f"""// The key-tile loop of one wave: n_kt >= 1 tiles; tiles 0 and 1 of K and
-// tile 0 of V^T are already in LDS (buffers 0, 1 and 0). krb / vrb: this
-// lane's operand read address in K buffer 0 / V^T buffer 0; kdst / vdst:
-// this wave's first load destination in K / V^T buffer 0; kg / vg: global
-// address of K tile 2 / V^T tile 1 (advanced by the loop); koff / voff: the
-// lane's load offsets; k5 / v5: whether the wave issues a fifth load per
-// tile; first_mask: first tile needing the causal mask; nal0 / nal1: keys
-// visible to the lane's row of block 0 / 1, minus 8 for the upper half of
-// the wave; perm: byte address of lane ^ 32. Returns O, m and l of both
-// blocks (O^T layout, exponent reference m, sum l).
+    out.append(f"""// The key-tile loop of one wave: n_kt >= 1 tiles; K tiles 0 .. kKBufs-1
+// (those the block has) are in K buffers 0 .. kKBufs-1 and V^T tile 0 in
+// V^T buffer 0. krb / vrb: this lane's operand read address in K buffer 0 /
+// V^T buffer 0; kdst / vdst: this wave's first load destination in K / V^T
+// buffer 0; kg: global address of K tile min(kKBufs, n_kt - 1), vg: of V^T
+// tile 1 (both advanced by the loop); koff / voff: the lane's load offsets;
+// k5 / v5: whether the wave issues a fifth load per tile; first_mask: first
+// tile needing the causal mask; nal0 / nal1: keys visible to the lane's row
+// of block 0 / 1, minus 8 for the upper half of the wave; perm: byte address
+// of lane ^ 32. Returns O, m and l of both blocks (O^T layout, exponent
+// reference m, sum l).
 __device__ __forceinline__ void attn_loop(
     int n_kt, int first_mask, unsigned kdst, unsigned vdst, int k5, int v5, float c,
     unsigned krb, unsigned vrb, int nal0, int nal1, unsigned perm, const void* kg,
@@ -399,6 +443,7 @@ __device__ __forceinline__ void attn_loop(
   long long stmp;
   const long long x5k = k5 ? -1ll : 0ll, x5v = v5 ? -1ll : 0ll;
   unsigned long long kgv = (unsigned long long)(size_t)kg, vgv = (unsigned long long)(size_t)vg;
+  unsigned kw = 0, kr = {(KBUFS - 1) * KBUF};  // K buffer offsets: next load, next prefetch
   asm volatile(
 {body}
       : {", ".join(outs)}
