@@ -198,6 +198,7 @@ __device__ __forceinline__ void epilogue_w64(const AttnArgs& a, const WorkItem& 
   const int n = lane & 31, hh = lane >> 5;
   if (qw0 >= a.Cq) return;  // the whole wave lies past the block
   const int rmax = a.Cq - 1 - qw0;  // last row of the wave inside the block
+  const bool full = rmax >= 63;
   // wave-uniform bases at the wave's first row; per-lane 32-bit byte offsets
   unsigned char* ro = reinterpret_cast<unsigned char*>(a.run_out + it.b * a.ro_bs + it.h * a.ro_hs +
                                                        (int64_t)qw0 * D);
@@ -273,13 +274,17 @@ __device__ __forceinline__ void epilogue_w64(const AttnArgs& a, const WorkItem& 
         const uint32_t e = (uint32_t)((32 * b + 2 * i + hh) * D + 4 * n);  // element offset
         float4 r = rs[k];
         if (ACC) {
-          const bool use_old = fs[k].x != 0.f;
-          r.x = use_old ? fmaf(old[b][i].x, fs[k].x, r.x) : r.x;
-          r.y = use_old ? fmaf(old[b][i].y, fs[k].x, r.y) : r.y;
-          r.z = use_old ? fmaf(old[b][i].z, fs[k].x, r.z) : r.z;
-          r.w = use_old ? fmaf(old[b][i].w, fs[k].x, r.w) : r.w;
+          // rows left as they are (no key of the block) store their old value
+          const bool use_old = fs[k].x != 0.f, keep = fs[k].y == 0.f;
+          r.x = keep ? old[b][i].x : use_old ? fmaf(old[b][i].x, fs[k].x, r.x) : r.x;
+          r.y = keep ? old[b][i].y : use_old ? fmaf(old[b][i].y, fs[k].x, r.y) : r.y;
+          r.z = keep ? old[b][i].z : use_old ? fmaf(old[b][i].z, fs[k].x, r.z) : r.z;
+          r.w = keep ? old[b][i].w : use_old ? fmaf(old[b][i].w, fs[k].x, r.w) : r.w;
         }
-        if (fs[k].y != 0.f) {
+        // A wave whose 64 rows all lie in the block stores every row without
+        // a branch; in the last, partial wave of a block rows past its end
+        // are skipped.
+        if (full || 32 * b + 2 * i + hh <= rmax) {
           if (FIN) {
             bf16x4 pk;
             pk[0] = (__bf16)r.x;
@@ -757,6 +762,10 @@ __global__ __launch_bounds__(kThreadsW64, 1) void attn_fwd_bf16_w64(const AttnAr
 
   // Per-lane byte offsets of this wave's direct loads within a K tile and a
   // V^T tile (instruction j fills 1 KiB chunk wv + NW*j of the tile).
+  // The tail chunks of a tile (K: 17 KiB, V^T: 18 KiB) go to different waves
+  // (K to wave 0, V^T to waves 2 and 3), so no wave issues more than nine
+  // loads per tile: V^T chunks are dealt starting from wave 2.
+  const int vw = (wv + 2) % NW;
   uint32_t koff[KI], voff[VI];
 #pragma unroll
   for (int j = 0; j < KI; ++j) {
@@ -766,7 +775,7 @@ __global__ __launch_bounds__(kThreadsW64, 1) void attn_fwd_bf16_w64(const AttnAr
   }
 #pragma unroll
   for (int j = 0; j < VI; ++j) {
-    const int P = (wv + NW * j) * 64 + lane;
+    const int P = (vw + NW * j) * 64 + lane;
     const int cch = P % 9;
     voff[j] = ((uint32_t)(P / 9) * (uint32_t)a.v_ld + (uint32_t)(cch < 8 ? cch : 0) * 8u) * 2u;
   }
@@ -782,10 +791,10 @@ __global__ __launch_bounds__(kThreadsW64, 1) void attn_fwd_bf16_w64(const AttnAr
   };
   auto load_v = [&](int kt, int buf) {
     const unsigned char* base = reinterpret_cast<const unsigned char*>(vtb + kt * 64);
-    unsigned char* dst = Vs + buf * VBUF + wv * 1024;
+    unsigned char* dst = Vs + buf * VBUF + vw * 1024;
 #pragma unroll
     for (int j = 0; j < VI; ++j)
-      if (wv + NW * j < VINS) load_lds16(base + voff[j], dst + j * NW * 1024);
+      if (vw + NW * j < VINS) load_lds16(base + voff[j], dst + j * NW * 1024);
   };
 
   // Prologue loads, issued before anything else is worked out: the wave's
@@ -846,8 +855,8 @@ __global__ __launch_bounds__(kThreadsW64, 1) void attn_fwd_bf16_w64(const AttnAr
       return (const void*)(size_t)(((uint64_t)hi << 32) | lo);
     };
     w64::attn_loop(uni(n_kt), uni(first_mask), uni(lds_addr(Ks) + wv * 1024),
-                   uni(lds_addr(Vs) + wv * 1024), uni((wv + NW * (KI - 1)) < KINS),
-                   uni((wv + NW * (VI - 1)) < VINS), c,
+                   uni(lds_addr(Vs) + vw * 1024), uni((wv + NW * (KI - 1)) < KINS),
+                   uni((vw + NW * (VI - 1)) < VINS), c,
                    lds_addr(Ks) + kperm(n) * KROW + hh * 16, lds_addr(Vs) + n * VROW + hh * 16,
                    nal0 - 8 * hh, nal1 - 8 * hh, (unsigned)((lane ^ 32) * 4),
                    uni_ptr(kbp + (int64_t)min(w64::kKBufs, n_kt - 1) * 64 * D), uni_ptr(vtb + 64), koff, voff,
