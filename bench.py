@@ -83,6 +83,18 @@ def measured_traffic(workload_name: str, summary=PMC_SUMMARY, sources=KERNEL_SOU
         return None, f"counter summary unreadable: {e}"
 
 
+def fwd_kernel_name(w, block_keys=None) -> str:
+    """The forward kernel a launch on key blocks of `block_keys` keys (default:
+    the zigzag half chunk S / 2N) runs: D = 128 bf16 blocks of whole 64-key
+    tiles run the one-wave-per-SIMD kernel."""
+    if w.dtype != "bf16":
+        return f"attn_fwd_f32<{w.D}>"
+    ck = w.S // (2 * w.N) if block_keys is None else block_keys
+    if w.D == 128 and ck % 64 == 0:
+        return "attn_fwd_bf16_w64"
+    return f"attn_fwd_bf16<{w.D}>"
+
+
 def useful_pairs(S: int, causal: bool) -> int:
     """Allowed (query, key) pairs of one head over the whole sequence."""
     return S * (S + 1) // 2 if causal else S * S
@@ -398,7 +410,7 @@ def bench_ulysses(args, w, q_cpu, k_cpu, v_cpu, dev) -> int:
         "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "useful_flops_per_step": flops_step,
         "roofline": {
-            "kernel": f"attn_fwd_bf16<{w.D}>",
+            "kernel": fwd_kernel_name(w, w.S),
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": round(PEAK_BF16_TFLOPS, 1),
@@ -494,7 +506,7 @@ def bench_usp(args, w, q_cpu, k_cpu, v_cpu, dev) -> int:
         "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "useful_flops_per_step": flops_step,
         "roofline": {
-            "kernel": f"attn_fwd_bf16<{w.D}>",
+            "kernel": fwd_kernel_name(w, w.S // (2 * P_r)),
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": round(PEAK_BF16_TFLOPS, 1),
@@ -645,7 +657,7 @@ def main(argv=None) -> int:
         "pct_peak": round(100.0 * value / peak, 2),
         "useful_flops_per_step": flops_step,
         "roofline": {
-            "kernel": f"attn_fwd_{'bf16' if bf16 else 'f32'}<{w.D}>",
+            "kernel": fwd_kernel_name(w),
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": round(peak, 1),

@@ -418,7 +418,8 @@ ra_status ra_usp_sim_fwd(const void* q, const void* k, const void* v, void* out,
  * scores and the four gradient products), and clears the record. Up to
  * 65536 launches are recorded between reads; later ones are
  * not timed (launches still counts them; total_ms then covers only the
- * first 65536). Enabling creates the events once per process.
+ * first 65536). Enabling creates the events of the first 4096 launches
+ * (once per process; later ones are created as launches need them).
  * ---------------------------------------------------------------------- */
 ra_status ra_kernel_timing_enable(int32_t enable);
 ra_status ra_kernel_timing_read(double* total_ms, int64_t* launches, double* useful_flops);

@@ -126,6 +126,7 @@ struct Timing {
 };
 Timing g_timing;
 constexpr size_t kMaxTimed = 65536;
+constexpr size_t kPreTimed = 4096;  // launch event pairs created when timing is enabled
 
 // Launch an attention kernel (forward or backward), bracketed by timing events
 // when enabled; `flops` is its useful work.
@@ -1120,6 +1121,16 @@ ra_status ra_kernel_timing_enable(int32_t enable) {
   g_err[0] = 0;
   std::lock_guard<std::mutex> lk(g_timing.mu);
   g_timing.enabled = enable != 0;
+  // the events of the first kPreTimed launches exist before any is recorded,
+  // so a timed region does not pay for creating them (with no device there is
+  // nothing to time: they are created when a launch needs them)
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess) ndev = 0;
+  while (g_timing.enabled && ndev > 0 && g_timing.ev.size() < 2 * kPreTimed) {
+    hipEvent_t e;
+    RA_HIP(hipEventCreate(&e));
+    g_timing.ev.push_back(e);
+  }
   return RA_OK;
 }
 
