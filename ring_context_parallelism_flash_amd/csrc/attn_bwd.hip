@@ -30,6 +30,7 @@
 #include <vector>
 
 #include "attn_common.h"
+#include "attn_bwd_dq_w64_loop.h"
 
 namespace ra {
 namespace {
@@ -303,6 +304,18 @@ struct NoWork {
   template <int I>
   __device__ __forceinline__ void operator()(std::integral_constant<int, I>) {}
 };
+// A stream's per-MFMA work followed by one tile load (loads(step) decides
+// which, if any).
+template <class W, class LD>
+struct WithLoads {
+  W& work;
+  LD& loads;
+  template <int I>
+  __device__ __forceinline__ void operator()(std::integral_constant<int, I> i) {
+    work(i);
+    loads(i);
+  }
+};
 
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup = 4 waves x 32 keys of one KV head, one wave per SIMD.
@@ -447,7 +460,22 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
     return lds_addr(lds + ((jn >> 1) & 1) * ROWS_BUF) + rbase + (jn & 1) * 32 * L::ROW;
   };
 
-  bool issued = false;  // this wave issued a load batch at the start of the previous iteration
+  // Per-lane parts of this wave's direct loads (chunk ins = wv + 4j of a
+  // tile): row and byte offset within a 64-row tile, byte offset within a
+  // transposed tile. The loads of an iteration go out one per MFMA of its
+  // S / dP stream rather than in a burst after the barrier, where they would
+  // stall all four waves at once.
+  constexpr int LJ = (L::TINS + 3) / 4;  // most chunk loads of one tile per wave
+  static_assert(L::RINS <= L::TINS, "row tiles take no more loads than transposed ones");
+  uint32_t rrow[LJ], rch[LJ], tofs[LJ];
+#pragma unroll
+  for (int jj = 0; jj < LJ; ++jj) {
+    const int P = (wv + 4 * jj) * 64 + lane;
+    const int cr = P % L::RCPR, ct = P % 9;
+    rrow[jj] = (uint32_t)(P / L::RCPR);
+    rch[jj] = (uint32_t)(cr < L::CPR ? cr : 0) * 16u;
+    tofs[jj] = ((uint32_t)(P / 9) * (uint32_t)a.Cqp + (uint32_t)(ct < 8 ? ct : 0) * 8u) * 2u;
+  }
   // lse2 / delta of sub-tile j (8 LDS reads into lx, dx). Sub-tiles 2m and
   // 2m+1 read the same Q^T / dO^T tile, published by the barrier of
   // iteration 2m and not overwritten before iteration 2m+2: the reads of the
@@ -467,28 +495,61 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
     dx[3] = ds_read_f4<OFF_DL + 80>(la);
   };
   f32x4 lx[4], dx[4];
-  auto iter = [&](auto mask, int j, const floatx16& Sc, const floatx16& dPc, floatx16& Sn,
-                  floatx16& dPn) {
+  auto iter = [&](auto mask, auto odd, int j, const floatx16& Sc, const floatx16& dPc,
+                  floatx16& Sn, floatx16& dPn) {
+    constexpr bool ODD = decltype(odd)::value;
     if (j > 0) {
       // the batch of two iterations ago has landed in this wave ...
-      if (issued)
-        vm_wait<VM_MIN>();
-      else
-        vm_wait<0>();
+      vm_wait<VM_MIN>();
       // ... and in every wave; every wave is done with iteration j-1 (its LDS
       // reads were all waited for)
       workgroup_barrier();
     }
-    issued = false;
-    if (j & 1) {
-      if ((j >> 1) + 2 < NT) {
-        load_rows((j >> 1) + 2);
-        issued = true;
-      }
-    } else if (j >= 2 && (j >> 1) + 1 < NT) {
-      load_trans((j >> 1) + 1);
-      issued = true;
+    // This iteration's loads: an odd one the Q / dO rows of stream tile
+    // (j >> 1) + 2, an even one the Q^T / dO^T tile (j >> 1) + 1 with its
+    // lse2 / delta, each into the buffer that tile will use; a tile past the
+    // stream's end repeats the last one (into a buffer nobody reads before it
+    // is loaded again), so every iteration issues the same loads.
+    const int Tu = ODD ? (j >> 1) + 2 : (j >> 1) + 1;
+    const TileSrc ls = tile_src(min(Tu, NT - 1));
+    const int rows_left = a.Cq - 1 - ls.q0;
+    const unsigned char* src0;
+    const unsigned char* src1;
+    const float* src2;
+    unsigned char* dst;
+    if constexpr (ODD) {
+      const int64_t off = b * a.q_bs + ls.h * a.q_hs + (int64_t)ls.q0 * D;
+      src0 = reinterpret_cast<const unsigned char*>(reinterpret_cast<const __bf16*>(a.q) + off);
+      src1 = reinterpret_cast<const unsigned char*>(reinterpret_cast<const __bf16*>(a.dout) + off);
+      src2 = nullptr;
+      dst = lds + (Tu & 1) * ROWS_BUF;
+    } else {
+      const int64_t toff = b * a.qt_bs + ls.h * a.qt_hs + ls.q0;
+      src0 = reinterpret_cast<const unsigned char*>(reinterpret_cast<const __bf16*>(a.qt) + toff);
+      src1 = reinterpret_cast<const unsigned char*>(reinterpret_cast<const __bf16*>(a.dot) + toff);
+      src2 = (wv == 0 ? a.lse2 : a.delta) + b * a.l_bs + ls.h * a.l_hs + ls.q0 + 4 * (lane & 15);
+      dst = lds + OFF_TRANS + (Tu & 1) * TRANS_BUF;
     }
+    // step I < J: chunk I of the first tensor, J <= I < 2J: chunk I - J of
+    // the second, I = 2J: lse2 (wave 0) or delta (wave 1)
+    auto loads = [&](auto ic) {
+      constexpr int I = decltype(ic)::value;
+      static_assert(2 * LJ < G1::N, "every load has a step");
+      if constexpr (I < 2 * LJ) {
+        constexpr int jj = I % LJ;
+        const int ins = wv + 4 * jj;
+        if constexpr (ODD) {
+          if (ins < L::RINS)
+            load_lds16((I < LJ ? src0 : src1) + (min(rrow[jj], (uint32_t)rows_left) * (D * 2) + rch[jj]),
+                       dst + (I < LJ ? 0 : L::RBUF) + ins * 1024);
+        } else {
+          if (ins < L::TINS)
+            load_lds16((I < LJ ? src0 : src1) + tofs[jj], dst + (I < LJ ? 0 : L::TBUF) + ins * 1024);
+        }
+      } else if constexpr (I == 2 * LJ && !ODD) {
+        if (wv < 2) load_lds16(src2, dst + (wv == 0 ? OFF_L : OFF_DL));
+      }
+    };
     const unsigned char* TB = lds + OFF_TRANS + ((j >> 1) & 1) * TRANS_BUF;
     const int r0 = 32 * (j & 1) + 8 * hh;  // rows r0 + 16w + jj of the tile
     // (tile_src reads the head table with a wait of its own: before the
@@ -497,11 +558,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
     if (!(j & 1)) lse_reads(j, lx, dx);  // odd sub-tiles: issued by the even iteration
     bf16x8 Pb[2], dSb[2];
     DkdvProbs<16 / G1::N, decltype(mask)::value> pr{Sc, dPc, lx, dx, c, lim, Pb, dSb};
+    WithLoads<decltype(pr), decltype(loads)> work{pr, loads};
     // the S, dP MFMAs of sub-tile j+1 (past the end: a stale but valid
-    // buffer, result unused) with this sub-tile's arithmetic between them,
-    // then this sub-tile's dV, dK MFMAs, in one operand stream
+    // buffer, result unused) with this sub-tile's arithmetic and the tile
+    // loads between them, then this sub-tile's dV, dK MFMAs, in one operand
+    // stream
     SdpDkdvStream<G1, G2>::run(g1_addr(min(j + 1, NJ - 1)), lds_addr(TB) + n * L::TROW + r0 * 2,
-                               kreg, vreg, Sn, dPn, dVt, dKt, Pb, dSb, pr);
+                               kreg, vreg, Sn, dPn, dVt, dKt, Pb, dSb, work);
     if (!(j & 1)) lse_reads(j + 1, lx, dx);  // NJ is even: an odd sub-tile follows
   };
 
@@ -530,12 +593,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
     const int j_free = 2 * ng * min(n_t, max(0, t_lo + n_t - (rmax + 63) / 64));
     int j = 0;
     for (; j < j_free; j += 2) {  // NJ and j_free are even
-      iter(std::false_type{}, j, SA, dPA, SB, dPB);
-      iter(std::false_type{}, j + 1, SB, dPB, SA, dPA);
+      iter(std::false_type{}, std::false_type{}, j, SA, dPA, SB, dPB);
+      iter(std::false_type{}, std::true_type{}, j + 1, SB, dPB, SA, dPA);
     }
     for (; j < NJ; j += 2) {
-      iter(std::true_type{}, j, SA, dPA, SB, dPB);
-      iter(std::true_type{}, j + 1, SB, dPB, SA, dPA);
+      iter(std::true_type{}, std::false_type{}, j, SA, dPA, SB, dPB);
+      iter(std::true_type{}, std::true_type{}, j + 1, SB, dPB, SA, dPA);
     }
   }
 
@@ -766,6 +829,161 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void attn_bwd_dq(const BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// dQ for D = 128 blocks of whole 64-key tiles, one wave per SIMD: 4 waves x
+// 64 query rows (two 32-row blocks per wave), so every K, V or K^T operand
+// read from LDS feeds two MFMAs, one per row block. Q and dO stay in AGPRs;
+// the key loop -- the S^T / dP^T MFMAs of the next 32-key sub-tile with this
+// one's dS arithmetic between them, then this sub-tile's dQ^T MFMAs, the
+// causal mask and the tile loads -- is one inline-asm statement with a fixed
+// schedule and fixed registers (attn_bwd_dq_w64_loop.h, written by
+// gen_bwd_dq_w64.py). K and V row tiles rotate through three LDS buffers,
+// K^T tiles through two; one barrier per 64-key tile.
+// ---------------------------------------------------------------------------
+constexpr int kDqW64Waves = 4;
+
+constexpr size_t dq_w64_lds_bytes() {
+  return (size_t)dqw64::kRowBufs * dqw64::kRowTileBytes + 2 * (size_t)dqw64::kKtBufBytes;
+}
+
+__global__ __launch_bounds__(64 * kDqW64Waves, 1) void attn_bwd_dq_w64(const BwdArgs a) {
+  constexpr int D = 128, NW = kDqW64Waves;
+  using L = BwdLds<D>;
+  constexpr int KS = D / 16, DT = D / 32;
+  static_assert(dqw64::kRowTileBytes == 2 * L::RBUF && dqw64::kKtBufBytes == L::TBUF &&
+                    L::RINS == 17 && L::TINS == 18 && dq_w64_lds_bytes() <= 160 * 1024,
+                "LDS layout of the one-wave-per-SIMD dQ kernel");
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  unsigned char* Rows = lds;                                           // [3][K 64 rows | V 64 rows]
+  unsigned char* Kt = lds + dqw64::kRowBufs * dqw64::kRowTileBytes;  // [2][D][64 + 8]
+
+  const int item = xcd_item(a.n_items, a.per_xcd);
+  if (item < 0) return;
+  const int qt_rel = item % a.n_tiles;
+  const int rest = item / a.n_tiles;
+  const int hidx = rest % a.Hq, b = rest / a.Hq;
+  const int h = __builtin_amdgcn_readfirstlane((int)a.head_order[hidx]);
+  const int g = __builtin_amdgcn_readfirstlane((int)a.kv_of[h]);
+  const int q0 = (a.n_tiles - 1 - qt_rel) * (64 * NW);  // latest (heaviest) query tiles first
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hh = lane >> 5;
+  const int qw0 = q0 + 64 * wv;
+  const int qlast = a.Cq - 1;
+
+  // the workgroup's keys: a prefix of the block (its last row sees the most)
+  const int wg_qmax = pos_of(a.qp, min(q0 + 64 * NW - 1, qlast));
+  const int n_keys = a.causal ? allowed_prefix(a.kp, wg_qmax) : a.Ck;
+  const int n_kt = (n_keys + 63) / 64;
+  if (n_kt == 0) return;  // nothing to add to dq
+
+  const __bf16* kb = reinterpret_cast<const __bf16*>(a.k) + b * a.k_bs + g * a.k_hs;
+  const __bf16* vb = reinterpret_cast<const __bf16*>(a.v) + b * a.k_bs + g * a.k_hs;
+  const __bf16* ktb = reinterpret_cast<const __bf16*>(a.kt) + b * a.kt_bs + g * a.kt_hs;
+  // The 1 KiB chunk loads of a tile are dealt round-robin to the waves, K
+  // from wave 0, V from wave 1, K^T from wave 2, so each wave issues exactly
+  // one fifth chunk load per tile (K: 17 chunks, V: 17, K^T: 18).
+  const int wk = wv, wvv = (wv + 3) % NW, wt = (wv + 2) % NW;
+  uint32_t koff[5], voff[5], toff[5];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const int pk = (wk + NW * j) * 64 + lane, pv = (wvv + NW * j) * 64 + lane;
+    const int pt = (wt + NW * j) * 64 + lane;
+    const int ck = pk % L::RCPR, cv = pv % L::RCPR, ct = pt % 9;
+    koff[j] = (uint32_t)((pk / L::RCPR) * D + (ck < L::CPR ? ck : 0) * 8) * 2u;
+    voff[j] = (uint32_t)((pv / L::RCPR) * D + (cv < L::CPR ? cv : 0) * 8) * 2u;
+    toff[j] = ((uint32_t)(pt / 9) * (uint32_t)a.Ckp + (uint32_t)(ct < 8 ? ct : 0) * 8u) * 2u;
+  }
+  // tile loads of the prologue (the loop issues the same ones)
+  auto load_rows = [&](int t, int buf) {
+    const unsigned char* ks = reinterpret_cast<const unsigned char*>(kb + (int64_t)t * 64 * D);
+    const unsigned char* vs = reinterpret_cast<const unsigned char*>(vb + (int64_t)t * 64 * D);
+    unsigned char* dst = Rows + buf * dqw64::kRowTileBytes;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      if (wk + NW * j < L::RINS) load_lds16(ks + koff[j], dst + (wk + NW * j) * 1024);
+      if (wvv + NW * j < L::RINS) load_lds16(vs + voff[j], dst + L::RBUF + (wvv + NW * j) * 1024);
+    }
+  };
+  auto load_kt = [&](int t, int buf) {
+    const unsigned char* ts = reinterpret_cast<const unsigned char*>(ktb + t * 64);
+    unsigned char* dst = Kt + buf * dqw64::kKtBufBytes;
+#pragma unroll
+    for (int j = 0; j < 5; ++j)
+      if (wt + NW * j < L::TINS) load_lds16(ts + toff[j], dst + (wt + NW * j) * 1024);
+  };
+  load_rows(0, 0);
+  if (n_kt > 1) load_rows(1, 1);
+  load_kt(0, 0);
+
+  // Q and dO of the wave's two blocks (rows past the block repeat the last
+  // one: their dq is never written), lse2 / delta of each row (rows past the
+  // padded length read its last one), keys each row sees
+  const __bf16* qb = reinterpret_cast<const __bf16*>(a.q) + b * a.q_bs + h * a.q_hs;
+  const __bf16* db = reinterpret_cast<const __bf16*>(a.dout) + b * a.q_bs + h * a.q_hs;
+  bf16x8 q0r[KS], q1r[KS], d0r[KS], d1r[KS];
+  const int r0 = min(qw0 + n, qlast), r1 = min(qw0 + 32 + n, qlast);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    q0r[s] = *reinterpret_cast<const bf16x8*>(qb + (int64_t)r0 * D + 16 * s + 8 * hh);
+    q1r[s] = *reinterpret_cast<const bf16x8*>(qb + (int64_t)r1 * D + 16 * s + 8 * hh);
+    d0r[s] = *reinterpret_cast<const bf16x8*>(db + (int64_t)r0 * D + 16 * s + 8 * hh);
+    d1r[s] = *reinterpret_cast<const bf16x8*>(db + (int64_t)r1 * D + 16 * s + 8 * hh);
+  }
+  const int l0 = min(qw0 + n, a.Cqp - 1), l1 = min(qw0 + 32 + n, a.Cqp - 1);
+  const float* lb = a.lse2 + b * a.l_bs + h * a.l_hs;
+  const float* dlb = a.delta + b * a.l_bs + h * a.l_hs;
+  const float nl20 = -lb[l0], nl21 = -lb[l1];
+  const float dlt0 = dlb[l0], dlt1 = dlb[l1];
+  const int nal0 = a.causal ? allowed_prefix(a.kp, pos_of(a.qp, r0)) : a.Ck;
+  const int nal1 = a.causal ? allowed_prefix(a.kp, pos_of(a.qp, r1)) : a.Ck;
+  // first 32-key sub-tile with a key some row of the wave may not see (its
+  // first row sees the fewest)
+  const int first_mask =
+      (a.causal ? allowed_prefix(a.kp, pos_of(a.qp, min(qw0, qlast))) : a.Ck) / 32;
+  lds_loads_barrier();
+
+  auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+  auto uni_ptr = [](const void* p) {
+    const uint64_t v = (uint64_t)(size_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(size_t)(((uint64_t)hi << 32) | lo);
+  };
+  floatx16 dq0[DT], dq1[DT];
+  dqw64::dq_loop(uni(n_kt), uni(first_mask), uni(lds_addr(Rows) + wk * 1024),
+                 uni(lds_addr(Rows) + L::RBUF + wvv * 1024), uni(lds_addr(Kt) + wt * 1024),
+                 uni(wk + NW * 4 < L::RINS), uni(wvv + NW * 4 < L::RINS), uni(wt + NW * 4 < L::TINS),
+                 a.scale_log2, lds_addr(Rows) + kperm(n) * L::ROW + hh * 16,
+                 lds_addr(Kt) + n * L::TROW + hh * 16, nl20, nl21, dlt0, dlt1, nal0 - 8 * hh,
+                 nal1 - 8 * hh, uni_ptr(kb + (int64_t)min(2, n_kt - 1) * 64 * D),
+                 uni_ptr(vb + (int64_t)min(2, n_kt - 1) * 64 * D),
+                 uni_ptr(ktb + min(1, n_kt - 1) * 64), koff, voff, toff, q0r, q1r, d0r, d1r, dq0,
+                 dq1);
+
+  // add into the fp32 accumulators; lane holds query n of each block,
+  // d = 32T + 8(i/4) + 4hh + i%4
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int qi = qw0 + 32 * blk + n;
+    if (qi >= a.Cq) continue;
+    floatx16(&dQt)[DT] = blk ? dq1 : dq0;
+    float* dqr = a.dq + b * a.dq_bs + h * a.dq_hs + (int64_t)qi * D;
+#pragma unroll
+    for (int T = 0; T < DT; ++T)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * T + 8 * q4 + 4 * hh;
+        float4 x = *reinterpret_cast<float4*>(dqr + d0);
+        x.x += a.scale * dQt[T][4 * q4 + 0];
+        x.y += a.scale * dQt[T][4 * q4 + 1];
+        x.z += a.scale * dQt[T][4 * q4 + 2];
+        x.w += a.scale * dQt[T][4 * q4 + 3];
+        *reinterpret_cast<float4*>(dqr + d0) = x;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // delta = <dout, out> and lse in exp2 units, per query row, padded.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -877,6 +1095,15 @@ hipError_t launch_bwd_dkdv(BwdArgs a, int D, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dq(BwdArgs a, int D, hipStream_t s) {
+  if (D == 128 && a.Ck % 64 == 0) {
+    // whole 64-key tiles: the one-wave-per-SIMD kernel, 256 queries per workgroup
+    a.n_tiles = (a.Cq + 64 * kDqW64Waves - 1) / (64 * kDqW64Waves);
+    a.n_items = a.B * a.Hq * a.n_tiles;
+    a.per_xcd = (a.n_items + kXcds - 1) / kXcds;
+    if (a.n_items <= 0) return hipSuccess;
+    return launch_big(attn_bwd_dq_w64, dq_w64_lds_bytes(), a.per_xcd * kXcds, a, s,
+                      64 * kDqW64Waves);
+  }
   constexpr int NW = kDqWaves;
   a.n_tiles = (a.Cq + 32 * NW - 1) / (32 * NW);  // 256-query workgroups, per (batch, query head)
   a.n_items = a.B * a.Hq * a.n_tiles;

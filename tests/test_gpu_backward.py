@@ -74,6 +74,10 @@ BLOCK_CASES = [
     (64, 96, (1, 64, 0), (1, 96, 40), True, 2, 2, 128),            # rows 0..39 see no key
     (256, 256, None, None, True, 2, 1, 64),    # D=64 diagonal: mask-free and masked sub-tiles
     (192, 192, None, None, True, 1, 1, 64),
+    # D=128 blocks of whole 64-key tiles (the one-wave-per-SIMD dq kernel)
+    (300, 192, None, None, True, 4, 2, 128),                       # ragged query rows
+    (384, 128, (1, 384, 0), (1, 128, 200), True, 8, 2, 128),       # keys inside the rows' span
+    (96, 512, (1, 96, 500), None, False, 2, 2, 128),               # non-causal, few rows
 ]
 
 
