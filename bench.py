@@ -43,7 +43,8 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_bf16_gqa128k_pmc.txt")
 KERNEL_SOURCES = ("attn_fwd.hip", "attn_fwd_w64_phases.h", "attn_common.h", "attn_fwd_args.h")
 # The same for the backward kernels, per block pair (one dk/dv + one dq launch).
 BWD_PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_bwd_bf16_gqa128k_pmc.txt")
-BWD_KERNEL_SOURCES = ("attn_bwd.hip", "attn_bwd_dq_w64_loop.h", "attn_common.h", "attn_bwd_args.h")
+BWD_KERNEL_SOURCES = ("attn_bwd.hip", "attn_bwd_dkdv_loop.h", "attn_bwd_dq_w64_loop.h",
+                      "attn_common.h", "attn_bwd_args.h")
 
 
 def kernel_sources_sha256(sources=KERNEL_SOURCES) -> str:
@@ -81,6 +82,15 @@ def measured_traffic(workload_name: str, summary=PMC_SUMMARY, sources=KERNEL_SOU
         return int(float(kv["traffic_bytes_per_launch"])), summary[len(ROOT) + 1:]
     except (OSError, KeyError, ValueError) as e:
         return None, f"counter summary unreadable: {e}"
+
+
+def bwd_kernel_name(w):
+    """The dk/dv and dq kernels a backward block pair of workload w launches
+    (the one-wave-per-SIMD ones for D = 128; dq's needs whole 64-key tiles)."""
+    block = w.S // (2 * w.N) if w.layout == "zigzag" else w.S // w.N
+    if w.D != 128:
+        return f"attn_bwd_dkdv<{w.D}> + attn_bwd_dq<{w.D}>"
+    return "attn_bwd_dkdv_w32 + " + ("attn_bwd_dq_w64" if block % 64 == 0 else "attn_bwd_dq<128>")
 
 
 def fwd_kernel_name(w, block_keys=None) -> str:
@@ -303,7 +313,7 @@ def bench_backward(args, w, q, k, v, runner, out, lse) -> int:
         "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "useful_flops_per_step": flops_step,
         "roofline": {
-            "kernel": f"attn_bwd_dkdv<{w.D}> + " + ("attn_bwd_dq_w64" if w.D == 128 and (w.S // (2 * w.N)) % 64 == 0 else f"attn_bwd_dq<{w.D}>"),
+            "kernel": bwd_kernel_name(w),
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": round(PEAK_BF16_TFLOPS, 1),

@@ -26,10 +26,12 @@
 //    contributions of all block pairs.
 #include <string.h>
 
+#include <algorithm>
 #include <type_traits>
 #include <vector>
 
 #include "attn_common.h"
+#include "attn_bwd_dkdv_loop.h"
 #include "attn_bwd_dq_w64_loop.h"
 
 namespace ra {
@@ -629,6 +631,160 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// dK, dV for D = 128, one wave per SIMD: the workgroup and its query-tile
+// stream are those of attn_bwd_dkdv, the loop over the stream -- the S / dP
+// MFMAs of the next 32-query sub-tile with this one's P / dS arithmetic
+// between them, then this sub-tile's dV / dK MFMAs, the causal mask and the
+// tile loads -- is one inline-asm statement with a fixed schedule and fixed
+// registers (attn_bwd_dkdv_loop.h, written by gen_bwd_dkdv_w32.py). The
+// rows buffers also hold the tile's lse2 / delta, so a sub-tile's are read
+// during the phase before its arithmetic.
+// ---------------------------------------------------------------------------
+constexpr size_t dkdv_w32_lds_bytes() {
+  return 2 * (size_t)dkdvw::kRowsBuf + 2 * (size_t)dkdvw::kTransBuf;
+}
+
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_w32(const BwdArgs a) {
+  constexpr int D = 128, NW = 4;
+  using L = BwdLds<D>;
+  constexpr int KS = D / 16, DT = D / 32;
+  static_assert(dkdvw::kRowsBuf == 2 * L::RBUF + 2048 && dkdvw::kTransBuf == 2 * L::TBUF &&
+                    dkdvw::kOffL == 2 * L::RBUF && L::RINS == 17 && L::TINS == 18 &&
+                    dkdv_w32_lds_bytes() <= 160 * 1024,
+                "LDS layout of the one-wave-per-SIMD dK / dV kernel");
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  unsigned char* Rows = lds;                            // [2][Q | dO | lse2 | delta]
+  unsigned char* Trans = lds + 2 * dkdvw::kRowsBuf;     // [2][Q^T | dO^T]
+
+  const int item = xcd_item(a.n_items, a.per_xcd);
+  if (item < 0) return;
+  const int kt = item % a.n_tiles;
+  const int rest = item / a.n_tiles;
+  const int g = rest % a.Hkv, b = rest / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hh = lane >> 5;
+  const int k0 = kt * 128, kw0 = k0 + 32 * wv;
+  const int keyc = min(kw0 + n, a.Ck - 1);
+
+  const int kpos = pos_of(a.kp, keyc);
+  // causal: this lane's key is seen by query rows >= row_min only
+  const int row_min = a.causal ? first_row_at(a.qp, a.Cq, kpos) : 0;
+  const int wg_kmin = pos_of(a.kp, min(k0, a.Ck - 1));
+  const int q_lo = a.causal ? allowed_prefix(a.qp, wg_kmin - 1) : 0;
+  const int t_lo = q_lo / 64;
+  const int n_t = max(0, (a.Cq + 63) / 64 - t_lo);
+  const int g0 = a.grp_off[g], ng = a.grp_off[g + 1] - g0;
+  const int NT = __builtin_amdgcn_readfirstlane(ng * n_t);  // tiles in the stream
+  if (NT == 0) return;  // no query sees these keys: nothing to add
+
+  const __bf16* kbase = reinterpret_cast<const __bf16*>(a.k) + b * a.k_bs + g * a.k_hs;
+  const __bf16* vbase = reinterpret_cast<const __bf16*>(a.v) + b * a.k_bs + g * a.k_hs;
+  bf16x8 kreg[KS], vreg[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    kreg[s] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)keyc * D + 16 * s + 8 * hh);
+    vreg[s] = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)keyc * D + 16 * s + 8 * hh);
+  }
+
+  // The group's query heads, one per lane (ng <= 64): tile T of the stream
+  // is head lane T % ng, queries from (t_lo + n_t - 1 - T / ng) * 64.
+  const int vhead = (lane < ng) ? (int)a.head_order[g0 + lane] : 0;
+  auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+  auto head_at = [&](int i) { return uni(__builtin_amdgcn_readlane(vhead, i)); };
+  auto q0_at = [&](int T) { return uni((t_lo + n_t - 1 - T / ng) * 64); };
+  auto uni_ptr = [](const void* p) {
+    const uint64_t v = (uint64_t)(size_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(size_t)(((uint64_t)hi << 32) | lo);
+  };
+  const __bf16* qb = reinterpret_cast<const __bf16*>(a.q) + b * a.q_bs;
+  const __bf16* db = reinterpret_cast<const __bf16*>(a.dout) + b * a.q_bs;
+  const __bf16* qtb = reinterpret_cast<const __bf16*>(a.qt) + b * a.qt_bs;
+  const __bf16* dotb = reinterpret_cast<const __bf16*>(a.dot) + b * a.qt_bs;
+
+  // prologue loads: rows (with lse2 / delta) of tiles 0 and 1 (the last if
+  // the stream has one tile), the transposed tile 0
+  auto load_rows = [&](int T, int buf) {
+    const int h = head_at(T % ng), q0 = q0_at(T);
+    unsigned char* B0 = Rows + buf * dkdvw::kRowsBuf;
+    load_row_tile<D>(qb + h * a.q_hs + (int64_t)q0 * D, a.Cq - 1 - q0, B0, wv, lane);
+    load_row_tile<D>(db + h * a.q_hs + (int64_t)q0 * D, a.Cq - 1 - q0, B0 + L::RBUF, wv, lane);
+    if (wv == 1) load_lds16(a.lse2 + b * a.l_bs + h * a.l_hs + q0 + 4 * (lane & 15), B0 + dkdvw::kOffL);
+    if (wv == 2)
+      load_lds16(a.delta + b * a.l_bs + h * a.l_hs + q0 + 4 * (lane & 15), B0 + dkdvw::kOffL + 1024);
+  };
+  load_rows(0, 0);
+  load_rows(min(1, NT - 1), 1);
+  {
+    const int h = head_at(0), q0 = q0_at(0);
+    load_trans_tile<D>(qtb + h * a.qt_hs + q0, a.Cqp, Trans, wv, lane);
+    load_trans_tile<D>(dotb + h * a.qt_hs + q0, a.Cqp, Trans + L::TBUF, wv, lane);
+  }
+
+  // Per-lane parts of this wave's loop loads (chunk wv + 4j of a tile): row
+  // and byte offset within a 64-row tile, byte offset within a transposed
+  // tile
+  uint32_t rrow[5], rch[5], tofs[5];
+#pragma unroll
+  for (int jj = 0; jj < 5; ++jj) {
+    const int P = (wv + NW * jj) * 64 + lane;
+    const int cr = P % L::RCPR, ct = P % 9;
+    rrow[jj] = (uint32_t)(P / L::RCPR);
+    rch[jj] = (uint32_t)(cr < L::CPR ? cr : 0) * 16u;
+    tofs[jj] = ((uint32_t)(P / 9) * (uint32_t)a.Cqp + (uint32_t)(ct < 8 ? ct : 0) * 8u) * 2u;
+  }
+  // Query tiles that start at or after every lane's first allowed row hold
+  // no masked pair; the stream walks tiles latest first, so they are its
+  // leading sub-tiles. row_min grows with the key, so the wave's largest is
+  // its last key's.
+  const int rmax =
+      a.causal ? first_row_at(a.qp, a.Cq, pos_of(a.kp, min(kw0 + 31, a.Ck - 1))) : 0;
+  const int j_free = 2 * ng * min(n_t, max(0, t_lo + n_t - (rmax + 63) / 64));
+  const unsigned lrows = lds_addr(Rows), ltrans = lds_addr(Trans);
+  lds_loads_barrier();
+
+  floatx16 dVt[DT], dKt[DT];
+  dkdvw::dkdv_loop(
+      NT, uni(j_free), uni(ng), head_at((NT - 1) % ng), q0_at(NT - 1), uni(a.Cq - 1),
+      uni(lrows + wv * 1024), uni(ltrans + wv * 1024), uni(wv == 0), uni(wv <= 1),
+      uni(wv == 1 || wv == 2), uni(dkdvw::kOffL + (wv == 2 ? 1024 : 0) - wv * 1024),
+      uni((int)(a.q_hs * 2)), uni((int)(a.qt_hs * 2)), uni((int)(a.l_hs * 4)), a.scale_log2,
+      uni_ptr(qb), uni_ptr(db), uni_ptr(qtb), uni_ptr(dotb),
+      uni_ptr((wv == 1 ? a.lse2 : a.delta) + b * a.l_bs), lrows + kperm(n) * L::ROW + hh * 16,
+      ltrans + n * L::TROW + hh * 16, lrows + 32 * hh, row_min - 8 * hh, vhead, 16 * (lane & 15),
+      rrow, rch, tofs, kreg, vreg, q0_at(0), q0_at(1), q0_at(2), head_at(1 % ng),
+      head_at(2 % ng), uni(2 % ng), dVt, dKt);
+
+  // epilogue: add into the fp32 accumulators; lane holds key kw0+n,
+  // d = 32T + 8(i/4) + 4hh + i%4
+  const int key = kw0 + n;
+  if (key < a.Ck) {
+    float* dkr = a.dk + b * a.dk_bs + g * a.dk_hs + (int64_t)key * D;
+    float* dvr = a.dv + b * a.dk_bs + g * a.dk_hs + (int64_t)key * D;
+#pragma unroll
+    for (int T = 0; T < DT; ++T)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * T + 8 * q4 + 4 * hh;
+        float4 k4 = *reinterpret_cast<float4*>(dkr + d0);
+        float4 v4 = *reinterpret_cast<float4*>(dvr + d0);
+        k4.x += a.scale * dKt[T][4 * q4 + 0];
+        k4.y += a.scale * dKt[T][4 * q4 + 1];
+        k4.z += a.scale * dKt[T][4 * q4 + 2];
+        k4.w += a.scale * dKt[T][4 * q4 + 3];
+        v4.x += dVt[T][4 * q4 + 0];
+        v4.y += dVt[T][4 * q4 + 1];
+        v4.z += dVt[T][4 * q4 + 2];
+        v4.w += dVt[T][4 * q4 + 3];
+        *reinterpret_cast<float4*>(dkr + d0) = k4;
+        *reinterpret_cast<float4*>(dvr + d0) = v4;
+      }
+  }
+}
+
 // dQ^T += K^T dS^T for one 32-key sub-tile: 2*DT MFMAs whose A operands
 // (rows d of the K^T tile, 16 keys each) stream from LDS through a ring of PF
 // registers. Operand i: u = i / DT (16-key half), T = i % DT (32-wide d tile).
@@ -1057,6 +1213,20 @@ constexpr size_t dq_lds_bytes() {
   return (size_t)2 * (2 * BwdLds<D>::RBUF + BwdLds<D>::TBUF);
 }
 
+// The one-wave-per-SIMD dK / dV loop keeps a group's query heads one per
+// lane (at most 64) and forms a tile's source addresses from 32-bit byte
+// offsets (head * head stride + first query) added to the batch's base.
+bool dkdv_w32_fits(const BwdArgs& a) {
+  int ng_max = 0;
+  for (int g = 0; g < a.Hkv; ++g) ng_max = std::max(ng_max, (int)(a.grp_off[g + 1] - a.grp_off[g]));
+  const uint64_t h = (uint64_t)std::max(a.Hq - 1, 0), lim = 0xffffffffull;
+  const uint64_t rows = h * (uint64_t)a.q_hs * 2 + (uint64_t)a.Cq * 256;
+  const uint64_t trans = h * (uint64_t)a.qt_hs * 2 + (uint64_t)a.Cqp * 2;
+  const uint64_t lse = h * (uint64_t)a.l_hs * 4 + (uint64_t)a.Cqp * 4;
+  return ng_max <= 64 && (uint64_t)a.q_hs * 2 < (1ull << 31) && (uint64_t)a.qt_hs * 2 < (1ull << 31) &&
+         (uint64_t)a.l_hs * 4 < (1ull << 31) && rows <= lim && trans <= lim && lse <= lim;
+}
+
 template <typename K>
 hipError_t launch_big(K kern, size_t lds, int grid, const BwdArgs& a, hipStream_t s, int threads = 256) {
   static_assert(sizeof(BwdArgs) <= 4096, "kernel arguments");
@@ -1090,6 +1260,8 @@ hipError_t launch_bwd_dkdv(BwdArgs a, int D, hipStream_t s) {
   a.per_xcd = (a.n_items + kXcds - 1) / kXcds;
   if (a.n_items <= 0) return hipSuccess;
   const int grid = a.per_xcd * kXcds;
+  if (D == 128 && dkdv_w32_fits(a))
+    return launch_big(attn_bwd_dkdv_w32, dkdv_w32_lds_bytes(), grid, a, s);
   if (D == 128) return launch_big(attn_bwd_dkdv<128>, dkdv_lds_bytes<128>(), grid, a, s);
   return launch_big(attn_bwd_dkdv<64>, dkdv_lds_bytes<64>(), grid, a, s);
 }

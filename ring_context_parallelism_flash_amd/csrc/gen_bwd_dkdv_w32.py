@@ -1,0 +1,510 @@
+"""Writes attn_bwd_dkdv_loop.h: the query loop of the dK / dV kernel of the
+attention backward (bf16, D = 128) as one inline-asm statement with a fixed
+instruction schedule and a fixed register plan.
+
+A wave owns 32 keys of one KV head: their K and V rows and the dK^T / dV^T
+accumulators stay in AGPRs. The workgroup's four waves walk one stream of
+64-query tiles (every query head of the group, latest tile first) in 32-query
+sub-tiles j. With p = exp2(S c - lse2) and dS = p (dP - delta):
+  phase A(j): the S = Q K^T and dP = dO V^T MFMAs of sub-tile j+1 (Q and dO
+              rows from LDS) with the p / dS arithmetic of sub-tile j between
+              them;
+  phase B(j): dV^T += dO^T P and dK^T += Q^T dS of sub-tile j (dO^T and Q^T
+              tiles from LDS).
+The probabilities use the saved lse ("Sequence Parallelism in Large Language
+Models ...", section "The Activation Memory Wall": recomputation instead of
+stored activations), so there is no running max; the causal mask is applied
+out of line to the sub-tiles from the stream's first partly visible one.
+
+Every LDS operand read goes through one ring of four registers; the last four
+reads of each phase are the next phase's first. A sub-tile's lse2 / delta are
+read during the phase B before its arithmetic. The generator tracks every LDS
+read it emits and gives each use the exact lgkmcnt wait it needs (LDS reads
+return in order, and the statement issues no other LGKM operation).
+
+LDS holds two row buffers [Q rows | dO rows | lse2 | delta] and two
+transposed buffers [Q^T | dO^T], filled by direct global->LDS loads, each
+placed after one MFMA of a phase A: the even sub-tile 2t loads the transposed
+tile t+1, the odd one the rows (with lse2 / delta) of tile t+2; a tile past
+the stream's end repeats the last one. Two barriers per tile:
+  even barrier (before phase A(2t)): publishes the transposed tile t and
+    frees the other transposed buffer (phase B(2t-1) is done);
+  odd barrier (after MFMA 11 of phase B(2t)): publishes the rows of tile t+1
+    and frees the rows of tile t (both of its phases A and its lse2 / delta
+    reads, waited for right before the barrier, are done); the last four
+    MFMAs of phase B(2t) then issue the first reads of tile t+1.
+Each barrier waits only for the loads before the latest batch (vmcnt(8):
+every batch gives each wave at least eight loads), so a batch has about two
+sub-tiles to land.
+
+Register plan (one wave per SIMD):
+  a[0:63] dV^T, a[64:127] dK^T (four 32-wide d tiles of 16 registers each)
+  a[128:159] K, a[160:191] V of the wave's keys (eight k-steps of 4)
+  v56 rows read address, v57 Q^T read address, v58 lse2 / delta read address,
+  v[59:62] temporaries, v[64:79] operand ring
+  v[80:111], v[112:143]: lse2 (16) then delta (16) of a sub-tile, per parity
+  v[144:175], v[176:207]: S (16) then dP (16), per parity
+  v[208:223], v[224:239]: bf16 P (8) then dS (8), per parity
+  v[240:244]: row offsets of the row tile loads
+  s[80:81], s[82:83], s[84:85]: global bases of the loads in flight
+The compiler keeps everything else in v[0:55], v[245:255], a[192:255] and the
+other SGPRs.
+
+Hazards the statement respects by construction: a transcendental result is
+read no earlier than the second instruction after it; MFMA results are read
+by vector instructions only a phase later, or by the out-of-line mask and
+after the statement, each behind s_nop 7 x 3; S and dP accumulate in two
+alternating chains, dV^T / dK^T in eight; the P / dS a phase B reads are
+rewritten only two phases later; an M0 write is followed by one wait state
+before the LDS-DMA load that reads it; an SALU write of the lane select is
+four wait states before the v_readlane that uses it.
+
+Run: python gen_bwd_dkdv_w32.py  (writes the header next to this file)
+"""
+import os
+
+D = 128
+KS = D // 16                # k-steps of the S / dP products
+DT = D // 32                # d tiles of dK / dV
+ROW = (D // 8 + 1) * 16     # padded Q / dO row, bytes
+TROW = 9 * 16               # padded row of a transposed tile (64 queries + pad)
+RBUF = 64 * ROW
+TBUF = D * TROW
+OFF_L, OFF_DL = 2 * RBUF, 2 * RBUF + 1024
+ROWS_BUF = 2 * RBUF + 2048  # Q rows, dO rows, lse2, delta
+TRANS_BUF = 2 * TBUF        # Q^T, dO^T
+HALF_R = 32 * ROW           # second 32-query half of a row tile
+HALF_T = 64                 # ... of a transposed tile (bytes)
+HALF_L = 128                # ... of lse2 / delta (bytes)
+N = 2 * KS                  # MFMAs (and operand reads) per phase
+assert N == 4 * DT == 16
+PF = 4
+NEG_INF = "0xff800000"
+
+DV_, DK_, K_, V_ = 0, 64, 128, 160
+V_RADDR, V_TADDR, V_LADDR = 56, 57, 58
+T0, T1, T2, T3 = 59, 60, 61, 62
+RING = 64
+LX_ = {0: 80, 1: 112}        # lse2 at +0..15, delta at +16..31
+SD_ = {0: 144, 1: 176}       # S at +0..15, dP at +16..31
+PD_ = {0: 208, 1: 224}       # P at +0..7, dS at +8..15
+VOFF = 240
+SB_A, SB_B, SB_L = 80, 82, 84
+PAD = ["s_nop 7", "s_nop 7", "s_nop 7"]
+BARRIER_STEP = 11            # phase B(2t): the odd barrier follows this MFMA
+
+
+def vr(base, n):
+    return f"v[{base}:{base + n - 1}]"
+
+
+def ar(base, n):
+    return f"a[{base}:{base + n - 1}]"
+
+
+def ring(i):
+    return vr(RING + 4 * (i % PF), 4)
+
+
+def a_off(i):
+    """Phase A read i: even = Q row (k-step i/2), odd = dO row."""
+    return (i & 1) * RBUF + 32 * (i >> 1)
+
+
+def b_off(i):
+    """Phase B read i: even = dO^T (dV), odd = Q^T (dK); d tile (i/2) % DT,
+    16-query half i / (2 DT)."""
+    return (0 if i & 1 else TBUF) + 32 * ((i >> 1) % DT) * TROW + 32 * (i // (2 * DT))
+
+
+class Gen:
+    """The statement's lines (in order) and its out-of-line blocks, plus the
+    wave's outstanding LDS reads in issue order (they return in order)."""
+
+    def __init__(self):
+        self.lines = []
+        self.ool = []
+        self.q = []          # outstanding reads: (id, tag)
+        self.n = 0
+        self.ring_id = [None] * PF
+        self.lx_id = {}      # (parity, register base) -> read id
+
+    def add(self, lines):
+        self.lines += lines
+
+    def lab(self, name):
+        return f".L{name}_%="
+
+    def place(self, name):
+        self.lines.append(f"{self.lab(name)}:")
+
+    def issue(self, tag):
+        self.n += 1
+        self.q.append((self.n, tag))
+        return self.n
+
+    def wait(self, x):
+        """s_waitcnt that retires read x (nothing if it already is)."""
+        ids = [i for i, _ in self.q]
+        if x not in ids:
+            return []
+        k = len(ids) - 1 - ids.index(x)
+        self.q = self.q[ids.index(x) + 1:]
+        assert k <= 15
+        return [f"s_waitcnt lgkmcnt({k})"]
+
+    def shape(self):
+        """The outstanding reads as tags: the loop's entry and back edge
+        must agree, since the same waits serve both."""
+        return [tag for _, tag in self.q]
+
+    def read(self, slot, addr, off):
+        self.ring_id[slot] = self.issue(("ring", slot))
+        return [f"ds_read_b128 {ring(slot)}, v{addr} offset:{off}"]
+
+    def lse_read(self, par, k, half):
+        """Read k (0..7) of a sub-tile's lse2 (k < 4) / delta, four floats:
+        rows 16w + 4m' .. +3 of the sub-tile for k % 4 = 2w + m'."""
+        base = LX_[par] + (16 if k >= 4 else 0) + 4 * (k % 4)
+        off = (OFF_DL if k >= 4 else OFF_L) + [0, 16, 64, 80][k % 4] + (HALF_L if half else 0)
+        self.lx_id[(par, base)] = self.issue(("lx", par, base))
+        return [f"ds_read_b128 {vr(base, 4)}, v{V_LADDR} offset:{off}"]
+
+    def need_lx(self, par, e):
+        out = []
+        for base in (LX_[par] + 4 * (e // 4), LX_[par] + 16 + 4 * (e // 4)):
+            x = self.lx_id.pop((par, base), None)
+            if x is not None:
+                out += self.wait(x)
+        return out
+
+    def phase(self, mfma, addr, off, work=None, pre_in=False, nxt=None, extra=None):
+        """N MFMAs; MFMA i reads operand i (address register addr, offset
+        off(i)) through the ring. After MFMA i: the read of operand i + PF
+        (the last PF steps issue the first reads of the next phase: nxt()
+        gives (addr, off) then, after the extras before it), work(i) (items:
+        instruction strings, or (parity, element) for the lse2 / delta that
+        the next instructions use) and extra(i)."""
+        if not pre_in:
+            for i in range(PF):
+                self.add(self.read(i, addr, off(i)))
+        for i in range(N):
+            self.add(self.wait(self.ring_id[i % PF]))
+            self.add([mfma(i)])
+            if i + PF < N:
+                self.add(self.read(i % PF, addr, off(i + PF)))
+            elif nxt:
+                a, o = nxt()
+                self.add(self.read(i % PF, a, o(i + PF - N)))
+            if work:
+                for item in work(i):
+                    if isinstance(item, tuple):
+                        self.add(self.need_lx(*item))
+                    else:
+                        self.add([item])
+            if extra:
+                self.add(extra(i))
+
+
+def a_mfma(par):
+    """S (even i) and dP (odd i) of parity par, k-step i / 2; C = 0 first."""
+    S, P = SD_[par], SD_[par] + 16
+
+    def f(i):
+        s = i >> 1
+        dst, b = (P, V_) if i & 1 else (S, K_)
+        c = "0" if s == 0 else vr(dst, 16)
+        return f"v_mfma_f32_32x32x16_bf16 {vr(dst, 16)}, {ring(i)}, {ar(b + 4 * s, 4)}, {c}"
+    return f
+
+
+def b_mfma(par):
+    """dV^T (even i) / dK^T (odd i), d tile (i/2) % DT, 16-query half
+    i / (2 DT), from P / dS of parity par."""
+    P, dS = PD_[par], PD_[par] + 8
+
+    def f(i):
+        T, u = (i >> 1) % DT, i // (2 * DT)
+        acc, b = (DK_ + 16 * T, dS + 4 * u) if i & 1 else (DV_ + 16 * T, P + 4 * u)
+        return f"v_mfma_f32_32x32x16_bf16 {ar(acc, 16)}, {ring(i)}, {vr(b, 4)}, {ar(acc, 16)}"
+    return f
+
+
+def arith(par):
+    """p and dS of the sub-tile of parity par: elements 2k, 2k+1 in two
+    parts, after MFMAs 2k and 2k+1. Element e of a lane is query 16(e/8) +
+    8hh + e%8 of the sub-tile; bf16 pairs pack as register 4(e/8) + (e%8)/2."""
+    S, dP = SD_[par], SD_[par] + 16
+    LX, DX = LX_[par], LX_[par] + 16
+    Pr, dSr = PD_[par], PD_[par] + 8
+
+    def f(i):
+        e = 2 * (i // 2)
+        reg = 4 * (e >> 3) + ((e & 7) >> 1)
+        if i % 2 == 0:
+            return [(par, e),
+                    f"v_fma_f32 v{T0}, v{S + e}, %[c], -v{LX + e}",
+                    f"v_fma_f32 v{T1}, v{S + e + 1}, %[c], -v{LX + e + 1}",
+                    f"v_exp_f32 v{T0}, v{T0}",
+                    f"v_exp_f32 v{T1}, v{T1}"]
+        return [f"v_sub_f32 v{T2}, v{dP + e}, v{DX + e}",
+                f"v_sub_f32 v{T3}, v{dP + e + 1}, v{DX + e + 1}",
+                f"v_cvt_pk_bf16_f32 v{Pr + reg}, v{T0}, v{T1}",
+                f"v_mul_f32 v{T2}, v{T0}, v{T2}",
+                f"v_mul_f32 v{T3}, v{T1}, v{T3}",
+                f"v_cvt_pk_bf16_f32 v{dSr + reg}, v{T2}, v{T3}"]
+    return f
+
+
+def mask(G, par, q_sgpr, site):
+    """Causal mask of the S of parity par, out of line: the sub-tile's
+    index is in %[js], its first query in q_sgpr; a query offset below the
+    lane's limit (%[lmin] - q) does not see the lane's key."""
+    S = SD_[par]
+    G.add(["s_cmp_ge_u32 %[js], %[jfree]", f"s_cbranch_scc1 {G.lab('mask' + site)}"])
+    G.place("mback" + site)
+    body = [f"{G.lab('mask' + site)}:"] + PAD + [
+            f"v_subrev_u32 v{T1}, {q_sgpr}, %[lmin]",
+            f"v_mov_b32 v{T0}, {NEG_INF}"]
+    for e in range(16):
+        k = 16 * (e >> 3) + (e & 7)
+        body += [f"v_cmp_lt_i32 vcc, {k}, v{T1}",
+                 f"v_cndmask_b32 v{S + e}, v{S + e}, v{T0}, vcc"]
+    G.ool += body + [f"s_branch {G.lab('mback' + site)}"]
+
+
+def chunk_loads(dst_base, lo, x5, sb, vaddr):
+    """The five 1 KiB chunk loads of one tensor of a tile (the fifth under
+    the exec mask x5): chunk j of this wave lands at dst_base + lo + 4096 j."""
+    g = []
+    for j in range(5):
+        pre = [f"s_add_u32 m0, {dst_base}, {lo + 4096 * j}"]
+        pre += ["s_nop 0"] if j < 4 else [f"s_mov_b64 exec, {x5}"]
+        g.append(pre + [f"global_load_lds_dwordx4 {vaddr(j)}, s[{sb}:{sb + 1}]"] +
+                 (["s_mov_b64 exec, -1"] if j == 4 else []))
+    return g
+
+
+def trans_setup():
+    """Sources and destination of the transposed tile t+1 (the last one
+    past the end): %[sz] = its LDS buffer (this wave's part)."""
+    return ["s_add_u32 %[sx], %[t], 1", "s_cmp_lt_u32 %[sx], %[nt]",
+            "s_cselect_b32 %[sh], %[hn], %[hlast]", "s_cselect_b32 %[sq], %[q0n], %[q0last]",
+            "s_mul_i32 %[sx], %[sh], %[qths]", "s_lshl_b32 %[sy], %[sq], 1",
+            "s_add_u32 %[sx], %[sx], %[sy]",
+            f"s_add_u32 s{SB_A}, %[qtb_lo], %[sx]", f"s_addc_u32 s{SB_A + 1}, %[qtb_hi], 0",
+            f"s_add_u32 s{SB_B}, %[dotb_lo], %[sx]", f"s_addc_u32 s{SB_B + 1}, %[dotb_hi], 0",
+            f"s_xor_b32 %[sz], %[tb], {TRANS_BUF}", "s_add_u32 %[sz], %[sz], %[tdst]"]
+
+
+def rows_setup():
+    """Sources, row offsets and destination of the row tile t+2 (the last
+    one past the end), in four parts (one per MFMA after the odd barrier):
+    rows past the block re-read its last row (their lse2 is +inf)."""
+    return [
+        ["s_add_u32 %[sx], %[t], 2", "s_cmp_lt_u32 %[sx], %[nt]",
+         "s_cselect_b32 %[sh], %[hf], %[hlast]", "s_cselect_b32 %[sq], %[q0f], %[q0last]",
+         "s_mul_i32 %[sx], %[sh], %[qhs]", "s_lshl_b32 %[sy], %[sq], 8",
+         "s_add_u32 %[sx], %[sx], %[sy]"],
+        [f"s_add_u32 s{SB_A}, %[qb_lo], %[sx]", f"s_addc_u32 s{SB_A + 1}, %[qb_hi], 0",
+         f"s_add_u32 s{SB_B}, %[db_lo], %[sx]", f"s_addc_u32 s{SB_B + 1}, %[db_hi], 0",
+         "s_mul_i32 %[sx], %[sh], %[lhs]", "s_lshl_b32 %[sy], %[sq], 2",
+         "s_add_u32 %[sx], %[sx], %[sy]",
+         f"s_add_u32 s{SB_L}, %[lsb_lo], %[sx]", f"s_addc_u32 s{SB_L + 1}, %[lsb_hi], 0"],
+        ["s_sub_u32 %[sx], %[cqm1], %[sq]"] +
+        [f"v_min_u32 v{VOFF + j}, %[sx], %[rrow{j}]" for j in range(5)],
+        [f"v_lshl_add_u32 v{VOFF + j}, v{VOFF + j}, 8, %[rch{j}]" for j in range(5)] +
+        ["s_add_u32 %[sz], %[rb], %[rdst]"],
+    ]
+
+
+def advance():
+    """Next tile: tile t+1 becomes current, t+2 next, and the tile after
+    them (stream order: every head of the group, then the tile row below)
+    becomes the far one; the buffers flip. In pieces, one per MFMA."""
+    return [
+        ["s_add_u32 %[t], %[t], 1", "s_mov_b32 %[q0c], %[q0n]", "s_mov_b32 %[hn], %[hf]",
+         "s_mov_b32 %[q0n], %[q0f]"],
+        ["s_add_u32 %[hi], %[hi], 1", "s_cmp_eq_u32 %[hi], %[ng]",
+         "s_cselect_b32 %[hi], 0, %[hi]", "s_cselect_b32 %[sx], 64, 0",
+         "s_sub_u32 %[q0f], %[q0f], %[sx]", "s_nop 3"],
+        ["v_readlane_b32 %[hf], %[vhead], %[hi]",
+         f"s_xor_b32 %[rb], %[rb], {ROWS_BUF}", f"s_xor_b32 %[tb], %[tb], {TRANS_BUF}"],
+    ]
+
+
+def loop_asm():
+    G = Gen()
+    G.add(["s_waitcnt lgkmcnt(0)"] + [f"v_accvgpr_write_b32 a{r}, 0" for r in range(128)])
+    # prologue: S / dP of sub-tile 0 (rows buffer 0, first half) and its
+    # lse2 / delta; the last steps start the reads of sub-tile 1
+    G.add([f"v_mov_b32 v{V_RADDR}, %[rbase]", f"v_mov_b32 v{V_LADDR}, %[lbase]",
+           f"v_mov_b32 v{V_TADDR}, %[tbase]"])
+    G.phase(a_mfma(0), V_RADDR, a_off, nxt=lambda: (V_RADDR, lambda i: a_off(i) + HALF_R),
+            extra=lambda i: (G.lse_read(0, 2 * i, False) + G.lse_read(0, 2 * i + 1, False))
+            if i < 4 else [])
+    G.add(PAD + ["s_mov_b32 %[js], 0"])
+    mask(G, 0, "%[q0c]", "pro")
+    G.add(["s_mov_b32 %[t], 0"] + trans_setup())
+    entry = G.shape()
+    G.place("loop")
+
+    # ================= even sub-tile 2t (tile t, first half)
+    G.add(["s_waitcnt vmcnt(8)", "s_barrier"])
+    tl = chunk_loads("%[sz]", 0, "%[x5t]", SB_A, lambda j: f"%[to{j}]") + \
+        chunk_loads("%[sz]", TBUF, "%[x5t]", SB_B, lambda j: f"%[to{j}]")
+    G.phase(a_mfma(1), V_RADDR, lambda i: a_off(i) + HALF_R, work=arith(0), pre_in=True,
+            nxt=lambda: (V_TADDR, b_off), extra=lambda i: tl[i] if i < len(tl) else [])
+    G.add(["s_add_u32 %[js], %[js], 1", "s_add_u32 %[sq], %[q0c], 32"])
+    mask(G, 1, "%[sq]", "e")
+    G.add([f"v_add_u32 v{V_LADDR}, %[rb], %[lbase]"])
+    rs = rows_setup()
+
+    def even_b_extra(i):
+        out = []
+        if i < 4:   # lse2 / delta of sub-tile 2t+1 (this tile's second half)
+            out += G.lse_read(1, 2 * i, True) + G.lse_read(1, 2 * i + 1, True)
+        if i == BARRIER_STEP:
+            # the rows of tile t are read for the last time: wait for this
+            # wave's lse2 / delta reads, then the odd barrier
+            for key in [k for k in G.lx_id if k[0] == 1]:
+                out += G.wait(G.lx_id.pop(key))
+            out += ["s_waitcnt vmcnt(8)", "s_barrier", f"s_xor_b32 %[sx], %[rb], {ROWS_BUF}",
+                    f"v_add_u32 v{V_RADDR}, %[sx], %[rbase]"]
+        if i > BARRIER_STEP:
+            out += rs[i - BARRIER_STEP - 1]
+        return out
+    G.phase(b_mfma(0), V_TADDR, b_off, pre_in=True, nxt=lambda: (V_RADDR, a_off),
+            extra=even_b_extra)
+
+    # ================= odd sub-tile 2t+1 (tile t, second half)
+    rl = chunk_loads("%[sz]", 0, "%[x5r]", SB_A, lambda j: f"v{VOFF + j}") + \
+        chunk_loads("%[sz]", RBUF, "%[x5r]", SB_B, lambda j: f"v{VOFF + j}") + \
+        [["s_add_u32 m0, %[sz], %[loffl]", "s_mov_b64 exec, %[xl]",
+          f"global_load_lds_dwordx4 %[lo], s[{SB_L}:{SB_L + 1}]", "s_mov_b64 exec, -1"]]
+    G.phase(a_mfma(0), V_RADDR, a_off, work=arith(1), pre_in=True,
+            nxt=lambda: (V_TADDR, lambda i: b_off(i) + HALF_T),
+            extra=lambda i: rl[i] if i < len(rl) else [])
+    G.add(["s_add_u32 %[js], %[js], 1"])
+    mask(G, 0, "%[q0n]", "o")
+    G.add([f"s_xor_b32 %[sx], %[rb], {ROWS_BUF}", f"v_add_u32 v{V_LADDR}, %[sx], %[lbase]"])
+    adv = advance()
+    ts = trans_setup()
+
+    def odd_b_extra(i):
+        out = []
+        if i < 4:   # lse2 / delta of sub-tile 2t+2 (tile t+1, first half)
+            out += G.lse_read(0, 2 * i, False) + G.lse_read(0, 2 * i + 1, False)
+        if 4 <= i < 4 + len(adv):
+            out += adv[i - 4]
+        if i == 12:  # the last read of the transposed tile t went out at MFMA 11
+            out += [f"v_add_u32 v{V_TADDR}, %[tb], %[tbase]"] + ts
+        return out
+    # V_RADDR stays at tile t+1's rows: the next phase A reads their second half
+    G.phase(b_mfma(1), V_TADDR, lambda i: b_off(i) + HALF_T, pre_in=True,
+            nxt=lambda: (V_RADDR, lambda i: a_off(i) + HALF_R), extra=odd_b_extra)
+    assert G.shape() == entry, (G.shape(), entry)
+    G.add(["s_cmp_lt_u32 %[t], %[nt]", f"s_cbranch_scc1 {G.lab('loop')}"])
+    # no load or read is left in flight when the statement ends
+    G.add(["s_waitcnt vmcnt(0)", "s_waitcnt lgkmcnt(0)", f"s_branch {G.lab('done')}"])
+    G.add(G.ool)
+    G.place("done")
+    G.add(PAD)
+    return G.lines
+
+
+def main():
+    lines = loop_asm()
+    outs = ([f'"={{{ar(DV_ + 16 * T, 16)}}}"(dv[{T}])' for T in range(DT)] +
+            [f'"={{{ar(DK_ + 16 * T, 16)}}}"(dk[{T}])' for T in range(DT)] +
+            ['[t] "=&s"(t)', '[js] "=&s"(js)', '[sx] "=&s"(sx)', '[sy] "=&s"(sy)',
+             '[sz] "=&s"(sz)', '[sh] "=&s"(sh)', '[sq] "=&s"(sq)',
+             '[q0c] "+s"(q0c)', '[q0n] "+s"(q0n)', '[q0f] "+s"(q0f)', '[hn] "+s"(hn)',
+             '[hf] "+s"(hf)', '[hi] "+s"(hi)', '[rb] "+s"(rb)', '[tb] "+s"(tb)'])
+    ins = (['[nt] "s"(n_t)', '[jfree] "s"(j_free)', '[ng] "s"(ng)', '[hlast] "s"(h_last)',
+            '[q0last] "s"(q0_last)', '[cqm1] "s"(cq_m1)', '[rdst] "s"(rdst)', '[tdst] "s"(tdst)',
+            '[x5r] "s"(x5r)', '[x5t] "s"(x5t)', '[xl] "s"(xl)', '[loffl] "s"(loffl)',
+            '[qhs] "s"(qhs)', '[qths] "s"(qths)', '[lhs] "s"(lhs)', '[c] "s"(c)',
+            '[qb_lo] "s"(qb_lo)', '[qb_hi] "s"(qb_hi)', '[db_lo] "s"(db_lo)', '[db_hi] "s"(db_hi)',
+            '[qtb_lo] "s"(qtb_lo)', '[qtb_hi] "s"(qtb_hi)', '[dotb_lo] "s"(dotb_lo)',
+            '[dotb_hi] "s"(dotb_hi)', '[lsb_lo] "s"(lsb_lo)', '[lsb_hi] "s"(lsb_hi)',
+            '[rbase] "v"(rbase)', '[tbase] "v"(tbase)', '[lbase] "v"(lbase)', '[lmin] "v"(lmin)',
+            '[vhead] "v"(vhead)', '[lo] "v"(lo)'] +
+           [f'[rrow{j}] "v"(rrow[{j}])' for j in range(5)] +
+           [f'[rch{j}] "v"(rch[{j}])' for j in range(5)] +
+           [f'[to{j}] "v"(tofs[{j}])' for j in range(5)] +
+           [f'"{{{ar(K_ + 4 * s, 4)}}}"(kr[{s}])' for s in range(KS)] +
+           [f'"{{{ar(V_ + 4 * s, 4)}}}"(vr_[{s}])' for s in range(KS)])
+    clob = ([f'"v{r}"' for r in range(V_RADDR, VOFF + 5)] +
+            [f'"s{r}"' for r in range(SB_A, SB_L + 2)] +
+            ['"vcc"', '"scc"', '"m0"', '"exec"', '"memory"'])
+    body = "\n".join(f'      "{ln}\\n\\t"' for ln in lines)
+    out = f'''// Generated by gen_bwd_dkdv_w32.py -- do not edit by hand.
+//
+// The query loop of attn_bwd_dkdv_w32 (D = {D}) as one inline-asm statement
+// with a fixed schedule and fixed registers; gen_bwd_dkdv_w32.py documents
+// the register plan, the schedule and the hazards it respects.
+#pragma once
+
+namespace ra {{
+namespace dkdvw {{
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kRowsBuf = {ROWS_BUF};    // [Q rows | dO rows | lse2 1 KiB | delta 1 KiB]; two buffers
+constexpr int kTransBuf = {TRANS_BUF};  // [Q^T | dO^T]; two buffers
+constexpr int kOffL = {OFF_L};          // lse2 in a rows buffer (delta 1 KiB later)
+
+// The query-tile stream of one wave: n_t >= 1 tiles of 64 queries. The rows
+// (with lse2 / delta) of tiles 0 and min(1, n_t - 1) are in rows buffers 0
+// and 1, the transposed tile 0 in transposed buffer 0. Tile T is query head
+// lane (T % ng) of vhead, first query q0(T) (the tiles of each query range
+// for every head, ranges from the last down); the caller passes q0 of tiles
+// 0, 1, 2 (q0c, q0n, q0f), the heads of tiles 1, 2 (hn, hf), hi = 2 % ng,
+// and head and q0 of the last tile (h_last, q0_last). rbase / tbase / lbase:
+// this lane's read addresses in rows / transposed / lse2 of buffer 0; rdst /
+// tdst: this wave's first load destination in rows / transposed buffer 0;
+// qb / db / qtb / dotb: global bases of q, dout, q^T, dout^T of the batch and
+// lsb of lse2 or delta (by wave); qhs / qths / lhs: head strides in bytes;
+// rrow / rch: the lane's row and byte offset in its row tile chunks, tofs its
+// transposed tile offsets, lo its lse2 / delta offset; r5 / t5 / l1: whether
+// the wave issues the fifth row / transposed chunk load and an lse2 / delta
+// load, loffl that load's LDS offset from the wave's row destination;
+// cq_m1: rows of the block minus one; j_free: the first sub-tile that needs
+// the causal mask; lmin: the first row that sees the lane's key, minus 8 for
+// the upper half of the wave. Returns dV^T and dK^T (unscaled).
+__device__ __forceinline__ void dkdv_loop(
+    int n_t, int j_free, int ng, int h_last, int q0_last, int cq_m1, unsigned rdst,
+    unsigned tdst, int r5, int t5, int l1, unsigned loffl, unsigned qhs,
+    unsigned qths, unsigned lhs, float c, const void* qb, const void* db, const void* qtb,
+    const void* dotb, const void* lsb, unsigned rbase, unsigned tbase, unsigned lbase, int lmin,
+    int vhead, unsigned lo, const unsigned (&rrow)[5], const unsigned (&rch)[5],
+    const unsigned (&tofs)[5], const bf16x8 (&kr)[8], const bf16x8 (&vr_)[8], int q0c, int q0n,
+    int q0f, int hn, int hf, int hi, floatx16 (&dv)[4], floatx16 (&dk)[4]) {{
+  int t, js, sx, sy, sz, sh, sq;
+  int rb = 0, tb = 0;
+  const long long x5r = r5 ? -1ll : 0ll, x5t = t5 ? -1ll : 0ll, xl = l1 ? -1ll : 0ll;
+  auto lo32 = [](const void* p) {{ return (unsigned)(unsigned long long)(size_t)p; }};
+  auto hi32 = [](const void* p) {{ return (unsigned)((unsigned long long)(size_t)p >> 32); }};
+  const unsigned qb_lo = lo32(qb), qb_hi = hi32(qb), db_lo = lo32(db), db_hi = hi32(db);
+  const unsigned qtb_lo = lo32(qtb), qtb_hi = hi32(qtb), dotb_lo = lo32(dotb), dotb_hi = hi32(dotb);
+  const unsigned lsb_lo = lo32(lsb), lsb_hi = hi32(lsb);
+  asm volatile(
+{body}
+      : {", ".join(outs)}
+      : {", ".join(ins)}
+      : {", ".join(clob)});
+}}
+
+}}  // namespace dkdvw
+}}  // namespace ra
+'''
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "attn_bwd_dkdv_loop.h")
+    with open(path, "w") as f:
+        f.write(out)
+    return path
+
+
+if __name__ == "__main__":
+    print(main())
