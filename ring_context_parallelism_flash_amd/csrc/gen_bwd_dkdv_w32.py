@@ -7,10 +7,11 @@ accumulators stay in AGPRs. The workgroup's four waves walk one stream of
 64-query tiles (every query head of the group, latest tile first) in 32-query
 sub-tiles j. With p = exp2(S c - lse2) and dS = p (dP - delta):
   phase A(j): the S = Q K^T and dP = dO V^T MFMAs of sub-tile j+1 (Q and dO
-              rows from LDS) with the p / dS arithmetic of sub-tile j between
-              them;
-  phase B(j): dV^T += dO^T P and dK^T += Q^T dS of sub-tile j (dO^T and Q^T
-              tiles from LDS).
+              rows from LDS) with p of sub-tile j between them;
+  phase B(j): dV^T += dO^T P, then dK^T += Q^T dS of sub-tile j (dO^T and
+              Q^T tiles from LDS), with dS computed between the dV MFMAs.
+Splitting the arithmetic this way keeps each phase's vector work inside the
+matrix pipe's shadow (the exp is a quarter-rate instruction).
 The probabilities use the saved lse ("Sequence Parallelism in Large Language
 Models ...", section "The Activation Memory Wall": recomputation instead of
 stored activations), so there is no running max; the causal mask is applied
@@ -42,7 +43,8 @@ Register plan (one wave per SIMD):
   a[128:159] K, a[160:191] V of the wave's keys (eight k-steps of 4)
   v56 rows read address, v57 Q^T read address, v58 lse2 / delta read address,
   v[59:62] temporaries, v[64:79] operand ring
-  v[80:111], v[112:143]: lse2 (16) then delta (16) of a sub-tile, per parity
+  v[80:95]: lse2 of a sub-tile; v[96:111], v[112:127]: delta, per parity
+  v[128:143]: fp32 p of the sub-tile between its phases A and B
   v[144:175], v[176:207]: S (16) then dP (16), per parity
   v[208:223], v[224:239]: bf16 P (8) then dS (8), per parity
   v[240:244]: row offsets of the row tile loads
@@ -54,10 +56,12 @@ Hazards the statement respects by construction: a transcendental result is
 read no earlier than the second instruction after it; MFMA results are read
 by vector instructions only a phase later, or by the out-of-line mask and
 after the statement, each behind s_nop 7 x 3; S and dP accumulate in two
-alternating chains, dV^T / dK^T in eight; the P / dS a phase B reads are
-rewritten only two phases later; an M0 write is followed by one wait state
-before the LDS-DMA load that reads it; an SALU write of the lane select is
-four wait states before the v_readlane that uses it.
+alternating chains, each dV^T / dK^T tile every fourth MFMA; a dS register
+is written at least one MFMA before the MFMA that reads it, and P / dS are
+rewritten only a phase after their last reader; an M0 write is followed by
+one wait state (the step's MFMA) before the LDS-DMA load that reads it; an
+SALU write of the lane select is four wait states before the v_readlane
+that uses it.
 
 Run: python gen_bwd_dkdv_w32.py  (writes the header next to this file)
 """
@@ -85,7 +89,9 @@ DV_, DK_, K_, V_ = 0, 64, 128, 160
 V_RADDR, V_TADDR, V_LADDR = 56, 57, 58
 T0, T1, T2, T3 = 59, 60, 61, 62
 RING = 64
-LX_ = {0: 80, 1: 112}        # lse2 at +0..15, delta at +16..31
+LX = 80                      # lse2 of the sub-tile whose p is next
+DX_ = {0: 96, 1: 112}        # delta, per parity
+P32 = 128                    # fp32 p
 SD_ = {0: 144, 1: 176}       # S at +0..15, dP at +16..31
 PD_ = {0: 208, 1: 224}       # P at +0..7, dS at +8..15
 VOFF = 240
@@ -111,10 +117,16 @@ def a_off(i):
     return (i & 1) * RBUF + 32 * (i >> 1)
 
 
+def b_kind(i):
+    """Phase B MFMA i: (dK?, 16-query half u, d tile T); the dV MFMAs (both
+    halves) come first."""
+    return i >= 2 * DT, (i // DT) % 2, i % DT
+
+
 def b_off(i):
-    """Phase B read i: even = dO^T (dV), odd = Q^T (dK); d tile (i/2) % DT,
-    16-query half i / (2 DT)."""
-    return (0 if i & 1 else TBUF) + 32 * ((i >> 1) % DT) * TROW + 32 * (i // (2 * DT))
+    """Phase B read i: dO^T (dV) or Q^T (dK) rows of d tile T, half u."""
+    dk, u, T = b_kind(i)
+    return (0 if dk else TBUF) + 32 * T * TROW + 32 * u
 
 
 class Gen:
@@ -127,7 +139,7 @@ class Gen:
         self.q = []          # outstanding reads: (id, tag)
         self.n = 0
         self.ring_id = [None] * PF
-        self.lx_id = {}      # (parity, register base) -> read id
+        self.lx_id = {}      # register base -> read id of an lse2 / delta read
 
     def add(self, lines):
         self.lines += lines
@@ -163,33 +175,35 @@ class Gen:
         return [f"ds_read_b128 {ring(slot)}, v{addr} offset:{off}"]
 
     def lse_read(self, par, k, half):
-        """Read k (0..7) of a sub-tile's lse2 (k < 4) / delta, four floats:
-        rows 16w + 4m' .. +3 of the sub-tile for k % 4 = 2w + m'."""
-        base = LX_[par] + (16 if k >= 4 else 0) + 4 * (k % 4)
+        """Read k (0..7) of a sub-tile's lse2 (k < 4, into LX) / delta (into
+        DX_[par]), four floats: rows 16w + 4m' .. +3 of the sub-tile for
+        k % 4 = 2w + m' (element e of a lane is register e)."""
+        base = (DX_[par] if k >= 4 else LX) + 4 * (k % 4)
         off = (OFF_DL if k >= 4 else OFF_L) + [0, 16, 64, 80][k % 4] + (HALF_L if half else 0)
-        self.lx_id[(par, base)] = self.issue(("lx", par, base))
+        self.lx_id[base] = self.issue(("lx", base))
         return [f"ds_read_b128 {vr(base, 4)}, v{V_LADDR} offset:{off}"]
 
-    def need_lx(self, par, e):
-        out = []
-        for base in (LX_[par] + 4 * (e // 4), LX_[par] + 16 + 4 * (e // 4)):
-            x = self.lx_id.pop((par, base), None)
-            if x is not None:
-                out += self.wait(x)
-        return out
+    def need(self, base):
+        """Waits before a use of the four registers at base (an lse2 or
+        delta read)."""
+        x = self.lx_id.pop(base, None)
+        return self.wait(x) if x is not None else []
 
-    def phase(self, mfma, addr, off, work=None, pre_in=False, nxt=None, extra=None):
+    def phase(self, mfma, addr, off, work=None, pre_in=False, nxt=None, extra=None,
+              pre=None):
         """N MFMAs; MFMA i reads operand i (address register addr, offset
-        off(i)) through the ring. After MFMA i: the read of operand i + PF
-        (the last PF steps issue the first reads of the next phase: nxt()
-        gives (addr, off) then, after the extras before it), work(i) (items:
-        instruction strings, or (parity, element) for the lse2 / delta that
-        the next instructions use) and extra(i)."""
+        off(i)) through the ring. Step i: pre(i), MFMA i, the read of operand
+        i + PF (the last PF steps issue the first reads of the next phase:
+        nxt() gives (addr, off) then, after the extras before it), work(i)
+        (instruction strings, or the register base of an lse2 / delta read
+        the next ones use) and extra(i)."""
         if not pre_in:
             for i in range(PF):
                 self.add(self.read(i, addr, off(i)))
         for i in range(N):
             self.add(self.wait(self.ring_id[i % PF]))
+            if pre:
+                self.add(pre(i))
             self.add([mfma(i)])
             if i + PF < N:
                 self.add(self.read(i % PF, addr, off(i + PF)))
@@ -198,10 +212,7 @@ class Gen:
                 self.add(self.read(i % PF, a, o(i + PF - N)))
             if work:
                 for item in work(i):
-                    if isinstance(item, tuple):
-                        self.add(self.need_lx(*item))
-                    else:
-                        self.add([item])
+                    self.add(self.need(item) if isinstance(item, int) else [item])
             if extra:
                 self.add(extra(i))
 
@@ -219,40 +230,53 @@ def a_mfma(par):
 
 
 def b_mfma(par):
-    """dV^T (even i) / dK^T (odd i), d tile (i/2) % DT, 16-query half
-    i / (2 DT), from P / dS of parity par."""
+    """dV^T / dK^T MFMA i (b_kind), from P / dS of parity par."""
     P, dS = PD_[par], PD_[par] + 8
 
     def f(i):
-        T, u = (i >> 1) % DT, i // (2 * DT)
-        acc, b = (DK_ + 16 * T, dS + 4 * u) if i & 1 else (DV_ + 16 * T, P + 4 * u)
+        dk, u, T = b_kind(i)
+        acc, b = (DK_ + 16 * T, dS + 4 * u) if dk else (DV_ + 16 * T, P + 4 * u)
         return f"v_mfma_f32_32x32x16_bf16 {ar(acc, 16)}, {ring(i)}, {vr(b, 4)}, {ar(acc, 16)}"
     return f
 
 
-def arith(par):
-    """p and dS of the sub-tile of parity par: elements 2k, 2k+1 in two
-    parts, after MFMAs 2k and 2k+1. Element e of a lane is query 16(e/8) +
-    8hh + e%8 of the sub-tile; bf16 pairs pack as register 4(e/8) + (e%8)/2."""
-    S, dP = SD_[par], SD_[par] + 16
-    LX, DX = LX_[par], LX_[par] + 16
-    Pr, dSr = PD_[par], PD_[par] + 8
+def p_work(par):
+    """p = exp2(S c - lse2) of the sub-tile of parity par (into P32) and its
+    bf16 copy: elements 2k, 2k+1 after MFMA 2k, their packing after MFMA
+    2k+1 (a transcendental result is not read by the next instruction).
+    Element e of a lane is query 16(e/8) + 8hh + e%8 of the sub-tile; bf16
+    pairs pack as register 4(e/8) + (e%8)/2."""
+    S, Pr = SD_[par], PD_[par]
 
     def f(i):
         e = 2 * (i // 2)
-        reg = 4 * (e >> 3) + ((e & 7) >> 1)
         if i % 2 == 0:
-            return [(par, e),
-                    f"v_fma_f32 v{T0}, v{S + e}, %[c], -v{LX + e}",
-                    f"v_fma_f32 v{T1}, v{S + e + 1}, %[c], -v{LX + e + 1}",
-                    f"v_exp_f32 v{T0}, v{T0}",
-                    f"v_exp_f32 v{T1}, v{T1}"]
-        return [f"v_sub_f32 v{T2}, v{dP + e}, v{DX + e}",
+            return [LX + 4 * (e // 4),
+                    f"v_fma_f32 v{P32 + e}, v{S + e}, %[c], -v{LX + e}",
+                    f"v_fma_f32 v{P32 + e + 1}, v{S + e + 1}, %[c], -v{LX + e + 1}",
+                    f"v_exp_f32 v{P32 + e}, v{P32 + e}",
+                    f"v_exp_f32 v{P32 + e + 1}, v{P32 + e + 1}"]
+        return [f"v_cvt_pk_bf16_f32 v{Pr + 4 * (e >> 3) + ((e & 7) >> 1)}, v{P32 + e}, "
+                f"v{P32 + e + 1}"]
+    return f
+
+
+def ds_work(par):
+    """dS = p (dP - delta) of the sub-tile of parity par, bf16: elements
+    2k, 2k+1 after MFMA k of its phase B (k < 8): the first half's before
+    the last dV MFMA of that half, the second's a dK tile ahead of use."""
+    dP, DX, dSr = SD_[par] + 16, DX_[par], PD_[par] + 8
+
+    def f(i):
+        if i >= 8:
+            return []
+        e = 2 * i
+        return [DX + 4 * (e // 4),
+                f"v_sub_f32 v{T2}, v{dP + e}, v{DX + e}",
                 f"v_sub_f32 v{T3}, v{dP + e + 1}, v{DX + e + 1}",
-                f"v_cvt_pk_bf16_f32 v{Pr + reg}, v{T0}, v{T1}",
-                f"v_mul_f32 v{T2}, v{T0}, v{T2}",
-                f"v_mul_f32 v{T3}, v{T1}, v{T3}",
-                f"v_cvt_pk_bf16_f32 v{dSr + reg}, v{T2}, v{T3}"]
+                f"v_mul_f32 v{T2}, v{P32 + e}, v{T2}",
+                f"v_mul_f32 v{T3}, v{P32 + e + 1}, v{T3}",
+                f"v_cvt_pk_bf16_f32 v{dSr + 4 * (e >> 3) + ((e & 7) >> 1)}, v{T2}, v{T3}"]
     return f
 
 
@@ -275,14 +299,25 @@ def mask(G, par, q_sgpr, site):
 
 def chunk_loads(dst_base, lo, x5, sb, vaddr):
     """The five 1 KiB chunk loads of one tensor of a tile (the fifth under
-    the exec mask x5): chunk j of this wave lands at dst_base + lo + 4096 j."""
+    the exec mask x5): chunk j of this wave lands at dst_base + lo + 4096 j.
+    Each is (M0 write, load): the write goes before a step's MFMA, the load
+    after it."""
     g = []
     for j in range(5):
-        pre = [f"s_add_u32 m0, {dst_base}, {lo + 4096 * j}"]
-        pre += ["s_nop 0"] if j < 4 else [f"s_mov_b64 exec, {x5}"]
-        g.append(pre + [f"global_load_lds_dwordx4 {vaddr(j)}, s[{sb}:{sb + 1}]"] +
-                 (["s_mov_b64 exec, -1"] if j == 4 else []))
+        ld = [f"global_load_lds_dwordx4 {vaddr(j)}, s[{sb}:{sb + 1}]"]
+        if j == 4:
+            ld = [f"s_mov_b64 exec, {x5}"] + ld + ["s_mov_b64 exec, -1"]
+        g.append(([f"s_add_u32 m0, {dst_base}, {lo + 4096 * j}"], ld))
     return g
+
+
+# phase A steps that take a tile load, the light (odd) ones first
+LOAD_STEPS = [1, 3, 5, 7, 9, 11, 13, 15, 0, 2, 4, 6, 8]
+
+
+def place_loads(loads):
+    at = {LOAD_STEPS[k]: g for k, g in enumerate(loads)}
+    return (lambda i: at[i][0] if i in at else []), (lambda i: at[i][1] if i in at else [])
 
 
 def trans_setup():
@@ -353,8 +388,9 @@ def loop_asm():
     G.add(["s_waitcnt vmcnt(8)", "s_barrier"])
     tl = chunk_loads("%[sz]", 0, "%[x5t]", SB_A, lambda j: f"%[to{j}]") + \
         chunk_loads("%[sz]", TBUF, "%[x5t]", SB_B, lambda j: f"%[to{j}]")
-    G.phase(a_mfma(1), V_RADDR, lambda i: a_off(i) + HALF_R, work=arith(0), pre_in=True,
-            nxt=lambda: (V_TADDR, b_off), extra=lambda i: tl[i] if i < len(tl) else [])
+    pre, post = place_loads(tl)
+    G.phase(a_mfma(1), V_RADDR, lambda i: a_off(i) + HALF_R, work=p_work(0), pre_in=True,
+            nxt=lambda: (V_TADDR, b_off), pre=pre, extra=post)
     G.add(["s_add_u32 %[js], %[js], 1", "s_add_u32 %[sq], %[q0c], 32"])
     mask(G, 1, "%[sq]", "e")
     G.add([f"v_add_u32 v{V_LADDR}, %[rb], %[lbase]"])
@@ -367,24 +403,25 @@ def loop_asm():
         if i == BARRIER_STEP:
             # the rows of tile t are read for the last time: wait for this
             # wave's lse2 / delta reads, then the odd barrier
-            for key in [k for k in G.lx_id if k[0] == 1]:
-                out += G.wait(G.lx_id.pop(key))
+            for base in [LX + 4 * m for m in range(4)] + [DX_[1] + 4 * m for m in range(4)]:
+                out += G.need(base)
             out += ["s_waitcnt vmcnt(8)", "s_barrier", f"s_xor_b32 %[sx], %[rb], {ROWS_BUF}",
                     f"v_add_u32 v{V_RADDR}, %[sx], %[rbase]"]
         if i > BARRIER_STEP:
             out += rs[i - BARRIER_STEP - 1]
         return out
-    G.phase(b_mfma(0), V_TADDR, b_off, pre_in=True, nxt=lambda: (V_RADDR, a_off),
-            extra=even_b_extra)
+    G.phase(b_mfma(0), V_TADDR, b_off, work=ds_work(0), pre_in=True,
+            nxt=lambda: (V_RADDR, a_off), extra=even_b_extra)
 
     # ================= odd sub-tile 2t+1 (tile t, second half)
     rl = chunk_loads("%[sz]", 0, "%[x5r]", SB_A, lambda j: f"v{VOFF + j}") + \
         chunk_loads("%[sz]", RBUF, "%[x5r]", SB_B, lambda j: f"v{VOFF + j}") + \
-        [["s_add_u32 m0, %[sz], %[loffl]", "s_mov_b64 exec, %[xl]",
-          f"global_load_lds_dwordx4 %[lo], s[{SB_L}:{SB_L + 1}]", "s_mov_b64 exec, -1"]]
-    G.phase(a_mfma(0), V_RADDR, a_off, work=arith(1), pre_in=True,
-            nxt=lambda: (V_TADDR, lambda i: b_off(i) + HALF_T),
-            extra=lambda i: rl[i] if i < len(rl) else [])
+        [(["s_add_u32 m0, %[sz], %[loffl]"],
+          ["s_mov_b64 exec, %[xl]", f"global_load_lds_dwordx4 %[lo], s[{SB_L}:{SB_L + 1}]",
+           "s_mov_b64 exec, -1"])]
+    pre, post = place_loads(rl)
+    G.phase(a_mfma(0), V_RADDR, a_off, work=p_work(1), pre_in=True,
+            nxt=lambda: (V_TADDR, lambda i: b_off(i) + HALF_T), pre=pre, extra=post)
     G.add(["s_add_u32 %[js], %[js], 1"])
     mask(G, 0, "%[q0n]", "o")
     G.add([f"s_xor_b32 %[sx], %[rb], {ROWS_BUF}", f"v_add_u32 v{V_LADDR}, %[sx], %[lbase]"])
@@ -395,13 +432,13 @@ def loop_asm():
         out = []
         if i < 4:   # lse2 / delta of sub-tile 2t+2 (tile t+1, first half)
             out += G.lse_read(0, 2 * i, False) + G.lse_read(0, 2 * i + 1, False)
-        if 4 <= i < 4 + len(adv):
-            out += adv[i - 4]
+        if 8 <= i < 8 + len(adv):
+            out += adv[i - 8]
         if i == 12:  # the last read of the transposed tile t went out at MFMA 11
             out += [f"v_add_u32 v{V_TADDR}, %[tb], %[tbase]"] + ts
         return out
     # V_RADDR stays at tile t+1's rows: the next phase A reads their second half
-    G.phase(b_mfma(1), V_TADDR, lambda i: b_off(i) + HALF_T, pre_in=True,
+    G.phase(b_mfma(1), V_TADDR, lambda i: b_off(i) + HALF_T, work=ds_work(1), pre_in=True,
             nxt=lambda: (V_RADDR, lambda i: a_off(i) + HALF_R), extra=odd_b_extra)
     assert G.shape() == entry, (G.shape(), entry)
     G.add(["s_cmp_lt_u32 %[t], %[nt]", f"s_cbranch_scc1 {G.lab('loop')}"])
