@@ -672,7 +672,7 @@ ra_status ra_block_attn_bwd(const void* q, const void* k, const void* v, const v
   memset(&a, 0, sizeof a);
   a.q = q; a.k = k; a.v = v; a.dout = dout;
   a.qt = ws + L.qt; a.dot = ws + L.dot; a.kt = ws + L.kt;
-  a.lse2 = (const float*)(ws + L.lse2); a.delta = (const float*)(ws + L.delta);
+  a.lse2 = (const float*)(ws + L.lse2); a.ndelta = (const float*)(ws + L.delta);
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.q_hs = Cq * D;            a.q_bs = (int64_t)Hq * a.q_hs;
   a.k_hs = Ck * D;            a.k_bs = (int64_t)Hkv * a.k_hs;
@@ -800,7 +800,7 @@ ra_status ra_ring_sim_bwd(const void* q, const void* k, const void* v, const voi
       a.dot = pw + L.P.dot + (size_t)r * D * Cp * 2;
       a.kt = pw + L.P.kt + (size_t)src * D * Cp * 2;
       a.lse2 = (const float*)(pw + L.P.lse2) + (size_t)r * Cp;
-      a.delta = (const float*)(pw + L.P.delta) + (size_t)r * Cp;
+      a.ndelta = (const float*)(pw + L.P.delta) + (size_t)r * Cp;
       a.dq = dq_acc + (size_t)r * C * D;
       a.dk = dk_acc + (size_t)src * C * D;
       a.dv = dv_acc + (size_t)src * C * D;

@@ -275,7 +275,7 @@ struct DkdvProbs {
   const floatx16& S;
   const floatx16& dP;
   f32x4 (&lx)[4];  // lse2 of rows 16w + jj: lx[2w + jj/4][jj%4]
-  f32x4 (&dx)[4];  // delta, same layout
+  f32x4 (&dx)[4];  // minus delta, same layout
   float c;
   int lim;
   bf16x8 (&Pb)[2];
@@ -293,12 +293,12 @@ struct DkdvProbs {
     for (int e = I * PER; e < (I + 1) * PER; ++e) {
       const int w = e >> 3, jj = e & 7;
       const float l2 = lx[2 * w + (jj >> 2)][jj & 3];
-      const float dl = dx[2 * w + (jj >> 2)][jj & 3];
+      const float ndl = dx[2 * w + (jj >> 2)][jj & 3];
       float sc = fmaf(S[e], c, -l2);
       if constexpr (MASK) sc = (16 * w + jj < lim) ? -INFINITY : sc;
       const float p = __builtin_amdgcn_exp2f(sc);
       Pb[w][jj] = (__bf16)p;
-      dSb[w][jj] = (__bf16)(p * (dP[e] - dl));
+      dSb[w][jj] = (__bf16)(p * (dP[e] + ndl));
     }
   }
 };
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
     load_trans_tile<D>(reinterpret_cast<const __bf16*>(a.dot) + toff, a.Cqp, B0 + L::TBUF, wv,
                        lane);
     if (wv == 0) load_lds16(a.lse2 + loff + 4 * (lane & 15), B0 + OFF_L);
-    if (wv == 1) load_lds16(a.delta + loff + 4 * (lane & 15), B0 + OFF_DL);
+    if (wv == 1) load_lds16(a.ndelta + loff + 4 * (lane & 15), B0 + OFF_DL);
   };
   // LDS address of the A operands of S / dP for sub-tile jn: kperm'd rows, so
   // element i of a lane's result is query 32(jn%2) + 16(i/8) + 8hh + i%8
@@ -529,7 +529,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(const BwdArgs a) {
       const int64_t toff = b * a.qt_bs + ls.h * a.qt_hs + ls.q0;
       src0 = reinterpret_cast<const unsigned char*>(reinterpret_cast<const __bf16*>(a.qt) + toff);
       src1 = reinterpret_cast<const unsigned char*>(reinterpret_cast<const __bf16*>(a.dot) + toff);
-      src2 = (wv == 0 ? a.lse2 : a.delta) + b * a.l_bs + ls.h * a.l_hs + ls.q0 + 4 * (lane & 15);
+      src2 = (wv == 0 ? a.lse2 : a.ndelta) + b * a.l_bs + ls.h * a.l_hs + ls.q0 + 4 * (lane & 15);
       dst = lds + OFF_TRANS + (Tu & 1) * TRANS_BUF;
     }
     // step I < J: chunk I of the first tensor, J <= I < 2J: chunk I - J of
@@ -714,7 +714,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_w32(const BwdArgs a) {
     load_row_tile<D>(db + h * a.q_hs + (int64_t)q0 * D, a.Cq - 1 - q0, B0 + L::RBUF, wv, lane);
     if (wv == 1) load_lds16(a.lse2 + b * a.l_bs + h * a.l_hs + q0 + 4 * (lane & 15), B0 + dkdvw::kOffL);
     if (wv == 2)
-      load_lds16(a.delta + b * a.l_bs + h * a.l_hs + q0 + 4 * (lane & 15), B0 + dkdvw::kOffL + 1024);
+      load_lds16(a.ndelta + b * a.l_bs + h * a.l_hs + q0 + 4 * (lane & 15), B0 + dkdvw::kOffL + 1024);
   };
   load_rows(0, 0);
   load_rows(min(1, NT - 1), 1);
@@ -753,7 +753,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_w32(const BwdArgs a) {
       uni(wv == 1 || wv == 2), uni(dkdvw::kOffL + (wv == 2 ? 1024 : 0) - wv * 1024),
       uni((int)(a.q_hs * 2)), uni((int)(a.qt_hs * 2)), uni((int)(a.l_hs * 4)), a.scale_log2,
       uni_ptr(qb), uni_ptr(db), uni_ptr(qtb), uni_ptr(dotb),
-      uni_ptr((wv == 1 ? a.lse2 : a.delta) + b * a.l_bs), lrows + kperm(n) * L::ROW + hh * 16,
+      uni_ptr((wv == 1 ? a.lse2 : a.ndelta) + b * a.l_bs), lrows + kperm(n) * L::ROW + hh * 16,
       ltrans + n * L::TROW + hh * 16, lrows + 32 * hh, row_min - 8 * hh, vhead, 16 * (lane & 15),
       rrow, rch, tofs, kreg, vreg, q0_at(0), q0_at(1), q0_at(2), head_at(1 % ng),
       head_at(2 % ng), uni(2 % ng), dVt, dKt);
@@ -892,7 +892,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void attn_bwd_dq(const BwdArgs a)
   // read its last row; those rows' dq is never written)
   const int ql = min(qi, a.Cqp - 1);
   const float lse2 = a.lse2[b * a.l_bs + h * a.l_hs + ql];
-  const float dlt = a.delta[b * a.l_bs + h * a.l_hs + ql];
+  const float dlt = -a.ndelta[b * a.l_bs + h * a.l_hs + ql];
   const int qpos = pos_of(a.qp, qc);
   // keys this lane's query sees: a prefix of the block (positions increase)
   const int n_allow = a.causal ? allowed_prefix(a.kp, qpos) : a.Ck;
@@ -1087,9 +1087,9 @@ __global__ __launch_bounds__(64 * kDqW64Waves, 1) void attn_bwd_dq_w64(const Bwd
   }
   const int l0 = min(qw0 + n, a.Cqp - 1), l1 = min(qw0 + 32 + n, a.Cqp - 1);
   const float* lb = a.lse2 + b * a.l_bs + h * a.l_hs;
-  const float* dlb = a.delta + b * a.l_bs + h * a.l_hs;
+  const float* ndlb = a.ndelta + b * a.l_bs + h * a.l_hs;
   const float nl20 = -lb[l0], nl21 = -lb[l1];
-  const float dlt0 = dlb[l0], dlt1 = dlb[l1];
+  const float dlt0 = -ndlb[l0], dlt1 = -ndlb[l1];
   const int nal0 = a.causal ? allowed_prefix(a.kp, pos_of(a.qp, r0)) : a.Ck;
   const int nal1 = a.causal ? allowed_prefix(a.kp, pos_of(a.qp, r1)) : a.Ck;
   // first 32-key sub-tile with a key some row of the wave may not see (its
@@ -1140,14 +1140,15 @@ __global__ __launch_bounds__(64 * kDqW64Waves, 1) void attn_bwd_dq_w64(const Bwd
 }
 
 // ---------------------------------------------------------------------------
-// delta = <dout, out> and lse in exp2 units, per query row, padded.
+// -delta = -<dout, out> (stored negated: the dK / dV kernel starts its dP
+// accumulation from it) and lse in exp2 units, per query row, padded.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict__ out,
                                                        const __bf16* __restrict__ dout,
                                                        const float* __restrict__ lse,
                                                        float* __restrict__ lse2p,
-                                                       float* __restrict__ deltap,
+                                                       float* __restrict__ ndeltap,
                                                        int64_t rows_total, int64_t nblk,
                                                        int64_t C, int64_t Cp, int64_t o_bh,
                                                        int64_t l_bh) {
@@ -1183,7 +1184,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict_
         const float l = lse[bh * l_bh + blk * C + i];
         l2 = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
       }
-      deltap[row] = valid ? acc : 0.f;
+      ndeltap[row] = valid ? -acc : 0.f;
       lse2p[row] = l2;
     }
   }
@@ -1287,7 +1288,7 @@ hipError_t launch_bwd_dq(BwdArgs a, int D, hipStream_t s) {
 }
 
 hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, float* lse2p,
-                           float* deltap, int64_t BH, int64_t nblk, int64_t C, int64_t Cp, int D,
+                           float* ndeltap, int64_t BH, int64_t nblk, int64_t C, int64_t Cp, int D,
                            int64_t o_bh, int64_t l_bh, hipStream_t s) {
   const int64_t rows = BH * nblk * Cp;
   if (rows == 0) return hipSuccess;
@@ -1297,10 +1298,10 @@ hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, 
   const __bf16* o = reinterpret_cast<const __bf16*>(out);
   const __bf16* d = reinterpret_cast<const __bf16*>(dout);
   if (D == 128)
-    hipLaunchKernelGGL(bwd_prep_kernel<128>, grid, dim3(256), 0, s, o, d, lse, lse2p, deltap, rows,
+    hipLaunchKernelGGL(bwd_prep_kernel<128>, grid, dim3(256), 0, s, o, d, lse, lse2p, ndeltap, rows,
                        nblk, C, Cp, o_bh, l_bh);
   else
-    hipLaunchKernelGGL(bwd_prep_kernel<64>, grid, dim3(256), 0, s, o, d, lse, lse2p, deltap, rows,
+    hipLaunchKernelGGL(bwd_prep_kernel<64>, grid, dim3(256), 0, s, o, d, lse, lse2p, ndeltap, rows,
                        nblk, C, Cp, o_bh, l_bh);
   return hipGetLastError();
 }

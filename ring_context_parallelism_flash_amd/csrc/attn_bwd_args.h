@@ -15,7 +15,7 @@ namespace ra {
 // Backward of one (query block, key block) pair, bf16 inputs. Element strides;
 // rows of q/dout and k/v are contiguous (row stride D). The transposed copies
 // qt/dot ([.., D, Cqp]) and kt ([.., D, Ckp]) and the per-row arrays
-// lse2/delta ([.., Cqp]) are padded (zero columns / +inf, 0 rows).
+// lse2/ndelta ([.., Cqp]) are padded (zero columns / +inf, 0 rows).
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -25,7 +25,7 @@ struct BwdArgs {
   const void* dot;     // dO^T
   const void* kt;      // K^T
   const float* lse2;   // lse * log2(e), +inf for rows without a key or padding
-  const float* delta;  // <dout, out> per row, 0 for padding
+  const float* ndelta;  // minus <dout, out> per row, 0 for padding
   float* dq;           // fp32 accumulators (added to)
   float* dk;
   float* dv;

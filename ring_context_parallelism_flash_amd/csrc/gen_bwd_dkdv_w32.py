@@ -7,21 +7,25 @@ accumulators stay in AGPRs. The workgroup's four waves walk one stream of
 64-query tiles (every query head of the group, latest tile first) in 32-query
 sub-tiles j. With p = exp2(S c - lse2) and dS = p (dP - delta):
   phase A(j): the S = Q K^T and dP = dO V^T MFMAs of sub-tile j+1 (Q and dO
-              rows from LDS) with p of sub-tile j between them;
+              rows from LDS) with dS of sub-tile j between them;
   phase B(j): dV^T += dO^T P, then dK^T += Q^T dS of sub-tile j (dO^T and
-              Q^T tiles from LDS), with dS computed between the dV MFMAs.
-Splitting the arithmetic this way keeps each phase's vector work inside the
-matrix pipe's shadow (the exp is a quarter-rate instruction).
+              Q^T tiles from LDS), with p of sub-tile j+1 between them.
+Each MFMA thus carries about a third of its shadow in vector work (the exp
+is a quarter-rate instruction), and no phase waits on its own arithmetic.
 The probabilities use the saved lse ("Sequence Parallelism in Large Language
 Models ...", section "The Activation Memory Wall": recomputation instead of
 stored activations), so there is no running max; the causal mask is applied
 out of line to the sub-tiles from the stream's first partly visible one.
 
-Every LDS operand read goes through one ring of four registers; the last four
-reads of each phase are the next phase's first. A sub-tile's lse2 / delta are
-read during the phase B before its arithmetic. The generator tracks every LDS
-read it emits and gives each use the exact lgkmcnt wait it needs (LDS reads
-return in order, and the statement issues no other LGKM operation).
+Every LDS operand read goes through one ring of eight 4-register slots (the
+latency of LDS reads under this load is several MFMAs long); the last eight
+reads of each phase are the next phase's first. The lse2 of sub-tile j+1 is
+read during phase A(j), minus its delta (stored negated) during phase B(j-1):
+it is the starting accumulator of the dP chain, which so ends at dP - delta. The generator tracks
+every LDS read it emits and gives each use the exact lgkmcnt wait it needs
+(LDS reads return in order, and the statement issues no other LGKM
+operation), and it checks the wait states between each MFMA and the vector
+instructions that read its result.
 
 LDS holds two row buffers [Q rows | dO rows | lse2 | delta] and two
 transposed buffers [Q^T | dO^T], filled by direct global->LDS loads, each
@@ -30,9 +34,9 @@ tile t+1, the odd one the rows (with lse2 / delta) of tile t+2; a tile past
 the stream's end repeats the last one. Two barriers per tile:
   even barrier (before phase A(2t)): publishes the transposed tile t and
     frees the other transposed buffer (phase B(2t-1) is done);
-  odd barrier (after MFMA 11 of phase B(2t)): publishes the rows of tile t+1
+  odd barrier (after MFMA 7 of phase B(2t)): publishes the rows of tile t+1
     and frees the rows of tile t (both of its phases A and its lse2 / delta
-    reads, waited for right before the barrier, are done); the last four
+    reads, waited for right before the barrier, are done); the last eight
     MFMAs of phase B(2t) then issue the first reads of tile t+1.
 Each barrier waits only for the loads before the latest batch (vmcnt(8):
 every batch gives each wave at least eight loads), so a batch has about two
@@ -42,9 +46,8 @@ Register plan (one wave per SIMD):
   a[0:63] dV^T, a[64:127] dK^T (four 32-wide d tiles of 16 registers each)
   a[128:159] K, a[160:191] V of the wave's keys (eight k-steps of 4)
   v56 rows read address, v57 Q^T read address, v58 lse2 / delta read address,
-  v[59:62] temporaries, v[64:79] operand ring
-  v[80:95]: lse2 of a sub-tile; v[96:111], v[112:127]: delta, per parity
-  v[128:143]: fp32 p of the sub-tile between its phases A and B
+  v[59:62] temporaries, v[64:79] and v[128:143] operand ring
+  v[80:95] lse2, v[96:111] minus delta, v[112:127] fp32 p, each of one sub-tile
   v[144:175], v[176:207]: S (16) then dP (16), per parity
   v[208:223], v[224:239]: bf16 P (8) then dS (8), per parity
   v[240:244]: row offsets of the row tile loads
@@ -56,9 +59,9 @@ Hazards the statement respects by construction: a transcendental result is
 read no earlier than the second instruction after it; MFMA results are read
 by vector instructions only a phase later, or by the out-of-line mask and
 after the statement, each behind s_nop 7 x 3; S and dP accumulate in two
-alternating chains, each dV^T / dK^T tile every fourth MFMA; a dS register
-is written at least one MFMA before the MFMA that reads it, and P / dS are
-rewritten only a phase after their last reader; an M0 write is followed by
+alternating chains, each dV^T / dK^T tile every fourth MFMA; P / dS are
+written a phase before the MFMAs that read them and rewritten only after
+them; an M0 write is followed by
 one wait state (the step's MFMA) before the LDS-DMA load that reads it; an
 SALU write of the lane select is four wait states before the v_readlane
 that uses it.
@@ -66,6 +69,7 @@ that uses it.
 Run: python gen_bwd_dkdv_w32.py  (writes the header next to this file)
 """
 import os
+import re
 
 D = 128
 KS = D // 16                # k-steps of the S / dP products
@@ -82,22 +86,23 @@ HALF_T = 64                 # ... of a transposed tile (bytes)
 HALF_L = 128                # ... of lse2 / delta (bytes)
 N = 2 * KS                  # MFMAs (and operand reads) per phase
 assert N == 4 * DT == 16
-PF = 4
+PF = 8                      # operand reads in flight
 NEG_INF = "0xff800000"
 
 DV_, DK_, K_, V_ = 0, 64, 128, 160
 V_RADDR, V_TADDR, V_LADDR = 56, 57, 58
 T0, T1, T2, T3 = 59, 60, 61, 62
-RING = 64
+RING, RING2 = 64, 128         # operand ring: slots 0-3, 4-7
 LX = 80                      # lse2 of the sub-tile whose p is next
-DX_ = {0: 96, 1: 112}        # delta, per parity
-P32 = 128                    # fp32 p
+DX = 96                      # delta of the sub-tile whose dS is next
+P32 = 112                    # fp32 p of that sub-tile
+XDL_WAIT = 19                # wait states between an MFMA and a vector read of its result
 SD_ = {0: 144, 1: 176}       # S at +0..15, dP at +16..31
 PD_ = {0: 208, 1: 224}       # P at +0..7, dS at +8..15
 VOFF = 240
 SB_A, SB_B, SB_L = 80, 82, 84
 PAD = ["s_nop 7", "s_nop 7", "s_nop 7"]
-BARRIER_STEP = 11            # phase B(2t): the odd barrier follows this MFMA
+BARRIER_STEP = N - PF - 1    # phase B(2t): the odd barrier follows this MFMA
 
 
 def vr(base, n):
@@ -109,7 +114,8 @@ def ar(base, n):
 
 
 def ring(i):
-    return vr(RING + 4 * (i % PF), 4)
+    slot = i % PF
+    return vr(RING + 4 * slot if slot < 4 else RING2 + 4 * (slot - 4), 4)
 
 
 def a_off(i):
@@ -153,6 +159,7 @@ class Gen:
     def issue(self, tag):
         self.n += 1
         self.q.append((self.n, tag))
+        assert len(self.q) <= 15, "more LDS reads in flight than lgkmcnt counts"
         return self.n
 
     def wait(self, x):
@@ -174,14 +181,19 @@ class Gen:
         self.ring_id[slot] = self.issue(("ring", slot))
         return [f"ds_read_b128 {ring(slot)}, v{addr} offset:{off}"]
 
-    def lse_read(self, par, k, half):
+    def lse_read(self, k, half):
         """Read k (0..7) of a sub-tile's lse2 (k < 4, into LX) / delta (into
-        DX_[par]), four floats: rows 16w + 4m' .. +3 of the sub-tile for
-        k % 4 = 2w + m' (element e of a lane is register e)."""
-        base = (DX_[par] if k >= 4 else LX) + 4 * (k % 4)
+        DX), four floats: rows 16w + 4m' .. +3 of the sub-tile for k % 4 =
+        2w + m' (element e of a lane is register e)."""
+        base = (DX if k >= 4 else LX) + 4 * (k % 4)
         off = (OFF_DL if k >= 4 else OFF_L) + [0, 16, 64, 80][k % 4] + (HALF_L if half else 0)
         self.lx_id[base] = self.issue(("lx", base))
         return [f"ds_read_b128 {vr(base, 4)}, v{V_LADDR} offset:{off}"]
+
+    def need_all(self, bases):
+        """One wait for the youngest of several lse2 / delta reads."""
+        ids = [self.lx_id.pop(b) for b in bases if b in self.lx_id]
+        return self.wait(max(ids)) if ids else []
 
     def need(self, base):
         """Waits before a use of the four registers at base (an lse2 or
@@ -201,7 +213,12 @@ class Gen:
             for i in range(PF):
                 self.add(self.read(i, addr, off(i)))
         for i in range(N):
-            self.add(self.wait(self.ring_id[i % PF]))
+            # one wait serves a pair of MFMAs (an instruction slot is the
+            # scarce resource with one wave per SIMD)
+            if i % 2 == 0:
+                self.add(self.wait(self.ring_id[(i + 1) % PF]))
+            else:
+                self.add(self.wait(self.ring_id[i % PF]))
             if pre:
                 self.add(pre(i))
             self.add([mfma(i)])
@@ -218,13 +235,14 @@ class Gen:
 
 
 def a_mfma(par):
-    """S (even i) and dP (odd i) of parity par, k-step i / 2; C = 0 first."""
+    """S (even i) and dP (odd i) of parity par, k-step i / 2. S starts from
+    0, dP from minus delta (DX), so the chain ends at dP - delta."""
     S, P = SD_[par], SD_[par] + 16
 
     def f(i):
         s = i >> 1
         dst, b = (P, V_) if i & 1 else (S, K_)
-        c = "0" if s == 0 else vr(dst, 16)
+        c = vr(dst, 16) if s else (vr(DX, 16) if i & 1 else "0")
         return f"v_mfma_f32_32x32x16_bf16 {vr(dst, 16)}, {ring(i)}, {ar(b + 4 * s, 4)}, {c}"
     return f
 
@@ -240,43 +258,49 @@ def b_mfma(par):
     return f
 
 
-def p_work(par):
-    """p = exp2(S c - lse2) of the sub-tile of parity par (into P32) and its
-    bf16 copy: elements 2k, 2k+1 after MFMA 2k, their packing after MFMA
-    2k+1 (a transcendental result is not read by the next instruction).
-    Element e of a lane is query 16(e/8) + 8hh + e%8 of the sub-tile; bf16
-    pairs pack as register 4(e/8) + (e%8)/2."""
-    S, Pr = SD_[par], PD_[par]
+def p_pair(par, k):
+    """p = exp2(S c - lse2) of elements 2k, 2k+1 of the sub-tile of parity
+    par, into P32, in two parts (the second exp a step later); the bf16
+    packing of pair k - 1 leads the first part (a transcendental result is
+    not read by the next instruction). Element e of a lane is query 16(e/8)
+    + 8hh + e%8 of the sub-tile; bf16 pairs pack as register 4(e/8) + (e%8)/2."""
+    S, e = SD_[par], 2 * k
+    first = ([p_pack(par, k - 1)] if k else []) + [
+        LX + 4 * (e // 4),
+        f"v_fma_f32 v{P32 + e}, v{S + e}, %[c], -v{LX + e}",
+        f"v_fma_f32 v{P32 + e + 1}, v{S + e + 1}, %[c], -v{LX + e + 1}",
+        f"v_exp_f32 v{P32 + e}, v{P32 + e}"]
+    return first, [f"v_exp_f32 v{P32 + e + 1}, v{P32 + e + 1}"]
 
+
+def p_pack(par, k):
+    e = 2 * k
+    return f"v_cvt_pk_bf16_f32 v{PD_[par] + 4 * (e >> 3) + ((e & 7) >> 1)}, v{P32 + e}, v{P32 + e + 1}"
+
+
+def p_work(par):
+    """p of the sub-tile of parity par over the 16 steps of a phase B; the
+    last pair's packing is left to the next phase A."""
     def f(i):
-        e = 2 * (i // 2)
-        if i % 2 == 0:
-            return [LX + 4 * (e // 4),
-                    f"v_fma_f32 v{P32 + e}, v{S + e}, %[c], -v{LX + e}",
-                    f"v_fma_f32 v{P32 + e + 1}, v{S + e + 1}, %[c], -v{LX + e + 1}",
-                    f"v_exp_f32 v{P32 + e}, v{P32 + e}",
-                    f"v_exp_f32 v{P32 + e + 1}, v{P32 + e + 1}"]
-        return [f"v_cvt_pk_bf16_f32 v{Pr + 4 * (e >> 3) + ((e & 7) >> 1)}, v{P32 + e}, "
-                f"v{P32 + e + 1}"]
+        first, second = p_pair(par, i // 2)
+        return first if i % 2 == 0 else second
     return f
 
 
 def ds_work(par):
-    """dS = p (dP - delta) of the sub-tile of parity par, bf16: elements
-    2k, 2k+1 after MFMA k of its phase B (k < 8): the first half's before
-    the last dV MFMA of that half, the second's a dK tile ahead of use."""
-    dP, DX, dSr = SD_[par] + 16, DX_[par], PD_[par] + 8
+    """dS = p (dP - delta) of the sub-tile of parity par, bf16, over the 16
+    steps of its phase A (dP - delta comes out of the MFMA chain): elements
+    2k, 2k+1 after MFMA 2k, their packing after MFMA 2k+1; step 0 first packs
+    the last pair of p."""
+    dP, dSr = SD_[par] + 16, PD_[par] + 8
 
     def f(i):
-        if i >= 8:
-            return []
-        e = 2 * i
-        return [DX + 4 * (e // 4),
-                f"v_sub_f32 v{T2}, v{dP + e}, v{DX + e}",
-                f"v_sub_f32 v{T3}, v{dP + e + 1}, v{DX + e + 1}",
-                f"v_mul_f32 v{T2}, v{P32 + e}, v{T2}",
-                f"v_mul_f32 v{T3}, v{P32 + e + 1}, v{T3}",
-                f"v_cvt_pk_bf16_f32 v{dSr + 4 * (e >> 3) + ((e & 7) >> 1)}, v{T2}, v{T3}"]
+        e = 2 * (i // 2)
+        if i % 2 == 0:
+            return ([p_pack(par, 7)] if i == 0 else []) + [
+                f"v_mul_f32 v{T2}, v{P32 + e}, v{dP + e}",
+                f"v_mul_f32 v{T3}, v{P32 + e + 1}, v{dP + e + 1}"]
+        return [f"v_cvt_pk_bf16_f32 v{dSr + 4 * (e >> 3) + ((e & 7) >> 1)}, v{T2}, v{T3}"]
     return f
 
 
@@ -371,46 +395,75 @@ def advance():
 def loop_asm():
     G = Gen()
     G.add(["s_waitcnt lgkmcnt(0)"] + [f"v_accvgpr_write_b32 a{r}, 0" for r in range(128)])
-    # prologue: S / dP of sub-tile 0 (rows buffer 0, first half) and its
-    # lse2 / delta; the last steps start the reads of sub-tile 1
+    LXB = [LX + 4 * m for m in range(4)]
+    DXB = [DX + 4 * m for m in range(4)]
+
+    def lx_reads(half):
+        """lse2 of a sub-tile: one read at each of steps 0..3."""
+        return lambda i: G.lse_read(i, half) if i < 4 else []
+
+    def dx_reads(half, first):
+        """minus delta of a sub-tile: one read at each of steps first..first+3."""
+        return lambda i: G.lse_read(4 + i - first, half) if first <= i < first + 4 else []
+
+    def dx_wait(pre=None):
+        """Before MFMA 1 (the first dP MFMA, which starts from minus delta):
+        wait for the delta reads."""
+        return lambda i: (G.need_all(DXB) if i == 1 else []) + (pre(i) if pre else [])
+
+    # prologue: lse2 / delta of sub-tile 0, its S / dP (the last steps start
+    # the reads of sub-tile 1; delta of sub-tile 1 is read once the first dP
+    # MFMA has taken sub-tile 0's) and its p. V_LADDR stays at the rows
+    # buffer of tile t+1 from the middle of sub-tile 2t on.
     G.add([f"v_mov_b32 v{V_RADDR}, %[rbase]", f"v_mov_b32 v{V_LADDR}, %[lbase]",
            f"v_mov_b32 v{V_TADDR}, %[tbase]"])
+    for k in range(8):
+        G.add(G.lse_read(k, False))
+    G.add(G.need_all(LXB + DXB))
     G.phase(a_mfma(0), V_RADDR, a_off, nxt=lambda: (V_RADDR, lambda i: a_off(i) + HALF_R),
-            extra=lambda i: (G.lse_read(0, 2 * i, False) + G.lse_read(0, 2 * i + 1, False))
-            if i < 4 else [])
+            extra=dx_reads(True, 3))
     G.add(PAD + ["s_mov_b32 %[js], 0"])
     mask(G, 0, "%[q0c]", "pro")
+    for k in range(8):
+        first, second = p_pair(0, k)
+        for item in first + ["s_nop 0"] + second + ["s_nop 0"]:
+            G.add(G.need(item) if isinstance(item, int) else [item])
     G.add(["s_mov_b32 %[t], 0"] + trans_setup())
     entry = G.shape()
     G.place("loop")
+
+    def work(a, b):
+        return lambda i: a(i) + b(i)
 
     # ================= even sub-tile 2t (tile t, first half)
     G.add(["s_waitcnt vmcnt(8)", "s_barrier"])
     tl = chunk_loads("%[sz]", 0, "%[x5t]", SB_A, lambda j: f"%[to{j}]") + \
         chunk_loads("%[sz]", TBUF, "%[x5t]", SB_B, lambda j: f"%[to{j}]")
     pre, post = place_loads(tl)
-    G.phase(a_mfma(1), V_RADDR, lambda i: a_off(i) + HALF_R, work=p_work(0), pre_in=True,
-            nxt=lambda: (V_TADDR, b_off), pre=pre, extra=post)
+    # S / dP of sub-tile 2t+1, dS of 2t; lse2 of 2t+1 (this tile's second half)
+    G.phase(a_mfma(1), V_RADDR, lambda i: a_off(i) + HALF_R,
+            work=work(ds_work(0), lx_reads(True)), pre_in=True,
+            nxt=lambda: (V_TADDR, b_off), pre=dx_wait(pre), extra=post)
     G.add(["s_add_u32 %[js], %[js], 1", "s_add_u32 %[sq], %[q0c], 32"])
     mask(G, 1, "%[sq]", "e")
-    G.add([f"v_add_u32 v{V_LADDR}, %[rb], %[lbase]"])
+    G.add(["s_nop 1",   # wait states before phase B's first read of S
+           f"s_xor_b32 %[sx], %[rb], {ROWS_BUF}", f"v_add_u32 v{V_LADDR}, %[sx], %[lbase]"])
     rs = rows_setup()
+    dxr = dx_reads(False, BARRIER_STEP + 1)
 
     def even_b_extra(i):
         out = []
-        if i < 4:   # lse2 / delta of sub-tile 2t+1 (this tile's second half)
-            out += G.lse_read(1, 2 * i, True) + G.lse_read(1, 2 * i + 1, True)
         if i == BARRIER_STEP:
-            # the rows of tile t are read for the last time: wait for this
-            # wave's lse2 / delta reads, then the odd barrier
-            for base in [LX + 4 * m for m in range(4)] + [DX_[1] + 4 * m for m in range(4)]:
-                out += G.need(base)
+            # the rows of tile t are read for the last time (this wave's
+            # lse2 / delta reads of them have been waited for): odd barrier
+            out += G.need_all(LXB + DXB)
             out += ["s_waitcnt vmcnt(8)", "s_barrier", f"s_xor_b32 %[sx], %[rb], {ROWS_BUF}",
                     f"v_add_u32 v{V_RADDR}, %[sx], %[rbase]"]
-        if i > BARRIER_STEP:
+        if BARRIER_STEP < i <= BARRIER_STEP + len(rs):
             out += rs[i - BARRIER_STEP - 1]
-        return out
-    G.phase(b_mfma(0), V_TADDR, b_off, work=ds_work(0), pre_in=True,
+        return out + dxr(i)   # delta of sub-tile 2t+2 (tile t+1, just published)
+    # dV / dK of sub-tile 2t, p of 2t+1
+    G.phase(b_mfma(0), V_TADDR, b_off, work=p_work(1), pre_in=True,
             nxt=lambda: (V_RADDR, a_off), extra=even_b_extra)
 
     # ================= odd sub-tile 2t+1 (tile t, second half)
@@ -420,34 +473,82 @@ def loop_asm():
           ["s_mov_b64 exec, %[xl]", f"global_load_lds_dwordx4 %[lo], s[{SB_L}:{SB_L + 1}]",
            "s_mov_b64 exec, -1"])]
     pre, post = place_loads(rl)
-    G.phase(a_mfma(0), V_RADDR, a_off, work=p_work(1), pre_in=True,
-            nxt=lambda: (V_TADDR, lambda i: b_off(i) + HALF_T), pre=pre, extra=post)
+    # S / dP of sub-tile 2t+2, dS of 2t+1; lse2 of 2t+2 (tile t+1, first half)
+    G.phase(a_mfma(0), V_RADDR, a_off, work=work(ds_work(1), lx_reads(False)),
+            pre_in=True, nxt=lambda: (V_TADDR, lambda i: b_off(i) + HALF_T), pre=dx_wait(pre),
+            extra=post)
     G.add(["s_add_u32 %[js], %[js], 1"])
     mask(G, 0, "%[q0n]", "o")
-    G.add([f"s_xor_b32 %[sx], %[rb], {ROWS_BUF}", f"v_add_u32 v{V_LADDR}, %[sx], %[lbase]"])
+    G.add(["s_nop 3"])   # wait states before phase B's first read of S
     adv = advance()
     ts = trans_setup()
+    dxr1 = dx_reads(True, 0)
 
     def odd_b_extra(i):
-        out = []
-        if i < 4:   # lse2 / delta of sub-tile 2t+2 (tile t+1, first half)
-            out += G.lse_read(0, 2 * i, False) + G.lse_read(0, 2 * i + 1, False)
+        out = dxr1(i)   # delta of sub-tile 2t+3 (tile t+1, second half)
         if 8 <= i < 8 + len(adv):
             out += adv[i - 8]
-        if i == 12:  # the last read of the transposed tile t went out at MFMA 11
+        if i == 12:  # the last read of the transposed tile t went out earlier
             out += [f"v_add_u32 v{V_TADDR}, %[tb], %[tbase]"] + ts
         return out
-    # V_RADDR stays at tile t+1's rows: the next phase A reads their second half
-    G.phase(b_mfma(1), V_TADDR, lambda i: b_off(i) + HALF_T, work=ds_work(1), pre_in=True,
+    # dV / dK of sub-tile 2t+1, p of 2t+2. V_RADDR stays at tile t+1's rows:
+    # the next phase A reads their second half
+    G.phase(b_mfma(1), V_TADDR, lambda i: b_off(i) + HALF_T, work=p_work(0), pre_in=True,
             nxt=lambda: (V_RADDR, lambda i: a_off(i) + HALF_R), extra=odd_b_extra)
     assert G.shape() == entry, (G.shape(), entry)
     G.add(["s_cmp_lt_u32 %[t], %[nt]", f"s_cbranch_scc1 {G.lab('loop')}"])
+    body = G.lines[G.lines.index(f"{G.lab('loop')}:"):]
+    check_hazards(G.lines[:G.lines.index(f"{G.lab('loop')}:")] + body + body)
     # no load or read is left in flight when the statement ends
     G.add(["s_waitcnt vmcnt(0)", "s_waitcnt lgkmcnt(0)", f"s_branch {G.lab('done')}"])
     G.add(G.ool)
     G.place("done")
     G.add(PAD)
     return G.lines
+
+
+REG = re.compile(r"\bv(\d+)\b|\bv\[(\d+):(\d+)\]")
+
+
+def regs(text):
+    out = set()
+    for m in REG.finditer(text):
+        if m.group(1):
+            out.add(int(m.group(1)))
+        else:
+            out.update(range(int(m.group(2)), int(m.group(3)) + 1))
+    return out
+
+
+def check_hazards(lines):
+    """The straight-line path (prologue, then the loop body twice): every
+    vector instruction that reads or writes an MFMA result register is at
+    least XDL_WAIT wait states after that MFMA, and no instruction reads a
+    transcendental result right after it is written."""
+    last = {}       # register -> wait-state index of the MFMA that writes it
+    trans = set()   # registers written by the previous instruction, if a transcendental
+    ws = 0
+    for ln in lines:
+        if ln.endswith(":"):
+            continue
+        op, _, rest = ln.partition(" ")
+        if op == "s_nop":
+            ws += int(rest) + 1
+            trans = set()
+            continue
+        ops = rest.split(",")
+        if op.startswith("v_mfma"):
+            for r in regs(",".join(ops[1:3])):   # A, B operands: no result reads
+                assert ws - last.get(r, -99) >= XDL_WAIT, ln
+            for r in regs(ops[0]):
+                last[r] = ws
+        elif op.startswith("v_") and not op.startswith("v_accvgpr"):
+            used = regs(rest)
+            for r in used:
+                assert ws - last.get(r, -99) >= XDL_WAIT, (ln, ws - last[r])
+            assert not (regs(",".join(ops[1:])) & trans), ln
+        trans = regs(ops[0]) if op in ("v_exp_f32",) else set()
+        ws += 1
 
 
 def main():

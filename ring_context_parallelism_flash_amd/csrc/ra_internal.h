@@ -19,9 +19,9 @@ namespace ra {
 // delta[row] = <dout, out> and lse2[row] = lse * log2(e) (+inf for -inf) for
 // rows (bh, blk, i), i < C, of [BH][nblk*C][D] bf16 arrays (bh stride o_bh
 // elements; lse bh stride l_bh); written to [BH][nblk][Cp] with padding rows
-// i >= C set to delta 0, lse2 +inf.
+// i >= C set to 0, lse2 +inf. ndeltap receives minus delta.
 hipError_t launch_bwd_prep(const void* out, const void* dout, const float* lse, float* lse2p,
-                           float* deltap, int64_t BH, int64_t nblk, int64_t C, int64_t Cp, int D,
+                           float* ndeltap, int64_t BH, int64_t nblk, int64_t C, int64_t Cp, int D,
                            int64_t o_bh, int64_t l_bh, hipStream_t s);
 
 // dst[i] = bf16(src[i]) (round to nearest even), n a multiple of 4.
