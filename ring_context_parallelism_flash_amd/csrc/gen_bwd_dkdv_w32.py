@@ -17,9 +17,8 @@ Models ...", section "The Activation Memory Wall": recomputation instead of
 stored activations), so there is no running max; the causal mask is applied
 out of line to the sub-tiles from the stream's first partly visible one.
 
-Every LDS operand read goes through one ring of eight 4-register slots (the
-latency of LDS reads under this load is several MFMAs long); the last eight
-reads of each phase are the next phase's first. The lse2 of sub-tile j+1 is
+Every LDS operand read goes through one ring of four 4-register slots; the
+last four reads of each phase are the next phase's first. The lse2 of sub-tile j+1 is
 read during phase A(j), minus its delta (stored negated) during phase B(j-1):
 it is the starting accumulator of the dP chain, which so ends at dP - delta. The generator tracks
 every LDS read it emits and gives each use the exact lgkmcnt wait it needs
@@ -34,10 +33,11 @@ tile t+1, the odd one the rows (with lse2 / delta) of tile t+2; a tile past
 the stream's end repeats the last one. Two barriers per tile:
   even barrier (before phase A(2t)): publishes the transposed tile t and
     frees the other transposed buffer (phase B(2t-1) is done);
-  odd barrier (after MFMA 7 of phase B(2t)): publishes the rows of tile t+1
+  odd barrier (after MFMA 11 of phase B(2t)): publishes the rows of tile t+1
     and frees the rows of tile t (both of its phases A and its lse2 / delta
-    reads, waited for right before the barrier, are done); the last eight
-    MFMAs of phase B(2t) then issue the first reads of tile t+1.
+    reads, waited for right before the barrier, are done); the last four
+    MFMAs of phase B(2t) then issue the first reads of tile t+1. (Placed as
+    late as the ring allows: the rows loads it waits for get the most time.)
 Each barrier waits only for the loads before the latest batch (vmcnt(8):
 every batch gives each wave at least eight loads), so a batch has about two
 sub-tiles to land.
@@ -46,7 +46,7 @@ Register plan (one wave per SIMD):
   a[0:63] dV^T, a[64:127] dK^T (four 32-wide d tiles of 16 registers each)
   a[128:159] K, a[160:191] V of the wave's keys (eight k-steps of 4)
   v56 rows read address, v57 Q^T read address, v58 lse2 / delta read address,
-  v[59:62] temporaries, v[64:79] and v[128:143] operand ring
+  v[59:62] temporaries, v[64:79] operand ring
   v[80:95] lse2, v[96:111] minus delta, v[112:127] fp32 p, each of one sub-tile
   v[144:175], v[176:207]: S (16) then dP (16), per parity
   v[208:223], v[224:239]: bf16 P (8) then dS (8), per parity
@@ -86,13 +86,13 @@ HALF_T = 64                 # ... of a transposed tile (bytes)
 HALF_L = 128                # ... of lse2 / delta (bytes)
 N = 2 * KS                  # MFMAs (and operand reads) per phase
 assert N == 4 * DT == 16
-PF = 8                      # operand reads in flight
+PF = 4                      # operand reads in flight
 NEG_INF = "0xff800000"
 
 DV_, DK_, K_, V_ = 0, 64, 128, 160
 V_RADDR, V_TADDR, V_LADDR = 56, 57, 58
 T0, T1, T2, T3 = 59, 60, 61, 62
-RING, RING2 = 64, 128         # operand ring: slots 0-3, 4-7
+RING, RING2 = 64, 128         # operand ring: slots 0-3 (4-7 if PF = 8)
 LX = 80                      # lse2 of the sub-tile whose p is next
 DX = 96                      # delta of the sub-tile whose dS is next
 P32 = 112                    # fp32 p of that sub-tile
@@ -260,17 +260,17 @@ def b_mfma(par):
 
 def p_pair(par, k):
     """p = exp2(S c - lse2) of elements 2k, 2k+1 of the sub-tile of parity
-    par, into P32, in two parts (the second exp a step later); the bf16
-    packing of pair k - 1 leads the first part (a transcendental result is
-    not read by the next instruction). Element e of a lane is query 16(e/8)
-    + 8hh + e%8 of the sub-tile; bf16 pairs pack as register 4(e/8) + (e%8)/2."""
+    par, into P32, in two parts: (fma, fma, exp) and (exp, packing of pair
+    k - 1), so both steps of a pair carry a similar share of the issue slots
+    (a transcendental result is not read by the next instruction). Element e
+    of a lane is query 16(e/8) + 8hh + e%8 of the sub-tile; bf16 pairs pack
+    as register 4(e/8) + (e%8)/2."""
     S, e = SD_[par], 2 * k
-    first = ([p_pack(par, k - 1)] if k else []) + [
-        LX + 4 * (e // 4),
-        f"v_fma_f32 v{P32 + e}, v{S + e}, %[c], -v{LX + e}",
-        f"v_fma_f32 v{P32 + e + 1}, v{S + e + 1}, %[c], -v{LX + e + 1}",
-        f"v_exp_f32 v{P32 + e}, v{P32 + e}"]
-    return first, [f"v_exp_f32 v{P32 + e + 1}, v{P32 + e + 1}"]
+    first = [LX + 4 * (e // 4),
+             f"v_fma_f32 v{P32 + e}, v{S + e}, %[c], -v{LX + e}",
+             f"v_fma_f32 v{P32 + e + 1}, v{S + e + 1}, %[c], -v{LX + e + 1}",
+             f"v_exp_f32 v{P32 + e}, v{P32 + e}"]
+    return first, [f"v_exp_f32 v{P32 + e + 1}, v{P32 + e + 1}"] + ([p_pack(par, k - 1)] if k else [])
 
 
 def p_pack(par, k):
@@ -290,17 +290,17 @@ def p_work(par):
 def ds_work(par):
     """dS = p (dP - delta) of the sub-tile of parity par, bf16, over the 16
     steps of its phase A (dP - delta comes out of the MFMA chain): elements
-    2k, 2k+1 after MFMA 2k, their packing after MFMA 2k+1; step 0 first packs
+    2k, 2k+1 after MFMA 2k, their packing after MFMA 2k+1; step 1 also packs
     the last pair of p."""
     dP, dSr = SD_[par] + 16, PD_[par] + 8
 
     def f(i):
         e = 2 * (i // 2)
         if i % 2 == 0:
-            return ([p_pack(par, 7)] if i == 0 else []) + [
-                f"v_mul_f32 v{T2}, v{P32 + e}, v{dP + e}",
-                f"v_mul_f32 v{T3}, v{P32 + e + 1}, v{dP + e + 1}"]
-        return [f"v_cvt_pk_bf16_f32 v{dSr + 4 * (e >> 3) + ((e & 7) >> 1)}, v{T2}, v{T3}"]
+            return [f"v_mul_f32 v{T2}, v{P32 + e}, v{dP + e}",
+                    f"v_mul_f32 v{T3}, v{P32 + e + 1}, v{dP + e + 1}"]
+        return ([p_pack(par, 7)] if i == 1 else []) + [
+            f"v_cvt_pk_bf16_f32 v{dSr + 4 * (e >> 3) + ((e & 7) >> 1)}, v{T2}, v{T3}"]
     return f
 
 
@@ -399,8 +399,8 @@ def loop_asm():
     DXB = [DX + 4 * m for m in range(4)]
 
     def lx_reads(half):
-        """lse2 of a sub-tile: one read at each of steps 0..3."""
-        return lambda i: G.lse_read(i, half) if i < 4 else []
+        """lse2 of a sub-tile: one read at each of steps 1, 3, 5, 7."""
+        return lambda i: G.lse_read(i // 2, half) if i % 2 and i < 8 else []
 
     def dx_reads(half, first):
         """minus delta of a sub-tile: one read at each of steps first..first+3."""
