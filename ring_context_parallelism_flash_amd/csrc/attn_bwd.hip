@@ -645,17 +645,19 @@ constexpr size_t dkdv_w32_lds_bytes() {
   return 2 * (size_t)dkdvw::kRowsBuf + 2 * (size_t)dkdvw::kTransBuf;
 }
 
+template <bool RAGGED>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_w32(const BwdArgs a) {
-  constexpr int D = 128, NW = 4;
+  constexpr int D = 128, NW = 4, NC = dkdvw::kChunks;
   using L = BwdLds<D>;
   constexpr int KS = D / 16, DT = D / 32;
-  static_assert(dkdvw::kRowsBuf == 2 * L::RBUF + 2048 && dkdvw::kTransBuf == 2 * L::TBUF &&
-                    dkdvw::kOffL == 2 * L::RBUF && L::RINS == 17 && L::TINS == 18 &&
+  static_assert(dkdvw::kOffL == L::RBUF && dkdvw::kOffDO == L::RBUF + 1024 &&
+                    dkdvw::kRowsBuf == 2 * L::RBUF + 2048 && dkdvw::kTransBuf == 2 * L::TBUF &&
+                    L::RINS == 17 && L::TINS == 18 && NC * NW * 1024 == dkdvw::kRowsBuf &&
                     dkdv_w32_lds_bytes() <= 160 * 1024,
                 "LDS layout of the one-wave-per-SIMD dK / dV kernel");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  unsigned char* Rows = lds;                            // [2][Q | dO | lse2 | delta]
-  unsigned char* Trans = lds + 2 * dkdvw::kRowsBuf;     // [2][Q^T | dO^T]
+  unsigned char* Rows = lds;                         // [2][Q | lse2 | dO | minus delta]
+  unsigned char* Trans = lds + 2 * dkdvw::kRowsBuf;  // [2][Q^T | dO^T]
 
   const int item = xcd_item(a.n_items, a.per_xcd);
   if (item < 0) return;
@@ -704,17 +706,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_w32(const BwdArgs a) {
   const __bf16* db = reinterpret_cast<const __bf16*>(a.dout) + b * a.q_bs;
   const __bf16* qtb = reinterpret_cast<const __bf16*>(a.qt) + b * a.qt_bs;
   const __bf16* dotb = reinterpret_cast<const __bf16*>(a.dot) + b * a.qt_bs;
+  const float* lse2b = a.lse2 + b * a.l_bs;
+  const float* ndlb = a.ndelta + b * a.l_bs;
 
-  // prologue loads: rows (with lse2 / delta) of tiles 0 and 1 (the last if
-  // the stream has one tile), the transposed tile 0
+  // prologue loads: rows (with lse2 / minus delta) of tiles 0 and 1 (the
+  // last if the stream has one tile), the transposed tile 0
   auto load_rows = [&](int T, int buf) {
     const int h = head_at(T % ng), q0 = q0_at(T);
     unsigned char* B0 = Rows + buf * dkdvw::kRowsBuf;
     load_row_tile<D>(qb + h * a.q_hs + (int64_t)q0 * D, a.Cq - 1 - q0, B0, wv, lane);
-    load_row_tile<D>(db + h * a.q_hs + (int64_t)q0 * D, a.Cq - 1 - q0, B0 + L::RBUF, wv, lane);
-    if (wv == 1) load_lds16(a.lse2 + b * a.l_bs + h * a.l_hs + q0 + 4 * (lane & 15), B0 + dkdvw::kOffL);
-    if (wv == 2)
-      load_lds16(a.ndelta + b * a.l_bs + h * a.l_hs + q0 + 4 * (lane & 15), B0 + dkdvw::kOffL + 1024);
+    load_row_tile<D>(db + h * a.q_hs + (int64_t)q0 * D, a.Cq - 1 - q0, B0 + dkdvw::kOffDO, wv,
+                     lane);
+    if (wv == 1) load_lds16(lse2b + h * a.l_hs + q0 + 4 * (lane & 15), B0 + dkdvw::kOffL);
+    if (wv == 3) load_lds16(ndlb + h * a.l_hs + q0 + 4 * (lane & 15), B0 + dkdvw::kOffDL);
   };
   load_rows(0, 0);
   load_rows(min(1, NT - 1), 1);
@@ -724,17 +728,35 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_w32(const BwdArgs a) {
     load_trans_tile<D>(dotb + h * a.qt_hs + q0, a.Cqp, Trans + L::TBUF, wv, lane);
   }
 
-  // Per-lane parts of this wave's loop loads (chunk wv + 4j of a tile): row
-  // and byte offset within a 64-row tile, byte offset within a transposed
-  // tile
-  uint32_t rrow[5], rch[5], tofs[5];
+  // The loop's loads: wave w fills chunks 9w .. 9w+8 of each buffer. Rows:
+  // waves 0 / 1 the Q rows (chunks 0-8 / 9-16) and w1 also lse2, waves 2 / 3
+  // the dO rows and w3 also minus delta; transposed: waves 0 / 1 Q^T, 2 / 3
+  // dO^T (chunks 0-8 / 9-17 of the tensor). Lane offsets of each load within
+  // the tile, minus the load's own offset (loads 0-4 are placed from chunk
+  // 4, loads 5-8 from chunk 8).
+  unsigned rv[NC], rc[NC], tv[NC];
 #pragma unroll
-  for (int jj = 0; jj < 5; ++jj) {
-    const int P = (wv + NW * jj) * 64 + lane;
-    const int cr = P % L::RCPR, ct = P % 9;
-    rrow[jj] = (uint32_t)(P / L::RCPR);
-    rch[jj] = (uint32_t)(cr < L::CPR ? cr : 0) * 16u;
-    tofs[jj] = ((uint32_t)(P / 9) * (uint32_t)a.Cqp + (uint32_t)(ct < 8 ? ct : 0) * 8u) * 2u;
+  for (int j = 0; j < NC; ++j) {
+    const unsigned adj = (unsigned)((j < 5 ? 4 - j : 8 - j) * 1024);
+    const int cj = NC * (wv & 1) + j;  // chunk within the tensor
+    unsigned row, rch;
+    if ((wv & 1) && j == NC - 1) {     // lse2 / minus delta: 64 floats, lanes 16+ repeat
+      row = 0;
+      rch = 16u * (lane & 15);
+    } else {
+      const int P = cj * 64 + lane, cr = P % L::RCPR;
+      row = (unsigned)(P / L::RCPR);
+      rch = (unsigned)(cr < L::CPR ? cr : 0) * 16u;
+    }
+    if (RAGGED) {
+      rv[j] = row;
+      rc[j] = rch + adj;
+    } else {
+      rv[j] = row * (D * 2) + rch + adj;
+      rc[j] = 0;
+    }
+    const int P = cj * 64 + lane, ct = P % 9;
+    tv[j] = ((unsigned)(P / 9) * (unsigned)a.Cqp + (unsigned)(ct < 8 ? ct : 0) * 8u) * 2u + adj;
   }
   // Query tiles that start at or after every lane's first allowed row hold
   // no masked pair; the stream walks tiles latest first, so they are its
@@ -744,19 +766,21 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_w32(const BwdArgs a) {
       a.causal ? first_row_at(a.qp, a.Cq, pos_of(a.kp, min(kw0 + 31, a.Ck - 1))) : 0;
   const int j_free = 2 * ng * min(n_t, max(0, t_lo + n_t - (rmax + 63) / 64));
   const unsigned lrows = lds_addr(Rows), ltrans = lds_addr(Trans);
+  const void* lastb = wv == 0 ? (const void*)qb : wv == 1 ? (const void*)lse2b
+                    : wv == 2 ? (const void*)db : (const void*)ndlb;
   lds_loads_barrier();
 
   floatx16 dVt[DT], dKt[DT];
-  dkdvw::dkdv_loop(
+  (RAGGED ? dkdvw::dkdv_loop_ragged : dkdvw::dkdv_loop)(
       NT, uni(j_free), uni(ng), head_at((NT - 1) % ng), q0_at(NT - 1), uni(a.Cq - 1),
-      uni(lrows + wv * 1024), uni(ltrans + wv * 1024), uni(wv == 0), uni(wv <= 1),
-      uni(wv == 1 || wv == 2), uni(dkdvw::kOffL + (wv == 2 ? 1024 : 0) - wv * 1024),
-      uni((int)(a.q_hs * 2)), uni((int)(a.qt_hs * 2)), uni((int)(a.l_hs * 4)), a.scale_log2,
-      uni_ptr(qb), uni_ptr(db), uni_ptr(qtb), uni_ptr(dotb),
-      uni_ptr((wv == 1 ? a.lse2 : a.ndelta) + b * a.l_bs), lrows + kperm(n) * L::ROW + hh * 16,
-      ltrans + n * L::TROW + hh * 16, lrows + 32 * hh, row_min - 8 * hh, vhead, 16 * (lane & 15),
-      rrow, rch, tofs, kreg, vreg, q0_at(0), q0_at(1), q0_at(2), head_at(1 % ng),
-      head_at(2 % ng), uni(2 % ng), dVt, dKt);
+      uni(lrows + (NC * wv + 4) * 1024), uni(ltrans + (NC * wv + 4) * 1024),
+      uni((int)(a.q_hs * 2)), uni((int)(a.qt_hs * 2)),
+      uni((wv & 1) ? (int)(a.l_hs * 4) : (int)(a.q_hs * 2)), uni((wv & 1) ? 2 : 8), a.scale_log2,
+      uni_ptr(wv < 2 ? (const void*)qb : (const void*)db), uni_ptr(lastb),
+      uni_ptr(wv < 2 ? (const void*)qtb : (const void*)dotb), lrows + kperm(n) * L::ROW + hh * 16,
+      ltrans + n * L::TROW + hh * 16, lrows + 32 * hh, row_min - 8 * hh, vhead, rv, rc, tv, kreg,
+      vreg, q0_at(0), q0_at(1), q0_at(2), head_at(1 % ng), head_at(2 % ng), uni(2 % ng), dVt,
+      dKt);
 
   // epilogue: add into the fp32 accumulators; lane holds key kw0+n,
   // d = 32T + 8(i/4) + 4hh + i%4
@@ -1261,8 +1285,10 @@ hipError_t launch_bwd_dkdv(BwdArgs a, int D, hipStream_t s) {
   a.per_xcd = (a.n_items + kXcds - 1) / kXcds;
   if (a.n_items <= 0) return hipSuccess;
   const int grid = a.per_xcd * kXcds;
-  if (D == 128 && dkdv_w32_fits(a))
-    return launch_big(attn_bwd_dkdv_w32, dkdv_w32_lds_bytes(), grid, a, s);
+  if (D == 128 && dkdv_w32_fits(a)) {
+    if (a.Cq % 64 == 0) return launch_big(attn_bwd_dkdv_w32<false>, dkdv_w32_lds_bytes(), grid, a, s);
+    return launch_big(attn_bwd_dkdv_w32<true>, dkdv_w32_lds_bytes(), grid, a, s);
+  }
   if (D == 128) return launch_big(attn_bwd_dkdv<128>, dkdv_lds_bytes<128>(), grid, a, s);
   return launch_big(attn_bwd_dkdv<64>, dkdv_lds_bytes<64>(), grid, a, s);
 }

@@ -78,9 +78,13 @@ ROW = (D // 8 + 1) * 16     # padded Q / dO row, bytes
 TROW = 9 * 16               # padded row of a transposed tile (64 queries + pad)
 RBUF = 64 * ROW
 TBUF = D * TROW
-OFF_L, OFF_DL = 2 * RBUF, 2 * RBUF + 1024
-ROWS_BUF = 2 * RBUF + 2048  # Q rows, dO rows, lse2, delta
-TRANS_BUF = 2 * TBUF        # Q^T, dO^T
+OFF_L = RBUF                # rows buffer: [Q rows | lse2 | dO rows | minus delta],
+OFF_DO = RBUF + 1024        # 36 chunks of 1 KiB, nine loaded by each wave
+OFF_DL = OFF_DO + RBUF
+ROWS_BUF = OFF_DL + 1024
+TRANS_BUF = 2 * TBUF        # Q^T, dO^T: 36 chunks, nine per wave
+CHUNKS = 9                  # tile loads per wave and batch
+assert ROWS_BUF == TRANS_BUF == 4 * CHUNKS * 1024
 HALF_R = 32 * ROW           # second 32-query half of a row tile
 HALF_T = 64                 # ... of a transposed tile (bytes)
 HALF_L = 128                # ... of lse2 / delta (bytes)
@@ -99,8 +103,8 @@ P32 = 112                    # fp32 p of that sub-tile
 XDL_WAIT = 19                # wait states between an MFMA and a vector read of its result
 SD_ = {0: 144, 1: 176}       # S at +0..15, dP at +16..31
 PD_ = {0: 208, 1: 224}       # P at +0..7, dS at +8..15
-VOFF = 240
-SB_A, SB_B, SB_L = 80, 82, 84
+VOFF = 240                   # v[240:248]: row-load offsets (ragged blocks)
+SB_A, SB_T, SB_L = 80, 82, 84   # rows (Q / dO), transposed, ninth rows load
 PAD = ["s_nop 7", "s_nop 7", "s_nop 7"]
 BARRIER_STEP = N - PF - 1    # phase B(2t): the odd barrier follows this MFMA
 
@@ -120,7 +124,7 @@ def ring(i):
 
 def a_off(i):
     """Phase A read i: even = Q row (k-step i/2), odd = dO row."""
-    return (i & 1) * RBUF + 32 * (i >> 1)
+    return (i & 1) * OFF_DO + 32 * (i >> 1)
 
 
 def b_kind(i):
@@ -321,22 +325,25 @@ def mask(G, par, q_sgpr, site):
     G.ool += body + [f"s_branch {G.lab('mback' + site)}"]
 
 
-def chunk_loads(dst_base, lo, x5, sb, vaddr):
-    """The five 1 KiB chunk loads of one tensor of a tile (the fifth under
-    the exec mask x5): chunk j of this wave lands at dst_base + lo + 4096 j.
-    Each is (M0 write, load): the write goes before a step's MFMA, the load
-    after it."""
+def tile_loads(sb, vaddr):
+    """The nine 1 KiB loads of a wave's share of a tile: its chunks are
+    contiguous in LDS, so one M0 value (%[sz] = chunk 4, then %[sz] + 4 KiB
+    = chunk 8) and the load's own offset, which moves the global address and
+    the LDS destination alike, place loads 0-4 and 5-8. The lane offsets
+    vaddr(j) include minus that offset. sb(j): the SGPR pair of load j's
+    source. Each is (instructions before the step's MFMA, after it)."""
     g = []
-    for j in range(5):
-        ld = [f"global_load_lds_dwordx4 {vaddr(j)}, s[{sb}:{sb + 1}]"]
-        if j == 4:
-            ld = [f"s_mov_b64 exec, {x5}"] + ld + ["s_mov_b64 exec, -1"]
-        g.append(([f"s_add_u32 m0, {dst_base}, {lo + 4096 * j}"], ld))
+    for j in range(CHUNKS):
+        off = (j - 4) * 1024 if j < 5 else (j - 8) * 1024
+        pre = ["s_mov_b32 m0, %[sz]"] if j == 0 else (["s_add_u32 m0, %[sz], 4096"] if j == 5 else [])
+        b = sb(j)
+        g.append((pre, [f"global_load_lds_dwordx4 {vaddr(j)}, s[{b}:{b + 1}] offset:{off}"]))
     return g
 
 
-# phase A steps that take a tile load, the light (odd) ones first
-LOAD_STEPS = [1, 3, 5, 7, 9, 11, 13, 15, 0, 2, 4, 6, 8]
+# phase A steps of the nine loads, in load order (the M0 change between
+# loads 4 and 5 must fall between them): the light (odd) steps first
+LOAD_STEPS = [1, 3, 5, 7, 9, 11, 13, 15, 14]
 
 
 def place_loads(loads):
@@ -345,36 +352,40 @@ def place_loads(loads):
 
 
 def trans_setup():
-    """Sources and destination of the transposed tile t+1 (the last one
-    past the end): %[sz] = its LDS buffer (this wave's part)."""
+    """Source and destination of the transposed tile t+1 (the last one past
+    the end): s[SB_T] = this wave's tensor (Q^T or dO^T) at the tile, %[sz] =
+    its chunk 4 in the other transposed buffer."""
     return ["s_add_u32 %[sx], %[t], 1", "s_cmp_lt_u32 %[sx], %[nt]",
             "s_cselect_b32 %[sh], %[hn], %[hlast]", "s_cselect_b32 %[sq], %[q0n], %[q0last]",
             "s_mul_i32 %[sx], %[sh], %[qths]", "s_lshl_b32 %[sy], %[sq], 1",
             "s_add_u32 %[sx], %[sx], %[sy]",
-            f"s_add_u32 s{SB_A}, %[qtb_lo], %[sx]", f"s_addc_u32 s{SB_A + 1}, %[qtb_hi], 0",
-            f"s_add_u32 s{SB_B}, %[dotb_lo], %[sx]", f"s_addc_u32 s{SB_B + 1}, %[dotb_hi], 0",
+            f"s_add_u32 s{SB_T}, %[tb_lo], %[sx]", f"s_addc_u32 s{SB_T + 1}, %[tb_hi], 0",
             f"s_xor_b32 %[sz], %[tb], {TRANS_BUF}", "s_add_u32 %[sz], %[sz], %[tdst]"]
 
 
-def rows_setup():
-    """Sources, row offsets and destination of the row tile t+2 (the last
-    one past the end), in four parts (one per MFMA after the odd barrier):
-    rows past the block re-read its last row (their lse2 is +inf)."""
-    return [
+def rows_setup(ragged):
+    """Sources and destination of the row tile t+2 (the last one past the
+    end), in pieces (one per MFMA after the odd barrier): s[SB_A] = this
+    wave's tensor (Q or dO) at the tile, s[SB_L] = its ninth load's (the
+    same tensor, or lse2 / minus delta: per-wave head stride %[lhsw] and
+    query shift %[shw]), %[sz] = its chunk 4. Ragged blocks: rows past the
+    block re-read its last row (their lse2 is +inf), so the lane offsets are
+    rebuilt per tile."""
+    pieces = [
         ["s_add_u32 %[sx], %[t], 2", "s_cmp_lt_u32 %[sx], %[nt]",
          "s_cselect_b32 %[sh], %[hf], %[hlast]", "s_cselect_b32 %[sq], %[q0f], %[q0last]",
          "s_mul_i32 %[sx], %[sh], %[qhs]", "s_lshl_b32 %[sy], %[sq], 8",
          "s_add_u32 %[sx], %[sx], %[sy]"],
-        [f"s_add_u32 s{SB_A}, %[qb_lo], %[sx]", f"s_addc_u32 s{SB_A + 1}, %[qb_hi], 0",
-         f"s_add_u32 s{SB_B}, %[db_lo], %[sx]", f"s_addc_u32 s{SB_B + 1}, %[db_hi], 0",
-         "s_mul_i32 %[sx], %[sh], %[lhs]", "s_lshl_b32 %[sy], %[sq], 2",
+        [f"s_add_u32 s{SB_A}, %[mb_lo], %[sx]", f"s_addc_u32 s{SB_A + 1}, %[mb_hi], 0",
+         "s_mul_i32 %[sx], %[sh], %[lhsw]", "s_lshl_b32 %[sy], %[sq], %[shw]",
          "s_add_u32 %[sx], %[sx], %[sy]",
-         f"s_add_u32 s{SB_L}, %[lsb_lo], %[sx]", f"s_addc_u32 s{SB_L + 1}, %[lsb_hi], 0"],
-        ["s_sub_u32 %[sx], %[cqm1], %[sq]"] +
-        [f"v_min_u32 v{VOFF + j}, %[sx], %[rrow{j}]" for j in range(5)],
-        [f"v_lshl_add_u32 v{VOFF + j}, v{VOFF + j}, 8, %[rch{j}]" for j in range(5)] +
-        ["s_add_u32 %[sz], %[rb], %[rdst]"],
-    ]
+         f"s_add_u32 s{SB_L}, %[lb_lo], %[sx]", f"s_addc_u32 s{SB_L + 1}, %[lb_hi], 0",
+         "s_add_u32 %[sz], %[rb], %[rdst]"]]
+    if ragged:
+        pieces += [["s_sub_u32 %[sx], %[cqm1], %[sq]"] +
+                   [f"v_min_u32 v{VOFF + j}, %[sx], %[rv{j}]" for j in range(CHUNKS)],
+                   [f"v_lshl_add_u32 v{VOFF + j}, v{VOFF + j}, 8, %[rc{j}]" for j in range(CHUNKS)]]
+    return pieces
 
 
 def advance():
@@ -392,7 +403,7 @@ def advance():
     ]
 
 
-def loop_asm():
+def loop_asm(ragged):
     G = Gen()
     G.add(["s_waitcnt lgkmcnt(0)"] + [f"v_accvgpr_write_b32 a{r}, 0" for r in range(128)])
     LXB = [LX + 4 * m for m in range(4)]
@@ -436,10 +447,8 @@ def loop_asm():
         return lambda i: a(i) + b(i)
 
     # ================= even sub-tile 2t (tile t, first half)
-    G.add(["s_waitcnt vmcnt(8)", "s_barrier"])
-    tl = chunk_loads("%[sz]", 0, "%[x5t]", SB_A, lambda j: f"%[to{j}]") + \
-        chunk_loads("%[sz]", TBUF, "%[x5t]", SB_B, lambda j: f"%[to{j}]")
-    pre, post = place_loads(tl)
+    G.add([f"s_waitcnt vmcnt({CHUNKS})", "s_barrier"])
+    pre, post = place_loads(tile_loads(lambda j: SB_T, lambda j: f"%[tv{j}]"))
     # S / dP of sub-tile 2t+1, dS of 2t; lse2 of 2t+1 (this tile's second half)
     G.phase(a_mfma(1), V_RADDR, lambda i: a_off(i) + HALF_R,
             work=work(ds_work(0), lx_reads(True)), pre_in=True,
@@ -448,7 +457,7 @@ def loop_asm():
     mask(G, 1, "%[sq]", "e")
     G.add(["s_nop 1",   # wait states before phase B's first read of S
            f"s_xor_b32 %[sx], %[rb], {ROWS_BUF}", f"v_add_u32 v{V_LADDR}, %[sx], %[lbase]"])
-    rs = rows_setup()
+    rs = rows_setup(ragged)
     dxr = dx_reads(False, BARRIER_STEP + 1)
 
     def even_b_extra(i):
@@ -457,7 +466,7 @@ def loop_asm():
             # the rows of tile t are read for the last time (this wave's
             # lse2 / delta reads of them have been waited for): odd barrier
             out += G.need_all(LXB + DXB)
-            out += ["s_waitcnt vmcnt(8)", "s_barrier", f"s_xor_b32 %[sx], %[rb], {ROWS_BUF}",
+            out += [f"s_waitcnt vmcnt({CHUNKS})", "s_barrier", f"s_xor_b32 %[sx], %[rb], {ROWS_BUF}",
                     f"v_add_u32 v{V_RADDR}, %[sx], %[rbase]"]
         if BARRIER_STEP < i <= BARRIER_STEP + len(rs):
             out += rs[i - BARRIER_STEP - 1]
@@ -467,12 +476,9 @@ def loop_asm():
             nxt=lambda: (V_RADDR, a_off), extra=even_b_extra)
 
     # ================= odd sub-tile 2t+1 (tile t, second half)
-    rl = chunk_loads("%[sz]", 0, "%[x5r]", SB_A, lambda j: f"v{VOFF + j}") + \
-        chunk_loads("%[sz]", RBUF, "%[x5r]", SB_B, lambda j: f"v{VOFF + j}") + \
-        [(["s_add_u32 m0, %[sz], %[loffl]"],
-          ["s_mov_b64 exec, %[xl]", f"global_load_lds_dwordx4 %[lo], s[{SB_L}:{SB_L + 1}]",
-           "s_mov_b64 exec, -1"])]
-    pre, post = place_loads(rl)
+    pre, post = place_loads(tile_loads(lambda j: SB_L if j == CHUNKS - 1 else SB_A,
+                                       (lambda j: f"v{VOFF + j}") if ragged else
+                                       (lambda j: f"%[rv{j}]")))
     # S / dP of sub-tile 2t+2, dS of 2t+1; lse2 of 2t+2 (tile t+1, first half)
     G.phase(a_mfma(0), V_RADDR, a_off, work=work(ds_work(1), lx_reads(False)),
             pre_in=True, nxt=lambda: (V_TADDR, lambda i: b_off(i) + HALF_T), pre=dx_wait(pre),
@@ -551,8 +557,8 @@ def check_hazards(lines):
         ws += 1
 
 
-def main():
-    lines = loop_asm()
+def asm_function(name, ragged):
+    lines = loop_asm(ragged)
     outs = ([f'"={{{ar(DV_ + 16 * T, 16)}}}"(dv[{T}])' for T in range(DT)] +
             [f'"={{{ar(DK_ + 16 * T, 16)}}}"(dk[{T}])' for T in range(DT)] +
             ['[t] "=&s"(t)', '[js] "=&s"(js)', '[sx] "=&s"(sx)', '[sy] "=&s"(sy)',
@@ -560,23 +566,44 @@ def main():
              '[q0c] "+s"(q0c)', '[q0n] "+s"(q0n)', '[q0f] "+s"(q0f)', '[hn] "+s"(hn)',
              '[hf] "+s"(hf)', '[hi] "+s"(hi)', '[rb] "+s"(rb)', '[tb] "+s"(tb)'])
     ins = (['[nt] "s"(n_t)', '[jfree] "s"(j_free)', '[ng] "s"(ng)', '[hlast] "s"(h_last)',
-            '[q0last] "s"(q0_last)', '[cqm1] "s"(cq_m1)', '[rdst] "s"(rdst)', '[tdst] "s"(tdst)',
-            '[x5r] "s"(x5r)', '[x5t] "s"(x5t)', '[xl] "s"(xl)', '[loffl] "s"(loffl)',
-            '[qhs] "s"(qhs)', '[qths] "s"(qths)', '[lhs] "s"(lhs)', '[c] "s"(c)',
-            '[qb_lo] "s"(qb_lo)', '[qb_hi] "s"(qb_hi)', '[db_lo] "s"(db_lo)', '[db_hi] "s"(db_hi)',
-            '[qtb_lo] "s"(qtb_lo)', '[qtb_hi] "s"(qtb_hi)', '[dotb_lo] "s"(dotb_lo)',
-            '[dotb_hi] "s"(dotb_hi)', '[lsb_lo] "s"(lsb_lo)', '[lsb_hi] "s"(lsb_hi)',
+            '[q0last] "s"(q0_last)', '[rdst] "s"(rdst)', '[tdst] "s"(tdst)',
+            '[qhs] "s"(qhs)', '[qths] "s"(qths)', '[lhsw] "s"(lhsw)', '[shw] "s"(shw)',
+            '[c] "s"(c)', '[mb_lo] "s"(mb_lo)', '[mb_hi] "s"(mb_hi)', '[lb_lo] "s"(lb_lo)',
+            '[lb_hi] "s"(lb_hi)', '[tb_lo] "s"(tb_lo)', '[tb_hi] "s"(tb_hi)',
             '[rbase] "v"(rbase)', '[tbase] "v"(tbase)', '[lbase] "v"(lbase)', '[lmin] "v"(lmin)',
-            '[vhead] "v"(vhead)', '[lo] "v"(lo)'] +
-           [f'[rrow{j}] "v"(rrow[{j}])' for j in range(5)] +
-           [f'[rch{j}] "v"(rch[{j}])' for j in range(5)] +
-           [f'[to{j}] "v"(tofs[{j}])' for j in range(5)] +
+            '[vhead] "v"(vhead)'] +
+           [f'[rv{j}] "v"(rv[{j}])' for j in range(CHUNKS)] +
+           [f'[tv{j}] "v"(tv[{j}])' for j in range(CHUNKS)] +
+           (['[cqm1] "s"(cq_m1)'] + [f'[rc{j}] "v"(rc[{j}])' for j in range(CHUNKS)]
+            if ragged else []) +
            [f'"{{{ar(K_ + 4 * s, 4)}}}"(kr[{s}])' for s in range(KS)] +
            [f'"{{{ar(V_ + 4 * s, 4)}}}"(vr_[{s}])' for s in range(KS)])
-    clob = ([f'"v{r}"' for r in range(V_RADDR, VOFF + 5)] +
+    last_v = (VOFF + CHUNKS - 1) if ragged else PD_[1] + 15
+    clob = ([f'"v{r}"' for r in range(V_RADDR, last_v + 1)] +
             [f'"s{r}"' for r in range(SB_A, SB_L + 2)] +
-            ['"vcc"', '"scc"', '"m0"', '"exec"', '"memory"'])
+            ['"vcc"', '"scc"', '"m0"', '"memory"'])
     body = "\n".join(f'      "{ln}\\n\\t"' for ln in lines)
+    return f'''__device__ __forceinline__ void {name}(
+    int n_t, int j_free, int ng, int h_last, int q0_last, int cq_m1, unsigned rdst, unsigned tdst,
+    unsigned qhs, unsigned qths, unsigned lhsw, unsigned shw, float c, const void* mb,
+    const void* lb, const void* tbp, unsigned rbase, unsigned tbase, unsigned lbase, int lmin,
+    int vhead, const unsigned (&rv)[{CHUNKS}], const unsigned (&rc)[{CHUNKS}],
+    const unsigned (&tv)[{CHUNKS}], const bf16x8 (&kr)[8], const bf16x8 (&vr_)[8], int q0c,
+    int q0n, int q0f, int hn, int hf, int hi, floatx16 (&dv)[4], floatx16 (&dk)[4]) {{
+  int t, js, sx, sy, sz, sh, sq;
+  int rb = 0, tb = 0;
+  const unsigned mb_lo = lo32(mb), mb_hi = hi32(mb), lb_lo = lo32(lb), lb_hi = hi32(lb);
+  const unsigned tb_lo = lo32(tbp), tb_hi = hi32(tbp);
+  asm volatile(
+{body}
+      : {", ".join(outs)}
+      : {", ".join(ins)}
+      : {", ".join(clob)});
+}}
+'''
+
+
+def main():
     out = f'''// Generated by gen_bwd_dkdv_w32.py -- do not edit by hand.
 //
 // The query loop of attn_bwd_dkdv_w32 (D = {D}) as one inline-asm statement
@@ -590,51 +617,45 @@ namespace dkdvw {{
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kRowsBuf = {ROWS_BUF};    // [Q rows | dO rows | lse2 1 KiB | delta 1 KiB]; two buffers
-constexpr int kTransBuf = {TRANS_BUF};  // [Q^T | dO^T]; two buffers
-constexpr int kOffL = {OFF_L};          // lse2 in a rows buffer (delta 1 KiB later)
+// A rows buffer is [Q rows | lse2 | dO rows | minus delta] (lse2 and minus
+// delta: 1 KiB each, the first 256 bytes used), a transposed buffer [Q^T |
+// dO^T]; two of each. A wave loads nine contiguous 1 KiB chunks of each.
+constexpr int kRowsBuf = {ROWS_BUF};
+constexpr int kTransBuf = {TRANS_BUF};
+constexpr int kOffL = {OFF_L};
+constexpr int kOffDO = {OFF_DO};
+constexpr int kOffDL = {OFF_DL};
+constexpr int kChunks = {CHUNKS};
 
-// The query-tile stream of one wave: n_t >= 1 tiles of 64 queries. The rows
-// (with lse2 / delta) of tiles 0 and min(1, n_t - 1) are in rows buffers 0
-// and 1, the transposed tile 0 in transposed buffer 0. Tile T is query head
-// lane (T % ng) of vhead, first query q0(T) (the tiles of each query range
-// for every head, ranges from the last down); the caller passes q0 of tiles
-// 0, 1, 2 (q0c, q0n, q0f), the heads of tiles 1, 2 (hn, hf), hi = 2 % ng,
-// and head and q0 of the last tile (h_last, q0_last). rbase / tbase / lbase:
-// this lane's read addresses in rows / transposed / lse2 of buffer 0; rdst /
-// tdst: this wave's first load destination in rows / transposed buffer 0;
-// qb / db / qtb / dotb: global bases of q, dout, q^T, dout^T of the batch and
-// lsb of lse2 or delta (by wave); qhs / qths / lhs: head strides in bytes;
-// rrow / rch: the lane's row and byte offset in its row tile chunks, tofs its
-// transposed tile offsets, lo its lse2 / delta offset; r5 / t5 / l1: whether
-// the wave issues the fifth row / transposed chunk load and an lse2 / delta
-// load, loffl that load's LDS offset from the wave's row destination;
-// cq_m1: rows of the block minus one; j_free: the first sub-tile that needs
-// the causal mask; lmin: the first row that sees the lane's key, minus 8 for
-// the upper half of the wave. Returns dV^T and dK^T (unscaled).
-__device__ __forceinline__ void dkdv_loop(
-    int n_t, int j_free, int ng, int h_last, int q0_last, int cq_m1, unsigned rdst,
-    unsigned tdst, int r5, int t5, int l1, unsigned loffl, unsigned qhs,
-    unsigned qths, unsigned lhs, float c, const void* qb, const void* db, const void* qtb,
-    const void* dotb, const void* lsb, unsigned rbase, unsigned tbase, unsigned lbase, int lmin,
-    int vhead, unsigned lo, const unsigned (&rrow)[5], const unsigned (&rch)[5],
-    const unsigned (&tofs)[5], const bf16x8 (&kr)[8], const bf16x8 (&vr_)[8], int q0c, int q0n,
-    int q0f, int hn, int hf, int hi, floatx16 (&dv)[4], floatx16 (&dk)[4]) {{
-  int t, js, sx, sy, sz, sh, sq;
-  int rb = 0, tb = 0;
-  const long long x5r = r5 ? -1ll : 0ll, x5t = t5 ? -1ll : 0ll, xl = l1 ? -1ll : 0ll;
-  auto lo32 = [](const void* p) {{ return (unsigned)(unsigned long long)(size_t)p; }};
-  auto hi32 = [](const void* p) {{ return (unsigned)((unsigned long long)(size_t)p >> 32); }};
-  const unsigned qb_lo = lo32(qb), qb_hi = hi32(qb), db_lo = lo32(db), db_hi = hi32(db);
-  const unsigned qtb_lo = lo32(qtb), qtb_hi = hi32(qtb), dotb_lo = lo32(dotb), dotb_hi = hi32(dotb);
-  const unsigned lsb_lo = lo32(lsb), lsb_hi = hi32(lsb);
-  asm volatile(
-{body}
-      : {", ".join(outs)}
-      : {", ".join(ins)}
-      : {", ".join(clob)});
+__device__ __forceinline__ unsigned lo32(const void* p) {{
+  return (unsigned)(unsigned long long)(size_t)p;
+}}
+__device__ __forceinline__ unsigned hi32(const void* p) {{
+  return (unsigned)((unsigned long long)(size_t)p >> 32);
 }}
 
+// The query-tile stream of one wave: n_t >= 1 tiles of 64 queries. The rows
+// (with lse2 / minus delta) of tiles 0 and min(1, n_t - 1) are in rows
+// buffers 0 and 1, the transposed tile 0 in transposed buffer 0. Tile T is
+// query head lane (T % ng) of vhead, first query q0(T) (the tiles of each
+// query range for every head, ranges from the last down); the caller passes
+// q0 of tiles 0, 1, 2 (q0c, q0n, q0f), the heads of tiles 1, 2 (hn, hf), hi
+// = 2 % ng, and head and q0 of the last tile (h_last, q0_last). rbase /
+// tbase / lbase: this lane's read addresses in rows / transposed / lse2 of
+// buffer 0; rdst / tdst: this wave's chunk 4 in rows / transposed buffer 0.
+// mb: the batch base of this wave's rows tensor (q for waves 0 and 1, dout
+// for 2 and 3); lb: of its ninth rows load (q, lse2, dout, minus delta by
+// wave), lhsw / shw that one's head stride (bytes) and query shift; tbp: of
+// its transposed tensor (q^T, q^T, dout^T, dout^T); qhs / qths: head strides
+// of q / dout and of q^T / dout^T in bytes. rv / tv: the lane's byte offset
+// of each of its nine rows / transposed loads within the tile, minus the
+// load's own offset; in the ragged form rv holds the rows and rc the byte
+// offsets within the row (minus the same), and rows are clamped to cq_m1,
+// the block's last one. j_free: the first sub-tile that needs the causal
+// mask; lmin: the first row that sees the lane's key, minus 8 for the upper
+// half of the wave. Returns dV^T and dK^T (unscaled).
+{asm_function("dkdv_loop", False)}
+{asm_function("dkdv_loop_ragged", True)}
 }}  // namespace dkdvw
 }}  // namespace ra
 '''
