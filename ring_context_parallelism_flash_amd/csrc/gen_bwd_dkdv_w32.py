@@ -31,13 +31,15 @@ transposed buffers [Q^T | dO^T], filled by direct global->LDS loads, each
 placed after one MFMA of a phase A: the even sub-tile 2t loads the transposed
 tile t+1, the odd one the rows (with lse2 / delta) of tile t+2; a tile past
 the stream's end repeats the last one. Two barriers per tile:
-  even barrier (before phase A(2t)): publishes the transposed tile t and
-    frees the other transposed buffer (phase B(2t-1) is done);
-  odd barrier (after MFMA 11 of phase B(2t)): publishes the rows of tile t+1
+  even barrier (after MFMA 0 of phase A(2t)): publishes the transposed tile
+    t and frees the other transposed buffer (phase B(2t-1) is done);
+  odd barrier (after MFMA 12 of phase B(2t)): publishes the rows of tile t+1
     and frees the rows of tile t (both of its phases A and its lse2 / delta
-    reads, waited for right before the barrier, are done); the last four
-    MFMAs of phase B(2t) then issue the first reads of tile t+1. (Placed as
-    late as the ring allows: the rows loads it waits for get the most time.)
+    reads, waited for right before that MFMA, are done); the last four steps
+    of phase B(2t) then issue the first reads of tile t+1. (Placed as late as
+    the ring allows: the rows loads it waits for get the most time.)
+Each barrier follows an MFMA issue, so the matrix pipe has work while the
+wave waits.
 Each barrier waits only for the loads before the latest batch (vmcnt(8):
 every batch gives each wave at least eight loads), so a batch has about two
 sub-tiles to land.
@@ -106,7 +108,7 @@ PD_ = {0: 208, 1: 224}       # P at +0..7, dS at +8..15
 VOFF = 240                   # v[240:248]: row-load offsets (ragged blocks)
 SB_A, SB_T, SB_L = 80, 82, 84   # rows (Q / dO), transposed, ninth rows load
 PAD = ["s_nop 7", "s_nop 7", "s_nop 7"]
-BARRIER_STEP = N - PF - 1    # phase B(2t): the odd barrier follows this MFMA
+BARRIER_STEP = N - PF        # phase B(2t): the odd barrier follows this MFMA
 
 
 def vr(base, n):
@@ -206,10 +208,10 @@ class Gen:
         return self.wait(x) if x is not None else []
 
     def phase(self, mfma, addr, off, work=None, pre_in=False, nxt=None, extra=None,
-              pre=None):
+              pre=None, mid=None):
         """N MFMAs; MFMA i reads operand i (address register addr, offset
-        off(i)) through the ring. Step i: pre(i), MFMA i, the read of operand
-        i + PF (the last PF steps issue the first reads of the next phase:
+        off(i)) through the ring. Step i: pre(i), MFMA i, mid(i), the read of
+        operand i + PF (the last PF steps issue the first reads of the next phase:
         nxt() gives (addr, off) then, after the extras before it), work(i)
         (instruction strings, or the register base of an lse2 / delta read
         the next ones use) and extra(i)."""
@@ -226,6 +228,8 @@ class Gen:
             if pre:
                 self.add(pre(i))
             self.add([mfma(i)])
+            if mid:
+                self.add(mid(i))
             if i + PF < N:
                 self.add(self.read(i % PF, addr, off(i + PF)))
             elif nxt:
@@ -447,33 +451,40 @@ def loop_asm(ragged):
         return lambda i: a(i) + b(i)
 
     # ================= even sub-tile 2t (tile t, first half)
-    G.add([f"s_waitcnt vmcnt({CHUNKS})", "s_barrier"])
     pre, post = place_loads(tile_loads(lambda j: SB_T, lambda j: f"%[tv{j}]"))
+    # the even barrier right behind MFMA 0, which keeps the matrix pipe busy
+    # while the wave waits there
+    bar_e = lambda i: [f"s_waitcnt vmcnt({CHUNKS})", "s_barrier"] if i == 0 else []
     # S / dP of sub-tile 2t+1, dS of 2t; lse2 of 2t+1 (this tile's second half)
     G.phase(a_mfma(1), V_RADDR, lambda i: a_off(i) + HALF_R,
             work=work(ds_work(0), lx_reads(True)), pre_in=True,
-            nxt=lambda: (V_TADDR, b_off), pre=dx_wait(pre), extra=post)
+            nxt=lambda: (V_TADDR, b_off), pre=dx_wait(pre), extra=post, mid=bar_e)
     G.add(["s_add_u32 %[js], %[js], 1", "s_add_u32 %[sq], %[q0c], 32"])
     mask(G, 1, "%[sq]", "e")
     G.add(["s_nop 1",   # wait states before phase B's first read of S
            f"s_xor_b32 %[sx], %[rb], {ROWS_BUF}", f"v_add_u32 v{V_LADDR}, %[sx], %[lbase]"])
     rs = rows_setup(ragged)
-    dxr = dx_reads(False, BARRIER_STEP + 1)
+    dxr = dx_reads(False, BARRIER_STEP)
+
+    def even_b_pre(i):
+        # the rows of tile t are read for the last time: this wave's lse2 /
+        # delta reads of them are waited for before the odd barrier
+        return G.need_all(LXB + DXB) if i == BARRIER_STEP else []
+
+    def even_b_mid(i):
+        # the odd barrier right behind an MFMA; the first reads of tile t+1
+        # follow it
+        if i != BARRIER_STEP:
+            return []
+        return [f"s_waitcnt vmcnt({CHUNKS})", "s_barrier", f"s_xor_b32 %[sx], %[rb], {ROWS_BUF}",
+                f"v_add_u32 v{V_RADDR}, %[sx], %[rbase]"]
 
     def even_b_extra(i):
-        out = []
-        if i == BARRIER_STEP:
-            # the rows of tile t are read for the last time (this wave's
-            # lse2 / delta reads of them have been waited for): odd barrier
-            out += G.need_all(LXB + DXB)
-            out += [f"s_waitcnt vmcnt({CHUNKS})", "s_barrier", f"s_xor_b32 %[sx], %[rb], {ROWS_BUF}",
-                    f"v_add_u32 v{V_RADDR}, %[sx], %[rbase]"]
-        if BARRIER_STEP < i <= BARRIER_STEP + len(rs):
-            out += rs[i - BARRIER_STEP - 1]
+        out = rs[i - BARRIER_STEP] if BARRIER_STEP <= i < BARRIER_STEP + len(rs) else []
         return out + dxr(i)   # delta of sub-tile 2t+2 (tile t+1, just published)
     # dV / dK of sub-tile 2t, p of 2t+1
     G.phase(b_mfma(0), V_TADDR, b_off, work=p_work(1), pre_in=True,
-            nxt=lambda: (V_RADDR, a_off), extra=even_b_extra)
+            nxt=lambda: (V_RADDR, a_off), extra=even_b_extra, pre=even_b_pre, mid=even_b_mid)
 
     # ================= odd sub-tile 2t+1 (tile t, second half)
     pre, post = place_loads(tile_loads(lambda j: SB_L if j == CHUNKS - 1 else SB_A,
