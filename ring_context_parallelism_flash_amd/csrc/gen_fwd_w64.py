@@ -26,10 +26,21 @@ rescaled output, "Algorithmic Mechanics"): probabilities are taken against a
 per-row reference m that moves only when a lane's probabilities of one tile
 sum past 2^8 (or it has none yet); then the row max is taken, O and l are
 rescaled by exp2((m_old - m_new) * c) and the tile's probabilities redone.
-l and O always share the reference, so the result is the same. That slow
-path and the causal mask (tiles from the wave's first partly visible one)
-are placed out of line, so the common path has no taken branch but the
-loop's back edge.
+l and O always share the reference, so the result is the same. A row with
+no reference yet (m = -inf) takes exponent offset -m*c = +inf on the common
+path, so its probabilities come out +inf (or NaN where masked) and the sum
+test alone sends it to the slow path, which redoes the tile with offset 0
+for such rows (their p are then exp2 of -inf scores: 0). That slow path and
+the causal mask (tiles from the wave's first partly visible one) are placed
+out of line, so the common path has no taken branch but the loop's back
+edge.
+
+With one wave per SIMD the wave's own instruction issue sets the pace (an
+MFMA pair of the common path takes about as long as the two MFMAs, one
+softmax pair and its operand read take to issue), so the common path keeps
+instructions out: one running row sum started by a move, one offset
+instruction per phase, one LDS wait per two MFMA pairs, a four-instruction
+sum test.
 
 Register plan (one wave per SIMD: 256 VGPRs + 256 AGPRs):
   a[0:63]    O of block 0, four 32-wide d tiles of 16 registers (O^T layout)
@@ -37,8 +48,9 @@ Register plan (one wave per SIMD: 256 VGPRs + 256 AGPRs):
   a[128:159] Q of block 0, eight k-steps of 4 registers (bf16x8)
   a[160:191] Q of block 1
   v52 m0, v53 l0, v54 m1, v55 l1: reference and running sum of each block
-  v56 row sum, v57 K read address, v58 minus the exponent offset,
-  v59 V^T read address, v[60:63] temporaries
+  v57 K read address, v58 minus the exponent offset of the block in hand,
+  v59 V^T read address, v[60:61] temporaries, v62 the tile's row sum,
+  v63 the slow path's exponent offset
   v[64:79]   LDS operand ring, four 16-byte reads in flight
   v[80:95]   P0a  bf16 probabilities of block 0 (tile parity 0)
   v[96:111]  P0b  (tile parity 1)
@@ -48,22 +60,26 @@ Register plan (one wave per SIMD: 256 VGPRs + 256 AGPRs):
   v[192:223] SB0, v[224:255] SB1: the other score buffer pair
   s[80:81], s[82:83]: global addresses of the next K and V^T tiles
 The compiler keeps everything else (the load offsets, the lane addresses,
-its own values) in v[0:51], a[192:255] and the other SGPRs.
+its own values) in v[0:51], v56, a[192:255] and the other SGPRs.
 
-Hazards the statement respects by construction: a transcendental result is
-read no earlier than the second instruction after it; an MFMA result is
-read by a vector instruction only after at least 24 wait states (phase A's
-scores are first read two MFMA pairs into phase B, or by the out-of-line
-mask, which starts with s_nop 7 x 3; O is read only by the out-of-line slow
-path, which starts the same way, and after the statement, which ends with
-the same pad); an MFMA accumulator is reused no sooner than three MFMAs
-later; an M0 write is followed by one wait state before the LDS-DMA load
-that reads it; LDS reads wait on counted lgkmcnt and return in order, with
-no other LGKM operation in flight on the common path.
+Hazards the statement respects by construction, and check_hazards verifies
+on the executed paths (the common path for several trip counts, and paths
+through each out-of-line branch) before the header is written: a
+transcendental result is read no earlier than the second instruction after
+it; an MFMA result is read by a vector instruction only after at least 19
+wait states (phase A's scores are first read two MFMA pairs into phase B,
+or by the out-of-line mask, which starts with s_nop 7 x 3; O is read only by
+the out-of-line slow path, which starts the same way, and after the
+statement, which ends with the same pad); an M0 write is not directly
+followed by the LDS-DMA load that reads it; an MFMA operand read from LDS
+has returned when the MFMA issues (LDS reads return in order; lgkmcnt
+counts them, and no other LGKM operation is in flight on the common path).
+An MFMA accumulator is reused no sooner than three MFMAs later.
 
 Run: python gen_fwd_w64.py  (writes the header next to this file)
 """
 import os
+import re
 
 D = 128
 KS = D // 16           # score k-steps
@@ -82,13 +98,12 @@ O_ = (0, 64)                     # O of block 0 / 1 (AGPR base)
 Q_ = (128, 160)                  # Q of block 0 / 1 (AGPR base)
 M_ = (52, 54)
 L_ = (53, 55)
-V_RS, V_KADDR, V_NMOFF, V_VADDR = 56, 57, 58, 59
+V_KADDR, V_NMOFF, V_VADDR = 57, 58, 59
 T0, T1, T2, T3 = 60, 61, 62, 63
 RING = 64
 P0A, P0B, P1 = 80, 96, 112
 SA0, SA1, SB0, SB1 = 128, 160, 192, 224
 PAD = ["s_nop 7", "s_nop 7", "s_nop 7"]   # 24 wait states after an MFMA
-ZERO_SUMS = [f"v_mov_b32 v{T2}, 0", f"v_mov_b32 v{T3}, 0"]
 KG_S, VG_S = 80, 82              # SGPR pairs of the global K / V^T tile addresses
 
 
@@ -110,26 +125,35 @@ def elem(S, e):
     return S + 16 * (u >> 1) + 8 * (u & 1) + j
 
 
-def nmoff_lines(m):
-    """v58 = -(m == -inf ? 0 : m) * c."""
-    return [f"v_mul_f32 v{V_NMOFF}, %[c], v{m}",
-            f"v_sub_f32 v{V_NMOFF}, 0, v{V_NMOFF}",
+def nmoff_lines(m, dst):
+    """dst = -m * c, or 0 where m = -inf (the slow path's redo: a row with no
+    visible key yet gets p = 0 from its -inf scores)."""
+    return [f"v_mul_f32 v{dst}, %[c], v{m}",
+            f"v_sub_f32 v{dst}, 0, v{dst}",
             f"v_cmp_class_f32_e64 vcc, v{m}, 4",
-            f"v_cndmask_b32_e64 v{V_NMOFF}, v{V_NMOFF}, 0, vcc"]
+            f"v_cndmask_b32_e64 v{dst}, v{dst}, 0, vcc"]
 
 
-def softmax_pair(i, S, P):
+def fast_off(m):
+    """The common path's exponent offset: v58 = -m * c, which is +inf where m
+    = -inf, so a row without a reference gets +inf (or NaN) probabilities
+    and fails the sum test below."""
+    return [f"v_mul_f32_e64 v{V_NMOFF}, -%[c], v{m}"]
+
+
+def softmax_pair(i, S, P, nm=V_NMOFF):
     """Vector work for scores e = 2i, 2i+1 in two parts, one after each MFMA
-    of a pair: the exponentials, then the row sums and the bf16 packing."""
+    of a pair: the exponentials, then the row sum (v62, started by the first
+    pair) and the bf16 packing."""
     s0 = elem(S, 2 * i)
     u, j = (2 * i) >> 3, (2 * i) & 7
-    first = [f"v_fma_f32 v{T0}, v{s0}, %[c], v{V_NMOFF}",
-             f"v_fma_f32 v{T1}, v{s0 + 1}, %[c], v{V_NMOFF}",
+    first = [f"v_fma_f32 v{T0}, v{s0}, %[c], v{nm}",
+             f"v_fma_f32 v{T1}, v{s0 + 1}, %[c], v{nm}",
              f"v_exp_f32 v{T0}, v{T0}",
              f"v_exp_f32 v{T1}, v{T1}"]
-    second = [f"v_add_f32 v{T2}, v{T2}, v{T0}",
-              f"v_add_f32 v{T3}, v{T3}, v{T1}",
-              f"v_cvt_pk_bf16_f32 v{P + 4 * u + j // 2}, v{T0}, v{T1}"]
+    second = [f"v_mov_b32 v{T2}, v{T0}" if i == 0 else f"v_add_f32 v{T2}, v{T2}, v{T0}",
+              f"v_cvt_pk_bf16_f32 v{P + 4 * u + j // 2}, v{T0}, v{T1}",
+              f"v_add_f32 v{T2}, v{T2}, v{T1}"]
     return first, second
 
 
@@ -151,12 +175,16 @@ def phase(mfmas, addr, off, work, pre_in=False, nxt=None, extra=()):
     instructions after pair i."""
     lines = [] if pre_in else ["s_waitcnt lgkmcnt(0)"]
     if work:
-        lines += nmoff_lines(M_[work[2]]) + ZERO_SUMS
+        lines += fast_off(M_[work[2]])
     if not pre_in:
         for i in range(PF):
             lines.append(f"ds_read_b128 {ring(i)}, v{addr} offset:{off(i)}")
     for i in range(N):
-        lines.append(f"s_waitcnt lgkmcnt({PF - 1 if nxt else min(PF - 1, N - 1 - i)})")
+        if i % 2 == 0:
+            # one wait per two pairs: reads 0 .. issued-1 are in flight or
+            # done, in order; pairs i and i+1 need reads i and i+1
+            issued = i + PF if nxt else min(N, i + PF)
+            lines.append(f"s_waitcnt lgkmcnt({issued - (i + 2)})")
         first, second = softmax_pair(i, work[0], work[1]) if work else ([], [])
         ma, mb = mfmas(i)
         lines += [ma] + first + [mb]
@@ -194,7 +222,7 @@ def pv_mfmas(P0, P1_):
     return f
 
 
-LOOP_CLOBBER = ([f'"v{r}"' for r in range(V_RS, 256)] +
+LOOP_CLOBBER = ([f'"v{r}"' for r in range(V_KADDR, 256)] +
                 ['"vcc"', '"scc"', '"m0"', '"exec"', '"memory"'])
 
 
@@ -223,13 +251,11 @@ class Loop:
         """Row sum check of block b; the fast path adds it to l, the slow
         path (out of line) redoes the tile's softmax."""
         m, l = M_[b], L_[b]
-        self.add([f"v_add_f32 v{V_RS}, v{T2}, v{T3}",
-                  f"v_cmp_ge_f32 vcc, {FAST_SUM}, v{V_RS}",
-                  f"v_cmp_class_f32_e64 %[stmp], v{m}, 4",
-                  "s_andn2_b64 vcc, vcc, %[stmp]",
+        # (a row without a reference has +inf or NaN probabilities and fails)
+        self.add([f"v_cmp_ge_f32 vcc, {FAST_SUM}, v{T2}",
                   "s_cmp_eq_u64 vcc, exec",
                   f"s_cbranch_scc0 {self.lab('slow' + site)}",
-                  f"v_add_f32 v{l}, v{l}, v{V_RS}"])
+                  f"v_add_f32 v{l}, v{l}, v{T2}"])
         self.place("cont" + site)
         self.ool += [f"{self.lab('slow' + site)}:"] + PAD
         self.ool += slow_path_body(S, P, b, self.lab("keep" + site))
@@ -289,11 +315,13 @@ def slow_path_body(S, P, b, keep_label):
                   f"v_mul_f32 v{t}, v{t}, v{T2}",
                   f"v_accvgpr_write_b32 a{Ob + r}, v{t}"]
     lines.append(f"{keep_label}:")
-    lines += nmoff_lines(m) + ZERO_SUMS
+    # the redo takes offset 0 where m is still -inf (no key of the row
+    # visible yet: every p is 0)
+    lines += nmoff_lines(m, T3)
     for i in range(16):
-        first, second = softmax_pair(i, S, P)
+        first, second = softmax_pair(i, S, P, T3)
         lines += first + second
-    lines += [f"v_add_f32 v{V_RS}, v{T2}, v{T3}", f"v_add_f32 v{l}, v{l}, v{V_RS}"]
+    lines += [f"v_add_f32 v{l}, v{l}, v{T2}"]
     return lines
 
 
@@ -344,7 +372,7 @@ def loop_asm():
     L.set_addr(V_KADDR, "%[krb]", KBUF)
     L.add(["s_mov_b32 %[t], 0"])
     L.mask(SA0, SA1, "%[t]", "pro", ["s_cmp_eq_u32 %[fmask], 0"])
-    L.add(nmoff_lines(M_[0]) + ZERO_SUMS)
+    L.add(fast_off(M_[0]))
     for i in range(16):
         first, second = softmax_pair(i, SA0, P0A)
         L.add(first + second)
@@ -374,8 +402,7 @@ def loop_asm():
         c0, c1, n0, n1 = S[p]
         pc, pn = P0[p]
         L.place(f"last{p}")
-        L.add(["s_waitcnt vmcnt(0)", "s_barrier", "s_waitcnt lgkmcnt(0)"] + nmoff_lines(M_[1]) +
-              ZERO_SUMS)
+        L.add(["s_waitcnt vmcnt(0)", "s_barrier", "s_waitcnt lgkmcnt(0)"] + fast_off(M_[1]))
         for i in range(16):
             first, second = softmax_pair(i, c1, P1)
             L.add(first + second)
@@ -387,6 +414,115 @@ def loop_asm():
     L.place("done")
     L.add(PAD)
     return L.lines
+
+
+XDL_WAIT = 19    # wait states between an MFMA and a vector access of its result
+REG = re.compile(r"\b([va])(?:(\d+)\b|\[(\d+):(\d+)\])")
+
+
+def regs(text):
+    out = set()
+    for m in REG.finditer(text):
+        if m.group(2):
+            out.add(m.group(1) + m.group(2))
+        else:
+            out.update(f"{m.group(1)}{r}" for r in range(int(m.group(3)), int(m.group(4)) + 1))
+    return out
+
+
+def trace(lines, policy, limit=20000):
+    """The instructions one wave executes, branches decided by policy(label,
+    count of earlier decisions at that label) -> taken."""
+    where = {ln[:-1]: i for i, ln in enumerate(lines) if ln.endswith(":")}
+    seen = {}
+    out, i = [], 0
+    while i < len(lines) and len(out) < limit:
+        ln = lines[i]
+        op, _, rest = ln.partition(" ")
+        if ln.endswith(":"):
+            if ln == ".Ldone_%=:":
+                break
+            i += 1
+            continue
+        out.append(ln)
+        if op == "s_branch":
+            i = where[rest.strip()]
+            continue
+        if op.startswith("s_cbranch"):
+            lab = rest.strip()
+            k = seen.get(lab, 0)
+            seen[lab] = k + 1
+            if policy(lab, k):
+                i = where[lab]
+                continue
+        i += 1
+    assert len(out) < limit, "trace did not reach the end"
+    return out
+
+
+def check_trace(tr):
+    """Along one executed path: a vector access of an MFMA result is at least
+    XDL_WAIT wait states after the MFMA; no instruction reads a
+    transcendental result right after it; an M0 write is not followed
+    directly by an LDS-DMA load; every MFMA operand read from LDS has
+    returned (LDS reads return in order) at the MFMA."""
+    last, trans, ws = {}, set(), 0
+    pending = []          # destination register sets of LDS reads in flight, oldest first
+    prev = ""
+    for ln in tr:
+        op, _, rest = ln.partition(" ")
+        if op == "s_nop":
+            ws += int(rest) + 1
+            trans, prev = set(), ln
+            continue
+        ops = [o.strip() for o in rest.split(",")]
+        if op == "s_waitcnt" and "lgkmcnt" in rest:
+            k = int(re.search(r"lgkmcnt\((\d+)\)", rest).group(1))
+            pending = pending[len(pending) - k:] if len(pending) > k else pending
+        if op.startswith("global_load_lds"):
+            assert "m0" not in prev.split(" ", 1)[-1].split(",")[0], (prev, ln)
+        if op.startswith("v_mfma"):
+            src = regs(",".join(ops[1:]))
+            for r in src:
+                assert all(r not in p for p in pending), ("LDS read not waited for", ln)
+            for r in regs(",".join(ops[1:3])):
+                assert ws - last.get(r, -99) >= XDL_WAIT, ln
+            for r in regs(ops[0]):
+                last[r] = ws
+        elif op.startswith("ds_"):
+            for r in regs(",".join(ops[1:])):
+                assert ws - last.get(r, -99) >= XDL_WAIT, ln
+                assert all(r not in p for p in pending), ("LDS result", ln)
+            pending.append(regs(ops[0]))
+        elif op.startswith("v_"):
+            for r in regs(rest):
+                assert ws - last.get(r, -99) >= XDL_WAIT, (ln, ws - last.get(r, -99))
+                assert all(r not in p for p in pending), ("LDS result", ln)
+            assert not (regs(",".join(ops[1:])) & trans), ln
+        trans = regs(ops[0]) if op == "v_exp_f32" else set()
+        prev = ln
+        ws += 1
+
+
+def check_hazards(lines):
+    """check_trace over paths through the loop: the common path for several
+    trip counts, and paths that take each out-of-line branch."""
+    for n_it in range(0, 4):
+        for lastp in (0, 1):
+            def pol(lab, k, n_it=n_it, lastp=lastp, extra=None):
+                if lab.startswith(".Llast"):
+                    return lab == f".Llast{lastp}_%=" and k >= n_it
+                return False
+            check_trace(trace(lines, pol))
+    fams = ["slowpro", "maskpro", "slowa0", "slowb0", "slowa1", "slowb1", "mask0", "mask1",
+            "slowl0", "slowl1", "keeppro", "keepa0", "keepb0", "keepa1", "keepb1", "keepl0", "keepl1"]
+    for fam in fams:
+        for when in (0, 1):
+            def pol(lab, k, fam=fam, when=when):
+                if lab.startswith(".Llast"):
+                    return lab == ".Llast1_%=" and k >= 2
+                return lab == f".L{fam}_%=" and k == when
+            check_trace(trace(lines, pol))
 
 
 def main():
@@ -407,6 +543,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int kKBufs = {KBUFS};
 ''']
     lines = loop_asm()
+    check_hazards(lines)
     outs = ([f'"={{{ar(O_[b] + 16 * T, 16)}}}"(o{b}[{T}])' for b in (0, 1) for T in range(DT)] +
             [f'"+{{v{M_[b]}}}"(m{b})' for b in (0, 1)] +
             [f'"+{{v{L_[b]}}}"(l{b})' for b in (0, 1)] +
