@@ -1012,8 +1012,9 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void attn_bwd_dq(const BwdArgs a)
 // dQ for D = 128 blocks of whole 64-key tiles, one wave per SIMD: 4 waves x
 // 64 query rows (two 32-row blocks per wave), so every K, V or K^T operand
 // read from LDS feeds two MFMAs, one per row block. Q and dO stay in AGPRs;
-// the key loop -- the S^T / dP^T MFMAs of the next 32-key sub-tile with this
-// one's dS arithmetic between them, then this sub-tile's dQ^T MFMAs, the
+// the key loop -- the S^T / dP^T MFMAs of the next 32-key sub-tile (dP^T
+// accumulated from minus delta) with this one's dS arithmetic between them,
+// then this sub-tile's dQ^T MFMAs, the
 // causal mask and the tile loads -- is one inline-asm statement with a fixed
 // schedule and fixed registers (attn_bwd_dq_w64_loop.h, written by
 // gen_bwd_dq_w64.py). K and V row tiles rotate through three LDS buffers,
@@ -1113,7 +1114,7 @@ __global__ __launch_bounds__(64 * kDqW64Waves, 1) void attn_bwd_dq_w64(const Bwd
   const float* lb = a.lse2 + b * a.l_bs + h * a.l_hs;
   const float* ndlb = a.ndelta + b * a.l_bs + h * a.l_hs;
   const float nl20 = -lb[l0], nl21 = -lb[l1];
-  const float dlt0 = -ndlb[l0], dlt1 = -ndlb[l1];
+  const float ndl0 = ndlb[l0], ndl1 = ndlb[l1];
   const int nal0 = a.causal ? allowed_prefix(a.kp, pos_of(a.qp, r0)) : a.Ck;
   const int nal1 = a.causal ? allowed_prefix(a.kp, pos_of(a.qp, r1)) : a.Ck;
   // first 32-key sub-tile with a key some row of the wave may not see (its
@@ -1134,7 +1135,7 @@ __global__ __launch_bounds__(64 * kDqW64Waves, 1) void attn_bwd_dq_w64(const Bwd
                  uni(lds_addr(Rows) + L::RBUF + wvv * 1024), uni(lds_addr(Kt) + wt * 1024),
                  uni(wk + NW * 4 < L::RINS), uni(wvv + NW * 4 < L::RINS), uni(wt + NW * 4 < L::TINS),
                  a.scale_log2, lds_addr(Rows) + kperm(n) * L::ROW + hh * 16,
-                 lds_addr(Kt) + n * L::TROW + hh * 16, nl20, nl21, dlt0, dlt1, nal0 - 8 * hh,
+                 lds_addr(Kt) + n * L::TROW + hh * 16, nl20, nl21, ndl0, ndl1, nal0 - 8 * hh,
                  nal1 - 8 * hh, uni_ptr(kb + (int64_t)min(2, n_kt - 1) * 64 * D),
                  uni_ptr(vb + (int64_t)min(2, n_kt - 1) * 64 * D),
                  uni_ptr(ktb + min(1, n_kt - 1) * 64), koff, voff, toff, q0r, q1r, d0r, d1r, dq0,

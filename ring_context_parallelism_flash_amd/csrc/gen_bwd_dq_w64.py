@@ -30,27 +30,34 @@ Register plan (one wave per SIMD: 256 VGPRs + 256 AGPRs):
   a[64:127]   dQ^T of block 1
   a[128:191]  Q of blocks 0 and 1 (eight k-steps of 4 registers each)
   a[192:255]  dO of blocks 0 and 1
+  v[40:55]    minus delta of block 1, 16 copies (the first dP^T MFMA's
+              accumulator input, so dP - delta comes out of the chain)
   v56 row-tile read address, v57 K^T read address, v[58:61] temporaries
   v[64:79]    LDS operand ring, four 16-byte reads in flight
   v[80:95]    dS_x: bf16 dS^T of blocks 0 / 1 (even sub-tiles)
   v[96:111]   dS_y (odd sub-tiles)
   v[112:175]  set x: S^T and dP^T of blocks 0 and 1 (even sub-tiles)
   v[176:239]  set y (odd sub-tiles)
+  v[240:255]  minus delta of block 0, 16 copies
   s[80:81], s[82:83], s[84:85]: global addresses of the next K rows, V rows
   and K^T tiles
-The compiler keeps everything else in v[0:55] and the other SGPRs.
+The compiler keeps everything else in v[0:39] and the other SGPRs.
 
-Hazards the statement respects by construction: a transcendental result is
-read no earlier than the second instruction after it; MFMA results are read
-by vector instructions only a phase later, or by the out-of-line mask and
-after the statement, each behind s_nop 7 x 3; an MFMA accumulator is reused
-no sooner than three MFMAs later; an M0 write is followed by one wait state
-before the LDS-DMA load that reads it; LDS reads wait on counted lgkmcnt and
-return in order, with no other LGKM operation in flight.
+Hazards the statement respects by construction, and check_hazards verifies
+on the executed paths (several trip counts, each out-of-line mask) before
+the header is written: a transcendental result is read no earlier than the
+second instruction after it; MFMA results are read by vector instructions
+only a phase later, or by the out-of-line mask and after the statement, each
+behind s_nop 7 x 3 (at least 19 wait states); an M0 write is not directly
+followed by the LDS-DMA load that reads it; an MFMA operand read from LDS
+has returned when the MFMA issues (LDS reads return in order; one lgkmcnt
+wait per two MFMA pairs counts them, and no other LGKM operation is in
+flight). An MFMA accumulator is reused no sooner than three MFMAs later.
 
 Run: python gen_bwd_dq_w64.py  (writes the header next to this file)
 """
 import os
+import re
 
 D = 128
 KS = D // 16            # k-steps of the S / dP products
@@ -75,6 +82,7 @@ T0, T1, T2, T3 = 58, 59, 60, 61
 RING = 64
 DS_ = {0: (80, 88), 1: (96, 104)}                  # per parity: block 0, block 1
 SET_ = {0: (112, 128, 144, 160), 1: (176, 192, 208, 224)}   # S0, S1, dP0, dP1
+NDL_ = (240, 40)        # minus delta of block 0 / 1, 16 copies: the dP^T accumulators' start
 PAD = ["s_nop 7", "s_nop 7", "s_nop 7"]
 KG_S, VG_S, TG_S = 80, 82, 84
 
@@ -102,8 +110,8 @@ def kt_off(i):
 
 
 def a_mfmas(par):
-    """S^T / dP^T of both blocks into the set of parity `par`; C = 0 at the
-    first k-step."""
+    """S^T / dP^T of both blocks into the set of parity `par`; the first
+    k-step starts S^T from 0 and dP^T from minus delta."""
     S0, S1, P0, P1 = SET_[par]
 
     def f(i):
@@ -112,8 +120,12 @@ def a_mfmas(par):
             d0, d1, b0, b1 = P0, P1, DO_[0], DO_[1]
         else:
             d0, d1, b0, b1 = S0, S1, Q_[0], Q_[1]
-        c0 = "0" if s == 0 else vr(d0, 16)
-        c1 = "0" if s == 0 else vr(d1, 16)
+        if s > 0:
+            c0, c1 = vr(d0, 16), vr(d1, 16)
+        elif i & 1:     # dP^T - delta comes out of the chain
+            c0, c1 = vr(NDL_[0], 16), vr(NDL_[1], 16)
+        else:
+            c0 = c1 = "0"
         return (f"v_mfma_f32_32x32x16_bf16 {vr(d0, 16)}, {ring(i)}, {ar(b0 + 4 * s, 4)}, {c0}",
                 f"v_mfma_f32_32x32x16_bf16 {vr(d1, 16)}, {ring(i)}, {ar(b1 + 4 * s, 4)}, {c1}")
     return f
@@ -144,10 +156,8 @@ def ds_pair(i, par):
              f"v_fma_f32 v{T1}, v{S + e + 1}, %[c], %[nl2{b}]",
              f"v_exp_f32 v{T0}, v{T0}",
              f"v_exp_f32 v{T1}, v{T1}"]
-    second = [f"v_sub_f32 v{T2}, v{P + e}, %[dlt{b}]",
-              f"v_sub_f32 v{T3}, v{P + e + 1}, %[dlt{b}]",
-              f"v_mul_f32 v{T0}, v{T0}, v{T2}",
-              f"v_mul_f32 v{T1}, v{T1}, v{T3}",
+    second = [f"v_mul_f32 v{T0}, v{T0}, v{P + e}",
+              f"v_mul_f32 v{T1}, v{T1}, v{P + e + 1}",
               f"v_cvt_pk_bf16_f32 v{dst}, v{T0}, v{T1}"]
     return first, second
 
@@ -163,7 +173,11 @@ def phase(n, mfmas, addr, off, work=None, pre_in=False, nxt=None, extra=()):
         for i in range(PF):
             lines.append(f"ds_read_b128 {ring(i)}, v{addr} offset:{off(i)}")
     for i in range(n):
-        lines.append(f"s_waitcnt lgkmcnt({PF - 1 if nxt else min(PF - 1, n - 1 - i)})")
+        if i % 2 == 0:
+            # one wait per two pairs: reads 0 .. issued-1 are in flight or
+            # done, in order; pairs i and i+1 need reads i and i+1
+            issued = i + PF if nxt else min(n, i + PF)
+            lines.append(f"s_waitcnt lgkmcnt({issued - min(i + 2, n)})")
         first, second = work(i) if work else ([], [])
         ma, mb = mfmas(i)
         lines += [ma] + first + [mb]
@@ -177,7 +191,8 @@ def phase(n, mfmas, addr, off, work=None, pre_in=False, nxt=None, extra=()):
     return lines
 
 
-LOOP_CLOBBER = ([f'"v{r}"' for r in range(V_RADDR, 256)] +
+LOOP_CLOBBER = ([f'"v{r}"' for r in range(NDL_[1], NDL_[1] + 16)] +
+                [f'"v{r}"' for r in range(V_RADDR, 256)] +
                 ['"vcc"', '"scc"', '"m0"', '"exec"', '"memory"'])
 
 
@@ -243,6 +258,7 @@ def load_groups():
 def loop_asm():
     L = Loop()
     L.add([f"v_accvgpr_write_b32 a{r}, 0" for r in range(128)])
+    L.add([f"v_mov_b32 v{NDL_[b] + r}, %[ndl{b}]" for b in (0, 1) for r in range(16)])
     # prologue: S^T / dP^T of sub-tile 0 (row buffer 0, first half), whose
     # last pairs start the reads of sub-tile 1 (second half)
     L.add([f"v_mov_b32 v{V_RADDR}, %[rbase]"])
@@ -290,8 +306,107 @@ def loop_asm():
     return L.lines
 
 
+XDL_WAIT = 19    # wait states between an MFMA and a vector access of its result
+REG = re.compile(r"\b([va])(?:(\d+)\b|\[(\d+):(\d+)\])")
+
+
+def regs(text):
+    out = set()
+    for m in REG.finditer(text):
+        if m.group(2):
+            out.add(m.group(1) + m.group(2))
+        else:
+            out.update(f"{m.group(1)}{r}" for r in range(int(m.group(3)), int(m.group(4)) + 1))
+    return out
+
+
+def trace(lines, policy, limit=40000):
+    """The instructions one wave executes, branches decided by policy(label,
+    count of earlier decisions at that label) -> taken."""
+    where = {ln[:-1]: i for i, ln in enumerate(lines) if ln.endswith(":")}
+    seen = {}
+    out, i = [], 0
+    while i < len(lines) and len(out) < limit:
+        ln = lines[i]
+        op, _, rest = ln.partition(" ")
+        if ln.endswith(":"):
+            if ln == ".Ldone_%=:":
+                break
+            i += 1
+            continue
+        out.append(ln)
+        if op == "s_branch":
+            i = where[rest.strip()]
+            continue
+        if op.startswith("s_cbranch"):
+            lab = rest.strip()
+            k = seen.get(lab, 0)
+            seen[lab] = k + 1
+            if policy(lab, k):
+                i = where[lab]
+                continue
+        i += 1
+    assert len(out) < limit, "trace did not reach the end"
+    return out
+
+
+def check_trace(tr):
+    """Along one executed path: vector accesses of MFMA results at least
+    XDL_WAIT wait states after the MFMA; no read of a transcendental result
+    by the next instruction; no LDS-DMA load right after an M0 write; every
+    register an LDS read is still writing left alone until a wait covers it."""
+    last, trans, ws, pending, prev = {}, set(), 0, [], ""
+    for ln in tr:
+        op, _, rest = ln.partition(" ")
+        if op == "s_nop":
+            ws += int(rest) + 1
+            trans, prev = set(), ln
+            continue
+        ops = [o.strip() for o in rest.split(",")]
+        if op == "s_waitcnt" and "lgkmcnt" in rest:
+            k = int(re.search(r"lgkmcnt\((\d+)\)", rest).group(1))
+            pending = pending[len(pending) - k:] if len(pending) > k else pending
+        if op.startswith("global_load_lds"):
+            assert "m0" not in prev.split(" ", 1)[-1].split(",")[0], (prev, ln)
+        if op.startswith("v_mfma"):
+            for r in regs(",".join(ops[1:])):
+                assert all(r not in p for p in pending), ("LDS read not waited for", ln)
+            for r in regs(",".join(ops[1:3])):
+                assert ws - last.get(r, -99) >= XDL_WAIT, ln
+            for r in regs(ops[0]):
+                last[r] = ws
+        elif op.startswith("ds_"):
+            for r in regs(",".join(ops[1:])):
+                assert ws - last.get(r, -99) >= XDL_WAIT, ln
+                assert all(r not in p for p in pending), ("LDS result", ln)
+            pending.append(regs(ops[0]))
+        elif op.startswith("v_"):
+            for r in regs(rest):
+                assert ws - last.get(r, -99) >= XDL_WAIT, (ln, ws - last.get(r, -99))
+                assert all(r not in p for p in pending), ("LDS result", ln)
+            assert not (regs(",".join(ops[1:])) & trans), ln
+        trans = regs(ops[0]) if op == "v_exp_f32" else set()
+        prev = ln
+        ws += 1
+
+
+def check_hazards(lines):
+    """check_trace over the common path for several trip counts and over
+    paths through each out-of-line mask."""
+    for n_it in range(0, 4):
+        check_trace(trace(lines, lambda lab, k, n_it=n_it: lab == ".Llast_%=" and k >= n_it))
+    for fam in ("maskpro", "maske", "masko"):
+        for when in (0, 1):
+            def pol(lab, k, fam=fam, when=when):
+                if lab == ".Llast_%=":
+                    return k >= 2
+                return lab == f".L{fam}_%=" and k == when
+            check_trace(trace(lines, pol))
+
+
 def main():
     lines = loop_asm()
+    check_hazards(lines)
     outs = ([f'"={{{ar(DQ_[b] + 16 * T, 16)}}}"(dq{b}[{T}])' for b in (0, 1) for T in range(DT)] +
             ['[t] "=&s"(t)', '[sx] "=&s"(sx)', '[sy] "=&s"(sy)', '[sz] "=&s"(sz)',
              f'[kg] "+{{s[{KG_S}:{KG_S + 1}]}}"(kgv)', f'[vg] "+{{s[{VG_S}:{VG_S + 1}]}}"(vgv)',
@@ -300,7 +415,7 @@ def main():
     ins = (['[nkt] "s"(n_kt)', '[fmask] "s"(first_mask)', '[kd] "s"(kd)', '[vd] "s"(vd)',
             '[td] "s"(td)', '[x5k] "s"(x5k)', '[x5v] "s"(x5v)', '[x5t] "s"(x5t)', '[c] "s"(c)',
             '[rbase] "v"(rbase)', '[tbase] "v"(tbase)', '[nl20] "v"(nl20)', '[nl21] "v"(nl21)',
-            '[dlt0] "v"(dlt0)', '[dlt1] "v"(dlt1)', '[nalh0] "v"(nalh0)', '[nalh1] "v"(nalh1)'] +
+            '[ndl0] "v"(ndl0)', '[ndl1] "v"(ndl1)', '[nalh0] "v"(nalh0)', '[nalh1] "v"(nalh1)'] +
            [f'[ko{j}] "v"(koff[{j}])' for j in range(5)] +
            [f'[vo{j}] "v"(voff[{j}])' for j in range(5)] +
            [f'[to{j}] "v"(toff[{j}])' for j in range(5)] +
@@ -335,11 +450,11 @@ constexpr int kKtBufBytes = {TBUF};      // one K^T tile; two buffers
 // / x5t: whether the wave issues the fifth load of a K, V, K^T tile;
 // first_mask: first 32-key sub-tile needing the causal mask; nalh0 / nalh1:
 // keys visible to the lane's row of block 0 / 1, minus 8 for the upper half
-// of the wave; nl20 / nl21: minus the rows' lse in exp2 units; dlt0 / dlt1:
-// the rows' delta. Returns dQ^T of both blocks (unscaled).
+// of the wave; nl20 / nl21: minus the rows' lse in exp2 units; ndl0 / ndl1:
+// minus the rows' delta. Returns dQ^T of both blocks (unscaled).
 __device__ __forceinline__ void dq_loop(
     int n_kt, int first_mask, unsigned kd, unsigned vd, unsigned td, int k5, int v5, int t5,
-    float c, unsigned rbase, unsigned tbase, float nl20, float nl21, float dlt0, float dlt1,
+    float c, unsigned rbase, unsigned tbase, float nl20, float nl21, float ndl0, float ndl1,
     int nalh0, int nalh1, const void* kg, const void* vg, const void* tg,
     const unsigned (&koff)[5], const unsigned (&voff)[5], const unsigned (&toff)[5],
     const bf16x8 (&q0)[8], const bf16x8 (&q1)[8], const bf16x8 (&do0)[8],
