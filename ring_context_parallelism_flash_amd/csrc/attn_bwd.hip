@@ -784,27 +784,34 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_w32(const BwdArgs a) {
 
   // epilogue: add into the fp32 accumulators; lane holds key kw0+n,
   // d = 32T + 8(i/4) + 4hh + i%4
+  // (all 32 loads of the old values go out before the first store, which
+  // the compiler cannot move them past: dk and dv might alias)
   const int key = kw0 + n;
   if (key < a.Ck) {
     float* dkr = a.dk + b * a.dk_bs + g * a.dk_hs + (int64_t)key * D;
     float* dvr = a.dv + b * a.dk_bs + g * a.dk_hs + (int64_t)key * D;
+    float4 k4[DT * 4], v4[DT * 4];
+#pragma unroll
+    for (int j = 0; j < DT * 4; ++j) {
+      const int d0 = 32 * (j >> 2) + 8 * (j & 3) + 4 * hh;
+      k4[j] = *reinterpret_cast<const float4*>(dkr + d0);
+      v4[j] = *reinterpret_cast<const float4*>(dvr + d0);
+    }
 #pragma unroll
     for (int T = 0; T < DT; ++T)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * T + 8 * q4 + 4 * hh;
-        float4 k4 = *reinterpret_cast<float4*>(dkr + d0);
-        float4 v4 = *reinterpret_cast<float4*>(dvr + d0);
-        k4.x += a.scale * dKt[T][4 * q4 + 0];
-        k4.y += a.scale * dKt[T][4 * q4 + 1];
-        k4.z += a.scale * dKt[T][4 * q4 + 2];
-        k4.w += a.scale * dKt[T][4 * q4 + 3];
-        v4.x += dVt[T][4 * q4 + 0];
-        v4.y += dVt[T][4 * q4 + 1];
-        v4.z += dVt[T][4 * q4 + 2];
-        v4.w += dVt[T][4 * q4 + 3];
-        *reinterpret_cast<float4*>(dkr + d0) = k4;
-        *reinterpret_cast<float4*>(dvr + d0) = v4;
+        const int j = 4 * T + q4, d0 = 32 * T + 8 * q4 + 4 * hh;
+        k4[j].x += a.scale * dKt[T][4 * q4 + 0];
+        k4[j].y += a.scale * dKt[T][4 * q4 + 1];
+        k4[j].z += a.scale * dKt[T][4 * q4 + 2];
+        k4[j].w += a.scale * dKt[T][4 * q4 + 3];
+        v4[j].x += dVt[T][4 * q4 + 0];
+        v4[j].y += dVt[T][4 * q4 + 1];
+        v4[j].z += dVt[T][4 * q4 + 2];
+        v4[j].w += dVt[T][4 * q4 + 3];
+        *reinterpret_cast<float4*>(dkr + d0) = k4[j];
+        *reinterpret_cast<float4*>(dvr + d0) = v4[j];
       }
   }
 }
@@ -1143,18 +1150,30 @@ __global__ __launch_bounds__(64 * kDqW64Waves, 1) void attn_bwd_dq_w64(const Bwd
 
   // add into the fp32 accumulators; lane holds query n of each block,
   // d = 32T + 8(i/4) + 4hh + i%4
+  // All 32 loads of the old values (both blocks; rows past the block
+  // re-read the last row and are not stored) go out before the first add,
+  // so their latencies overlap.
+  float* dqb = a.dq + b * a.dq_bs + h * a.dq_hs;
+  float4 old[2][DT * 4];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const float* row = dqb + (int64_t)min(qw0 + 32 * blk + n, qlast) * D;
+#pragma unroll
+    for (int j = 0; j < DT * 4; ++j)
+      old[blk][j] = *reinterpret_cast<const float4*>(row + 32 * (j >> 2) + 8 * (j & 3) + 4 * hh);
+  }
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     const int qi = qw0 + 32 * blk + n;
     if (qi >= a.Cq) continue;
     floatx16(&dQt)[DT] = blk ? dq1 : dq0;
-    float* dqr = a.dq + b * a.dq_bs + h * a.dq_hs + (int64_t)qi * D;
+    float* dqr = dqb + (int64_t)qi * D;
 #pragma unroll
     for (int T = 0; T < DT; ++T)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = 32 * T + 8 * q4 + 4 * hh;
-        float4 x = *reinterpret_cast<float4*>(dqr + d0);
+        float4 x = old[blk][4 * T + q4];
         x.x += a.scale * dQt[T][4 * q4 + 0];
         x.y += a.scale * dQt[T][4 * q4 + 1];
         x.z += a.scale * dQt[T][4 * q4 + 2];

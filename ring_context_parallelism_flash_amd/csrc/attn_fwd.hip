@@ -222,40 +222,57 @@ __device__ __forceinline__ void epilogue_w64(const AttnArgs& a, const WorkItem& 
       }
     }
   }
+  // Merge factors of both blocks first, so their dependent chains overlap.
+  // The row sum's two halves (lanes n and n + 32) meet through a lane swap;
+  // the logarithms and exponentials are the hardware base-2 ones (about one
+  // ulp; l >= 1 whenever the row saw a key, since the element that set the
+  // reference contributed 1).
+  constexpr float kLn2 = 0.693147180559945309f, kLog2e = 1.442695040888963407f;
+  float lse_new[2], ca[2], cb[2];
+  bool write[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part[b]),
+                                                     __float_as_uint(l_part[b]), false, false);
+    const float l = l_part[b] + __uint_as_float(hh ? sw[0] : sw[1]);
+    const float m_use = (m_run[b] == -INFINITY) ? 0.f : m_run[b];
+    const float lse_blk =
+        (l > 0.f) ? fmaf(m_use, a.scale, __builtin_amdgcn_logf(l) * kLn2) : -INFINITY;
+    write[b] = 32 * b + n <= rmax && !(ACC && !FIN && lse_blk == -INFINITY);
+    const float mx = fmaxf(lse_old[b], lse_blk);
+    if (mx == -INFINITY) {
+      lse_new[b] = -INFINITY;
+      ca[b] = 0.f;
+      cb[b] = 0.f;
+    } else {
+      const float mn = fminf(lse_old[b], lse_blk);
+      lse_new[b] = fmaf(__builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f((mn - mx) * kLog2e)),
+                        kLn2, mx);
+      ca[b] = (lse_old[b] == -INFINITY) ? 0.f
+                                        : __builtin_amdgcn_exp2f((lse_old[b] - lse_new[b]) * kLog2e);
+      cb[b] = (lse_blk == -INFINITY)
+                  ? 0.f
+                  : __builtin_amdgcn_exp2f((lse_blk - lse_new[b]) * kLog2e) * __builtin_amdgcn_rcpf(l);
+    }
+  }
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     floatx16(&O)[4] = b ? O1 : O0;
-    const float l = l_part[b] + __shfl_xor(l_part[b], 32);
-    const float m_use = (m_run[b] == -INFINITY) ? 0.f : m_run[b];
-    const float lse_blk = (l > 0.f) ? fmaf(m_use, a.scale, logf(l)) : -INFINITY;
-    const bool write = 32 * b + n <= rmax && !(ACC && !FIN && lse_blk == -INFINITY);
-    const float mx = fmaxf(lse_old[b], lse_blk);
-    float lse_new, ca, cb;
-    if (mx == -INFINITY) {
-      lse_new = -INFINITY;
-      ca = 0.f;
-      cb = 0.f;
-    } else {
-      const float mn = fminf(lse_old[b], lse_blk);
-      lse_new = mx + log1pf(expf(mn - mx));
-      ca = (lse_old[b] == -INFINITY) ? 0.f : expf(lse_old[b] - lse_new);
-      cb = (lse_blk == -INFINITY) ? 0.f : expf(lse_blk - lse_new) / l;
-    }
     // MFMA layout: lane (n, hh) holds d = 32T + 8g + 4hh + (0..3) of row n
 #pragma unroll
     for (int T = 0; T < 4; ++T)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         float4 r;
-        r.x = O[T][4 * g4 + 0] * cb;
-        r.y = O[T][4 * g4 + 1] * cb;
-        r.z = O[T][4 * g4 + 2] * cb;
-        r.w = O[T][4 * g4 + 3] * cb;
+        r.x = O[T][4 * g4 + 0] * cb[b];
+        r.y = O[T][4 * g4 + 1] * cb[b];
+        r.z = O[T][4 * g4 + 2] * cb[b];
+        r.w = O[T][4 * g4 + 3] * cb[b];
         *reinterpret_cast<float4*>(stage + n * kStageRow + (32 * T + 8 * g4 + 4 * hh) * 4) = r;
       }
     if (hh == 0) {
-      *reinterpret_cast<float2*>(stage + n * kStageRow + 4 * D) = make_float2(ca, write ? 1.f : 0.f);
-      if (write) (FIN ? fl : rl)[32 * b + n] = lse_new;
+      *reinterpret_cast<float2*>(stage + n * kStageRow + 4 * D) = make_float2(ca[b], write[b] ? 1.f : 0.f);
+      if (write[b]) (FIN ? fl : rl)[32 * b + n] = lse_new[b];
     }
 #pragma unroll
     for (int i0 = 0; i0 < 16; i0 += 8) {

@@ -9,7 +9,8 @@ tile). With p = exp2(S c - lse2) and dS = p (dP - delta):
               K or V row read from LDS feeds the MFMA of both blocks) with
               the dS arithmetic of sub-tile j of both blocks between them;
   phase B(j): dQ^T += K^T dS^T of sub-tile j (each K^T read feeds both
-              blocks).
+              blocks), with p of block 0 of sub-tile j+1 between them
+              (written over its S), so both phases carry vector work.
 The last pairs of each phase issue the first operand reads of the next one.
 The backward's probabilities use the saved lse ("Sequence Parallelism in
 Large Language Models ...", section "The Activation Memory Wall":
@@ -144,14 +145,31 @@ def b_mfmas(par):
     return f
 
 
+def p_early(k, par):
+    """p = exp2(S c - lse2) of block 0, elements 2k, 2k+1 of the set of
+    parity `par`, written over S: the work of phase B pair k of the sub-tile
+    before, whose MFMAs carry no vector work of their own."""
+    S0 = SET_[par][0]
+    e = 2 * k
+    return [f"v_fma_f32 v{T0}, v{S0 + e}, %[c], %[nl20]",
+            f"v_fma_f32 v{T1}, v{S0 + e + 1}, %[c], %[nl20]",
+            f"v_exp_f32 v{S0 + e}, v{T0}",
+            f"v_exp_f32 v{S0 + e + 1}, v{T1}"]
+
+
 def ds_pair(i, par):
     """dS of elements 2k, 2k+1 (k = i % 8) of block b = i // 8 from the set
-    of parity `par`, in two parts (one after each MFMA of a pair)."""
+    of parity `par`, in two parts (one after each MFMA of a pair); block 0
+    finds p already in place of S (p_early)."""
     b, k = i // 8, i % 8
     S0, S1, P0, P1 = SET_[par]
     S, P = (S0, P0) if b == 0 else (S1, P1)
     e = 2 * k
     dst = DS_[par][b] + 4 * (e >> 3) + ((e & 7) >> 1)
+    if b == 0:
+        return [], [f"v_mul_f32 v{T0}, v{S + e}, v{P + e}",
+                    f"v_mul_f32 v{T1}, v{S + e + 1}, v{P + e + 1}",
+                    f"v_cvt_pk_bf16_f32 v{dst}, v{T0}, v{T1}"]
     first = [f"v_fma_f32 v{T0}, v{S + e}, %[c], %[nl2{b}]",
              f"v_fma_f32 v{T1}, v{S + e + 1}, %[c], %[nl2{b}]",
              f"v_exp_f32 v{T0}, v{T0}",
@@ -265,6 +283,8 @@ def loop_asm():
     L.add(phase(NA, a_mfmas(0), V_RADDR, row_off, nxt=(V_RADDR, lambda i: row_off(i) + HALF_R)))
     L.add(PAD + ["s_mov_b32 %[t], 0"])
     L.mask(0, ["s_mov_b32 %[sy], 0"], "pro")
+    for k in range(8):
+        L.add(p_early(k, 0))
     L.place("loop")
     # ---- even sub-tile j = 2t
     L.add(["s_waitcnt vmcnt(0)", "s_barrier",
@@ -276,7 +296,8 @@ def loop_asm():
                 extra=load_groups()))
     L.mask(1, ["s_lshl_b32 %[sy], %[t], 1", "s_add_u32 %[sy], %[sy], 1"], "e")
     L.add([f"v_add_u32 v{V_RADDR}, %[rn], %[rbase]"])
-    L.add(phase(NB, b_mfmas(0), V_TADDR, kt_off, pre_in=True, nxt=(V_RADDR, row_off)))
+    L.add(phase(NB, b_mfmas(0), V_TADDR, kt_off, pre_in=True, nxt=(V_RADDR, row_off),
+                work=lambda i: (p_early(i, 1), [])))
     # ---- odd sub-tile j = 2t+1
     L.add(["s_add_u32 %[sx], %[t], 1", "s_cmp_ge_u32 %[sx], %[nkt]",
            f"s_cbranch_scc1 {L.lab('last')}"])
@@ -285,7 +306,8 @@ def loop_asm():
     L.mask(0, ["s_lshl_b32 %[sy], %[t], 1", "s_add_u32 %[sy], %[sy], 2"], "o")
     L.add([f"v_add_u32 v{V_RADDR}, %[rn], %[rbase]"])
     L.add(phase(NB, b_mfmas(1), V_TADDR, lambda i: kt_off(i) + HALF_T, pre_in=True,
-                nxt=(V_RADDR, lambda i: row_off(i) + HALF_R)))
+                nxt=(V_RADDR, lambda i: row_off(i) + HALF_R),
+                work=lambda i: (p_early(i, 0), [])))
     # next tile: rotate the row buffers and flip the K^T buffer
     L.add(["s_add_u32 %[t], %[t], 1", "s_mov_b32 %[sx], %[rt]", "s_mov_b32 %[rt], %[rn]",
            "s_mov_b32 %[rn], %[rw]", "s_mov_b32 %[rw], %[sx]",
