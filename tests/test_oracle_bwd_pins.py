@@ -7,6 +7,8 @@
               are those of single-device attention), every layout
   invariant-- sum_j dv_j = sum_i dout_i and sum_j dk_j = 0 per KV head
   mutation -- planted mistakes in a copy of the oracle are caught
+  count    -- backward_flops is twice the multiply-adds of a brute-force loop
+              backward whose gradients equal the oracle's
 """
 import math
 import types
@@ -145,8 +147,61 @@ def test_dq_rows_equal_full_backward(causal):
         np.testing.assert_allclose(got[0, h], full[0, h, rows[h]], atol=1e-12)
 
 
-def test_backward_flops_counts_ten_d_per_pair():
-    assert oracle.backward_flops(1, 64, 128, 1000) == 10 * 128 * 64 * 1000
+def _loop_backward_counting(q, k, v, dout, causal):
+    """Brute-force backward of one head pair with plain loops over (i, j, d),
+    counting the multiply-adds of its five products: the score recomputed,
+    dP, and the dV, dK, dQ updates (the probabilities come from a first
+    loop pass; delta from the forward output, as the pages' backward keeps
+    it). Returns (dq, dk, dv, multiply-adds, allowed pairs)."""
+    S, D = q.shape
+    scale = 1.0 / math.sqrt(D)
+    macs = 0
+    ok = [[(not causal) or j <= i for j in range(S)] for i in range(S)]
+    s = np.full((S, S), -np.inf)
+    for i in range(S):
+        for j in range(S):
+            if ok[i][j]:
+                acc = 0.0
+                for d in range(D):
+                    acc += q[i, d] * k[j, d]
+                    macs += 1
+                s[i, j] = scale * acc
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    out = p @ v                      # the forward's output (not a backward product)
+    delta = (dout * out).sum(axis=1)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    pairs = 0
+    for i in range(S):
+        for j in range(S):
+            if not ok[i][j]:
+                continue
+            pairs += 1
+            dp = 0.0
+            for d in range(D):
+                dp += dout[i, d] * v[j, d]
+                macs += 1
+            ds = p[i, j] * (dp - delta[i])
+            for d in range(D):
+                dv[j, d] += p[i, j] * dout[i, d]
+                dk[j, d] += scale * ds * q[i, d]
+                dq[i, d] += scale * ds * k[j, d]
+                macs += 3
+    return dq, dk, dv, macs, pairs
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_flops_counts_ten_d_per_pair(causal):
+    """The useful-work count equals twice the multiply-adds a brute-force
+    loop backward performs (whose gradients equal the oracle's)."""
+    q, k, v, dout = (_rand((6, 4), 60 + i) for i in range(4))
+    dq, dk, dv, macs, pairs = _loop_backward_counting(q, k, v, dout, causal)
+    ref = oracle.attention_backward(q[None, None], k[None, None], v[None, None],
+                                    dout[None, None], causal=causal)
+    for a, b in zip((dq, dk, dv), ref):
+        np.testing.assert_allclose(a, b[0, 0], atol=1e-12)
+    assert pairs == (21 if causal else 36)
+    assert oracle.backward_flops(1, 1, 4, pairs) == 2 * macs
 
 
 # ---------------------------------------------------------------- mutation
