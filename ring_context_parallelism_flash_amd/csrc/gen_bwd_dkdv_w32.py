@@ -220,7 +220,9 @@ class Gen:
                 self.add(self.read(i, addr, off(i)))
         for i in range(N):
             # one wait serves a pair of MFMAs (an instruction slot is the
-            # scarce resource with one wave per SIMD)
+            # scarce resource with one wave per SIMD); the pair after this
+            # one is waited for right after this pair's second MFMA, where
+            # the wave could not issue vector work anyway
             if i % 2 == 0:
                 self.add(self.wait(self.ring_id[(i + 1) % PF]))
             else:
@@ -228,6 +230,8 @@ class Gen:
             if pre:
                 self.add(pre(i))
             self.add([mfma(i)])
+            if i % 2 == 1 and (i + 2 < N or nxt):
+                self.add(self.wait(self.ring_id[(i + 2) % PF]))
             if mid:
                 self.add(mid(i))
             if i + PF < N:

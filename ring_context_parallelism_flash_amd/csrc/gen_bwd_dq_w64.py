@@ -51,9 +51,9 @@ second instruction after it; MFMA results are read by vector instructions
 only a phase later, or by the out-of-line mask and after the statement, each
 behind s_nop 7 x 3 (at least 19 wait states); an M0 write is not directly
 followed by the LDS-DMA load that reads it; an MFMA operand read from LDS
-has returned when the MFMA issues (LDS reads return in order; one lgkmcnt
-wait per two MFMA pairs counts them, and no other LGKM operation is in
-flight). An MFMA accumulator is reused no sooner than three MFMAs later.
+has returned when the MFMA issues (LDS reads return in order; each pair's
+lgkmcnt wait sits right after the previous pair's first MFMA, and no other
+LGKM operation is in flight). An MFMA accumulator is reused no sooner than three MFMAs later.
 
 Run: python gen_bwd_dq_w64.py  (writes the header next to this file)
 """
@@ -191,14 +191,19 @@ def phase(n, mfmas, addr, off, work=None, pre_in=False, nxt=None, extra=()):
         for i in range(PF):
             lines.append(f"ds_read_b128 {ring(i)}, v{addr} offset:{off(i)}")
     for i in range(n):
-        if i % 2 == 0:
-            # one wait per two pairs: reads 0 .. issued-1 are in flight or
-            # done, in order; pairs i and i+1 need reads i and i+1
-            issued = i + PF if nxt else min(n, i + PF)
-            lines.append(f"s_waitcnt lgkmcnt({issued - min(i + 2, n)})")
+        # reads 0 .. issued-1 are in flight or done, in order. Pair 0 waits
+        # for its read before its first MFMA; every other pair's read is
+        # waited for right after the previous pair's first MFMA, in the
+        # slot where the wave could not issue vector work anyway
+        issued = i + PF if nxt else min(n, i + PF)
+        if i == 0:
+            lines.append(f"s_waitcnt lgkmcnt({issued - 1})")
         first, second = work(i) if work else ([], [])
         ma, mb = mfmas(i)
-        lines += [ma] + first + [mb]
+        lines += [ma]
+        if i + 1 < n:
+            lines.append(f"s_waitcnt lgkmcnt({issued - (i + 2)})")
+        lines += first + [mb]
         if i + PF < n:
             lines.append(f"ds_read_b128 {ring(i)}, v{addr} offset:{off(i + PF)}")
         elif nxt:

@@ -37,10 +37,12 @@ edge.
 
 With one wave per SIMD the wave's own instruction issue sets the pace (an
 MFMA pair of the common path takes about as long as the two MFMAs, one
-softmax pair and its operand read take to issue), so the common path keeps
-instructions out: one running row sum started by a move, one offset
-instruction per phase, one LDS wait per two MFMA pairs, a four-instruction
-sum test.
+softmax pair and its operand read take to issue; after an MFMA the wave
+issues no vector instruction for about 12 cycles, other instructions after
+about 8), so the common path keeps vector instructions out: one running row
+sum started by a move, one offset instruction per phase, a four-instruction
+sum test; each pair's LDS wait sits right after the previous pair's first
+MFMA, where it costs no vector issue slot.
 
 Register plan (one wave per SIMD: 256 VGPRs + 256 AGPRs):
   a[0:63]    O of block 0, four 32-wide d tiles of 16 registers (O^T layout)
@@ -180,14 +182,19 @@ def phase(mfmas, addr, off, work, pre_in=False, nxt=None, extra=()):
         for i in range(PF):
             lines.append(f"ds_read_b128 {ring(i)}, v{addr} offset:{off(i)}")
     for i in range(N):
-        if i % 2 == 0:
-            # one wait per two pairs: reads 0 .. issued-1 are in flight or
-            # done, in order; pairs i and i+1 need reads i and i+1
-            issued = i + PF if nxt else min(N, i + PF)
-            lines.append(f"s_waitcnt lgkmcnt({issued - (i + 2)})")
+        # reads 0 .. issued-1 are in flight or done, in order. Pair 0 waits
+        # for its read before its first MFMA; every other pair's read is
+        # waited for right after the previous pair's first MFMA, in the
+        # slot where the wave could not issue vector work anyway
+        issued = i + PF if nxt else min(N, i + PF)
+        if i == 0:
+            lines.append(f"s_waitcnt lgkmcnt({issued - 1})")
         first, second = softmax_pair(i, work[0], work[1]) if work else ([], [])
         ma, mb = mfmas(i)
-        lines += [ma] + first + [mb]
+        lines += [ma]
+        if i + 1 < N:
+            lines.append(f"s_waitcnt lgkmcnt({issued - (i + 2)})")
+        lines += first + [mb]
         if i + PF < N:
             lines.append(f"ds_read_b128 {ring(i)}, v{addr} offset:{off(i + PF)}")
         elif nxt:
