@@ -23,8 +23,10 @@ read during phase A(j), minus its delta (stored negated) during phase B(j-1):
 it is the starting accumulator of the dP chain, which so ends at dP - delta. The generator tracks
 every LDS read it emits and gives each use the exact lgkmcnt wait it needs
 (LDS reads return in order, and the statement issues no other LGKM
-operation), and it checks the wait states between each MFMA and the vector
-instructions that read its result.
+operation); one wait serves a pair of MFMAs and sits right after the
+previous pair's second MFMA, where the wave could not issue a vector
+instruction anyway. It checks the wait states between each MFMA and the
+vector instructions that read its result.
 
 LDS holds two row buffers [Q rows | dO rows | lse2 | delta] and two
 transposed buffers [Q^T | dO^T], filled by direct global->LDS loads, each
