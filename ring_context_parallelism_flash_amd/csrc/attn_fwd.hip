@@ -777,8 +777,8 @@ __global__ __launch_bounds__(kThreadsW64, 1) void attn_fwd_bf16_w64(const AttnAr
   const __bf16* kbp = reinterpret_cast<const __bf16*>(a.k) + it.b * a.k_bs + it.g * a.k_hs;
   const __bf16* vtb = reinterpret_cast<const __bf16*>(a.v) + it.b * a.v_bs + it.g * a.v_hs;
 
-  // Per-lane byte offsets of this wave's direct loads within a K tile and a
-  // V^T tile (instruction j fills 1 KiB chunk wv + NW*j of the tile).
+  // Per-lane byte offsets of this wave's prologue loads within a K tile and
+  // a V^T tile (instruction j fills 1 KiB chunk wv + NW*j of the tile).
   // The tail chunks of a tile (K: 17 KiB, V^T: 18 KiB) go to different waves
   // (K to wave 0, V^T to waves 2 and 3), so no wave issues more than nine
   // loads per tile: V^T chunks are dealt starting from wave 2.
@@ -871,12 +871,32 @@ __global__ __launch_bounds__(kThreadsW64, 1) void attn_fwd_bf16_w64(const AttnAr
       const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
       return (const void*)(size_t)(((uint64_t)hi << 32) | lo);
     };
-    w64::attn_loop(uni(n_kt), uni(first_mask), uni(lds_addr(Ks) + wv * 1024),
-                   uni(lds_addr(Vs) + vw * 1024), uni((wv + NW * (KI - 1)) < KINS),
-                   uni((vw + NW * (VI - 1)) < VINS), c,
+    // In the loop every wave loads five contiguous chunks of each tile, from
+    // chunk kc0 of a K tile (17 chunks) and vc0 of a V^T tile (18); the
+    // ranges overlap on a few chunks, which two waves load with the same
+    // data. The loop places the five loads from M0 = the wave's last chunk
+    // with instruction offsets -4 KiB .. 0, which move the global address
+    // too: the lane offsets carry the opposite amount.
+    static_assert(KI == 5 && VI == 5 && KINS == 17 && VINS == 18, "five chunk loads per tile");
+    const int kc0 = wv == 0 ? 0 : wv == 1 ? 4 : wv == 2 ? 8 : 12;
+    const int vc0 = wv == 0 ? 0 : wv == 1 ? 4 : wv == 2 ? 9 : 13;
+    uint32_t koffa[KI], voffa[VI];
+#pragma unroll
+    for (int j = 0; j < KI; ++j) {
+      const int P = (kc0 + j) * 64 + lane, cch = P % KCPR;
+      koffa[j] = (uint32_t)((P / KCPR) * D + (cch < CPR ? cch : 0) * 8) * 2u + (uint32_t)(4 - j) * 1024u;
+    }
+#pragma unroll
+    for (int j = 0; j < VI; ++j) {
+      const int P = (vc0 + j) * 64 + lane, cch = P % 9;
+      voffa[j] = ((uint32_t)(P / 9) * (uint32_t)a.v_ld + (uint32_t)(cch < 8 ? cch : 0) * 8u) * 2u +
+                 (uint32_t)(4 - j) * 1024u;
+    }
+    w64::attn_loop(uni(n_kt), uni(first_mask), uni(lds_addr(Ks) + (kc0 + 4) * 1024),
+                   uni(lds_addr(Vs) + (vc0 + 4) * 1024), c,
                    lds_addr(Ks) + kperm(n) * KROW + hh * 16, lds_addr(Vs) + n * VROW + hh * 16,
                    nal0 - 8 * hh, nal1 - 8 * hh, (unsigned)((lane ^ 32) * 4),
-                   uni_ptr(kbp + (int64_t)min(w64::kKBufs, n_kt - 1) * 64 * D), uni_ptr(vtb + 64), koff, voff,
+                   uni_ptr(kbp + (int64_t)min(w64::kKBufs, n_kt - 1) * 64 * D), uni_ptr(vtb + 64), koffa, voffa,
                    q0, q1, O0, O1, m0, l0, m1, l1);
   } else {
 #pragma unroll

@@ -15,11 +15,13 @@ next one, so no phase starts by waiting for LDS.
 Tiles reach LDS through direct global->LDS loads: K tiles rotate through
 three buffers, V^T tiles through two. One barrier per iteration publishes
 the loads of the previous iteration and frees the buffers it refills; the
-ten loads of a wave (K tile t+3, V^T tile t+1) are then spread over the
-first ten MFMA pairs of phase A, where their issue overlaps the matrix pipe
-instead of stalling all four waves at once behind the barrier. A K tile
-past the last one repeats the last one (into a buffer nobody reads), so no
-wave branches around its loads.
+ten loads of a wave (five contiguous 1 KiB chunks of K tile t+3, five of
+V^T tile t+1, each five placed from one M0 by the instructions' offsets; the
+waves' ranges overlap on a few chunks, loaded twice with the same data) are
+then spread over the first ten MFMA pairs of phase A, where their issue
+overlaps the matrix pipe instead of stalling all four waves at once behind
+the barrier. A K tile past the last one repeats the last one (into a buffer
+nobody reads), so no wave branches around its loads.
 
 Online softmax with a lazy reference (the pages' running max / sum /
 rescaled output, "Algorithmic Mechanics"): probabilities are taken against a
@@ -342,27 +344,22 @@ def loads(L, p):
     """Barrier, then the tile loads of iteration t (parity p) as groups for
     the MFMA pairs of phase A: K(min(t+3, n_kt-1)) into K buffer %[kw] and
     V(t+1) into V^T buffer 1-p; the global tile addresses advance after them.
-    A wave's fifth load of a tile runs under %[x5k] / %[x5v] as its exec mask
-    (all lanes or none)."""
-    L.add(["s_waitcnt vmcnt(0)", "s_barrier", "s_add_u32 %[sx], %[kdst], %[kw]"] + rotate("%[kw]"))
+    Every wave loads five contiguous 1 KiB chunks of each tile (the four
+    waves' chunk ranges overlap on a few chunks, loaded twice with the same
+    data), all placed from one M0 value by the instructions' own offsets."""
+    L.add(["s_waitcnt vmcnt(0)", "s_barrier", "s_add_u32 m0, %[kdst], %[kw]"] + rotate("%[kw]"))
     groups = []
-    for j in range(4):
-        groups.append([f"s_add_u32 m0, %[sx], {j * 4096}", "s_nop 0",
-                       f"global_load_lds_dwordx4 %[ko{j}], %[kg]"])
-    groups.append([f"s_add_u32 m0, %[sx], 16384", "s_mov_b64 exec, %[x5k]",
-                   "global_load_lds_dwordx4 %[ko4], %[kg]", "s_mov_b64 exec, -1"])
-    for j in range(4):
-        groups.append([f"s_add_u32 m0, %[vdst], {(1 - p) * VBUF + j * 4096}", "s_nop 0",
-                       f"global_load_lds_dwordx4 %[vo{j}], %[vg]"])
-    groups.append([f"s_add_u32 m0, %[vdst], {(1 - p) * VBUF + 16384}",
-                   "s_mov_b64 exec, %[x5v]",
-                   "global_load_lds_dwordx4 %[vo4], %[vg]",
-                   "s_mov_b64 exec, -1",
+    for j in range(5):
+        groups.append([f"global_load_lds_dwordx4 %[ko{j}], %[kg] offset:{(j - 4) * 1024}"])
+    groups[4].append(f"s_add_u32 m0, %[vdst], {(1 - p) * VBUF}")
+    for j in range(5):
+        groups.append([f"global_load_lds_dwordx4 %[vo{j}], %[vg] offset:{(j - 4) * 1024}"])
+    groups[9] += [
                    # the next K tile, t+4, if it exists; else the last one again
                    f"s_add_u32 %[sx], %[t], {KBUFS + 1}", "s_cmp_lt_u32 %[sx], %[nkt]",
                    f"s_cselect_b32 %[sx], {64 * D * 2}, 0",
                    f"s_add_u32 s{KG_S}, s{KG_S}, %[sx]", f"s_addc_u32 s{KG_S + 1}, s{KG_S + 1}, 0",
-                   f"s_add_u32 s{VG_S}, s{VG_S}, 128", f"s_addc_u32 s{VG_S + 1}, s{VG_S + 1}, 0"])
+                   f"s_add_u32 s{VG_S}, s{VG_S}, 128", f"s_addc_u32 s{VG_S + 1}, s{VG_S + 1}, 0"]
     return groups
 
 
@@ -558,7 +555,7 @@ constexpr int kKBufs = {KBUFS};
              f'[kg] "+{{s[{KG_S}:{KG_S + 1}]}}"(kgv)', f'[vg] "+{{s[{VG_S}:{VG_S + 1}]}}"(vgv)',
              '[kw] "+s"(kw)', '[kr] "+s"(kr)'])
     ins = (['[nkt] "s"(n_kt)', '[fmask] "s"(first_mask)', '[kdst] "s"(kdst)',
-            '[vdst] "s"(vdst)', '[x5k] "s"(x5k)', '[x5v] "s"(x5v)', '[c] "s"(c)',
+            '[vdst] "s"(vdst)', '[c] "s"(c)',
             '[krb] "v"(krb)', '[vrb] "v"(vrb)', '[nal0] "v"(nal0)', '[nal1] "v"(nal1)',
             '[perm] "v"(perm)'] +
            [f'[ko{j}] "v"(koff[{j}])' for j in range(5)] +
@@ -569,23 +566,23 @@ constexpr int kKBufs = {KBUFS};
     out.append(f"""// The key-tile loop of one wave: n_kt >= 1 tiles; K tiles 0 .. kKBufs-1
 // (those the block has) are in K buffers 0 .. kKBufs-1 and V^T tile 0 in
 // V^T buffer 0. krb / vrb: this lane's operand read address in K buffer 0 /
-// V^T buffer 0; kdst / vdst: this wave's first load destination in K / V^T
-// buffer 0; kg: global address of K tile min(kKBufs, n_kt - 1), vg: of V^T
-// tile 1 (both advanced by the loop); koff / voff: the lane's load offsets;
-// k5 / v5: whether the wave issues a fifth load per tile; first_mask: first
+// V^T buffer 0; kdst / vdst: the LDS address of the last of this wave's five
+// chunks in K / V^T buffer 0 (the M0 of its loads); kg: global address of K
+// tile min(kKBufs, n_kt - 1), vg: of V^T tile 1 (both advanced by the loop);
+// koff / voff: the lane's byte offsets in a tile of its five chunks, load j
+// plus (4 - j) KiB (the loads' instruction offsets take that off); first_mask: first
 // tile needing the causal mask; nal0 / nal1: keys visible to the lane's row
 // of block 0 / 1, minus 8 for the upper half of the wave; perm: byte address
 // of lane ^ 32. Returns O, m and l of both blocks (O^T layout, exponent
 // reference m, sum l).
 __device__ __forceinline__ void attn_loop(
-    int n_kt, int first_mask, unsigned kdst, unsigned vdst, int k5, int v5, float c,
+    int n_kt, int first_mask, unsigned kdst, unsigned vdst, float c,
     unsigned krb, unsigned vrb, int nal0, int nal1, unsigned perm, const void* kg,
     const void* vg, const unsigned (&koff)[5], const unsigned (&voff)[5],
     const bf16x8 (&q0)[8], const bf16x8 (&q1)[8], floatx16 (&o0)[4], floatx16 (&o1)[4],
     float& m0, float& l0, float& m1, float& l1) {{
   int t, t1, sx;
   long long stmp;
-  const long long x5k = k5 ? -1ll : 0ll, x5v = v5 ? -1ll : 0ll;
   unsigned long long kgv = (unsigned long long)(size_t)kg, vgv = (unsigned long long)(size_t)vg;
   unsigned kw = 0, kr = {(KBUFS - 1) * KBUF};  // K buffer offsets: next load, next prefetch
   asm volatile(
