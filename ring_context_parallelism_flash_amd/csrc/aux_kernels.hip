@@ -8,6 +8,33 @@
 namespace ra {
 namespace {
 
+// Streaming (non-temporal) 16-byte loads and stores for the copies and the
+// merge: no kernel here reads its data twice, and with the non-temporal hint
+// a 2 GiB permute moves 6.2-6.3 TB/s instead of 5.7-5.8. Narrower element
+// types load and store plainly.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <typename V>
+__device__ __forceinline__ V stream_load(const V* p) {
+  if constexpr (sizeof(V) == 16) {
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    V v;
+    __builtin_memcpy(&v, &x, 16);
+    return v;
+  } else {
+    return *p;
+  }
+}
+template <typename V>
+__device__ __forceinline__ void stream_store(V* p, const V& v) {
+  if constexpr (sizeof(V) == 16) {
+    u32x4 x;
+    __builtin_memcpy(&x, &v, 16);
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p));
+  } else {
+    *p = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // V^T blocks. One workgroup transposes a 64-key x D tile through LDS: it reads
 // 16-byte chunks along D (coalesced) and writes 16-byte chunks along keys.
@@ -79,14 +106,14 @@ __global__ __launch_bounds__(256) void lse_merge_vec4(float* __restrict__ out,
     const float la = lse[r], lb = lse_b[r];
     float ln, ca, cb;
     merge_weights(la, lb, ln, ca, cb);
-    const float4 a = reinterpret_cast<const float4*>(out)[i];
-    const float4 b = reinterpret_cast<const float4*>(out_b)[i];
+    const float4 a = stream_load(reinterpret_cast<const float4*>(out) + i);
+    const float4 b = stream_load(reinterpret_cast<const float4*>(out_b) + i);
     float4 o;
     o.x = fmaf(a.x, ca, b.x * cb);
     o.y = fmaf(a.y, ca, b.y * cb);
     o.z = fmaf(a.z, ca, b.z * cb);
     o.w = fmaf(a.w, ca, b.w * cb);
-    reinterpret_cast<float4*>(out)[i] = o;
+    stream_store(reinterpret_cast<float4*>(out) + i, o);
   }
 }
 
@@ -105,14 +132,14 @@ __global__ __launch_bounds__(256) void lse_merge_rows(float* __restrict__ out,
     const int64_t r = i / dq;
     float ln, ca, cb;
     merge_weights(lse[r], lse_b[r], ln, ca, cb);
-    const float4 a = reinterpret_cast<const float4*>(out)[i];
-    const float4 b = reinterpret_cast<const float4*>(out_b)[i];
+    const float4 a = stream_load(reinterpret_cast<const float4*>(out) + i);
+    const float4 b = stream_load(reinterpret_cast<const float4*>(out_b) + i);
     float4 o;
     o.x = fmaf(a.x, ca, b.x * cb);
     o.y = fmaf(a.y, ca, b.y * cb);
     o.z = fmaf(a.z, ca, b.z * cb);
     o.w = fmaf(a.w, ca, b.w * cb);
-    reinterpret_cast<float4*>(out)[i] = o;
+    stream_store(reinterpret_cast<float4*>(out) + i, o);
     if (i - r * dq == 0) lse[r] = ln;
   }
 }
@@ -161,17 +188,15 @@ __global__ __launch_bounds__(256) void zigzag_permute_kernel(const char* __restr
     const int64_t to = o * twoN + (inverse ? sc : pc);
     const V* s = reinterpret_cast<const V*>(src) + from * chunk_vecs;
     V* d = reinterpret_cast<V*>(dst) + to * chunk_vecs;
-    // four loads in flight per thread before the stores
+    // two streaming loads in flight per thread before the stores
     const int64_t T = (int64_t)gridDim.x * blockDim.x;
     int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; e + 3 * T < chunk_vecs; e += 4 * T) {
-      const V v0 = s[e], v1 = s[e + T], v2 = s[e + 2 * T], v3 = s[e + 3 * T];
-      d[e] = v0;
-      d[e + T] = v1;
-      d[e + 2 * T] = v2;
-      d[e + 3 * T] = v3;
+    for (; e + T < chunk_vecs; e += 2 * T) {
+      const V v0 = stream_load(s + e), v1 = stream_load(s + e + T);
+      stream_store(d + e, v0);
+      stream_store(d + e + T, v1);
     }
-    for (; e < chunk_vecs; e += T) d[e] = s[e];
+    for (; e < chunk_vecs; e += T) stream_store(d + e, stream_load(s + e));
   }
 }
 
@@ -264,9 +289,9 @@ __global__ __launch_bounds__(256) void striped_permute_kernel(const char* __rest
     const V* sp = reinterpret_cast<const V*>(src) + (inverse ? row : seq) * row_vecs;
     V* dp = reinterpret_cast<V*>(dst) + (inverse ? seq : row) * row_vecs;
     if (rpb > 1) {
-      dp[e0] = sp[e0];
+      stream_store(dp + e0, stream_load(sp + e0));
     } else {
-      for (int64_t e = e0; e < row_vecs; e += 256) dp[e] = sp[e];
+      for (int64_t e = e0; e < row_vecs; e += 256) stream_store(dp + e, stream_load(sp + e));
     }
   }
 }
@@ -355,9 +380,9 @@ __global__ __launch_bounds__(256) void ulysses_a2a_kernel(const char* __restrict
       const V* sp = reinterpret_cast<const V*>(src) + from * row_vecs;
       V* dp = reinterpret_cast<V*>(dst) + to * row_vecs;
       if (rpb > 1) {
-        dp[e0] = sp[e0];
+        stream_store(dp + e0, stream_load(sp + e0));
       } else {
-        for (int64_t e = e0; e < row_vecs; e += 256) dp[e] = sp[e];
+        for (int64_t e = e0; e < row_vecs; e += 256) stream_store(dp + e, stream_load(sp + e));
       }
     }
   }
@@ -415,7 +440,7 @@ hipError_t launch_zigzag_permute(const void* src, void* dst, int64_t outer, int6
   while (vb > 1 && (al % vb)) vb >>= 1;
   const int64_t chunk_vecs = chunk_bytes / vb;
   const int64_t nchunks = outer * twoN;
-  const int64_t gx = (chunk_vecs + 1023) / 1024;  // four vectors per thread
+  const int64_t gx = (chunk_vecs + 511) / 512;  // two vectors per thread
   const dim3 grid((unsigned)(gx < 1024 ? gx : 1024), (unsigned)(nchunks < 65535 ? nchunks : 65535));
   const char* sp = reinterpret_cast<const char*>(src);
   char* dp = reinterpret_cast<char*>(dst);
