@@ -60,7 +60,8 @@ typedef enum {
   RA_ERR_ALIGN = 5,       /* pointer misaligned (16 B for tensors, 4 B lse)    */
   RA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required          */
   RA_ERR_ARG = 7,         /* other invalid value (scale not finite / <= 0)    */
-  RA_ERR_HIP = 8          /* a HIP runtime call failed; see ra_last_error()   */
+  RA_ERR_HIP = 8,         /* a HIP runtime call failed; see ra_last_error()   */
+  RA_ERR_TIMEOUT = 9      /* ra_stream_wait: the stream did not drain in time */
 } ra_status;
 
 typedef enum { RA_BF16 = 0, RA_F32 = 1 } ra_dtype;
@@ -448,6 +449,31 @@ ra_status ra_kernel_timing_read(double* total_ms, int64_t* launches, double* use
 ra_status ra_device_info(int32_t* compute_units, int32_t* max_clock_khz);
 ra_status ra_mfma_probe_bf16(int32_t iters, int64_t* out, int64_t out_len, int32_t* waves,
                              void* stream);
+
+/* ------------------------------------------------------------------------
+ * ra_stream_wait -- wait for a stream with a time limit (host watchdog).
+ *
+ * [CP "The causal imbalance": the slowest rank sets the pace of every step;
+ *  SCP "When it breaks": a ring whose transfers are not hidden degrades into
+ *  a chain of N hops.] A ring step cannot finish before the block it waits
+ *  for has landed, so a stalled neighbour or copy stalls the step with no
+ *  error of its own. This call lets the host bound that wait instead of
+ *  blocking in hipStreamSynchronize.
+ *
+ * Records an event on `stream` (a hipStream_t as void*, NULL = the default
+ * stream) behind everything enqueued there so far and polls it from the
+ * calling thread, sleeping between polls (20 us, doubling up to 1 ms).
+ * Returns RA_OK once the stream has reached the event, RA_ERR_TIMEOUT if it
+ * has not after timeout_ms milliseconds (0: poll once; reaching the event
+ * takes the device some microseconds even on an idle stream, so a zero limit
+ * can report a timeout there), RA_ERR_ARG for a
+ * negative timeout_ms (checked before any HIP call), RA_ERR_HIP if the query
+ * reports an error (for example a fault of earlier work). On a timeout the
+ * enqueued work is neither cancelled nor disturbed: it runs on, and a later
+ * call may wait for it again. Host-only apart from the recorded event; no
+ * device memory is touched.
+ * ---------------------------------------------------------------------- */
+ra_status ra_stream_wait(void* stream, int32_t timeout_ms);
 
 #ifdef __cplusplus
 }

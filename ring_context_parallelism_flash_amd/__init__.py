@@ -22,7 +22,8 @@ __all__ = [
     "ra_ring_sim_bwd_workspace_bytes", "ra_ring_sim_bwd", "ring_attention_sim_backward",
     "ra_ring_sim_fwd", "ra_kernel_timing_enable", "ra_kernel_timing_read", "ring_attention_sim", "ra_ulysses_all_to_all",
     "ra_ulysses_sim_workspace_bytes", "ra_ulysses_sim_fwd", "ra_usp_sim_workspace_bytes",
-    "ra_usp_sim_fwd", "ra_device_info", "ra_mfma_probe_bf16", "EXPORTS",
+    "ra_usp_sim_fwd", "ra_device_info", "ra_mfma_probe_bf16", "ra_stream_wait", "RA_ERR_TIMEOUT",
+    "EXPORTS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +31,7 @@ library_path = os.path.join(_PKG, "libringattn.so")
 
 RA_BF16, RA_F32 = 0, 1
 RA_CONTIGUOUS, RA_ZIGZAG, RA_STRIPED = 0, 1, 2
+RA_ERR_TIMEOUT = 9
 _DTYPES = {torch.bfloat16: RA_BF16, torch.float32: RA_F32}
 _LAYOUTS = {"contiguous": RA_CONTIGUOUS, "zigzag": RA_ZIGZAG, "striped": RA_STRIPED}
 
@@ -41,7 +43,7 @@ EXPORTS = (
     "ra_ring_sim_bwd_workspace_bytes", "ra_ring_sim_bwd", "ra_ulysses_all_to_all",
     "ra_ulysses_sim_workspace_bytes", "ra_ulysses_sim_fwd", "ra_usp_sim_workspace_bytes",
     "ra_usp_sim_fwd", "ra_kernel_timing_enable", "ra_kernel_timing_read", "ra_device_info",
-    "ra_mfma_probe_bf16",
+    "ra_mfma_probe_bf16", "ra_stream_wait",
 )
 
 
@@ -124,6 +126,7 @@ def lib() -> ctypes.CDLL:
                                      c_void_p, c_size_t, c_void_p, c_void_p]),
         "ra_device_info": (c_int32, [P(c_int32), P(c_int32)]),
         "ra_mfma_probe_bf16": (c_int32, [c_int32, c_void_p, c_int64, P(c_int32), c_void_p]),
+        "ra_stream_wait": (c_int32, [c_void_p, c_int32]),
         "ra_kernel_timing_enable": (c_int32, [c_int32]),
         "ra_kernel_timing_read": (c_int32, [P(ctypes.c_double), P(c_int64),
                                             P(ctypes.c_double)]),
@@ -421,6 +424,13 @@ def ra_device_info():
     cus, khz = ctypes.c_int32(), ctypes.c_int32()
     _check(lib().ra_device_info(ctypes.byref(cus), ctypes.byref(khz)))
     return cus.value, khz.value
+
+
+def ra_stream_wait(stream=None, timeout_ms=60000):
+    """Wait until everything enqueued on `stream` so far has run, for at most
+    timeout_ms milliseconds; raises RAError with status RA_ERR_TIMEOUT when
+    the stream is still busy then (its work is left running)."""
+    _check(lib().ra_stream_wait(_stream(stream), int(timeout_ms)))
 
 
 def ra_mfma_probe_bf16(iters=100000, device=None):

@@ -14,7 +14,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <chrono>
 #include <mutex>
+#include <thread>
 #include <vector>
 
 #include "ra_internal.h"
@@ -236,6 +238,7 @@ const char* ra_status_str(ra_status s) {
     case RA_ERR_WORKSPACE: return "RA_ERR_WORKSPACE";
     case RA_ERR_ARG: return "RA_ERR_ARG";
     case RA_ERR_HIP: return "RA_ERR_HIP";
+    case RA_ERR_TIMEOUT: return "RA_ERR_TIMEOUT";
   }
   return "RA_ERR_UNKNOWN";
 }
@@ -1119,6 +1122,37 @@ ra_status ra_mfma_probe_bf16(int32_t iters, int64_t* out, int64_t out_len, int32
   if (e != hipSuccess) return hip_fail(e, "probe launch");
   *waves = (int32_t)n;
   return RA_OK;
+}
+
+ra_status ra_stream_wait(void* stream, int32_t timeout_ms) {
+  g_err[0] = 0;
+  if (timeout_ms < 0) return fail(RA_ERR_ARG, "timeout_ms must be >= 0 (got %d)", timeout_ms);
+  using clock = std::chrono::steady_clock;
+  hipEvent_t ev;
+  RA_HIP(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+  hipError_t e = hipEventRecord(ev, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    (void)hipEventDestroy(ev);
+    return hip_fail(e, "hipEventRecord");
+  }
+  const clock::time_point t0 = clock::now();
+  const clock::duration limit = std::chrono::milliseconds(timeout_ms);
+  clock::duration nap = std::chrono::microseconds(20);
+  for (;;) {
+    e = hipEventQuery(ev);
+    if (e != hipErrorNotReady) break;
+    const clock::duration waited = clock::now() - t0;
+    if (waited >= limit) break;
+    std::this_thread::sleep_for(std::min(nap, limit - waited));
+    if (nap < std::chrono::milliseconds(1)) nap *= 2;
+  }
+  // an event destroyed before the stream reaches it is released by the
+  // runtime once it completes
+  (void)hipEventDestroy(ev);
+  if (e == hipSuccess) return RA_OK;
+  if (e == hipErrorNotReady)
+    return fail(RA_ERR_TIMEOUT, "stream still busy after %d ms", timeout_ms);
+  return hip_fail(e, "hipEventQuery");
 }
 
 ra_status ra_kernel_timing_enable(int32_t enable) {

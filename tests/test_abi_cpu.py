@@ -39,9 +39,10 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    names = [ra.ra_status_str(s) for s in range(9)]
+    names = [ra.ra_status_str(s) for s in range(10)]
     assert names == ["RA_OK", "RA_ERR_NULL", "RA_ERR_SHAPE", "RA_ERR_DTYPE", "RA_ERR_UNSUPPORTED",
-                     "RA_ERR_ALIGN", "RA_ERR_WORKSPACE", "RA_ERR_ARG", "RA_ERR_HIP"]
+                     "RA_ERR_ALIGN", "RA_ERR_WORKSPACE", "RA_ERR_ARG", "RA_ERR_HIP",
+                     "RA_ERR_TIMEOUT"]
 
 
 def test_workspace_sizes():
@@ -260,3 +261,8 @@ def test_no_cpu_fallback_when_library_missing(monkeypatch, tmp_path):
     monkeypatch.setattr(ra, "library_path", str(tmp_path / "missing.so"))
     with pytest.raises(ra.RAError):
         ra.lib()
+
+
+def test_stream_wait_rejects_a_negative_timeout_before_any_hip_call():
+    assert ra.ra_status_str(ra.lib().ra_stream_wait(None, -1)) == "RA_ERR_ARG"
+    assert "timeout_ms" in ra.ra_last_error()
