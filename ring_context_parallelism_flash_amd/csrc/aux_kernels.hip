@@ -8,6 +8,10 @@
 namespace ra {
 namespace {
 
+// All-to-all tiles: at most this many bytes per workgroup, heads per table.
+constexpr int64_t kA2aTileBytes = 64 * 1024;
+constexpr int kA2aMaxHeads = 1024;
+
 // Streaming (non-temporal) 16-byte loads and stores for the copies and the
 // merge: no kernel here reads its data twice, and with the non-temporal hint
 // a 2 GiB permute moves 6.2-6.3 TB/s instead of 5.7-5.8. Narrower element
@@ -388,6 +392,59 @@ __global__ __launch_bounds__(256) void ulysses_a2a_kernel(const char* __restrict
   }
 }
 
+// Tiled form of the same all-to-all: one workgroup moves T consecutive
+// positions i0 .. i0+T-1 of one (rank p, batch b) for all H heads. On the
+// position-major side that tile is one contiguous run of T*H rows; on the
+// head-major side it is H runs of T consecutive rows, one per head. Reading
+// 256-byte rows at a 16 KiB (forward) or whole-plane (inverse) stride, as the
+// row-by-row gather does, keeps a DRAM page open for one row; the tile keeps
+// both sides in runs. A thread keeps one vector lane of the row (row_vecs
+// divides 256) and walks the tile's rows, head-major offsets coming from a
+// per-head table in LDS, so the loop has no integer division. T is a power
+// of two dividing S/P.
+template <typename V>
+__global__ __launch_bounds__(256) void ulysses_a2a_tiled(const char* __restrict__ src,
+                                                         char* __restrict__ dst, int B, int Sp,
+                                                         int Hp, int P, int row_vecs, int log2T,
+                                                         int inverse, int64_t hs_stride,
+                                                         int64_t hs_off) {
+  __shared__ int64_t head_off[kA2aMaxHeads];
+  const int H = Hp * P, T = 1 << log2T;
+  const int tiles = Sp >> log2T;
+  const int64_t pb = blockIdx.x / tiles;  // p * B + b
+  const int i0 = (int)(blockIdx.x - pb * tiles) << log2T;
+  const int b = (int)(pb % B), p = (int)(pb / B);
+  for (int h = threadIdx.x; h < H; h += 256) {
+    const int j = h / Hp, hh = h - j * Hp;
+    head_off[h] = ((int64_t)j * B * Hp + hh) * hs_stride;
+  }
+  __syncthreads();
+  const int64_t pm0 = (pb * Sp + i0) * H;  // position-major row of (i0, head 0)
+  const int64_t hm0 = (int64_t)b * Hp * hs_stride + hs_off + (int64_t)p * Sp + i0;
+  const int R = 256 / row_vecs;  // rows per pass of the workgroup
+  const int v = threadIdx.x % row_vecs;
+  const int rows = H << log2T;
+  const V* s = reinterpret_cast<const V*>(src);
+  V* d = reinterpret_cast<V*>(dst);
+  for (int n0 = threadIdx.x / row_vecs; n0 < rows; n0 += 4 * R) {
+    V x[4];
+    int64_t to[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int n = n0 + u * R;  // tile row: head n >> log2T, position i0 + (n & (T-1))
+      if (n < rows) {
+        const int h = n >> log2T, il = n & (T - 1);
+        const int64_t hm = hm0 + head_off[h] + il, pm = pm0 + (int64_t)il * H + h;
+        to[u] = (inverse ? pm : hm) * row_vecs + v;
+        x[u] = stream_load(s + (inverse ? hm : pm) * row_vecs + v);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (n0 + u * R < rows) stream_store(d + to[u], x[u]);
+  }
+}
+
 hipError_t launch_ulysses_a2a(const void* src, void* dst, int32_t B, int64_t S, int32_t H,
                               int64_t row_bytes, int32_t P, int inverse, hipStream_t s,
                               int64_t hs_stride, int64_t hs_off) {
@@ -397,6 +454,43 @@ hipError_t launch_ulysses_a2a(const void* src, void* dst, int32_t B, int64_t S, 
   int vb = 16;
   while (vb > 1 && (al % vb)) vb >>= 1;
   const int64_t row_vecs = row_bytes / vb;
+  const int64_t Sp = S / P;
+  // tiled form: the largest power-of-two T dividing S/P whose tile of T x H
+  // rows stays within kA2aTileBytes
+  if (256 % row_vecs == 0 && H <= kA2aMaxHeads) {
+    int log2T = 0;
+    while (Sp % (2LL << log2T) == 0 && (2LL << log2T) * H * row_bytes <= kA2aTileBytes) ++log2T;
+    const int64_t blocks = (int64_t)P * B * (Sp >> log2T);
+    if (blocks < (1LL << 31)) {
+      const char* sp = reinterpret_cast<const char*>(src);
+      char* dp = reinterpret_cast<char*>(dst);
+      const int Hp = H / P, Spi = (int)Sp, rv = (int)row_vecs;
+      const dim3 grid((unsigned)blocks);
+      switch (vb) {
+        case 16:
+          hipLaunchKernelGGL(ulysses_a2a_tiled<uint4>, grid, dim3(256), 0, s, sp, dp, B, Spi, Hp,
+                             P, rv, log2T, inverse, hs_stride, hs_off);
+          break;
+        case 8:
+          hipLaunchKernelGGL(ulysses_a2a_tiled<uint2>, grid, dim3(256), 0, s, sp, dp, B, Spi, Hp,
+                             P, rv, log2T, inverse, hs_stride, hs_off);
+          break;
+        case 4:
+          hipLaunchKernelGGL(ulysses_a2a_tiled<uint32_t>, grid, dim3(256), 0, s, sp, dp, B, Spi,
+                             Hp, P, rv, log2T, inverse, hs_stride, hs_off);
+          break;
+        case 2:
+          hipLaunchKernelGGL(ulysses_a2a_tiled<uint16_t>, grid, dim3(256), 0, s, sp, dp, B, Spi,
+                             Hp, P, rv, log2T, inverse, hs_stride, hs_off);
+          break;
+        default:
+          hipLaunchKernelGGL(ulysses_a2a_tiled<uint8_t>, grid, dim3(256), 0, s, sp, dp, B, Spi,
+                             Hp, P, rv, log2T, inverse, hs_stride, hs_off);
+          break;
+      }
+      return hipGetLastError();
+    }
+  }
   const int rpb = row_vecs <= 256 ? (int)(256 / row_vecs) : 1;
   const int64_t planes = inverse ? (int64_t)P * B : (int64_t)P * B * (H / P);
   const int64_t plane_rows = inverse ? (S / P) * H : S;
