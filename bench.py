@@ -223,8 +223,9 @@ def copy_overlap(kernel_trace_csv: str) -> dict:
 
 
 def aux_bandwidth(w, q, dev):
-    """HBM rates of the layout permute (one q-sized permute, read + write) and
-    of the lse merge (one rank's fp32 running state), timed with events."""
+    """HBM rates of the layout permute (one q-sized permute, read + write), of
+    the lse merge (one rank's fp32 running state) and of the Ulysses
+    all-to-all (q-sized, both directions), timed with events."""
     import torch
     import ring_context_parallelism_flash_amd as ra
     permute = ra.ra_striped_permute if w.layout == "striped" else ra.ra_zigzag_permute
@@ -249,10 +250,32 @@ def aux_bandwidth(w, q, dev):
     e1.record()
     torch.cuda.synchronize()
     merge_gbs = (3 * rows * w.D + 3 * rows) * 4 * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
-    return {f"{'striped' if w.layout == 'striped' else 'zigzag'}_permute_GBs": round(perm_gbs, 1),
-            "lse_merge_GBs": round(merge_gbs, 1), "hbm_peak_GBs": PEAK_HBM_GBS,
-            "permute_bytes": 2 * q.numel() * q.element_size(),
-            "lse_merge_bytes": (3 * rows * w.D + 3 * rows) * 4}
+    del mo, ml, mob, mlb
+    res = {f"{'striped' if w.layout == 'striped' else 'zigzag'}_permute_GBs": round(perm_gbs, 1),
+           "lse_merge_GBs": round(merge_gbs, 1), "hbm_peak_GBs": PEAK_HBM_GBS,
+           "permute_bytes": 2 * q.numel() * q.element_size(),
+           "lse_merge_bytes": (3 * rows * w.D + 3 * rows) * 4}
+    # Ulysses all-to-all of q's bytes taken as the N ranks' sequence slices
+    # [N, B, S/N, Hq, D], forward and back (the Ulysses step's q and out moves)
+    P = w.N
+    if w.Hq % P == 0 and w.S % P == 0:
+        src = q.view(P, w.B, w.S // P, w.Hq, w.D)
+        mid = torch.empty((P, w.B, w.Hq // P, w.S, w.D), dtype=q.dtype, device=dev)
+        back = torch.empty_like(src)
+        for inverse, a, b in ((False, src, mid), (True, mid, back)):
+            ra.ra_ulysses_all_to_all(a, b, P, inverse=inverse)
+            e0.record()
+            for _ in range(5):
+                ra.ra_ulysses_all_to_all(a, b, P, inverse=inverse)
+            e1.record()
+            torch.cuda.synchronize()
+            gbs = 2 * q.numel() * q.element_size() * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
+            res["ulysses_all_to_all_inverse_GBs" if inverse else "ulysses_all_to_all_GBs"] = \
+                round(gbs, 1)
+        if not torch.equal(back, src):
+            raise RuntimeError("all-to-all forward and back did not restore q")
+        del mid, back
+    return res
 
 
 def bench_backward(args, w, q, k, v, runner, out, lse) -> int:
@@ -565,7 +588,8 @@ def main(argv=None) -> int:
                    help="finish with one plain device copy of this many MiB (a known-size "
                         "reference for hardware byte counters)")
     p.add_argument("--aux-only", action="store_true",
-                   help="only the permute and lse-merge kernels (for hardware-counter runs)")
+                   help="only the permute, lse-merge and all-to-all kernels (for "
+                        "hardware-counter runs)")
     p.add_argument("--trace-overlap", metavar="KERNEL_TRACE_CSV", default=None,
                    help="print the block copies' overlap with attention kernels in a "
                         "rocprofv3 kernel trace and exit (no GPU use)")
