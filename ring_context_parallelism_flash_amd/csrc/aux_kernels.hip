@@ -461,7 +461,7 @@ hipError_t launch_ulysses_a2a(const void* src, void* dst, int32_t B, int64_t S, 
     int log2T = 0;
     while (Sp % (2LL << log2T) == 0 && (2LL << log2T) * H * row_bytes <= kA2aTileBytes) ++log2T;
     const int64_t blocks = (int64_t)P * B * (Sp >> log2T);
-    if (blocks < (1LL << 31)) {
+    if (blocks < (1LL << 24)) {  // a grid's x extent stays below 2^32 work-items
       const char* sp = reinterpret_cast<const char*>(src);
       char* dp = reinterpret_cast<char*>(dst);
       const int Hp = H / P, Spi = (int)Sp, rv = (int)row_vecs;
