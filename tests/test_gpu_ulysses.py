@@ -49,6 +49,11 @@ A2A_CASES = [
     (4, 1, 96, 8, (3,), torch.bfloat16),         # 6-byte rows: 2-byte accesses
     (2, 1, 16, 2, (2048,), torch.float32),       # 8 KiB rows: strided copy loop
     (1, 2, 40, 3, (16,), torch.bfloat16),        # P = 1
+    # the tiled form takes T positions x all heads per workgroup, T the largest
+    # power of two dividing S/P whose tile fits 64 KiB:
+    (3, 1, 999, 6, (128,), torch.bfloat16),      # S/P = 333 is odd: T = 1
+    (2, 1, 64, 512, (128,), torch.bfloat16),     # one position of 512 heads is 128 KiB: T = 1
+    (8, 1, 64, 1032, (64,), torch.bfloat16),     # more than 1024 heads: the row gather
 ]
 
 
