@@ -206,3 +206,36 @@ def test_usp_gqa_128k_sampled():
     got_out = np.stack([o[idx[h], h].double().numpy() for h in range(w.Hq)])
     got_lse = np.stack([l_[h, idx[h]].double().numpy() for h in range(w.Hq)])
     compare(got_out, got_lse, ref_out, ref_lse, TOL_BF16, "usp 128k gqa")
+
+
+def test_all_to_all_128k_q_sampled_bitexact():
+    """The q all-to-all of the 128k GQA workload in the launch configuration
+    bench.py times (P = 8, 64 heads of 256-byte rows, 2 GiB; the tiled form
+    with 4 positions x 64 heads per workgroup). The forward result is
+    compared bit for bit with the oracle's on 4096 seeded destination rows
+    plus the first and last row of every (rank, head) plane; the inverse
+    restores every byte."""
+    P, B, S, H, D = 8, 1, 131072, 64, 128
+    Sp, Hp = S // P, H // P
+    x = workloads.make_random((P, B, Sp, H, D), 990, torch.bfloat16)
+    xd = x.to(DEV)
+    y = torch.empty((P, B, Hp, S, D), dtype=torch.bfloat16, device=DEV)
+    ra.ra_ulysses_all_to_all(xd, y, P)
+    back = torch.empty_like(xd)
+    ra.ra_ulysses_all_to_all(y, back, P, inverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(back, xd)
+    del back, xd
+    ref = oracle.ulysses_all_to_all(x.view(torch.int16).numpy(), P)    # [P, B, S, H/P, D]
+    rng = np.random.default_rng(990)
+    j = rng.integers(0, P, 4096)
+    hh = rng.integers(0, Hp, 4096)
+    s = rng.integers(0, S, 4096)
+    jj, hb = np.meshgrid(np.arange(P), np.arange(Hp), indexing="ij")
+    j = np.concatenate([j, jj.ravel(), jj.ravel()])
+    hh = np.concatenate([hh, hb.ravel(), hb.ravel()])
+    s = np.concatenate([s, np.zeros(P * Hp, np.int64), np.full(P * Hp, S - 1)])
+    got = y.view(torch.int16)[torch.from_numpy(j), 0, torch.from_numpy(hh),
+                              torch.from_numpy(s)].cpu().numpy()
+    print(f"  128k q all-to-all: {len(j)} rows compared", flush=True)
+    np.testing.assert_array_equal(got, ref[j, 0, s, hh])
