@@ -116,6 +116,64 @@ def test_lse_merge_vs_oracle(rows, D):
     assert torch.all(l_.cpu()[both] == -math.inf) and torch.all(o.cpu()[both] == 0)
 
 
+def test_zigzag_permute_128k_q_sampled_bitexact():
+    """The 2 GiB q permute of the 128k GQA workload in the launch configuration
+    bench.py times (N = 8, 16 chunks of 8192 rows of 256 bytes per head
+    plane): 4096 seeded destination rows plus every chunk's first and last row
+    of every head, bit for bit against the oracle's zigzag order; the inverse
+    restores every byte."""
+    w = workloads.HEADLINE
+    B, H, S, D, N = w.B, w.Hq, w.S, w.D, w.N
+    src = workloads.make_random((B, H, S, D), 991, torch.bfloat16)
+    s_dev = src.to(DEV)
+    dst = torch.empty_like(s_dev)
+    ra.ra_zigzag_permute(s_dev, dst, N)
+    back = torch.empty_like(s_dev)
+    ra.ra_zigzag_permute(dst, back, N, inverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(back, s_dev)
+    del back, s_dev
+    order = oracle.zigzag_order(S, N)         # destination row t holds sequence row order[t]
+    rng = np.random.default_rng(991)
+    h = rng.integers(0, H, 4096)
+    t = rng.integers(0, S, 4096)
+    c = S // (2 * N)
+    ends = np.concatenate([np.arange(2 * N) * c, np.arange(2 * N) * c + c - 1])
+    hh, ee = np.meshgrid(np.arange(H), ends, indexing="ij")
+    h = np.concatenate([h, hh.ravel()])
+    t = np.concatenate([t, ee.ravel()])
+    got = dst.view(torch.int16)[0, torch.from_numpy(h), torch.from_numpy(t)].cpu().numpy()
+    want = src.view(torch.int16).numpy()[0, h, order[t]]
+    print(f"  128k q zigzag permute: {len(t)} rows compared", flush=True)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_lse_merge_rank_state_sampled():
+    """ra_lse_merge on one rank's running state of the 128k GQA workload (64
+    heads x 16384 rows of D = 128, the size bench.py times), with empty rows
+    on either side: 4096 seeded rows plus the first and last against the
+    oracle's merge of the same rows."""
+    rows, D = 64 * 16384, 128
+    g = torch.Generator().manual_seed(992)
+    out_a = torch.randn(rows, D, generator=g)
+    out_b = torch.randn(rows, D, generator=g)
+    lse_a = torch.randn(rows, generator=g) * 5
+    lse_b = torch.randn(rows, generator=g) * 5
+    lse_a[::7] = -math.inf
+    lse_b[::5] = -math.inf
+    out_a[::7] = 0
+    out_b[::5] = 0
+    o, l_ = out_a.to(DEV), lse_a.to(DEV)
+    ra.ra_lse_merge(o, l_, out_b.to(DEV), lse_b.to(DEV))
+    torch.cuda.synchronize()
+    pick = np.concatenate([np.random.default_rng(992).choice(rows, 4096, replace=False),
+                           [0, rows - 1]])
+    idx = torch.from_numpy(pick)
+    ref_out, ref_lse = oracle.merge(out_a[idx], lse_a[idx], out_b[idx], lse_b[idx])
+    compare(_np(o[idx.to(DEV)]), _np(l_[idx.to(DEV)]), ref_out, ref_lse,
+            dict(max_abs=1e-5, mean_abs=1e-6, lse=1e-5), f"merge {rows} rows, {len(pick)} compared")
+
+
 # ---------------------------------------------------------------- block
 def _block_case(dtype, D, Cq, Ck, q_pos, k_pos, causal, Hq=4, Hkv=2, kv_map=None, seed=0,
                 accumulate=False):
